@@ -1,0 +1,141 @@
+/*
+ * tri_attn.h — C ABI of the MI355X (gfx950) starting-node triangular
+ * self-attention forward.
+ *
+ * The operation is the one the POPCORNBENCH l2_p6 transcripts work on
+ * ("Kimi-K2.6 / l2_p6": its 18-step forward listing and its layer list;
+ * "FW-GLM-5-1 / l2_p6": the module's forward as restated while debugging).
+ * For a pair representation P of shape (B, N, N, D), a pair mask M of shape
+ * (B, N, N), h heads of size d = D / h:
+ *
+ *   x = LayerNorm_D(P)                          (biased variance, eps, affine)
+ *   g = sigmoid(x Wg^T + bg)
+ *   z[b,t,j,k] = x[b,j,k] . Wz[t]               (pair bias, shared by all rows i)
+ *   q, k, v = x Wq^T, x Wk^T, x Wv^T            (channel t*d+u is head t)
+ *   s[b,i,t,j,k] = q[b,i,j,t] . k[b,i,k,t] / sqrt(d) + z[b,t,j,k],
+ *                  replaced by mask_fill where M[b,j,k] == 0
+ *   a = softmax over k (dropout off: inference)
+ *   o[b,i,j,t*d+u] = sum_k a[b,i,t,j,k] v[b,i,k,t*d+u]
+ *   y = (g * o) Wo^T + bo                       -> output (B, N, N, D)
+ *
+ * All functions return 0 on success or a negative TRI_ATTN_ERR_* code; none
+ * prints, aborts or lets an exception out. Streams are hipStream_t values
+ * passed as void* (NULL = the default stream).
+ */
+#ifndef TRI_ATTN_H
+#define TRI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tri_attn *tri_attn_t; /* opaque handle */
+
+/* Element type of pair_repr, the weights and the output. Arithmetic is
+ * float32 throughout for TRI_ATTN_F32; for TRI_ATTN_BF16 the matrix-core
+ * operands are bf16 and every statistic and accumulator is float32. */
+enum { TRI_ATTN_F32 = 0, TRI_ATTN_BF16 = 1 };
+
+enum {
+  TRI_ATTN_OK = 0,
+  TRI_ATTN_ERR_INVALID_ARG = -1,  /* NULL pointer, negative size, D % h != 0, bad dtype */
+  TRI_ATTN_ERR_UNSUPPORTED = -2,  /* valid but not built: see tri_attn_create */
+  TRI_ATTN_ERR_WORKSPACE = -3,    /* workspace NULL or smaller than tri_attn_workspace_size */
+  TRI_ATTN_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
+  TRI_ATTN_ERR_OOM = -5           /* device allocation failed in tri_attn_create */
+};
+
+typedef struct {
+  int pair_dim;   /* D */
+  int num_heads;  /* h; head_dim d = D / h (integer division, as the module does) */
+  int dtype;      /* TRI_ATTN_F32 or TRI_ATTN_BF16 */
+  float ln_eps;   /* LayerNorm epsilon; nn.LayerNorm's default is 1e-5 */
+  /* Score written where M == 0. A finite value must be <= -1e4: masked keys
+   * then get weight exactly 0 on every query column with a valid key, and a
+   * column whose keys are all masked gets uniform weights over all N keys
+   * (the transcripts' kernels use -1e9). -INFINITY reproduces the module's
+   * masked_fill(-inf): such columns give NaN. */
+  float mask_fill;
+  /* Testing aid, 0 in normal use: a positive value is added to the per-column
+   * softmax shift, which pushes the kernel into its exact-maximum recovery
+   * path. Results are unchanged. */
+  float shift_slack;
+} tri_attn_config;
+
+/* Parameters in nn.LayerNorm / nn.Linear layouts (weight = (out, in)),
+ * row-major, element type = config dtype. Pointers may be device or host
+ * memory (they are copied with hipMemcpyDefault). */
+typedef struct {
+  const void *ln_weight, *ln_bias;        /* [D]                      */
+  const void *w_query, *w_key, *w_value;  /* [D, D], no bias          */
+  const void *w_gate, *b_gate;            /* [D, D], [D]              */
+  const void *w_bias_proj;                /* [h, D], no bias          */
+  const void *w_out, *b_out;              /* [D, D], [D]              */
+} tri_attn_weights;
+
+/* Build a handle: validates cfg, copies and packs the weights into
+ * handle-owned device memory on the current device (the caller may free its
+ * copies when this returns; the call synchronises `stream`).
+ * Supported: D in {64, 128} with d in {16, 32}; otherwise
+ * TRI_ATTN_ERR_UNSUPPORTED. On error *out is set to NULL. */
+int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void *stream, tri_attn_t *out);
+
+/* Bytes of device workspace tri_attn_forward needs for (B, N). B == 0 or
+ * N == 0 needs 0 bytes. */
+int tri_attn_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
+
+/* y = forward(pair_repr, pair_mask), enqueued on `stream`, asynchronous.
+ *   pair_repr [B, N, N, D] contiguous, config dtype, device memory
+ *   pair_mask [B, N, N] uint8, 0 = masked, device memory
+ *   out       [B, N, N, D] contiguous, config dtype, device memory
+ *   workspace device memory of at least tri_attn_workspace_size bytes, 256-byte aligned
+ * All pointers are borrowed until the stream work completes; out must not
+ * alias the inputs. B == 0 or N == 0 is a no-op. Kernel faults surface at
+ * the caller's next synchronisation. One handle is used by one stream at a
+ * time. Deterministic: no atomics, same bits on every call. */
+int tri_attn_forward(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* Free everything the handle owns (synchronises the device). NULL is a no-op. */
+int tri_attn_destroy(tri_attn_t h);
+
+/* Static message for an error code. */
+const char *tri_attn_strerror(int code);
+
+/* ---------------------------------------------------------------------------
+ * Stage access (tests and tools): the first of the two kernels alone, and
+ * where it leaves its results in the workspace.
+ * ------------------------------------------------------------------------ */
+
+/* Offsets are in bytes from the workspace start; Np = N rounded up to 64.
+ *   q, k, g : [B][N][D/16][Np][16] config dtype. Channel c of query column j
+ *             of row (b, i) is at [b][i][c/16][j][c%16]. q is pre-scaled by
+ *             log2(e)/sqrt(d); g is after the sigmoid. Columns j >= N hold
+ *             q = k = 0.
+ *   vt      : [B][N][h][d][Np] config dtype (value, transposed per head),
+ *             zero for j >= N.
+ *   zm      : [B][h][N][Np] float32: z[b,t,j,k] * log2(e) where M[b,j,k] != 0
+ *             and k < N, -inf elsewhere.
+ *   zmax    : [B][h][N][Np/64] float32: max of zm over each 64-key chunk.
+ *   kmax    : [B][N][h][Np/64] float32: max over each 64-column chunk of
+ *             |k|^2 of one head. */
+typedef struct {
+  size_t q, k, vt, g, zm, zmax, kmax;
+  size_t total;
+  int padded_n;
+} tri_attn_workspace_layout;
+
+int tri_attn_get_workspace_layout(tri_attn_t h, int B, int N, tri_attn_workspace_layout *out);
+
+/* Run only the LayerNorm + projection kernel (arguments as tri_attn_forward). */
+int tri_attn_project(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, int B, int N,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_ATTN_H */

@@ -1,0 +1,73 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run the
+library through its C ABI, and compare with the oracle."""
+import math
+import sys
+
+import numpy as np
+import torch
+
+from triangular_pair_attention_amd import binding as B
+from workloads import WEIGHT_NAMES
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}  # max abs error on y
+
+
+def torch_dtype(name):
+    return torch.float32 if name == "f32" else torch.bfloat16
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class Gpu:
+    """One library handle built from seeded inputs (numpy dict from workloads)."""
+
+    def __init__(self, inp, fill=-1e9, slack=0.0, device="cuda"):
+        self.inp = inp
+        self.dt = torch_dtype(inp["dtype"])
+        self.dev = torch.device(device)
+        self.w = {k: torch.from_numpy(inp[k]).to(self.dev).to(self.dt).contiguous() for k in WEIGHT_NAMES}
+        P = inp["pair_repr"]
+        self.B, self.N = int(P.shape[0]), int(P.shape[1])
+        self.D, self.h = int(P.shape[3]), int(inp["num_heads"])
+        self.P = torch.from_numpy(P).to(self.dev).to(self.dt).contiguous()
+        self.M = torch.from_numpy(inp["pair_mask"]).to(self.dev).contiguous()
+        code = B.TRI_ATTN_F32 if inp["dtype"] == "f32" else B.TRI_ATTN_BF16
+        self.cfg = B.tri_attn_config(self.D, self.h, code, 1e-5, fill if math.isfinite(fill) else -math.inf, slack)
+        self.handle = B.tri_attn_create(self.cfg, self.w, torch.cuda.current_stream())
+        self.ws_bytes = B.tri_attn_workspace_size(self.handle, self.B, self.N)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.dev)
+
+    def forward(self, out=None, stream=None):
+        if out is None:
+            out = torch.empty_like(self.P)
+        B.tri_attn_forward(self.handle, self.P, self.M, out, self.B, self.N, self.ws, self.ws_bytes,
+                           stream or torch.cuda.current_stream())
+        return out
+
+    def project(self):
+        B.tri_attn_project(self.handle, self.P, self.M, self.B, self.N, self.ws, self.ws_bytes,
+                           torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return B.tri_attn_get_workspace_layout(self.handle, self.B, self.N)
+
+    def region(self, off, count, dtype):
+        elem = torch.tensor([], dtype=dtype).element_size()
+        return self.ws[off:off + count * elem].view(dtype)
+
+    def close(self):
+        if self.handle:
+            B.tri_attn_destroy(self.handle)
+            self.handle = None
+
+
+def y_numpy(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def max_err(a, b):
+    d = np.abs(a - b)
+    i = np.unravel_index(np.argmax(d), d.shape)
+    return float(d[i]), i

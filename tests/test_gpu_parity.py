@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Tolerances (max abs error on y): 1e-4 for float32, 2e-2 for bf16 storage with
+float32 accumulation. bf16 inputs are the bf16-rounded values both sides see.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, Gpu, log, max_err, y_numpy
+from oracle import tri_attn_oracle as O
+from triangular_pair_attention_amd import binding as B
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+
+
+def run_case(inp, fill=-1e9, slack=0.0, rows=None):
+    g = Gpu(inp, fill=fill, slack=slack)
+    try:
+        y = y_numpy(g.forward())
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+    if rows is None:
+        ref = O.forward(inp, fill=fill)
+        return y, ref
+    ref = O.forward_rows(inp, rows, fill=fill)
+    return np.stack([y[b, i] for b, i in rows]), ref
+
+
+def check(y, ref, dtype, what):
+    finite = np.isfinite(ref)
+    assert (np.isfinite(y) == finite).all(), f"{what}: NaN pattern differs"
+    err, idx = max_err(np.where(finite, y, 0), np.where(finite, ref, 0))
+    log(f"{what}: max abs err {err:.3e} at {idx}, max|y| {np.abs(ref[finite]).max():.3f}")
+    assert err <= TOL[dtype], f"{what}: max abs err {err} > {TOL[dtype]} at {idx}"
+
+
+# ------------------------------------------------------------------ the five workloads
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_workload_full(k):
+    w = WORKLOADS[k]
+    log(f"workload {w.name}: full oracle comparison")
+    inp = make_inputs(w)
+    y, ref = run_case(inp)
+    check(y, ref, w.dtype, w.name)
+
+
+def test_workload5_sampled_rows():
+    """B=4, N=512, h=8: the full size in the benchmark's launch configuration;
+    compared on sampled rows (each needs its batch's pair bias)."""
+    w = WORKLOADS[5]
+    log(f"workload {w.name}: sampled rows")
+    inp = make_inputs(w)
+    M = inp["pair_mask"]
+    rng = np.random.default_rng(0)
+    rows = []
+    for b in range(w.B):
+        L = int(M[b].diagonal().sum())
+        cand = {0, L - 1, min(L, w.N - 1), w.N - 1, int(rng.integers(0, w.N))}
+        rows += [(b, i) for i in sorted(cand)]
+    y, ref = run_case(inp, rows=rows)
+    check(y, ref, w.dtype, w.name + " sampled")
+
+
+# ------------------------------------------------------------------ small and ragged shapes
+SHAPES = [
+    (1, 1, 64, 4), (2, 3, 64, 2), (2, 17, 64, 4), (1, 33, 128, 4), (1, 65, 128, 8),
+    (2, 100, 64, 2), (1, 130, 128, 4), (1, 70, 128, 8), (3, 64, 128, 8), (1, 129, 64, 4),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dN%dD%dh%d" % s)
+@pytest.mark.parametrize("mask", [("bernoulli", 0.7), ("pad", 0.6)], ids=["bern", "pad"])
+def test_small_ragged(shape, dtype, mask):
+    B_, N, D, h = shape
+    if mask[0] == "pad":
+        mask = ("pad", max(1, int(N * mask[1])))
+    w = Workload("small", B_, N, D, h, dtype, mask, seed=100 + N + D + h)
+    log(f"small {shape} {dtype} {mask}")
+    y, ref = run_case(make_inputs(w))
+    check(y, ref, dtype, f"{shape} {dtype} {mask}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_keys_masked(dtype):
+    """Mask all zero: every query column is fully masked -> mean of v over all N keys."""
+    w = Workload("allmasked", 2, 40, 128, 4, dtype, ("zeros",), seed=5)
+    log(f"all masked {dtype}")
+    y, ref = run_case(make_inputs(w))
+    check(y, ref, dtype, "all masked")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_minus_inf_fill_gives_nan_on_fully_masked_columns(dtype):
+    w = Workload("ninf", 1, 50, 64, 4, dtype, ("pad", 30), seed=6)
+    log(f"-inf fill {dtype}")
+    y, ref = run_case(make_inputs(w), fill=-math.inf)
+    assert np.isnan(ref[:, :, 30:]).all() and np.isnan(y[:, :, 30:]).all()
+    check(y, ref, dtype, "-inf fill")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dh", [16, 32])
+def test_recovery_path_with_loose_shift(dtype, dh):
+    """A huge shift_slack makes every softmax sum underflow, so each wave takes
+    the exact-maximum recovery path; the result must not change."""
+    w = Workload("slack", 1, 48, 128, 128 // dh, dtype, ("pad", 40), seed=7)
+    log(f"shift slack {dtype} d={dh}")
+    y, ref = run_case(make_inputs(w), slack=400.0)
+    check(y, ref, dtype, "recovery")
+
+
+def test_large_scores_stay_finite():
+    """Scaled-up query weights make the scores large (peaked softmax)."""
+    w = Workload("peaked", 1, 40, 64, 4, "f32", ("bernoulli", 0.8), seed=8)
+    inp = make_inputs(w)
+    inp["w_query"] *= 8
+    inp["w_bias_proj"] *= 8
+    log("peaked softmax")
+    y, ref = run_case(inp)
+    check(y, ref, "f32", "peaked")
+
+
+# ------------------------------------------------------------------ stage parity of kernel 1
+@pytest.mark.parametrize("dtype,shape", [("f32", (2, 40, 64, 4)), ("bf16", (1, 70, 128, 4)),
+                                         ("bf16", (1, 66, 128, 8)), ("f32", (1, 64, 128, 4))])
+def test_projection_stage(dtype, shape):
+    B_, N, D, h = shape
+    d = D // h
+    inp = make_inputs(Workload("stage", B_, N, D, h, dtype, ("bernoulli", 0.7), seed=9))
+    log(f"stage {dtype} {shape}")
+    g = Gpu(inp)
+    try:
+        lay = g.project()
+        Np = lay.padded_n
+        cap = {}
+        O.forward(inp, capture=cap)
+        dt = g.dt
+        f = lambda off, n, t=dt: g.region(off, n, t).float().cpu().numpy().astype(np.float64)  # noqa: E731
+        q = f(lay.q, B_ * N * D * Np).reshape(B_, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4)
+        k = f(lay.k, B_ * N * D * Np).reshape(B_, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4)
+        gg = f(lay.g, B_ * N * D * Np).reshape(B_, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4)
+        vt = f(lay.vt, B_ * N * D * Np).reshape(B_, N, h, d, Np)[..., :N]
+        zm = f(lay.zm, B_ * h * N * Np, torch.float32).reshape(B_, h, N, Np)
+        zmax = f(lay.zmax, B_ * h * N * (Np // 64), torch.float32).reshape(B_, h, N, Np // 64)
+        kmax = f(lay.kmax, B_ * N * h * (Np // 64), torch.float32).reshape(B_, N, h, Np // 64)
+    finally:
+        g.close()
+    q = q.reshape(B_, N, N, D)
+    k = k.reshape(B_, N, N, D)
+    gg = gg.reshape(B_, N, N, D)
+    rq = O.merge_heads(cap["q"]).reshape(B_, N, N, D) * LOG2E / math.sqrt(d)
+    rk = O.merge_heads(cap["k"]).reshape(B_, N, N, D)
+    rv = cap["v"].reshape(B_, N, h, N, d)  # (b, i, t, j, u)
+    rg = cap["g"].reshape(B_, N, N, D)
+    M = inp["pair_mask"]
+    rz = np.where(M[:, None] != 0, cap["z"] * LOG2E, -np.inf)  # (b, t, j, k)
+    atol, rtol = (1e-4, 1e-4) if dtype == "f32" else (2e-2, 1e-2)
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("g", gg, rg), ("v", vt, rv.transpose(0, 1, 2, 4, 3))):
+        np.testing.assert_allclose(got, ref, rtol=rtol, atol=atol, err_msg=name)
+    fin = np.isfinite(rz)
+    assert (np.isfinite(zm[..., :N]) == fin).all()
+    np.testing.assert_allclose(zm[..., :N][fin], rz[fin], rtol=rtol, atol=atol)
+    assert (zm[..., N:] == -np.inf).all()
+    # per-chunk maxima
+    pad = np.full((B_, h, N, Np), -np.inf)
+    pad[..., :N] = rz
+    np.testing.assert_allclose(zmax, pad.reshape(B_, h, N, Np // 64, 64).max(-1), rtol=rtol, atol=atol)
+    kn2 = np.zeros((B_, N, h, Np))
+    kn2[..., :N] = (cap["k"].reshape(B_, N, h, N, d) ** 2).sum(-1)
+    np.testing.assert_allclose(kmax, kn2.reshape(B_, N, h, Np // 64, 64).max(-1), rtol=2 * rtol, atol=atol)
+
+
+# ------------------------------------------------------------------ ABI behaviour on the GPU
+def test_deterministic_and_stream():
+    inp = make_inputs(WORKLOADS[3].replace(N=96))
+    log("determinism")
+    g = Gpu(inp)
+    try:
+        a = g.forward().clone()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            b = g.forward(stream=s)
+        s.synchronize()
+        assert torch.equal(a, b)
+    finally:
+        g.close()
+
+
+def test_empty_and_error_paths():
+    inp = make_inputs(Workload("err", 1, 20, 64, 4, "f32", ("bernoulli", 0.8), 3))
+    log("error paths")
+    g = Gpu(inp)
+    try:
+        assert B.tri_attn_workspace_size(g.handle, 0, 20) == 0
+        B.tri_attn_forward(g.handle, 0, 0, 0, 0, 20, 0, 0)  # B == 0: no-op
+        B.tri_attn_forward(g.handle, 0, 0, 0, 3, 0, 0, 0)  # N == 0: no-op
+        out = torch.empty_like(g.P)
+        with pytest.raises(B.TriAttnError) as e:
+            B.tri_attn_forward(g.handle, g.P, g.M, out, g.B, g.N, g.ws, g.ws_bytes - 1)
+        assert e.value.code == B.TRI_ATTN_ERR_WORKSPACE
+        with pytest.raises(B.TriAttnError) as e:
+            B.tri_attn_forward(g.handle, g.P, g.M, out, g.B, g.N, g.ws.data_ptr() + 8, g.ws_bytes)
+        assert e.value.code == B.TRI_ATTN_ERR_WORKSPACE
+        with pytest.raises(B.TriAttnError) as e:
+            B.tri_attn_forward(g.handle, g.P, g.M, 0, g.B, g.N, g.ws, g.ws_bytes)
+        assert e.value.code == B.TRI_ATTN_ERR_INVALID_ARG
+        with pytest.raises(B.TriAttnError) as e:
+            B.tri_attn_forward(g.handle, g.P, g.M, out, -1, g.N, g.ws, g.ws_bytes)
+        assert e.value.code == B.TRI_ATTN_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+
+
+def test_convenience_wrapper_matches_abi():
+    from triangular_pair_attention_amd import TriangularAttention
+    inp = make_inputs(Workload("wrap", 1, 36, 64, 2, "bf16", ("bernoulli", 0.8), 4))
+    log("wrapper")
+    g = Gpu(inp)
+    try:
+        a = g.forward()
+        m = TriangularAttention(g.w, num_heads=2)
+        b = m(g.P, g.M)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        m.close()
+    finally:
+        g.close()

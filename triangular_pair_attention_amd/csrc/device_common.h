@@ -1,0 +1,88 @@
+// Device helpers for gfx950 (CDNA4): matrix-core fragments, conversions,
+// wave reductions. Used by both kernels of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16_t {  // storage type tag for bfloat16 tensors
+  uint16_t bits;
+};
+
+template <typename T>
+struct is_bf16 {
+  static constexpr bool value = false;
+};
+template <>
+struct is_bf16<bf16_t> {
+  static constexpr bool value = true;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- MFMA
+// 16x16x32 bf16 -> f32. Lane l holds A[l%16][8(l/16)..+7], B[8(l/16)..+7][l%16];
+// the result lane l holds C[4(l/16)+r][l%16], r = 0..3.
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x16 bf16 -> f32 (A[l%16][4(l/16)..+3]).
+__device__ __forceinline__ f32x4 mfma(bf16x4 a, bf16x4 b, f32x4 c) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                   0, 0, 0);
+}
+// 16x16x4 f32. Lane l holds A[l%16][l/16], B[l/16][l%16].
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Round-to-nearest-even float -> bf16 (the hardware conversion on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+__device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+
+// ---------------------------------------------------------------- loads / stores
+template <typename V>
+__device__ __forceinline__ V ldg(const void *p) {
+  return *reinterpret_cast<const V *>(p);
+}
+template <typename V>
+__device__ __forceinline__ void stg(void *p, V v) {
+  *reinterpret_cast<V *>(p) = v;
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
+__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
+
+// Sum / max over the four lanes that share l % 16 (lane groups l / 16).
+__device__ __forceinline__ float group4_sum(float v) { return xor_sum(xor_sum(v, 16), 32); }
+__device__ __forceinline__ float group4_max(float v) { return xor_max(xor_max(v, 16), 32); }
+// Max over the 16 lanes of one lane group.
+__device__ __forceinline__ float row16_max(float v) {
+  v = xor_max(v, 1);
+  v = xor_max(v, 2);
+  v = xor_max(v, 4);
+  return xor_max(v, 8);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+}  // namespace tpa

@@ -1,0 +1,240 @@
+// Host side of the C ABI declared in include/tri_attn.h: argument checks,
+// weight packing, workspace layout and the two kernel launches.
+#include "tri_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "tri_attn_internal.h"
+
+struct tri_attn {
+  tri_attn_config cfg;
+  int D, h, dh, elem;
+  int device;
+  int k1_grid;     // persistent grid of kernel 1 (resident workgroups)
+  void *wpack;     // [(4D + 16)][D] Wq; Wk; Wv; Wg; Wz; zero rows
+  void *vecs;      // gamma, beta, bg, bo ([D] each), then Wo [D][D]
+  size_t wpack_bytes, vecs_bytes;
+};
+
+namespace tpa {
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout make_layout(int B, int N, int D, int h, int elem) {
+  Layout L{};
+  L.Np = ((N + kChunk - 1) / kChunk) * kChunk;
+  L.nchunk = L.Np / kChunk;
+  const size_t proj = (size_t)B * N * D * L.Np * elem;  // [B][N][D/16][Np][16] (and v^T)
+  size_t off = 0;
+  L.q = off, off = align256(off + proj);
+  L.k = off, off = align256(off + proj);
+  L.vt = off, off = align256(off + proj);
+  L.g = off, off = align256(off + proj);
+  L.zm = off, off = align256(off + (size_t)B * h * N * L.Np * 4);
+  L.zmax = off, off = align256(off + (size_t)B * h * N * L.nchunk * 4);
+  L.kmax = off, off = align256(off + (size_t)B * N * h * L.nchunk * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace tpa
+
+using namespace tpa;
+
+extern "C" {
+
+const char *tri_attn_strerror(int code) {
+  switch (code) {
+    case TRI_ATTN_OK: return "ok";
+    case TRI_ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case TRI_ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TRI_ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case TRI_ATTN_ERR_HIP: return "HIP runtime error";
+    case TRI_ATTN_ERR_OOM: return "device allocation failed";
+    default: return "unknown error code";
+  }
+}
+
+static int check_config(const tri_attn_config *cfg) {
+  if (!cfg) return TRI_ATTN_ERR_INVALID_ARG;
+  if (cfg->pair_dim <= 0 || cfg->num_heads <= 0 || cfg->pair_dim % cfg->num_heads != 0)
+    return TRI_ATTN_ERR_INVALID_ARG;
+  if (cfg->dtype != TRI_ATTN_F32 && cfg->dtype != TRI_ATTN_BF16) return TRI_ATTN_ERR_INVALID_ARG;
+  if (!(cfg->ln_eps > 0.f) || !std::isfinite(cfg->ln_eps)) return TRI_ATTN_ERR_INVALID_ARG;
+  const float f = cfg->mask_fill;
+  if (std::isnan(f) || !(f == -INFINITY || (std::isfinite(f) && f <= -1e4f))) return TRI_ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(cfg->shift_slack) || cfg->shift_slack < 0.f) return TRI_ATTN_ERR_INVALID_ARG;
+  if (!supported(cfg->pair_dim, cfg->pair_dim / cfg->num_heads)) return TRI_ATTN_ERR_UNSUPPORTED;
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void *stream, tri_attn_t *out) {
+  if (!out) return TRI_ATTN_ERR_INVALID_ARG;
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w || !w->ln_weight || !w->ln_bias || !w->w_query || !w->w_key || !w->w_value || !w->w_gate ||
+      !w->b_gate || !w->w_bias_proj || !w->w_out || !w->b_out)
+    return TRI_ATTN_ERR_INVALID_ARG;
+
+  tri_attn *t = new (std::nothrow) tri_attn();
+  if (!t) return TRI_ATTN_ERR_OOM;
+  t->cfg = *cfg;
+  t->D = cfg->pair_dim;
+  t->h = cfg->num_heads;
+  t->dh = t->D / t->h;
+  t->elem = cfg->dtype == TRI_ATTN_BF16 ? 2 : 4;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = t->D, h = t->h, e = t->elem;
+
+  if (hipGetDevice(&t->device) != hipSuccess) {
+    delete t;
+    return TRI_ATTN_ERR_HIP;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, t->device) != hipSuccess || cus <= 0) {
+    delete t;
+    return TRI_ATTN_ERR_HIP;
+  }
+  t->k1_grid = cus * (t->elem == 2 ? 2 : 1);
+
+  t->wpack_bytes = (size_t)(4 * D + 16) * D * e;
+  t->vecs_bytes = (size_t)4 * D * e + (size_t)D * D * e;
+  if (hipMalloc(&t->wpack, t->wpack_bytes) != hipSuccess) {
+    delete t;
+    return TRI_ATTN_ERR_OOM;
+  }
+  if (hipMalloc(&t->vecs, t->vecs_bytes) != hipSuccess) {
+    (void)hipFree(t->wpack);
+    delete t;
+    return TRI_ATTN_ERR_OOM;
+  }
+  char *wp = static_cast<char *>(t->wpack);
+  char *vp = static_cast<char *>(t->vecs);
+  const size_t mat = (size_t)D * D * e, vec = (size_t)D * e;
+  bool ok = hipMemsetAsync(t->wpack, 0, t->wpack_bytes, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(wp + 0 * mat, w->w_query, mat, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(wp + 1 * mat, w->w_key, mat, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(wp + 2 * mat, w->w_value, mat, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(wp + 3 * mat, w->w_gate, mat, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(wp + 4 * mat, w->w_bias_proj, (size_t)h * D * e, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(vp + 0 * vec, w->ln_weight, vec, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(vp + 1 * vec, w->ln_bias, vec, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(vp + 2 * vec, w->b_gate, vec, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(vp + 3 * vec, w->b_out, vec, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(vp + 4 * vec, w->w_out, mat, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && hipStreamSynchronize(s) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    (void)hipFree(t->wpack);
+    (void)hipFree(t->vecs);
+    delete t;
+    return TRI_ATTN_ERR_HIP;
+  }
+  *out = t;
+  return TRI_ATTN_OK;
+}
+
+static int check_sizes(tri_attn_t t, int B, int N) {
+  if (!t) return TRI_ATTN_ERR_INVALID_ARG;
+  if (B < 0 || N < 0) return TRI_ATTN_ERR_INVALID_ARG;
+  if (B == 0 || N == 0) return TRI_ATTN_OK;
+  // kernels index elements of one tensor with 64-bit bases but 32-bit item counts
+  const Layout L = make_layout(B, N, t->D, t->h, t->elem);
+  if ((double)B * N * ((N + 15) / 16) > 2.0e9 || (double)B * N * L.nchunk > 2.0e9) return TRI_ATTN_ERR_UNSUPPORTED;
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_workspace_size(tri_attn_t t, int B, int N, size_t *bytes) {
+  if (!bytes) return TRI_ATTN_ERR_INVALID_ARG;
+  int rc = check_sizes(t, B, N);
+  if (rc) return rc;
+  *bytes = (B == 0 || N == 0) ? 0 : make_layout(B, N, t->D, t->h, t->elem).total;
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_get_workspace_layout(tri_attn_t t, int B, int N, tri_attn_workspace_layout *out) {
+  if (!out) return TRI_ATTN_ERR_INVALID_ARG;
+  int rc = check_sizes(t, B, N);
+  if (rc) return rc;
+  std::memset(out, 0, sizeof(*out));
+  if (B == 0 || N == 0) return TRI_ATTN_OK;
+  const Layout L = make_layout(B, N, t->D, t->h, t->elem);
+  out->q = L.q, out->k = L.k, out->vt = L.vt, out->g = L.g;
+  out->zm = L.zm, out->zmax = L.zmax, out->kmax = L.kmax;
+  out->total = L.total;
+  out->padded_n = L.Np;
+  return TRI_ATTN_OK;
+}
+
+static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
+               void *ws, size_t ws_bytes, void *stream, bool attention) {
+  int rc = check_sizes(t, B, N);
+  if (rc) return rc;
+  if (B == 0 || N == 0) return TRI_ATTN_OK;
+  if (!pair_repr || !pair_mask || (attention && !out)) return TRI_ATTN_ERR_INVALID_ARG;
+  const Layout L = make_layout(B, N, t->D, t->h, t->elem);
+  if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) & 255)) return TRI_ATTN_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char *w = static_cast<char *>(ws);
+  const int D = t->D, e = t->elem;
+  const char *vp = static_cast<const char *>(t->vecs);
+
+  K1Args a1{};
+  a1.P = pair_repr;
+  a1.mask = pair_mask;
+  a1.W = t->wpack;
+  a1.gamma = vp;
+  a1.beta = vp + (size_t)D * e;
+  a1.bg = vp + (size_t)2 * D * e;
+  a1.q = w + L.q, a1.k = w + L.k, a1.vt = w + L.vt, a1.g = w + L.g;
+  a1.zm = reinterpret_cast<float *>(w + L.zm);
+  a1.zmax = reinterpret_cast<float *>(w + L.zmax);
+  a1.kmax = reinterpret_cast<float *>(w + L.kmax);
+  a1.eps = t->cfg.ln_eps;
+  a1.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->dh));
+  a1.B = B, a1.N = N, a1.Np = L.Np, a1.nchunk = L.nchunk;
+  a1.tiles = B * N * L.nchunk;
+  const int grid = a1.tiles < t->k1_grid ? a1.tiles : t->k1_grid;
+  if (launch_k1(t->cfg.dtype, D, t->dh, a1, grid, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
+  if (!attention) return TRI_ATTN_OK;
+
+  K2Args a2{};
+  a2.q = a1.q, a2.k = a1.k, a2.vt = a1.vt, a2.g = a1.g;
+  a2.zm = a1.zm, a2.zmax = a1.zmax, a2.kmax = a1.kmax;
+  a2.Wo = vp + (size_t)4 * D * e;
+  a2.bo = vp + (size_t)3 * D * e;
+  a2.out = out;
+  a2.mask_fill = t->cfg.mask_fill;
+  a2.shift_slack = t->cfg.shift_slack;
+  a2.B = B, a2.N = N, a2.Np = L.Np, a2.nchunk = L.nchunk;
+  a2.items = k2_items(D, t->dh, B, N);
+  if (launch_k2(t->cfg.dtype, D, t->dh, a2, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_forward(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
+                     void *workspace, size_t ws_bytes, void *stream) {
+  return run(t, pair_repr, pair_mask, out, B, N, workspace, ws_bytes, stream, true);
+}
+
+int tri_attn_project(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, int B, int N, void *workspace,
+                     size_t ws_bytes, void *stream) {
+  return run(t, pair_repr, pair_mask, nullptr, B, N, workspace, ws_bytes, stream, false);
+}
+
+int tri_attn_destroy(tri_attn_t t) {
+  if (!t) return TRI_ATTN_OK;
+  int rc = TRI_ATTN_OK;
+  if (hipDeviceSynchronize() != hipSuccess) rc = TRI_ATTN_ERR_HIP;
+  if (hipFree(t->wpack) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
+  if (hipFree(t->vecs) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
+  delete t;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal declarations shared by the host library and the two kernels.
+// Not part of the public ABI (include/tri_attn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpa {
+
+constexpr int kChunk = 64;  // key chunk of the per-chunk maxima; also K1's position tile
+
+// Workspace regions (byte offsets); see tri_attn_workspace_layout in the header.
+struct Layout {
+  size_t q, k, vt, g, zm, zmax, kmax, total;
+  int Np;      // N rounded up to kChunk
+  int nchunk;  // Np / kChunk
+};
+
+Layout make_layout(int B, int N, int D, int h, int elem_bytes);
+
+// Kernel 1: LayerNorm + one fused projection GEMM.
+struct K1Args {
+  const void *P;          // [B][N][N][D]
+  const uint8_t *mask;    // [B][N][N]
+  const void *W;          // packed [(4D + 16)][D]: Wq; Wk; Wv; Wg; Wz; zero rows
+  const void *gamma, *beta, *bg;  // [D]
+  void *q, *k, *vt, *g;
+  float *zm, *zmax, *kmax;
+  float eps;
+  float qscale;  // log2(e) / sqrt(d)
+  int B, N, Np, nchunk, tiles;
+};
+
+// Kernel 2: attention core + gate + output projection.
+struct K2Args {
+  const void *q, *k, *vt, *g;
+  const float *zm, *zmax, *kmax;
+  const void *Wo, *bo;
+  void *out;
+  float mask_fill;  // finite (uniform rule on fully masked columns) or -inf (NaN there)
+  float shift_slack;
+  int B, N, Np, nchunk, items;
+};
+
+// Launchers: return the launch status. `dtype` is TRI_ATTN_F32 / TRI_ATTN_BF16.
+hipError_t launch_k1(int dtype, int D, int dh, const K1Args &a, int grid, hipStream_t s);
+hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, hipStream_t s);
+int k2_items(int D, int dh, int B, int N);
+bool supported(int D, int dh);
+
+}  // namespace tpa
