@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the starting-node triangular self-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config k]
+
+A step is one tri_attn_forward (kernel 1: LayerNorm + fused projection,
+kernel 2: attention + gate + output projection) over one batch of seeded
+synthetic inputs already resident in HBM. Prints ONE JSON line.
+
+The default workload is B=1, N=128, D=128, h=4 (d=32), float32, Bernoulli(0.9)
+mask with the diagonal set. `--config k` selects another of the five
+workloads (1..5). Each kernel is also timed alone (stage entry points
+tri_attn_project / tri_attn_attend) with HIP events on the stream it runs on;
+the slower one is reported in `roofline`.
+
+`--copy-probe` runs only a plain device copy of a known size (the reference
+for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "pair-positions/sec + TFLOP/s, triangular-attn fwd; % MFMA/HBM roofline"
+PEAK = {  # MI355X published dense peaks
+    "hbm_GBps": 8000.0,
+    "mfma_f32_TFLOPs": 157.3,
+    "mfma_bf16_TFLOPs": 2500.0,
+}
+KERNEL_SOURCES = {
+    "k1_ln_proj": "triangular_pair_attention_amd/csrc/k1_ln_proj.hip",
+    "k2_attention": "triangular_pair_attention_amd/csrc/k2_attention.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[kernel], "triangular_pair_attention_amd/csrc/device_common.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def work_model(w):
+    """Algorithmic flops and bytes of each kernel per launch (dense counts)."""
+    B, N, D, h = w.B, w.N, w.D, w.h
+    s = 2 if w.dtype == "bf16" else 4
+    P = B * N * N
+    f1 = 2 * P * D * (4 * D + h)
+    f2 = 4 * B * N ** 3 * D + 2 * P * D * D
+    # kernel 1: read pair_repr and mask, write q, k, v, gate (s bytes each) and the fp32 bias+mask tile
+    b1 = P * D * s + P + 4 * P * D * s + 4 * B * h * N * N
+    # kernel 2: read q, k, v, gate and the bias+mask tile once, write y
+    b2 = 4 * P * D * s + 4 * B * h * N * N + P * D * s
+    return {"positions": P, "k1_flops": f1, "k2_flops": f2, "k1_bytes": b1, "k2_bytes": b2}
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash(kernel):
+        return None
+    return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
+
+
+def cpu_baseline(inp, w, seconds):
+    """The oracle as it stands on the host cores: all N rows of batch 0 (with
+    that batch's LayerNorm and pair bias), repeated until `seconds` elapse."""
+    import numpy as np  # noqa: F401
+    from oracle.tri_attn_oracle import forward_rows
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    rows = [(0, i) for i in range(w.N)]
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        forward_rows(inp, rows)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    pos = done * w.N * w.N
+    return {
+        "value": pos / el,
+        "unit": "pair-positions/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} x all {w.N} rows of batch 0 of {w.name} ({pos} pair positions, "
+                  f"{el:.1f} s, float64 numpy, BLAS threads = {cores})",
+    }
+
+
+def copy_probe(mib: int = 256, reps: int = 5):
+    import torch
+
+    a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": mib << 20, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the multi-GPU path is a design "
+              "(row sharding with an all-gather of the pair bias), not built. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    from triangular_pair_attention_amd import binding as B
+    from workloads import WEIGHT_NAMES, WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    inp = make_inputs(w)
+    weights = {k: torch.from_numpy(inp[k]).to(dev).to(dt).contiguous() for k in WEIGHT_NAMES}
+    P = torch.from_numpy(inp["pair_repr"]).to(dev).to(dt).contiguous()
+    M = torch.from_numpy(inp["pair_mask"]).to(dev).contiguous()
+    out = torch.empty_like(P)
+    stream = torch.cuda.current_stream(dev)
+    cfg = B.tri_attn_config(w.D, w.h, B.TRI_ATTN_F32 if w.dtype == "f32" else B.TRI_ATTN_BF16, 1e-5, -1e9, 0.0)
+    h = B.tri_attn_create(cfg, weights, stream)
+    nws = B.tri_attn_workspace_size(h, w.B, w.N)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def fwd():
+        B.tri_attn_forward(h, P, M, out, w.B, w.N, ws, nws, stream)
+
+    def k1():
+        B.tri_attn_project(h, P, M, w.B, w.N, ws, nws, stream)
+
+    def k2():
+        B.tri_attn_attend(h, out, w.B, w.N, ws, nws, stream)
+
+    def timed(fn, steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per call
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    # the timed region: exactly `steps` forwards, synchronised on both sides
+    t0 = time.perf_counter()
+    ms_fwd_ev = timed(fwd, args.steps)
+    wall = time.perf_counter() - t0
+    ms_fwd = max(ms_fwd_ev, 0.0)
+    # each kernel alone, same stream, for the roofline
+    for _ in range(5):
+        k1()
+        k2()
+    ms_k1 = timed(k1, args.steps)
+    ms_k2 = timed(k2, args.steps)
+    torch.cuda.synchronize()
+    B.tri_attn_destroy(h)
+
+    m = work_model(w)
+    pos_per_s = m["positions"] / (ms_fwd * 1e-3)
+    tflops = (m["k1_flops"] + m["k2_flops"]) / (ms_fwd * 1e-3) / 1e12
+    dom = "k1_ln_proj" if ms_k1 >= ms_k2 else "k2_attention"
+    ms_dom = ms_k1 if dom == "k1_ln_proj" else ms_k2
+    if dom == "k1_ln_proj" and w.dtype == "bf16":
+        roof = {"bound": "hbm", "achieved": m["k1_bytes"] / (ms_dom * 1e-3) / 1e9, "peak": PEAK["hbm_GBps"],
+                "unit": "GB/s"}
+    else:
+        fl = m["k1_flops"] if dom == "k1_ln_proj" else m["k2_flops"]
+        peak = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
+        roof = {"bound": "mfma", "achieved": fl / (ms_dom * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(w.name, dom)
+    roof["kernel"] = dom
+    roof["kernel_ms"] = ms_dom
+
+    result = {
+        "metric": METRIC,
+        "value": pos_per_s,
+        "unit": "pair-positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_fwd,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "h": w.h, "d": w.d,
+                   "mask": list(w.mask), "seed": w.seed, "parallelism": "none (1 GPU)"},
+        "tflops": tflops,
+        "kernels_ms": {"k1_ln_proj": ms_k1, "k2_attention": ms_k2},
+        "k1_hbm_GBps": m["k1_bytes"] / (ms_k1 * 1e-3) / 1e9,
+        "k2_tflops": m["k2_flops"] / (ms_k2 * 1e-3) / 1e12,
+        "k1_tflops": m["k1_flops"] / (ms_k1 * 1e-3) / 1e12,
+        "wall_s_timed": wall,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

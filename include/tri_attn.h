@@ -134,6 +134,11 @@ int tri_attn_get_workspace_layout(tri_attn_t h, int B, int N, tri_attn_workspace
 int tri_attn_project(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, int B, int N,
                      void *workspace, size_t ws_bytes, void *stream);
 
+/* Run only the attention kernel on a workspace that tri_attn_project (or a
+ * forward) filled for the same handle, B and N; writes out [B, N, N, D].
+ * tri_attn_project followed by tri_attn_attend equals tri_attn_forward. */
+int tri_attn_attend(tri_attn_t h, void *out, int B, int N, void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -220,6 +220,24 @@ def test_empty_and_error_paths():
         g.close()
 
 
+def test_project_then_attend_equals_forward():
+    inp = make_inputs(WORKLOADS[1])
+    log("project + attend")
+    g = Gpu(inp)
+    try:
+        a = g.forward().clone()
+        g.project()
+        b = torch.empty_like(g.P)
+        B.tri_attn_attend(g.handle, b, g.B, g.N, g.ws, g.ws_bytes, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        with pytest.raises(B.TriAttnError) as e:
+            B.tri_attn_attend(g.handle, 0, g.B, g.N, g.ws, g.ws_bytes)
+        assert e.value.code == B.TRI_ATTN_ERR_INVALID_ARG
+    finally:
+        g.close()
+
+
 def test_convenience_wrapper_matches_abi():
     from triangular_pair_attention_amd import TriangularAttention
     inp = make_inputs(Workload("wrap", 1, 36, 64, 2, "bf16", ("bernoulli", 0.8), 4))

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     TriAttnError,
     WEIGHT_FIELDS,
     load_library,
+    tri_attn_attend,
     tri_attn_config,
     tri_attn_create,
     tri_attn_destroy,

@@ -79,8 +79,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tri_attn_strerror.restype = ctypes.c_char_p
     lib.tri_attn_get_workspace_layout.argtypes = [vp, i, i, ctypes.POINTER(tri_attn_workspace_layout)]
     lib.tri_attn_project.argtypes = [vp, vp, vp, i, i, vp, sz, vp]
+    lib.tri_attn_attend.argtypes = [vp, vp, i, i, vp, sz, vp]
     for name in ("tri_attn_create", "tri_attn_workspace_size", "tri_attn_forward", "tri_attn_destroy",
-                 "tri_attn_get_workspace_layout", "tri_attn_project"):
+                 "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -160,6 +161,11 @@ def tri_attn_project(handle: int, pair_repr, pair_mask, B: int, N: int, workspac
                      stream=None) -> None:
     _check(load_library().tri_attn_project(handle, _ptr(pair_repr), _ptr(pair_mask), B, N, _ptr(workspace),
                                            ws_bytes, _stream(stream)), "tri_attn_project")
+
+
+def tri_attn_attend(handle: int, out, B: int, N: int, workspace, ws_bytes: int, stream=None) -> None:
+    _check(load_library().tri_attn_attend(handle, _ptr(out), B, N, _ptr(workspace), ws_bytes, _stream(stream)),
+           "tri_attn_attend")
 
 
 def raw_call(name: str, *args) -> int:

@@ -171,12 +171,13 @@ int tri_attn_get_workspace_layout(tri_attn_t t, int B, int N, tri_attn_workspace
   return TRI_ATTN_OK;
 }
 
+// stages: 1 = projection kernel, 2 = attention kernel, 3 = both
 static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
-               void *ws, size_t ws_bytes, void *stream, bool attention) {
+               void *ws, size_t ws_bytes, void *stream, int stages) {
   int rc = check_sizes(t, B, N);
   if (rc) return rc;
   if (B == 0 || N == 0) return TRI_ATTN_OK;
-  if (!pair_repr || !pair_mask || (attention && !out)) return TRI_ATTN_ERR_INVALID_ARG;
+  if (((stages & 1) && (!pair_repr || !pair_mask)) || ((stages & 2) && !out)) return TRI_ATTN_ERR_INVALID_ARG;
   const Layout L = make_layout(B, N, t->D, t->h, t->elem);
   if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) & 255)) return TRI_ATTN_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -200,8 +201,8 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a1.B = B, a1.N = N, a1.Np = L.Np, a1.nchunk = L.nchunk;
   a1.tiles = B * N * L.nchunk;
   const int grid = a1.tiles < t->k1_grid ? a1.tiles : t->k1_grid;
-  if (launch_k1(t->cfg.dtype, D, t->dh, a1, grid, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
-  if (!attention) return TRI_ATTN_OK;
+  if ((stages & 1) && launch_k1(t->cfg.dtype, D, t->dh, a1, grid, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
+  if (!(stages & 2)) return TRI_ATTN_OK;
 
   K2Args a2{};
   a2.q = a1.q, a2.k = a1.k, a2.vt = a1.vt, a2.g = a1.g;
@@ -219,12 +220,16 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
 
 int tri_attn_forward(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
                      void *workspace, size_t ws_bytes, void *stream) {
-  return run(t, pair_repr, pair_mask, out, B, N, workspace, ws_bytes, stream, true);
+  return run(t, pair_repr, pair_mask, out, B, N, workspace, ws_bytes, stream, 3);
 }
 
 int tri_attn_project(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, int B, int N, void *workspace,
                      size_t ws_bytes, void *stream) {
-  return run(t, pair_repr, pair_mask, nullptr, B, N, workspace, ws_bytes, stream, false);
+  return run(t, pair_repr, pair_mask, nullptr, B, N, workspace, ws_bytes, stream, 1);
+}
+
+int tri_attn_attend(tri_attn_t t, void *out, int B, int N, void *workspace, size_t ws_bytes, void *stream) {
+  return run(t, nullptr, nullptr, out, B, N, workspace, ws_bytes, stream, 2);
 }
 
 int tri_attn_destroy(tri_attn_t t) {
