@@ -19,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "lib", "libtri_attn.so")
+CALIB = os.path.join(PKG, "lib", "tri_attn_calib")
 SOURCES = ("tri_attn.cpp", "k1_ln_proj.hip", "k2_attention.hip")
 ARCH = "gfx950"
 
@@ -62,8 +63,14 @@ def build(verbose: bool = False, extra=()) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # calibration microbenchmarks (a separate executable, not part of the library)
+    cmd = [hipcc(), "-O3", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument", os.path.join(PKG, "calib", "calib.hip"), "-o", CALIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the calibration tool failed:\n{r.stdout}\n{r.stderr}")
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB}")
     return LIB
 
 

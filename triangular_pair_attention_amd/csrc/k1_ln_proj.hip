@@ -59,6 +59,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   static_assert(BPW >= 1 && (DH == 16 || BPW % 2 == 0), "a k head must not straddle two waves");
 
   __shared__ __align__(16) T xs[2][TILE * PITCH];
+  __shared__ uint8_t mask_s[2][TILE];  // the tile's mask bytes (0 also for j >= N)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -96,9 +97,10 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   // ---- LayerNorm thread mapping: TPP threads per position, EPT channels each
   const int lpos = tid / TPP, lpart = tid % TPP;
 
-  auto load_tile = [&](int tile, uint4 (&pre)[NV]) {
+  auto load_tile = [&](int tile, uint4 (&pre)[NV], uint32_t &mpre) {
     const int bi_row = tile / nch, chunk = tile - bi_row * nch;
     const int j = chunk * TILE + lpos;
+    mpre = (j < N && lpart == 0) ? a.mask[(size_t)bi_row * N + j] : 0u;
     if (j < N) {
       const char *src = reinterpret_cast<const char *>(a.P) + ((size_t)bi_row * N + j) * D * ES + lpart * EPT * ES;
 #pragma unroll
@@ -109,9 +111,10 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     }
   };
 
-  auto layer_norm_to_lds = [&](int tile, const uint4 (&pre)[NV], int buf) {
+  auto layer_norm_to_lds = [&](int tile, const uint4 (&pre)[NV], uint32_t mpre, int buf) {
     const int bi_row = tile / nch, chunk = tile - bi_row * nch;
     const int j = chunk * TILE + lpos;
+    if (lpart == 0) mask_s[buf][lpos] = (uint8_t)mpre;
     float v[EPT];
     const uint32_t *w32 = reinterpret_cast<const uint32_t *>(pre);
 #pragma unroll
@@ -282,8 +285,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
         float z[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = jb + r;
-          const bool keep = (j < N) && a.mask[(size_t)bi_row * N + j] != 0;
+          const bool keep = mask_s[buf][pb * 16 + 4 * g + r] != 0;
           z[r] = keep ? accz[r] * kLog2e : -INFINITY;
           z_run = fmaxf(z_run, z[r]);
         }
@@ -310,15 +312,16 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   int tile = blockIdx.x;
   if (tile >= a.tiles) return;
   uint4 pre[NV];
+  uint32_t mpre;
   int buf = 0;
   if constexpr (BF) {
-    // bf16 is HBM-bound: prefetch the next tile's pair_repr while this one computes
-    load_tile(tile, pre);
+    // bf16 is HBM-bound: prefetch the next tile's pair_repr and mask while this one computes
+    load_tile(tile, pre, mpre);
 #pragma unroll 1
     for (; tile < a.tiles; tile += gridDim.x) {
-      layer_norm_to_lds(tile, pre, buf);
+      layer_norm_to_lds(tile, pre, mpre, buf);
       __syncthreads();
-      if (tile + (int)gridDim.x < a.tiles) load_tile(tile + gridDim.x, pre);
+      if (tile + (int)gridDim.x < a.tiles) load_tile(tile + gridDim.x, pre, mpre);
       compute_tile(tile, buf);
       buf ^= 1;
     }
@@ -326,8 +329,8 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     // fp32 is matrix-core-bound and short of registers: no cross-tile prefetch
 #pragma unroll 1
     for (; tile < a.tiles; tile += gridDim.x) {
-      load_tile(tile, pre);
-      layer_norm_to_lds(tile, pre, buf);
+      load_tile(tile, pre, mpre);
+      layer_norm_to_lds(tile, pre, mpre, buf);
       __syncthreads();
       compute_tile(tile, buf);
       buf ^= 1;

@@ -38,10 +38,12 @@
 
 namespace tpa {
 
+// Rows i per workgroup (IG) and 16-column query blocks per wave (JW). The bias
+// tile is reused across the IG rows in registers; k and v across the JW*16
+// columns. Workgroups with 4 waves (h = 4) take 2 rows to keep 2 waves per SIMD.
 template <int D, int DH>
 struct K2Shape {
-  // rows per workgroup and 16-column query blocks per wave
-  static constexpr int IG = 4;
+  static constexpr int IG = (D / DH >= 8) ? 4 : 2;
   static constexpr int JW = 2;
 };
 
@@ -71,17 +73,33 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
   const int g = lane >> 4, r16 = lane & 15;
   const int N = a.N, Np = a.Np, nch = a.nchunk;
 
-  // ---- work item, XCD-aware: workgroups w, w+8, w+16... share an XCD (and its L2);
-  // give them consecutive items, which share (b, rows i) and so k and v.
-  int item = blockIdx.x;
+  // ---- work item, XCD-aware. Workgroup w runs on XCD w % 8; each XCD takes a
+  // contiguous range of the linear order below, in which consecutive items form
+  // super-tiles of SI row groups x SJ query ranges (about one item per CU of an
+  // XCD), so the concurrently running workgroups of an XCD share k, v (same
+  // rows) and the bias tile (same query columns) through its L2.
+  const int nJR = (N + NJ - 1) / NJ, nIG = (N + IG - 1) / IG;
+  int lin = blockIdx.x;
   {
     const int w8 = (a.items / 8) * 8;
-    if (item < w8) item = (item & 7) * (w8 / 8) + (item >> 3);
+    if (lin < w8) lin = (lin & 7) * (w8 / 8) + (lin >> 3);
   }
-  const int nJR = (N + NJ - 1) / NJ, nIG = (N + IG - 1) / IG;
-  const int jr = item % nJR;
-  const int ig = (item / nJR) % nIG;
-  const int b = item / (nJR * nIG);
+  const int per_b = nIG * nJR;
+  const int b = lin / per_b;
+  int ig, jr;
+  {
+    const int SJ = nJR < 8 ? nJR : 8;
+    const int SI = 32 / SJ;
+    const int rem = lin - b * per_b;
+    const int igs = (rem / (SI * nJR)) * SI;
+    const int si = min(SI, nIG - igs);
+    const int r2 = rem - igs * nJR;
+    const int jrs = (r2 / (si * SJ)) * SJ;
+    const int sj = min(SJ, nJR - jrs);
+    const int r3 = r2 - jrs * si;
+    ig = igs + r3 / sj;
+    jr = jrs + r3 % sj;
+  }
   const int i0 = ig * IG, j0 = jr * NJ;
 
   const T *Q = reinterpret_cast<const T *>(a.q);
@@ -207,17 +225,29 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
 
   // Score tiles of one (row, key step): bf16 -> sA (keys k0+8g+0..3), sB (k0+8g+4..7);
   // fp32 -> s (keys k0+4g+0..3). Shared by the main loop and the max pass.
+  // The bias+mask tile of the next key step is loaded one step ahead (it is
+  // the operand least likely to be in L2).
   auto main_loop = [&](bool max_pass, float (&mx)[IG][JW]) {
+    if (kend_keys == 0) return;
+    f32x4 zA[JW], zB[JW];  // bf16: keys k0+8g+0..3 and k0+8g+4..7; fp32: zA = keys k0+4g+0..3
+    auto load_z = [&](int k0, f32x4 (&za)[JW], f32x4 (&zb)[JW]) {
+#pragma unroll
+      for (int jb = 0; jb < JW; ++jb) {
+        if constexpr (BF) {
+          const float *zp = ZM + (size_t)jrow[jb] * Np + k0 + 8 * g;
+          za[jb] = ldg<f32x4>(zp);
+          zb[jb] = ldg<f32x4>(zp + 4);
+        } else {
+          za[jb] = ldg<f32x4>(ZM + (size_t)jrow[jb] * Np + k0 + 4 * g);
+        }
+      }
+    };
+    load_z(0, zA, zB);
 #pragma unroll 1
     for (int k0 = 0; k0 < kend_keys; k0 += KSTEP) {
+      f32x4 nA[JW], nB[JW];
+      load_z(k0 + KSTEP < kend_keys ? k0 + KSTEP : k0, nA, nB);
       if constexpr (BF) {
-        f32x4 zA[JW], zB[JW];
-#pragma unroll
-        for (int jb = 0; jb < JW; ++jb) {
-          const float *zp = ZM + (size_t)jrow[jb] * Np + k0 + 8 * g;
-          zA[jb] = ldg<f32x4>(zp);
-          zB[jb] = ldg<f32x4>(zp + 4);
-        }
         const int keyA = k0 + 8 * (r16 >> 2) + (r16 & 3);  // S^T row r16 of tile A
 #pragma unroll
         for (int i = 0; i < IG; ++i) {
@@ -262,9 +292,6 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
           }
         }
       } else {
-        f32x4 zf[JW];
-#pragma unroll
-        for (int jb = 0; jb < JW; ++jb) zf[jb] = ldg<f32x4>(ZM + (size_t)jrow[jb] * Np + k0 + 4 * g);
 #pragma unroll
         for (int i = 0; i < IG; ++i) {
           const size_t rowbase = (size_t)(b * N + rows[i]) * NB;
@@ -286,7 +313,7 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
                                 (((size_t)(b * N + rows[i]) * H + t) * DH + mb * 16 + r16) * Np + k0 + 4 * g);
 #pragma unroll
           for (int jb = 0; jb < JW; ++jb) {
-            f32x4 s = zf[jb];
+            f32x4 s = zA[jb];
 #pragma unroll
             for (int ss = 0; ss < QS; ++ss) s = mfma(kf[ss], qf[i][jb][ss], s);
             if (max_pass) {
@@ -307,6 +334,11 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
             }
           }
         }
+      }
+#pragma unroll
+      for (int jb = 0; jb < JW; ++jb) {
+        zA[jb] = nA[jb];
+        if constexpr (BF) zB[jb] = nB[jb];
       }
     }
   };
