@@ -120,8 +120,8 @@ const char *tri_attn_strerror(int code);
  *   zm      : [B][h][N][Np] float32: z[b,t,j,k] * log2(e) where M[b,j,k] != 0
  *             and k < N, -inf elsewhere.
  *   zmax    : [B][h][N][Np/64] float32: max of zm over each 64-key chunk.
- *   kmax    : [B][N][h][Np/64] float32: max over each 64-column chunk of
- *             |k|^2 of one head. */
+ *   kmax    : [B][N][D/16][Np/64] float32: max over each 64-column chunk of
+ *             the squared norm of k over one 16-channel block. */
 typedef struct {
   size_t q, k, vt, g, zm, zmax, kmax;
   size_t total;

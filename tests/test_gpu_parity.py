@@ -150,7 +150,7 @@ def test_projection_stage(dtype, shape):
         vt = f(lay.vt, B_ * N * D * Np).reshape(B_, N, h, d, Np)[..., :N]
         zm = f(lay.zm, B_ * h * N * Np, torch.float32).reshape(B_, h, N, Np)
         zmax = f(lay.zmax, B_ * h * N * (Np // 64), torch.float32).reshape(B_, h, N, Np // 64)
-        kmax = f(lay.kmax, B_ * N * h * (Np // 64), torch.float32).reshape(B_, N, h, Np // 64)
+        kmax = f(lay.kmax, B_ * N * (D // 16) * (Np // 64), torch.float32).reshape(B_, N, D // 16, Np // 64)
     finally:
         g.close()
     q = q.reshape(B_, N, N, D)
@@ -173,9 +173,9 @@ def test_projection_stage(dtype, shape):
     pad = np.full((B_, h, N, Np), -np.inf)
     pad[..., :N] = rz
     np.testing.assert_allclose(zmax, pad.reshape(B_, h, N, Np // 64, 64).max(-1), rtol=rtol, atol=atol)
-    kn2 = np.zeros((B_, N, h, Np))
-    kn2[..., :N] = (cap["k"].reshape(B_, N, h, N, d) ** 2).sum(-1)
-    np.testing.assert_allclose(kmax, kn2.reshape(B_, N, h, Np // 64, 64).max(-1), rtol=2 * rtol, atol=atol)
+    kn2 = np.zeros((B_, N, D // 16, Np))  # |k|^2 over each 16-channel block, per column
+    kn2[..., :N] = (rk.reshape(B_, N, N, D // 16, 16) ** 2).sum(-1).transpose(0, 1, 3, 2)
+    np.testing.assert_allclose(kmax, kn2.reshape(B_, N, D // 16, Np // 64, 64).max(-1), rtol=2 * rtol, atol=atol)
 
 
 # ------------------------------------------------------------------ ABI behaviour on the GPU

@@ -82,6 +82,12 @@ __device__ __forceinline__ float row16_max(float v) {
   return xor_max(v, 8);
 }
 
+// Workgroup barrier for data exchanged through LDS only. It waits for this
+// wave's LDS operations (lgkmcnt) and then for the other waves; unlike
+// __syncthreads() it does not drain the wave's outstanding global loads and
+// stores, so a prefetch or a burst of output stores stays in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 

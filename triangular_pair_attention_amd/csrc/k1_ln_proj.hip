@@ -4,23 +4,24 @@
 // and its layer list; FW-GLM-5-1 / l2_p6: the LayerNorm and linear kernels).
 //
 // Work unit: a tile of 64 consecutive pair positions (b, i, j0..j0+63) of one
-// row. A persistent grid walks the tiles; each workgroup (8 waves) keeps its
-// slice of the packed weight [Wq; Wk; Wv; Wg; Wz] in registers for its whole
-// life, so the weight is read from L2 once per workgroup, not once per tile.
+// row. A persistent grid walks the tiles; each workgroup keeps the packed
+// weight [Wq; Wk; Wv; Wg] in registers for its whole life (each wave holds
+// one 16-channel block of TPW projections), so the weight is read from L2
+// once per workgroup, not once per tile.
 //
-//  1. LayerNorm (fp32 statistics, two-pass in registers): 8 lanes per
-//     position, the normalised row goes to LDS in the operand type. The next
-//     tile's pair_repr is prefetched into registers meanwhile.
-//  2. Each wave owns D/32 16-channel blocks of one projection (waves 0-1: q,
-//     2-3: k, 4-5: v, 6-7: gate; wave 0 also the pair-bias block) and runs
-//     the 16x16 MFMA tiles against the LDS activations.
+//  1. LayerNorm (fp32 statistics, two-pass in registers), TPP lanes per
+//     position; the normalised rows go to LDS in the operand type. bf16 tiles
+//     prefetch pair_repr and the mask two tiles ahead.
+//  2. Wave w owns channel block w % NB of its TPW projections, so every wave
+//     has the same MFMA and epilogue work (the pair-bias block, whose weight
+//     sits in LDS, is the only extra: on the last wave).
 //  3. Epilogues write directly in the layouts kernel 2 reads:
 //     q (pre-scaled by log2(e)/sqrt(d)), k, gate (sigmoid(+bias)) as
-//     [b][i][c/16][j][16] (one 512-byte burst per tile); v transposed per
-//     head [b][i][t][u][j]; the pair bias z*log2(e) with the mask folded in
-//     (-inf where masked) as [b][t][i][j]; plus per-64-key-chunk maxima of
-//     zm and of |k|^2, used by kernel 2 to bound the softmax shift and skip
-//     fully masked key chunks.
+//     [b][i][c/16][j][16] (one 512-byte burst per 16x16 tile); v transposed
+//     per head [b][i][t][u][j]; the pair bias z*log2(e) with the mask folded
+//     in (-inf where masked) as [b][t][i][j]; per-64-key-chunk maxima of that
+//     tile and of the squared norm of k over each 16-channel block, which
+//     kernel 2 uses to bound the softmax shift and to skip masked key chunks.
 #include "device_common.h"
 #include "tri_attn_internal.h"
 
@@ -30,69 +31,69 @@
 
 namespace tpa {
 
-// Waves per projection: 2 (8 waves per workgroup), or 4 (16 waves) where the
-// per-wave weight slice would not fit the register file (fp32, D = 128).
+// TPW projections per wave; NW = 4 * NB / TPW waves per workgroup.
 template <typename T, int D>
 struct K1Shape {
-  static constexpr int WPP = (!is_bf16<T>::value && D == 128) ? 4 : 2;
-  static constexpr int THREADS = 4 * WPP * 64;
+  static constexpr int NB = D / 16;
+  static constexpr int TPW = (!is_bf16<T>::value && D == 128) ? 2 : 4;
+  static constexpr int NW = 4 * NB / TPW;
+  static constexpr int THREADS = NW * 64;
 };
 
 template <typename T, int D, int DH>
 __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a) {
   constexpr bool BF = is_bf16<T>::value;
-  constexpr int WPP = K1Shape<T, D>::WPP;
+  constexpr int ES = BF ? 2 : 4;           // element bytes
+  constexpr int H = D / DH;                // heads
+  constexpr int NB = K1Shape<T, D>::NB;    // 16-channel blocks per projection
+  constexpr int TPW = K1Shape<T, D>::TPW;  // projections per wave
+  constexpr int NW = K1Shape<T, D>::NW;
   constexpr int NT = K1Shape<T, D>::THREADS;
-  constexpr int ES = BF ? 2 : 4;        // element bytes
-  constexpr int H = D / DH;             // heads
-  constexpr int NB = D / 16;            // 16-channel blocks per projection
-  constexpr int BPW = NB / WPP;         // blocks per wave
-  constexpr int HPW = BPW * 16 / DH;    // k heads per k wave
-  constexpr int KQ = D / 4;             // K-dim elements per lane (lane group g owns [g*KQ, g*KQ+KQ))
+  constexpr int KQ = D / 4;                // K-dim elements per lane (lane group g owns [g*KQ, g*KQ+KQ))
   constexpr int KS = BF ? D / 32 : D / 4;  // MFMA steps over K = D
-  constexpr int PITCH = D + 16 / ES;    // LDS row pitch (elements), 16-byte pad against bank conflicts
-  constexpr int TPP = NT / 64;          // LayerNorm threads per position
-  constexpr int EPT = D / TPP;          // LayerNorm elements per thread
-  constexpr int NV = EPT * ES / 16;     // 16-byte loads per thread per tile
+  constexpr int PITCH = D + 16 / ES;       // LDS row pitch (elements), 16-byte pad against bank conflicts
+  constexpr int TPP = NT / 64;             // LayerNorm threads per position
+  constexpr int EPT = D / TPP;             // LayerNorm elements per thread
+  constexpr int NV = EPT * ES / 16;        // 16-byte loads per thread per tile
   constexpr int TILE = kChunk;
   using Frag = typename std::conditional<BF, bf16x8, float>::type;
-  static_assert(BPW >= 1 && (DH == 16 || BPW % 2 == 0), "a k head must not straddle two waves");
+  static_assert(NV >= 1 && EPT % 8 == 0, "");
 
   __shared__ __align__(16) T xs[2][TILE * PITCH];
-  __shared__ uint8_t mask_s[2][TILE];  // the tile's mask bytes (0 also for j >= N)
+  __shared__ uint8_t mask_s[2][TILE];           // the tile's mask bytes (0 also for j >= N)
+  __shared__ float vec_s[3][D];                 // gamma, beta, gate bias (fp32)
+  __shared__ __align__(16) T wz_s[16 * PITCH];  // pair-bias weight block (rows >= h are zero)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int ptype = wave / WPP;          // 0 q, 1 k, 2 v, 3 gate
-  const int cb0 = (wave % WPP) * BPW;  // first block of this wave inside its projection
+  const int cb = wave % NB;             // this wave's channel block in each of its projections
+  const int type0 = (wave / NB) * TPW;  // first projection of this wave (0 q, 1 k, 2 v, 3 gate)
   const int N = a.N, Np = a.Np, nch = a.nchunk;
-
-  // ---- weights into registers: lane (g, r16) holds row r16 of each block, K-range [g*KQ, g*KQ+KQ)
-  Frag wf[BPW][KS];
   const T *W = reinterpret_cast<const T *>(a.W);
+
+  // ---- weights into registers: lane (g, r16) holds row r16 of the block, K-range [g*KQ, g*KQ+KQ)
+  Frag wf[TPW][KS];
 #pragma unroll
-  for (int bi = 0; bi < BPW; ++bi) {
-    const T *wrow = W + (size_t)((ptype * NB + cb0 + bi) * 16 + r16) * D + g * KQ;
+  for (int p = 0; p < TPW; ++p) {
+    const T *wrow = W + (size_t)(((type0 + p) * NB + cb) * 16 + r16) * D + g * KQ;
     if constexpr (BF) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) wf[bi][s] = as_bf16x8(ldg<uint4>(wrow + 8 * s));
+      for (int s = 0; s < KS; ++s) wf[p][s] = as_bf16x8(ldg<uint4>(wrow + 8 * s));
     } else {
 #pragma unroll
       for (int s = 0; s < KS; s += 4) {
-        float4 v = ldg<float4>(wrow + s);
-        wf[bi][s] = v.x, wf[bi][s + 1] = v.y, wf[bi][s + 2] = v.z, wf[bi][s + 3] = v.w;
+        const float4 v = ldg<float4>(wrow + s);
+        wf[p][s] = v.x, wf[p][s + 1] = v.y, wf[p][s + 2] = v.z, wf[p][s + 3] = v.w;
       }
     }
   }
-  __shared__ float vec_s[3][D];  // gamma, beta, gate bias (fp32)
-  __shared__ __align__(16) T wz_s[16 * PITCH];  // pair-bias weight block (rows >= h are zero)
-  for (int e = tid; e < 16 * D; e += NT) wz_s[(e / D) * PITCH + e % D] = W[(size_t)4 * D * D + e];
   for (int c = tid; c < 3 * D; c += NT) {
     const int which = c / D, cc = c - which * D;
     const void *src = which == 0 ? a.gamma : (which == 1 ? a.beta : a.bg);
     vec_s[which][cc] = BF ? bf2f(reinterpret_cast<const uint16_t *>(src)[cc]) : reinterpret_cast<const float *>(src)[cc];
   }
-  __syncthreads();
+  for (int e = tid; e < 16 * D; e += NT) wz_s[(e / D) * PITCH + e % D] = W[(size_t)4 * D * D + e];
+  lds_barrier();
 
   // ---- LayerNorm thread mapping: TPP threads per position, EPT channels each
   const int lpos = tid / TPP, lpart = tid % TPP;
@@ -139,29 +140,31 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
 #pragma unroll
     for (int m = 1; m < TPP; m <<= 1) q = xor_sum(q, m);
     const float rstd = rsqrtf(q * (1.0f / D) + a.eps);
-    const bool valid = j < N;
+    const float scale = (j < N) ? rstd : 0.f;  // padding positions (j >= N) become zero rows
+    const float bmul = (j < N) ? 1.f : 0.f;
     const float *gam = &vec_s[0][lpart * EPT];
     const float *bet = &vec_s[1][lpart * EPT];
     T *dst = &xs[buf][lpos * PITCH + lpart * EPT];
     if constexpr (BF) {
-      uint32_t packed[EPT / 2];
 #pragma unroll
-      for (int e = 0; e < EPT; e += 2) {
-        const float x0 = valid ? (v[e] - mean) * rstd * gam[e] + bet[e] : 0.f;
-        const float x1 = valid ? (v[e + 1] - mean) * rstd * gam[e + 1] + bet[e + 1] : 0.f;
-        packed[e / 2] = pack_bf16x2(x0, x1);
+      for (int e = 0; e < EPT; e += 8) {
+        uint32_t p4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = e + 2 * u;
+          p4[u] = pack_bf16x2((v[c] - mean) * scale * gam[c] + bet[c] * bmul,
+                              (v[c + 1] - mean) * scale * gam[c + 1] + bet[c + 1] * bmul);
+        }
+        *reinterpret_cast<uint4 *>(dst + e) = make_uint4(p4[0], p4[1], p4[2], p4[3]);
       }
-#pragma unroll
-      for (int e = 0; e < EPT / 2; e += 4)
-        *reinterpret_cast<uint4 *>(dst + 2 * e) = make_uint4(packed[e], packed[e + 1], packed[e + 2], packed[e + 3]);
     } else {
 #pragma unroll
       for (int e = 0; e < EPT; e += 4) {
         float4 o;
-        o.x = valid ? (v[e] - mean) * rstd * gam[e] + bet[e] : 0.f;
-        o.y = valid ? (v[e + 1] - mean) * rstd * gam[e + 1] + bet[e + 1] : 0.f;
-        o.z = valid ? (v[e + 2] - mean) * rstd * gam[e + 2] + bet[e + 2] : 0.f;
-        o.w = valid ? (v[e + 3] - mean) * rstd * gam[e + 3] + bet[e + 3] : 0.f;
+        o.x = (v[e] - mean) * scale * gam[e] + bet[e] * bmul;
+        o.y = (v[e + 1] - mean) * scale * gam[e + 1] + bet[e + 1] * bmul;
+        o.z = (v[e + 2] - mean) * scale * gam[e + 2] + bet[e + 2] * bmul;
+        o.w = (v[e + 3] - mean) * scale * gam[e + 3] + bet[e + 3] * bmul;
         *reinterpret_cast<float4 *>(dst + e) = o;
       }
     }
@@ -174,165 +177,156 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
       stg<float4>(dst, make_float4(v0, v1, v2, v3));
   };
 
-  // acc[bi] = block bi of this wave's projection for one 16-position block
-  auto gemm = [&](auto is_v, const T *xrow, f32x4 (&acc)[BPW]) {
-#pragma unroll
-    for (int bi = 0; bi < BPW; ++bi) acc[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int KC = BF ? 1 : 4;
-#pragma unroll
-    for (int s0 = 0; s0 < KS; s0 += KC) {
-      Frag xf[KC];
-      if constexpr (BF) {
-        xf[0] = as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s0));
-      } else {
-        const float4 v = *reinterpret_cast<const float4 *>(xrow + s0);
-        xf[0] = v.x, xf[1] = v.y, xf[2] = v.z, xf[3] = v.w;
-      }
-#pragma unroll
-      for (int s = 0; s < KC; ++s)
-#pragma unroll
-        for (int bi = 0; bi < BPW; ++bi) {
-          if constexpr (decltype(is_v)::value)
-            acc[bi] = mfma(xf[s], wf[bi][s0 + s], acc[bi]);  // rows = positions
-          else
-            acc[bi] = mfma(wf[bi][s0 + s], xf[s], acc[bi]);  // rows = channels
-        }
-    }
-  };
-  // pair-bias block (weights in LDS): rows = positions, column = head
-  auto gemm_z = [&](const T *xrow) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const T *zrow = &wz_s[r16 * PITCH + g * KQ];
-    constexpr int KC = BF ? 1 : 4;
-#pragma unroll
-    for (int s0 = 0; s0 < KS; s0 += KC) {
-      if constexpr (BF) {
-        acc = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s0)),
-                   as_bf16x8(*reinterpret_cast<const uint4 *>(zrow + 8 * s0)), acc);
-      } else {
-        const float4 v = *reinterpret_cast<const float4 *>(xrow + s0);
-        const float4 u = *reinterpret_cast<const float4 *>(zrow + s0);
-        acc = mfma(v.x, u.x, acc);
-        acc = mfma(v.y, u.y, acc);
-        acc = mfma(v.z, u.z, acc);
-        acc = mfma(v.w, u.w, acc);
-      }
-    }
-    return acc;
-  };
-
-  auto compute_tile = [&](int tile, int buf) {
+  // One tile with this wave's projections starting at TYPE0 (compile time).
+  auto compute_tile = [&](auto type0_c, int tile, int buf) {
+    constexpr int TYPE0 = decltype(type0_c)::value;
     const int bi_row = tile / nch, chunk = tile - bi_row * nch;
     const int b = bi_row / N, i = bi_row - b * N;
     const int j0 = chunk * TILE;
-    float kn_run[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) kn_run[hh] = 0.f;
+    float kn_run = 0.f;  // running max over positions of |k|^2 over this channel block
     float z_run = -INFINITY;
+    const bool zwave = (wave == NW - 1);
 
 #pragma unroll 1
     for (int pb = 0; pb < TILE / 16; ++pb) {
-      // GEMM over K = D; lane (g, r16) reads position pb*16+r16, K-range
-      // [g*KQ, g*KQ+KQ) of the LDS activations. v tiles swap the operand roles
-      // so that their rows are positions (transposed store per head).
-      f32x4 acc[BPW];
+      // x fragments: lane (g, r16) = position pb*16 + r16, K-range [g*KQ, g*KQ+KQ)
       const T *xrow = &xs[buf][(pb * 16 + r16) * PITCH + g * KQ];
-      if (ptype == 2)
-        gemm(std::true_type{}, xrow, acc);
-      else
-        gemm(std::false_type{}, xrow, acc);
-      const int jcol = j0 + pb * 16 + r16;  // position of this lane's column (q/k/gate tiles)
-      float ksq = 0.f;
+      f32x4 acc[TPW];
 #pragma unroll
-      for (int bi = 0; bi < BPW; ++bi) {
-        const int cb = cb0 + bi;
-        if (ptype == 2) {
-          // v^T per head: lane (g, r16) holds channel r16 of positions 4g..4g+3
-          const int c = cb * 16 + r16, th = c / DH, uu = c - th * DH;
-          T *dst = reinterpret_cast<T *>(a.vt) + ((((size_t)bi_row * H + th) * DH + uu) * Np + j0 + pb * 16 + 4 * g);
-          store4(dst, acc[bi][0], acc[bi][1], acc[bi][2], acc[bi][3]);
+      for (int p = 0; p < TPW; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+      constexpr int KC = BF ? 1 : 4;
+#pragma unroll
+      for (int s0 = 0; s0 < KS; s0 += KC) {
+        Frag xf[KC];
+        if constexpr (BF) {
+          xf[0] = as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s0));
         } else {
-          float v0 = acc[bi][0], v1 = acc[bi][1], v2 = acc[bi][2], v3 = acc[bi][3];
-          T *base;
-          if (ptype == 0) {
-            v0 *= a.qscale, v1 *= a.qscale, v2 *= a.qscale, v3 *= a.qscale;
-            base = reinterpret_cast<T *>(a.q);
-          } else if (ptype == 1) {
-            base = reinterpret_cast<T *>(a.k);
-            ksq += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
-            if (DH == 16 || (bi & 1)) {
-              const float n2 = group4_sum(ksq);
-              const int hh = (DH == 16) ? bi : (bi >> 1);
-              kn_run[hh] = fmaxf(kn_run[hh], n2);
-              ksq = 0.f;
-            }
-          } else {
-            const float4 bgv = *reinterpret_cast<const float4 *>(&vec_s[2][cb * 16 + 4 * g]);
-            v0 = fast_rcp(1.f + fast_exp2(-(v0 + bgv.x) * kLog2e));
-            v1 = fast_rcp(1.f + fast_exp2(-(v1 + bgv.y) * kLog2e));
-            v2 = fast_rcp(1.f + fast_exp2(-(v2 + bgv.z) * kLog2e));
-            v3 = fast_rcp(1.f + fast_exp2(-(v3 + bgv.w) * kLog2e));
-            base = reinterpret_cast<T *>(a.g);
+          const float4 v = *reinterpret_cast<const float4 *>(xrow + s0);
+          xf[0] = v.x, xf[1] = v.y, xf[2] = v.z, xf[3] = v.w;
+        }
+#pragma unroll
+        for (int s = 0; s < KC; ++s)
+#pragma unroll
+          for (int p = 0; p < TPW; ++p) {
+            if (TYPE0 + p == 2)
+              acc[p] = mfma(xf[s], wf[p][s0 + s], acc[p]);  // v: rows = positions
+            else
+              acc[p] = mfma(wf[p][s0 + s], xf[s], acc[p]);  // q, k, gate: rows = channels
           }
-          T *dst = base + ((((size_t)bi_row * NB + cb) * Np + jcol) * 16 + 4 * g);
-          store4(dst, v0, v1, v2, v3);
+      }
+
+      const int jcol = j0 + pb * 16 + r16;  // position of this lane's column (q/k/gate tiles)
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) {
+        const int type = TYPE0 + p;
+        const f32x4 c = acc[p];
+        if (type == 2) {
+          // v^T per head: lane (g, r16) holds channel r16 of positions 4g..4g+3
+          const int ch = cb * 16 + r16, th = ch / DH, uu = ch - th * DH;
+          T *dst = reinterpret_cast<T *>(a.vt) + ((((size_t)bi_row * H + th) * DH + uu) * Np + j0 + pb * 16 + 4 * g);
+          store4(dst, c[0], c[1], c[2], c[3]);
+        } else if (type == 0) {
+          T *dst = reinterpret_cast<T *>(a.q) + ((((size_t)bi_row * NB + cb) * Np + jcol) * 16 + 4 * g);
+          store4(dst, c[0] * a.qscale, c[1] * a.qscale, c[2] * a.qscale, c[3] * a.qscale);
+        } else if (type == 1) {
+          T *dst = reinterpret_cast<T *>(a.k) + ((((size_t)bi_row * NB + cb) * Np + jcol) * 16 + 4 * g);
+          store4(dst, c[0], c[1], c[2], c[3]);
+          kn_run = fmaxf(kn_run, group4_sum(c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3]));
+        } else {
+          const float4 bgv = *reinterpret_cast<const float4 *>(&vec_s[2][cb * 16 + 4 * g]);
+          T *dst = reinterpret_cast<T *>(a.g) + ((((size_t)bi_row * NB + cb) * Np + jcol) * 16 + 4 * g);
+          store4(dst, fast_rcp(1.f + fast_exp2(-(c[0] + bgv.x) * kLog2e)),
+                 fast_rcp(1.f + fast_exp2(-(c[1] + bgv.y) * kLog2e)),
+                 fast_rcp(1.f + fast_exp2(-(c[2] + bgv.z) * kLog2e)),
+                 fast_rcp(1.f + fast_exp2(-(c[3] + bgv.w) * kLog2e)));
         }
       }
-      if (wave == 0) {
-        const f32x4 accz = gemm_z(xrow);
-        if (r16 < H) {
-        const int jb = j0 + pb * 16 + 4 * g;
-        float z[4];
+      if (zwave) {
+        // pair bias: rows = positions, column r16 = head
+        const T *zrow = &wz_s[r16 * PITCH + g * KQ];
+        f32x4 accz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool keep = mask_s[buf][pb * 16 + 4 * g + r] != 0;
-          z[r] = keep ? accz[r] * kLog2e : -INFINITY;
-          z_run = fmaxf(z_run, z[r]);
+        for (int s0 = 0; s0 < KS; s0 += (BF ? 1 : 4)) {
+          if constexpr (BF) {
+            accz = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s0)),
+                        as_bf16x8(*reinterpret_cast<const uint4 *>(zrow + 8 * s0)), accz);
+          } else {
+            const float4 v = *reinterpret_cast<const float4 *>(xrow + s0);
+            const float4 u = *reinterpret_cast<const float4 *>(zrow + s0);
+            accz = mfma(v.x, u.x, accz);
+            accz = mfma(v.y, u.y, accz);
+            accz = mfma(v.z, u.z, accz);
+            accz = mfma(v.w, u.w, accz);
+          }
         }
-        float *dst = a.zm + (((size_t)(b * H + r16) * N + i) * Np + jb);
-        stg<float4>(dst, make_float4(z[0], z[1], z[2], z[3]));
+        if (r16 < H) {
+          const int jb = j0 + pb * 16 + 4 * g;
+          float z[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool keep = mask_s[buf][pb * 16 + 4 * g + r] != 0;
+            z[r] = keep ? accz[r] * kLog2e : -INFINITY;
+            z_run = fmaxf(z_run, z[r]);
+          }
+          float *dst = a.zm + (((size_t)(b * H + r16) * N + i) * Np + jb);
+          stg<float4>(dst, make_float4(z[0], z[1], z[2], z[3]));
         }
       }
     }
     // per-chunk maxima
-    if (ptype == 1) {
-#pragma unroll
-      for (int hh = 0; hh < HPW; ++hh) {
-        const float m = row16_max(kn_run[hh]);
-        const int th = (cb0 * 16) / DH + hh;
-        if (lane == 0) a.kmax[((size_t)bi_row * H + th) * nch + chunk] = m;
-      }
+    if (TYPE0 <= 1 && TYPE0 + TPW > 1) {
+      const float m = row16_max(kn_run);
+      if (lane == 0) a.kmax[((size_t)bi_row * NB + cb) * nch + chunk] = m;
     }
-    if (wave == 0) {
+    if (zwave) {
       const float m = group4_max(z_run);
       if (g == 0 && r16 < H) a.zmax[((size_t)(b * H + r16) * N + i) * nch + chunk] = m;
     }
   };
 
+  auto compute = [&](int tile, int buf) {
+    if constexpr (TPW == 4) {
+      compute_tile(std::integral_constant<int, 0>{}, tile, buf);
+    } else {
+      if (type0 == 0)
+        compute_tile(std::integral_constant<int, 0>{}, tile, buf);
+      else
+        compute_tile(std::integral_constant<int, 2>{}, tile, buf);
+    }
+  };
+
   int tile = blockIdx.x;
   if (tile >= a.tiles) return;
-  uint4 pre[NV];
-  uint32_t mpre;
-  int buf = 0;
+  const int G = gridDim.x;
   if constexpr (BF) {
-    // bf16 is HBM-bound: prefetch the next tile's pair_repr and mask while this one computes
-    load_tile(tile, pre, mpre);
+    // bf16 is HBM-bound: pair_repr and the mask are prefetched two tiles ahead
+    uint4 preA[NV], preB[NV];
+    uint32_t mA, mB = 0;
+    load_tile(tile, preA, mA);
+    if (tile + G < a.tiles) load_tile(tile + G, preB, mB);
 #pragma unroll 1
-    for (; tile < a.tiles; tile += gridDim.x) {
-      layer_norm_to_lds(tile, pre, mpre, buf);
-      __syncthreads();
-      if (tile + (int)gridDim.x < a.tiles) load_tile(tile + gridDim.x, pre, mpre);
-      compute_tile(tile, buf);
-      buf ^= 1;
+    for (; tile < a.tiles; tile += 2 * G) {
+      layer_norm_to_lds(tile, preA, mA, 0);
+      lds_barrier();
+      if (tile + 2 * G < a.tiles) load_tile(tile + 2 * G, preA, mA);
+      compute(tile, 0);
+      if (tile + G >= a.tiles) break;
+      layer_norm_to_lds(tile + G, preB, mB, 1);
+      lds_barrier();
+      if (tile + 3 * G < a.tiles) load_tile(tile + 3 * G, preB, mB);
+      compute(tile + G, 1);
     }
   } else {
     // fp32 is matrix-core-bound and short of registers: no cross-tile prefetch
+    uint4 pre[NV];
+    uint32_t mpre;
+    int buf = 0;
 #pragma unroll 1
-    for (; tile < a.tiles; tile += gridDim.x) {
+    for (; tile < a.tiles; tile += G) {
       load_tile(tile, pre, mpre);
       layer_norm_to_lds(tile, pre, mpre, buf);
-      __syncthreads();
-      compute_tile(tile, buf);
+      lds_barrier();
+      compute(tile, buf);
       buf ^= 1;
     }
   }
@@ -360,6 +354,28 @@ hipError_t launch_k1(int dtype, int D, int dh, const K1Args &a, int grid, hipStr
   }
 #undef TRI_K1_CASE
   return hipErrorInvalidValue;
+}
+
+int k1_blocks_per_cu(int dtype, int D, int dh) {
+  int n = 0;
+#define TRI_K1_OCC(TT, DD, HH)                                                                                    \
+  if (D == DD && dh == HH &&                                                                                      \
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k1_ln_proj<TT, DD, HH>, K1Shape<TT, DD>::THREADS, 0) !=    \
+          hipSuccess)                                                                                             \
+    n = 1;
+  if (dtype == TRI_ATTN_BF16) {
+    TRI_K1_OCC(bf16_t, 128, 16)
+    TRI_K1_OCC(bf16_t, 128, 32)
+    TRI_K1_OCC(bf16_t, 64, 16)
+    TRI_K1_OCC(bf16_t, 64, 32)
+  } else {
+    TRI_K1_OCC(float, 128, 16)
+    TRI_K1_OCC(float, 128, 32)
+    TRI_K1_OCC(float, 64, 16)
+    TRI_K1_OCC(float, 64, 32)
+  }
+#undef TRI_K1_OCC
+  return n > 0 ? n : 1;
 }
 
 bool supported(int D, int dh) { return (D == 64 || D == 128) && (dh == 16 || dh == 32); }

@@ -112,10 +112,16 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
 #pragma unroll
   for (int i = 0; i < IG; ++i) {
     rows[i] = min(i0 + i, N - 1);
-    const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * H + t) * nch;
-    float m = 0.f;
-    for (int c = 0; c < nch; ++c) m = fmaxf(m, kp[c]);
-    kn2[i] = m;
+    // |k|^2 <= sum over the head's 16-channel blocks of each block's chunk maxima
+    float m2 = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
+      float m = 0.f;
+      for (int c = 0; c < nch; ++c) m = fmaxf(m, kp[c]);
+      m2 += m;
+    }
+    kn2[i] = m2;
   }
 
   // ---- per query column: bias+mask maximum, last live key chunk
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- output projection: y^T[c][pos] = Wo[c] . go[pos] + bo[c]
   const T *Wo = reinterpret_cast<const T *>(a.Wo);

@@ -36,7 +36,7 @@ Layout make_layout(int B, int N, int D, int h, int elem) {
   L.g = off, off = align256(off + proj);
   L.zm = off, off = align256(off + (size_t)B * h * N * L.Np * 4);
   L.zmax = off, off = align256(off + (size_t)B * h * N * L.nchunk * 4);
-  L.kmax = off, off = align256(off + (size_t)B * N * h * L.nchunk * 4);
+  L.kmax = off, off = align256(off + (size_t)B * N * (D / 16) * L.nchunk * 4);
   L.total = off;
   return L;
 }
@@ -100,7 +100,7 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
     delete t;
     return TRI_ATTN_ERR_HIP;
   }
-  t->k1_grid = cus * (t->elem == 2 ? 2 : 1);
+  t->k1_grid = cus * k1_blocks_per_cu(cfg->dtype, t->D, t->dh);
 
   t->wpack_bytes = (size_t)(4 * D + 16) * D * e;
   t->vecs_bytes = (size_t)4 * D * e + (size_t)D * D * e;

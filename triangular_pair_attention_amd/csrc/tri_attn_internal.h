@@ -47,6 +47,7 @@ struct K2Args {
 hipError_t launch_k1(int dtype, int D, int dh, const K1Args &a, int grid, hipStream_t s);
 hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, hipStream_t s);
 int k2_items(int D, int dh, int B, int N);
+int k1_blocks_per_cu(int dtype, int D, int dh);  // resident workgroups of kernel 1 per CU
 bool supported(int D, int dh);
 
 }  // namespace tpa
