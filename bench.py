@@ -3,15 +3,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config k]
 
-A step is one tri_attn_forward (kernel 1: LayerNorm + fused projection,
-kernel 2: attention + gate + output projection) over one batch of seeded
-synthetic inputs already resident in HBM. Prints ONE JSON line.
+A step is one tri_attn_forward (kernel 1: LayerNorm + fused projection;
+kernel 2: attention + gate; kernel 3: output projection) over one batch of
+seeded synthetic inputs already resident in HBM. Prints ONE JSON line.
 
 The default workload is B=1, N=128, D=128, h=4 (d=32), float32, Bernoulli(0.9)
 mask with the diagonal set. `--config k` selects another of the five
 workloads (1..5). Each kernel is also timed alone (stage entry points
-tri_attn_project / tri_attn_attend) with HIP events on the stream it runs on;
-the slower one is reported in `roofline`.
+tri_attn_project / tri_attn_attend / tri_attn_output) with HIP events on the
+stream it runs on; the slowest one is reported in `roofline`.
 
 `--copy-probe` runs only a plain device copy of a known size (the reference
 for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
@@ -37,6 +37,7 @@ PEAK = {  # MI355X published dense peaks
 KERNEL_SOURCES = {
     "k1_ln_proj": "triangular_pair_attention_amd/csrc/k1_ln_proj.hip",
     "k2_attention": "triangular_pair_attention_amd/csrc/k2_attention.hip",
+    "k3_out_proj": "triangular_pair_attention_amd/csrc/k3_out_proj.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -54,13 +55,29 @@ def work_model(w):
     B, N, D, h = w.B, w.N, w.D, w.h
     s = 2 if w.dtype == "bf16" else 4
     P = B * N * N
-    f1 = 2 * P * D * (4 * D + h)
-    f2 = 4 * B * N ** 3 * D + 2 * P * D * D
-    # kernel 1: read pair_repr and mask, write q, k, v, gate (s bytes each) and the fp32 bias+mask tile
-    b1 = P * D * s + P + 4 * P * D * s + 4 * B * h * N * N
-    # kernel 2: read q, k, v, gate and the bias+mask tile once, write y
-    b2 = 4 * P * D * s + 4 * B * h * N * N + P * D * s
-    return {"positions": P, "k1_flops": f1, "k2_flops": f2, "k1_bytes": b1, "k2_bytes": b2}
+    return {
+        "positions": P,
+        # LayerNorm + projection: read pair_repr and mask, write q, k, v, gate and the fp32 bias+mask tile
+        "k1_ln_proj": {"flops": 2 * P * D * (4 * D + h), "bytes": P * D * s + P + 4 * P * D * s + 4 * B * h * N * N},
+        # attention: q.k and p.v; read q, k, v, gate and the bias tile once, write g*o
+        "k2_attention": {"flops": 4 * B * N ** 3 * D, "bytes": 4 * P * D * s + 4 * B * h * N * N + P * D * s},
+        # output projection: read g*o, write y
+        "k3_out_proj": {"flops": 2 * P * D * D, "bytes": 2 * P * D * s},
+    }
+
+
+def roofline_of(kernel, w, m, ms):
+    """The bound of one kernel: HBM where its arithmetic intensity is below the
+    ridge of its dtype's matrix-core peak, else the matrix cores."""
+    mfma = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
+    ridge = mfma * 1e12 / (PEAK["hbm_GBps"] * 1e9)
+    fl, by = m[kernel]["flops"], m[kernel]["bytes"]
+    if kernel != "k2_attention" and fl / by < ridge:
+        r = {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK["hbm_GBps"], "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": mfma, "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    return r
 
 
 def stored_traffic(workload: str, kernel: str):
@@ -166,7 +183,10 @@ def main():
         B.tri_attn_project(h, P, M, w.B, w.N, ws, nws, stream)
 
     def k2():
-        B.tri_attn_attend(h, out, w.B, w.N, ws, nws, stream)
+        B.tri_attn_attend(h, w.B, w.N, ws, nws, stream)
+
+    def k3():
+        B.tri_attn_output(h, out, w.B, w.N, ws, nws, stream)
 
     def timed(fn, steps):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -188,30 +208,27 @@ def main():
     wall = time.perf_counter() - t0
     ms_fwd = max(ms_fwd_ev, 0.0)
     # each kernel alone, same stream, for the roofline
+    # (repeated attention calls consume the gate they overwrite: same work, other values)
     for _ in range(5):
         k1()
         k2()
+        k3()
     ms_k1 = timed(k1, args.steps)
     ms_k2 = timed(k2, args.steps)
+    ms_k3 = timed(k3, args.steps)
     torch.cuda.synchronize()
     B.tri_attn_destroy(h)
 
     m = work_model(w)
     pos_per_s = m["positions"] / (ms_fwd * 1e-3)
-    tflops = (m["k1_flops"] + m["k2_flops"]) / (ms_fwd * 1e-3) / 1e12
-    dom = "k1_ln_proj" if ms_k1 >= ms_k2 else "k2_attention"
-    ms_dom = ms_k1 if dom == "k1_ln_proj" else ms_k2
-    if dom == "k1_ln_proj" and w.dtype == "bf16":
-        roof = {"bound": "hbm", "achieved": m["k1_bytes"] / (ms_dom * 1e-3) / 1e9, "peak": PEAK["hbm_GBps"],
-                "unit": "GB/s"}
-    else:
-        fl = m["k1_flops"] if dom == "k1_ln_proj" else m["k2_flops"]
-        peak = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
-        roof = {"bound": "mfma", "achieved": fl / (ms_dom * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    total_flops = sum(m[k]["flops"] for k in KERNEL_SOURCES)
+    tflops = total_flops / (ms_fwd * 1e-3) / 1e12
+    ms_k = {"k1_ln_proj": ms_k1, "k2_attention": ms_k2, "k3_out_proj": ms_k3}
+    dom = max(ms_k, key=ms_k.get)
+    roof = roofline_of(dom, w, m, ms_k[dom])
     roof["traffic"] = stored_traffic(w.name, dom)
     roof["kernel"] = dom
-    roof["kernel_ms"] = ms_dom
+    roof["kernel_ms"] = ms_k[dom]
 
     result = {
         "metric": METRIC,
@@ -229,10 +246,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "h": w.h, "d": w.d,
                    "mask": list(w.mask), "seed": w.seed, "parallelism": "none (1 GPU)"},
         "tflops": tflops,
-        "kernels_ms": {"k1_ln_proj": ms_k1, "k2_attention": ms_k2},
-        "k1_hbm_GBps": m["k1_bytes"] / (ms_k1 * 1e-3) / 1e9,
-        "k2_tflops": m["k2_flops"] / (ms_k2 * 1e-3) / 1e12,
-        "k1_tflops": m["k1_flops"] / (ms_k1 * 1e-3) / 1e12,
+        "kernels_ms": ms_k,
+        "kernels_roofline": {k: roofline_of(k, w, m, v) for k, v in ms_k.items()},
         "wall_s_timed": wall,
         "roofline": roof,
     }

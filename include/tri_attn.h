@@ -113,8 +113,8 @@ const char *tri_attn_strerror(int code);
 /* Offsets are in bytes from the workspace start; Np = N rounded up to 64.
  *   q, k, g : [B][N][D/16][Np][16] config dtype. Channel c of query column j
  *             of row (b, i) is at [b][i][c/16][j][c%16]. q is pre-scaled by
- *             log2(e)/sqrt(d); g is after the sigmoid. Columns j >= N hold
- *             q = k = 0.
+ *             log2(e)/sqrt(d); g is after the sigmoid (the attention stage
+ *             overwrites it with g * o). Columns j >= N hold q = k = 0.
  *   vt      : [B][N][h][d][Np] config dtype (value, transposed per head),
  *             zero for j >= N.
  *   zm      : [B][h][N][Np] float32: z[b,t,j,k] * log2(e) where M[b,j,k] != 0
@@ -134,10 +134,16 @@ int tri_attn_get_workspace_layout(tri_attn_t h, int B, int N, tri_attn_workspace
 int tri_attn_project(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, int B, int N,
                      void *workspace, size_t ws_bytes, void *stream);
 
-/* Run only the attention kernel on a workspace that tri_attn_project (or a
- * forward) filled for the same handle, B and N; writes out [B, N, N, D].
- * tri_attn_project followed by tri_attn_attend equals tri_attn_forward. */
-int tri_attn_attend(tri_attn_t h, void *out, int B, int N, void *workspace, size_t ws_bytes, void *stream);
+/* Run only the attention kernel on a workspace that tri_attn_project filled
+ * for the same handle, B and N: it writes g * o over the gate region. The
+ * gate is consumed, so run tri_attn_project again before another
+ * tri_attn_attend. */
+int tri_attn_attend(tri_attn_t h, int B, int N, void *workspace, size_t ws_bytes, void *stream);
+
+/* Run only the output-projection kernel: out [B, N, N, D] = Wo (g * o) + bo
+ * from the gate region left by tri_attn_attend. tri_attn_project,
+ * tri_attn_attend, tri_attn_output in turn equal tri_attn_forward. */
+int tri_attn_output(tri_attn_t h, void *out, int B, int N, void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library 
 def test_header_declares_the_abi():
     names = B.declared_functions()
     for n in ("tri_attn_create", "tri_attn_workspace_size", "tri_attn_forward", "tri_attn_destroy",
-              "tri_attn_strerror", "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend"):
+              "tri_attn_strerror", "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend",
+              "tri_attn_output"):
         assert n in names
 
 
@@ -89,7 +90,8 @@ def test_null_handle_paths():
     assert B.raw_call("tri_attn_workspace_size", None, 1, 8, ctypes.byref(n)) == B.TRI_ATTN_ERR_INVALID_ARG
     assert B.raw_call("tri_attn_forward", None, 1, 1, 1, 1, 8, 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
     assert B.raw_call("tri_attn_project", None, 1, 1, 1, 8, 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
-    assert B.raw_call("tri_attn_attend", None, 1, 1, 8, 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
+    assert B.raw_call("tri_attn_attend", None, 1, 8, 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
+    assert B.raw_call("tri_attn_output", None, 1, 1, 8, 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
     lay = B.tri_attn_workspace_layout()
     assert B.raw_call("tri_attn_get_workspace_layout", None, 1, 8, ctypes.byref(lay)) == B.TRI_ATTN_ERR_INVALID_ARG
     assert B.raw_call("tri_attn_destroy", None) == B.TRI_ATTN_OK

@@ -220,19 +220,22 @@ def test_empty_and_error_paths():
         g.close()
 
 
-def test_project_then_attend_equals_forward():
+def test_stages_equal_forward():
+    """project, attend, output in turn give the forward's exact bits."""
     inp = make_inputs(WORKLOADS[1])
-    log("project + attend")
+    log("project + attend + output")
     g = Gpu(inp)
     try:
         a = g.forward().clone()
         g.project()
         b = torch.empty_like(g.P)
-        B.tri_attn_attend(g.handle, b, g.B, g.N, g.ws, g.ws_bytes, torch.cuda.current_stream())
+        st = torch.cuda.current_stream()
+        B.tri_attn_attend(g.handle, g.B, g.N, g.ws, g.ws_bytes, st)
+        B.tri_attn_output(g.handle, b, g.B, g.N, g.ws, g.ws_bytes, st)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
         with pytest.raises(B.TriAttnError) as e:
-            B.tri_attn_attend(g.handle, 0, g.B, g.N, g.ws, g.ws_bytes)
+            B.tri_attn_output(g.handle, 0, g.B, g.N, g.ws, g.ws_bytes)
         assert e.value.code == B.TRI_ATTN_ERR_INVALID_ARG
     finally:
         g.close()

@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     tri_attn_destroy,
     tri_attn_forward,
     tri_attn_get_workspace_layout,
+    tri_attn_output,
     tri_attn_project,
     tri_attn_strerror,
     tri_attn_workspace_size,

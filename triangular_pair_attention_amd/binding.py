@@ -79,9 +79,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tri_attn_strerror.restype = ctypes.c_char_p
     lib.tri_attn_get_workspace_layout.argtypes = [vp, i, i, ctypes.POINTER(tri_attn_workspace_layout)]
     lib.tri_attn_project.argtypes = [vp, vp, vp, i, i, vp, sz, vp]
-    lib.tri_attn_attend.argtypes = [vp, vp, i, i, vp, sz, vp]
+    lib.tri_attn_attend.argtypes = [vp, i, i, vp, sz, vp]
+    lib.tri_attn_output.argtypes = [vp, vp, i, i, vp, sz, vp]
     for name in ("tri_attn_create", "tri_attn_workspace_size", "tri_attn_forward", "tri_attn_destroy",
-                 "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend"):
+                 "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend",
+                 "tri_attn_output"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -163,9 +165,14 @@ def tri_attn_project(handle: int, pair_repr, pair_mask, B: int, N: int, workspac
                                            ws_bytes, _stream(stream)), "tri_attn_project")
 
 
-def tri_attn_attend(handle: int, out, B: int, N: int, workspace, ws_bytes: int, stream=None) -> None:
-    _check(load_library().tri_attn_attend(handle, _ptr(out), B, N, _ptr(workspace), ws_bytes, _stream(stream)),
+def tri_attn_attend(handle: int, B: int, N: int, workspace, ws_bytes: int, stream=None) -> None:
+    _check(load_library().tri_attn_attend(handle, B, N, _ptr(workspace), ws_bytes, _stream(stream)),
            "tri_attn_attend")
+
+
+def tri_attn_output(handle: int, out, B: int, N: int, workspace, ws_bytes: int, stream=None) -> None:
+    _check(load_library().tri_attn_output(handle, _ptr(out), B, N, _ptr(workspace), ws_bytes, _stream(stream)),
+           "tri_attn_output")
 
 
 def raw_call(name: str, *args) -> int:

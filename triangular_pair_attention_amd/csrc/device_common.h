@@ -88,6 +88,25 @@ __device__ __forceinline__ float row16_max(float v) {
 // stores, so a prefetch or a burst of output stores stays in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Direct global -> LDS copy, 16 bytes per lane: lane l's bytes land at
+// lds_base + 16*l (lds_base is the same for the whole wave). Issued through
+// inline assembly so that the compiler does not hold later LDS reads of other
+// ring stages behind it; the caller tracks completion with vmcnt_wait (vector
+// memory operations complete in issue order for vmcnt).
+__device__ __forceinline__ void dma16_to_lds(const void *gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base)
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 

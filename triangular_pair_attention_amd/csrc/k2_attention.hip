@@ -1,34 +1,43 @@
-// Kernel 2 of the triangular self-attention forward: per pair row (b, i),
-// attention of the query columns j over the key columns k with the shared
-// pair bias and mask, softmax over k, the value sum, the gate multiply and
-// the output projection (Kimi-K2.6 / l2_p6 transcript: steps 8-18 of its
-// forward listing, its attention and finalize kernels; FW-GLM-5-1 / l2_p6:
-// the fused attention and output kernels).
+// Kernel 2 of the triangular self-attention forward: for one head, rows i of
+// a row block attend over the key columns k of their own row, query columns j
+// of a query block, with the shared pair bias and mask; softmax over k; the
+// value sum; the gate multiply (Kimi-K2.6 / l2_p6 transcript: steps 8-17 of
+// its forward listing and its attention kernel; FW-GLM-5-1 / l2_p6: the
+// fused attention kernel). The output projection is kernel 3.
 //
-// Workgroup = (b, IG rows i, JW*16 query columns j), one wave per head. The
-// (B, N, h, N, N) scores are never stored: each wave streams key tiles.
+// Workgroup = (b, head t, RB rows i, QB query columns j); wave (wr, wq) takes
+// IG rows x JW*16 queries. The (B, N, h, N, N) scores are never stored.
+//
+// Key tiles through LDS. Per key step (KT keys) the workgroup needs k and v
+// of its RB rows and the bias+mask tile zm of its QB query columns. Every
+// piece is a 1 KB block laid out exactly as the consuming lanes read their
+// MFMA fragments (lane l's 16 bytes at 16*l), filled by direct global->LDS
+// loads (each loader lane supplies its own global address). A three-stage
+// ring keeps two steps in flight, with one LDS barrier per step. Each k/v
+// block is read by all WQ waves of its rows and each zm block by all WR waves
+// of its columns, so the L2 traffic per score is shared WQ (WR) ways.
 //
 // Softmax without a running maximum. Per (row i, query j) the kernel fixes
 // the shift m = |q'_j| * max_k |k_k| + max_k zm[j, k] before the key loop
 // (Cauchy-Schwarz: m >= every score of the row, so exp2(s - m) <= 1 and
 // nothing overflows). Softmax is invariant to the shift, so the result is
-// exact up to rounding; the loop then needs no max, no rescaling and no
-// cross-lane traffic. The shift enters the MFMA itself (an extra K-slot with
-// q' = -m, k = 1), and the score tile's accumulator starts from the bias+mask
-// tile zm, so the only VALU work per score is exp2 and the bf16 conversion.
-// The row sum comes out of the MFMA too (a row of ones next to V). If the
-// bound is so loose that a column's sum falls below 2^-64 (only with
-// pathological inputs or the shift_slack test knob), the wave recomputes that
-// column block with the exact maximum (a max pass, then the loop again).
+// exact up to rounding; the loop needs no max, no rescaling and no cross-lane
+// traffic. For bf16 the shift rides in the MFMA (d = 16: a spare contraction
+// slot holds q' = -m against k = 1; d = 32: one more MFMA), the score
+// accumulator starts from the zm tile and the row sum comes from a row of
+// ones in the PV MFMA: the VALU work per score is one exp2 and half a bf16
+// conversion. If a column's sum falls below 2^-64 (only with a pathological
+// bound, or the shift_slack test knob) the wave recomputes with the exact
+// maximum (a max pass, then the loop again).
 //
 // Mask: zm = -inf where masked, so masked keys get weight exactly 0. A query
 // column whose keys are all masked (max zm = -inf) gets the rule of the
 // finite fill value: uniform weights over all N keys, i.e. the mean of v; or
-// NaN when the fill is -inf. Key chunks of 64 that are masked for every query
-// of the wave are skipped.
+// NaN when the fill is -inf. Key chunks of 64 beyond the last live chunk of
+// the workgroup's columns are skipped.
 //
-// Epilogue: o / l, times the gate, into LDS as one [positions][D] tile for
-// all heads; then (gate*o) Wo^T + bo on MFMA with Wo fragments in registers.
+// Output: o / l times the gate, written over the gate in the workspace
+// ([b][i][c/16][j][16]); kernel 3 reads it from there.
 #include "device_common.h"
 #include "tri_attn_internal.h"
 
@@ -38,80 +47,92 @@
 
 namespace tpa {
 
-// Rows i per workgroup (IG) and 16-column query blocks per wave (JW). The bias
-// tile is reused across the IG rows in registers; k and v across the JW*16
-// columns. Workgroups with 4 waves (h = 4) take 2 rows to keep 2 waves per SIMD.
-template <int D, int DH>
+// IG rows x JW 16-query blocks per wave; WR x WQ waves per workgroup.
+template <typename T, int D, int DH>
 struct K2Shape {
-  static constexpr int IG = (D / DH >= 8) ? 4 : 2;
+  static constexpr bool BF = is_bf16<T>::value;
+  static constexpr int IG = (BF && DH == 16) ? 4 : 2;
   static constexpr int JW = 2;
+  static constexpr int WR = (BF && DH == 32) ? 4 : 2;
+  static constexpr int WQ = BF ? ((DH == 16) ? 4 : 2) : ((DH == 16) ? 1 : 2);
+  static constexpr int NW = WR * WQ;
+  static constexpr int RB = WR * IG;       // rows per workgroup
+  static constexpr int QB = WQ * JW * 16;  // query columns per workgroup
+  static constexpr int KBR = (DH == 16) ? 1 : 2;  // k blocks per row and key step
+  static constexpr int VBR = DH / 16;             // v blocks per row and key step
+  static constexpr int ZBJ = BF ? 2 : 1;          // zm blocks per 16 queries and key step
+  static constexpr int NBLK = RB * (KBR + VBR) + (QB / 16) * ZBJ;
+  static constexpr int LPW = (NBLK + NW - 1) / NW;  // loads per wave per step
+  static constexpr int NBLKP = LPW * NW;            // blocks per stage (the last ones pad)
+  static constexpr int NS = 3;                      // ring stages
+  static constexpr size_t LDS = (size_t)NS * NBLKP * 1024;
 };
 
 template <typename T, int D, int DH>
-__global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
+__global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2Args a) {
+  using S = K2Shape<T, D, DH>;
   constexpr bool BF = is_bf16<T>::value;
   constexpr int ES = BF ? 2 : 4;
   constexpr int H = D / DH;
   constexpr int NB = D / 16;
   constexpr int MB = DH / 16;  // 16-row blocks of one head's channels
-  constexpr int IG = K2Shape<D, DH>::IG;
-  constexpr int JW = K2Shape<D, DH>::JW;
-  constexpr int NJ = JW * 16;
-  constexpr int NPOS = IG * NJ;
-  constexpr int PITCH = D + 16 / ES;
-  constexpr int KQ = D / 4;
-  constexpr int KSO = BF ? D / 32 : D / 4;  // output-projection MFMA steps
-  constexpr int NBO = NB / H;               // output channel blocks per wave
-  constexpr int KSTEP = BF ? 32 : 16;       // keys per loop step
-  constexpr int QS = DH / 4;                // fp32: q/k elements per lane
+  constexpr int IG = S::IG, JW = S::JW, WQ = S::WQ, NW = S::NW, RB = S::RB, QB = S::QB;
+  constexpr int KT = BF ? 32 : 16;  // keys per step
+  constexpr int KBR = S::KBR, VBR = S::VBR, ZBJ = S::ZBJ, NBLK = S::NBLK, LPW = S::LPW, NBLKP = S::NBLKP;
+  constexpr int NS = S::NS;
+  constexpr int QS = DH / 4;  // fp32: q/k elements per lane
   using Frag = typename std::conditional<BF, bf16x8, float>::type;
-  static_assert(NBO >= 1, "");
+  static_assert(S::LDS <= 150 * 1024, "stage ring exceeds LDS");
 
-  __shared__ __align__(16) T go[NPOS * PITCH];
+  __shared__ __align__(16) uint4 ring[NS * NBLKP * 64];  // [NS][NBLKP][64] x 16 bytes
 
-  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;  // wave = head
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
+  const int wr = wave / WQ, wq = wave - wr * WQ;
   const int N = a.N, Np = a.Np, nch = a.nchunk;
 
   // ---- work item, XCD-aware. Workgroup w runs on XCD w % 8; each XCD takes a
-  // contiguous range of the linear order below, in which consecutive items form
-  // super-tiles of SI row groups x SJ query ranges (about one item per CU of an
-  // XCD), so the concurrently running workgroups of an XCD share k, v (same
-  // rows) and the bias tile (same query columns) through its L2.
-  const int nJR = (N + NJ - 1) / NJ, nIG = (N + IG - 1) / IG;
+  // contiguous range of the linear order below, in which consecutive items of
+  // one (b, t) form super-tiles of SI row blocks x SJ query blocks, so the
+  // concurrently running workgroups of an XCD share k/v (same rows) and zm
+  // (same query columns) through its L2.
+  const int nRB = (N + RB - 1) / RB, nQB = (N + QB - 1) / QB;
   int lin = blockIdx.x;
   {
     const int w8 = (a.items / 8) * 8;
     if (lin < w8) lin = (lin & 7) * (w8 / 8) + (lin >> 3);
   }
-  const int per_b = nIG * nJR;
-  const int b = lin / per_b;
-  int ig, jr;
+  const int per_bt = nRB * nQB;
+  const int bt = lin / per_bt;
+  const int b = bt / H, t = bt - b * H;
+  int rbk, qbk;
   {
-    const int SJ = nJR < 8 ? nJR : 8;
+    const int SJ = nQB < 8 ? nQB : 8;
     const int SI = 32 / SJ;
-    const int rem = lin - b * per_b;
-    const int igs = (rem / (SI * nJR)) * SI;
-    const int si = min(SI, nIG - igs);
-    const int r2 = rem - igs * nJR;
+    const int rem = lin - bt * per_bt;
+    const int igs = (rem / (SI * nQB)) * SI;
+    const int si = min(SI, nRB - igs);
+    const int r2 = rem - igs * nQB;
     const int jrs = (r2 / (si * SJ)) * SJ;
-    const int sj = min(SJ, nJR - jrs);
+    const int sj = min(SJ, nQB - jrs);
     const int r3 = r2 - jrs * si;
-    ig = igs + r3 / sj;
-    jr = jrs + r3 % sj;
+    rbk = igs + r3 / sj;
+    qbk = jrs + r3 % sj;
   }
-  const int i0 = ig * IG, j0 = jr * NJ;
+  const int i0 = rbk * RB, j0 = qbk * QB;
 
   const T *Q = reinterpret_cast<const T *>(a.q);
   const T *K = reinterpret_cast<const T *>(a.k);
   const T *VT = reinterpret_cast<const T *>(a.vt);
-  const T *G = reinterpret_cast<const T *>(a.g);
+  T *G = reinterpret_cast<T *>(a.g);
+  const float *ZM = a.zm + (size_t)(b * H + t) * N * Np;
 
+  // ---- this wave's rows: bound of |k| over the row's keys
   int rows[IG];
   float kn2[IG];
 #pragma unroll
   for (int i = 0; i < IG; ++i) {
-    rows[i] = min(i0 + i, N - 1);
+    rows[i] = min(i0 + wr * IG + i, N - 1);
     // |k|^2 <= sum over the head's 16-channel blocks of each block's chunk maxima
     float m2 = 0.f;
 #pragma unroll
@@ -124,14 +145,12 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
     kn2[i] = m2;
   }
 
-  // ---- per query column: bias+mask maximum, last live key chunk
+  // ---- this wave's query columns: bias+mask maximum, last live key chunk
   float zmx[JW];
-  int jrow[JW];
   int kend = 0;
 #pragma unroll
   for (int jb = 0; jb < JW; ++jb) {
-    const int j = j0 + jb * 16 + r16;
-    jrow[jb] = min(j, N - 1);
+    const int j = j0 + (wq * JW + jb) * 16 + r16;
     float zx = -INFINITY;
     if (j < N) {
       const float *zp = a.zmax + ((size_t)(b * H + t) * N + j) * nch;
@@ -143,26 +162,37 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
     }
     zmx[jb] = zx;
   }
+  // the workgroup steps through the keys together: its end is the max over all waves
   for (int m = 1; m < 64; m <<= 1) kend = max(kend, __shfl_xor(kend, m, 64));
-  const int kend_keys = __builtin_amdgcn_readfirstlane(kend) * kChunk;
+  __shared__ int kend_s[NW];
+  __shared__ int need_s;
+  if (lane == 0) kend_s[wave] = kend;
+  if (threadIdx.x == 0) need_s = 0;
+  lds_barrier();
+  {
+    int k = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) k = max(k, kend_s[w]);
+    kend = k;
+  }
+  const int nsteps = __builtin_amdgcn_readfirstlane(kend) * kChunk / KT;
 
   // ---- query fragments and their norms; the shift
   // bf16: lane (g, r16) holds q'[j = r16][8g..8g+7] (d = 16: groups 0-1 real, group 2 slot 0 = -m);
   // fp32: lane (g, r16) holds q'[j][g*d/4 .. +d/4).
   Frag qf[IG][JW][BF ? 1 : QS];
-  bf16x4 qsh[IG][JW];  // bf16, d = 32: B operand of the 16x16x16 shift MFMA
+  bf16x8 qsh[IG][JW];  // bf16, d = 32: B operand of the shift MFMA
   float msh[IG][JW];
 #pragma unroll
   for (int i = 0; i < IG; ++i)
 #pragma unroll
     for (int jb = 0; jb < JW; ++jb) {
-      const int j = j0 + jb * 16 + r16;  // < Np
+      const int j = min(j0 + (wq * JW + jb) * 16 + r16, Np - 1);
       const size_t rowbase = (size_t)(b * N + rows[i]) * NB;
+      const int cb = (DH == 16) ? t : 2 * t + (g >> 1);
       float n2 = 0.f;
       if constexpr (BF) {
-        const int cb = (DH == 16) ? t : 2 * t + (g >> 1);
-        const int off = (DH == 16) ? 8 * (g & 1) : 8 * (g & 1);
-        uint4 raw = ldg<uint4>(Q + ((rowbase + cb) * Np + j) * 16 + off);
+        uint4 raw = ldg<uint4>(Q + ((rowbase + cb) * Np + j) * 16 + 8 * (g & 1));
         if (DH == 16 && g >= 2) raw = make_uint4(0, 0, 0, 0);
         qf[i][jb][0] = as_bf16x8(raw);
 #pragma unroll
@@ -171,12 +201,11 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
           n2 += x * x;
         }
       } else {
-        const int cb = (DH == 16) ? t : 2 * t + (g >> 1);
         const int off = (DH == 16) ? 4 * g : 8 * (g & 1);
         const float *src = reinterpret_cast<const float *>(Q) + ((rowbase + cb) * Np + j) * 16 + off;
 #pragma unroll
         for (int s = 0; s < QS; s += 4) {
-          float4 v = ldg<float4>(src + s);
+          const float4 v = ldg<float4>(src + s);
           qf[i][jb][s] = v.x, qf[i][jb][s + 1] = v.y, qf[i][jb][s + 2] = v.z, qf[i][jb][s + 3] = v.w;
         }
 #pragma unroll
@@ -197,17 +226,75 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
           if (DH == 16) {
             if (g == 2) qf[i][jb][0] = bf16x8{nm, z, z, z, z, z, z, z};
           } else {
-            qsh[i][jb] = (g == 0) ? bf16x4{nm, z, z, z} : bf16x4{z, z, z, z};
+            qsh[i][jb] = (g == 0) ? bf16x8{nm, z, z, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
           }
         }
     }
   };
   set_shift(msh);
 
+  // ---- loader: this wave fills blocks wave + NW*l of each stage; each lane
+  // keeps the byte address of its 16 bytes at key step 0 and the per-step stride.
+  const char *src_ptr[LPW];
+  int src_step[LPW];
+#pragma unroll
+  for (int l = 0; l < LPW; ++l) {
+    int blk = wave + NW * l;
+    if (blk >= NBLK) blk = 0;  // padding block: a harmless duplicate of block 0
+    const char *p;
+    int step;
+    if (blk < RB * KBR) {
+      const int r = blk / KBR, kp = blk - r * KBR;
+      const int row = min(i0 + r, N - 1);
+      const size_t rowbase = (size_t)(b * N + row) * NB;
+      if constexpr (BF) {
+        if (DH == 16) {
+          // lanes 0-31: key tile A (keys 8(rho/4)+rho%4), lanes 32-63: tile B (+4); 16 channels in two halves
+          const int half = lane >> 5, gg = (lane >> 4) & 1, rho = lane & 15;
+          const int key = 4 * half + 8 * (rho >> 2) + (rho & 3);
+          p = reinterpret_cast<const char *>(K + ((rowbase + t) * Np + key) * 16 + 8 * gg);
+        } else {
+          const int key = 4 * kp + 8 * (r16 >> 2) + (r16 & 3);
+          p = reinterpret_cast<const char *>(K + ((rowbase + 2 * t + (g >> 1)) * Np + key) * 16 + 8 * (g & 1));
+        }
+      } else {
+        if (DH == 16)
+          p = reinterpret_cast<const char *>(K + ((rowbase + t) * Np + r16) * 16 + 4 * g);
+        else
+          p = reinterpret_cast<const char *>(K + ((rowbase + 2 * t + (g >> 1)) * Np + r16) * 16 + 8 * (g & 1) +
+                                             4 * kp);
+      }
+      step = KT * 16 * ES;
+    } else if (blk < RB * (KBR + VBR)) {
+      const int v = blk - RB * KBR;
+      const int r = v / VBR, mb = v - r * VBR;
+      const int row = min(i0 + r, N - 1);
+      p = reinterpret_cast<const char *>(VT + (((size_t)(b * N + row) * H + t) * DH + mb * 16 + r16) * Np +
+                                         (BF ? 8 : 4) * g);
+      step = KT * ES;
+    } else {
+      const int z = blk - RB * (KBR + VBR);
+      const int jb = z / ZBJ, zp = z - jb * ZBJ;
+      const int jrow = min(j0 + jb * 16 + r16, N - 1);
+      p = reinterpret_cast<const char *>(ZM + (size_t)jrow * Np + (BF ? 8 : 4) * g + 4 * zp);
+      step = KT * 4;
+    }
+    src_ptr[l] = p;
+    src_step[l] = step;
+  }
+  const uint32_t ring_base = lds_addr(ring);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int s) {  // global -> LDS: key step s into stage s % NS
+    const uint32_t stage = ring_base + (uint32_t)((s % NS) * NBLKP * 1024);
+#pragma unroll
+    for (int l = 0; l < LPW; ++l)
+      dma16_to_lds(src_ptr[l] + (size_t)s * src_step[l], stage + (uint32_t)((wave_u + NW * l) * 1024));
+  };
+
   // ---- accumulators
   f32x4 o[IG][JW][MB];
-  f32x4 ol[IG][JW];     // bf16: row 0 = sum of p (ones row)
-  float lacc[IG][JW];   // fp32: per-lane partial sums
+  f32x4 ol[IG][JW];    // bf16: row 0 = sum of p (ones row)
+  float lacc[IG][JW];  // fp32: per-lane partial sums
   auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < IG; ++i)
@@ -220,132 +307,134 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
       }
   };
 
-  const float *ZM = a.zm + (size_t)(b * H + t) * N * Np;
   const __bf16 one = (__bf16)1.f, zero = (__bf16)0.f;
   // constant operands: ones row for the sum, unit key slot for the shift
   const bf16x8 ones8 = (r16 == 0) ? bf16x8{one, one, one, one, one, one, one, one}
                                   : bf16x8{zero, zero, zero, zero, zero, zero, zero, zero};
   const bf16x8 kunit = (g == 2) ? bf16x8{one, zero, zero, zero, zero, zero, zero, zero}
                                 : bf16x8{zero, zero, zero, zero, zero, zero, zero, zero};
-  const bf16x4 kunit4 = (g == 0) ? bf16x4{one, zero, zero, zero} : bf16x4{zero, zero, zero, zero};
+  const bf16x8 kunit0 = (g == 0) ? bf16x8{one, zero, zero, zero, zero, zero, zero, zero}
+                                 : bf16x8{zero, zero, zero, zero, zero, zero, zero, zero};
 
-  // Score tiles of one (row, key step): bf16 -> sA (keys k0+8g+0..3), sB (k0+8g+4..7);
-  // fp32 -> s (keys k0+4g+0..3). Shared by the main loop and the max pass.
-  // The bias+mask tile of the next key step is loaded one step ahead (it is
-  // the operand least likely to be in L2).
-  auto main_loop = [&](bool max_pass, float (&mx)[IG][JW]) {
-    if (kend_keys == 0) return;
-    f32x4 zA[JW], zB[JW];  // bf16: keys k0+8g+0..3 and k0+8g+4..7; fp32: zA = keys k0+4g+0..3
-    auto load_z = [&](int k0, f32x4 (&za)[JW], f32x4 (&zb)[JW]) {
+  // One key step from a stage of the ring (max_pass: only the running maxima).
+  auto step_compute = [&](const uint4 *st, bool max_pass, float (&mx)[IG][JW]) {
+    const uint4 *kblk = st;
+    const uint4 *vblk = st + RB * KBR * 64;
+    const uint4 *zblk = st + RB * (KBR + VBR) * 64;
+    if constexpr (BF) {
+      f32x4 zA[JW], zB[JW];
 #pragma unroll
       for (int jb = 0; jb < JW; ++jb) {
-        if constexpr (BF) {
-          const float *zp = ZM + (size_t)jrow[jb] * Np + k0 + 8 * g;
-          za[jb] = ldg<f32x4>(zp);
-          zb[jb] = ldg<f32x4>(zp + 4);
+        const int q = wq * JW + jb;
+        zA[jb] = __builtin_bit_cast(f32x4, zblk[(q * ZBJ) * 64 + lane]);
+        zB[jb] = __builtin_bit_cast(f32x4, zblk[(q * ZBJ + 1) * 64 + lane]);
+      }
+#pragma unroll
+      for (int i = 0; i < IG; ++i) {
+        const int r = wr * IG + i;
+        bf16x8 kA, kB;
+        if (DH == 16) {
+          kA = kunit, kB = kunit;
+          if (g < 2) {
+            kA = as_bf16x8(kblk[r * 64 + lane]);
+            kB = as_bf16x8(kblk[r * 64 + 32 + lane]);
+          }
         } else {
-          za[jb] = ldg<f32x4>(ZM + (size_t)jrow[jb] * Np + k0 + 4 * g);
+          kA = as_bf16x8(kblk[(2 * r) * 64 + lane]);
+          kB = as_bf16x8(kblk[(2 * r + 1) * 64 + lane]);
+        }
+        bf16x8 vf[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) vf[mb] = as_bf16x8(vblk[(r * VBR + mb) * 64 + lane]);
+#pragma unroll
+        for (int jb = 0; jb < JW; ++jb) {
+          f32x4 sA = mfma(kA, qf[i][jb][0], zA[jb]);
+          f32x4 sB = mfma(kB, qf[i][jb][0], zB[jb]);
+          // The shift MFMA has the same shape as the score MFMA on purpose: a
+          // 16x16x16 MFMA reading, as its accumulator, the result that the
+          // 16x16x32 one wrote a few instructions before gave wrong sums on
+          // gfx950 (only where the two were closest), so only one opcode ever
+          // feeds an accumulator chain here.
+          if (DH == 32 && !max_pass) {
+            sA = mfma(kunit0, qsh[i][jb], sA);
+            sB = mfma(kunit0, qsh[i][jb], sB);
+          }
+          if (max_pass) {
+            float m = mx[i][jb];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(sA[e], sB[e]));
+            mx[i][jb] = m;
+          } else {
+            bf16x8 p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              p[e] = (__bf16)fast_exp2(sA[e]);
+              p[4 + e] = (__bf16)fast_exp2(sB[e]);
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) o[i][jb][mb] = mfma(vf[mb], p, o[i][jb][mb]);
+            ol[i][jb] = mfma(ones8, p, ol[i][jb]);
+          }
         }
       }
-    };
-    load_z(0, zA, zB);
+    } else {
+      f32x4 zA[JW];
+#pragma unroll
+      for (int jb = 0; jb < JW; ++jb) zA[jb] = __builtin_bit_cast(f32x4, zblk[(wq * JW + jb) * 64 + lane]);
+#pragma unroll
+      for (int i = 0; i < IG; ++i) {
+        const int r = wr * IG + i;
+        float kf[QS];
+#pragma unroll
+        for (int kp = 0; kp < KBR; ++kp) {
+          const float4 v = __builtin_bit_cast(float4, kblk[(r * KBR + kp) * 64 + lane]);
+          kf[4 * kp] = v.x, kf[4 * kp + 1] = v.y, kf[4 * kp + 2] = v.z, kf[4 * kp + 3] = v.w;
+        }
+        f32x4 vf[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) vf[mb] = __builtin_bit_cast(f32x4, vblk[(r * VBR + mb) * 64 + lane]);
+#pragma unroll
+        for (int jb = 0; jb < JW; ++jb) {
+          f32x4 s = zA[jb];
+#pragma unroll
+          for (int ss = 0; ss < QS; ++ss) s = mfma(kf[ss], qf[i][jb][ss], s);
+          if (max_pass) {
+            float m = mx[i][jb];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, s[e]);
+            mx[i][jb] = m;
+          } else {
+            float p[4];
+            const float sh = msh[i][jb];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(s[e] - sh);
+            lacc[i][jb] += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb) o[i][jb][mb] = mfma(vf[mb][e], p[e], o[i][jb][mb]);
+          }
+        }
+      }
+    }
+  };
+
+  // The key loop over the ring: stage s is waited for (this wave's own loads
+  // via vmcnt, everyone's via the barrier, which also retires every wave's
+  // reads of the stage that the next issue overwrites), then step s + 2 is
+  // issued and step s computed.
+  auto key_loop = [&](bool max_pass, float (&mx)[IG][JW]) {
+    if (nsteps > 0) issue(0);
+    if (nsteps > 1) issue(1);
 #pragma unroll 1
-    for (int k0 = 0; k0 < kend_keys; k0 += KSTEP) {
-      f32x4 nA[JW], nB[JW];
-      load_z(k0 + KSTEP < kend_keys ? k0 + KSTEP : k0, nA, nB);
-      if constexpr (BF) {
-        const int keyA = k0 + 8 * (r16 >> 2) + (r16 & 3);  // S^T row r16 of tile A
-#pragma unroll
-        for (int i = 0; i < IG; ++i) {
-          const size_t rowbase = (size_t)(b * N + rows[i]) * NB;
-          bf16x8 kA, kB;
-          {
-            const int cb = (DH == 16) ? t : 2 * t + (g >> 1);
-            const T *kp = K + ((rowbase + cb) * Np + keyA) * 16 + 8 * (g & 1);
-            kA = as_bf16x8(ldg<uint4>(kp));
-            kB = as_bf16x8(ldg<uint4>(kp + 4 * 16));
-            if (DH == 16 && g >= 2) kA = kunit, kB = kunit;
-          }
-          bf16x8 vf[MB];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            vf[mb] = as_bf16x8(
-                ldg<uint4>(VT + (((size_t)(b * N + rows[i]) * H + t) * DH + mb * 16 + r16) * Np + k0 + 8 * g));
-#pragma unroll
-          for (int jb = 0; jb < JW; ++jb) {
-            f32x4 sA = mfma(kA, qf[i][jb][0], zA[jb]);
-            f32x4 sB = mfma(kB, qf[i][jb][0], zB[jb]);
-            if (DH == 32 && !max_pass) {
-              sA = mfma(kunit4, qsh[i][jb], sA);
-              sB = mfma(kunit4, qsh[i][jb], sB);
-            }
-            if (max_pass) {
-              float m = mx[i][jb];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(sA[e], sB[e]));
-              mx[i][jb] = m;
-            } else {
-              bf16x8 p;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                p[e] = (__bf16)fast_exp2(sA[e]);
-                p[4 + e] = (__bf16)fast_exp2(sB[e]);
-              }
-#pragma unroll
-              for (int mb = 0; mb < MB; ++mb) o[i][jb][mb] = mfma(vf[mb], p, o[i][jb][mb]);
-              ol[i][jb] = mfma(ones8, p, ol[i][jb]);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < IG; ++i) {
-          const size_t rowbase = (size_t)(b * N + rows[i]) * NB;
-          float kf[QS];
-          {
-            const int cb = (DH == 16) ? t : 2 * t + (g >> 1);
-            const int off = (DH == 16) ? 4 * g : 8 * (g & 1);
-            const float *kp = reinterpret_cast<const float *>(K) + ((rowbase + cb) * Np + k0 + r16) * 16 + off;
-#pragma unroll
-            for (int s = 0; s < QS; s += 4) {
-              float4 v = ldg<float4>(kp + s);
-              kf[s] = v.x, kf[s + 1] = v.y, kf[s + 2] = v.z, kf[s + 3] = v.w;
-            }
-          }
-          f32x4 vf[MB];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            vf[mb] = ldg<f32x4>(reinterpret_cast<const float *>(VT) +
-                                (((size_t)(b * N + rows[i]) * H + t) * DH + mb * 16 + r16) * Np + k0 + 4 * g);
-#pragma unroll
-          for (int jb = 0; jb < JW; ++jb) {
-            f32x4 s = zA[jb];
-#pragma unroll
-            for (int ss = 0; ss < QS; ++ss) s = mfma(kf[ss], qf[i][jb][ss], s);
-            if (max_pass) {
-              float m = mx[i][jb];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) m = fmaxf(m, s[e]);
-              mx[i][jb] = m;
-            } else {
-              float p[4];
-              const float sh = msh[i][jb];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) p[e] = fast_exp2(s[e] - sh);
-              lacc[i][jb] += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) o[i][jb][mb] = mfma(vf[mb][e], p[e], o[i][jb][mb]);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int jb = 0; jb < JW; ++jb) {
-        zA[jb] = nA[jb];
-        if constexpr (BF) zB[jb] = nB[jb];
-      }
+    for (int s = 0; s < nsteps; ++s) {
+      if (s + 1 < nsteps)
+        vmcnt_wait<LPW>();
+      else
+        vmcnt_wait<0>();
+      lds_barrier();
+      if (s + 2 < nsteps) issue(s + 2);
+      step_compute(ring + (size_t)(s % NS) * NBLKP * 64, max_pass, mx);
     }
   };
 
@@ -364,17 +453,20 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
 
   float dummy[IG][JW];
   zero_acc();
-  main_loop(false, dummy);
+  key_loop(false, dummy);
   row_sums();
 
-  // ---- recovery: exact maximum where the bound was too loose
+  // ---- recovery: exact maximum where the bound was too loose. The decision is
+  // workgroup-wide: every wave runs the key loop and its barriers together.
   bool need = false;
 #pragma unroll
   for (int i = 0; i < IG; ++i)
 #pragma unroll
     for (int jb = 0; jb < JW; ++jb)
       if (zmx[jb] > -INFINITY && !(lsum[i][jb] >= 0x1p-64f)) need = true;
-  if (__ballot(need) != 0) {
+  if (__ballot(need) != 0 && lane == 0) need_s = 1;
+  lds_barrier();  // also: every wave is done with the ring
+  if (need_s) {
     float mx[IG][JW];
 #pragma unroll
     for (int i = 0; i < IG; ++i)
@@ -384,7 +476,7 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
         msh[i][jb] = 0.f;
       }
     set_shift(msh);  // no shift during the max pass
-    main_loop(true, mx);
+    key_loop(true, mx);
 #pragma unroll
     for (int i = 0; i < IG; ++i)
 #pragma unroll
@@ -394,11 +486,12 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
       }
     set_shift(msh);
     zero_acc();
-    main_loop(false, dummy);
+    lds_barrier();  // every wave is done with the ring before it is refilled
+    key_loop(false, dummy);
     row_sums();
   }
 
-  // ---- normalise, fully masked columns, gate -> LDS tile [NPOS][D]
+  // ---- normalise, fully masked columns, gate; write over the gate
   const bool fill_nan = (a.mask_fill == -INFINITY);
   const float inv_n = 1.0f / (float)N;
 #pragma unroll
@@ -431,88 +524,35 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
         for (int r = 0; r < 4; ++r) vmean[mb][r] = __shfl(s, 4 * g + r, 64);
       }
     }
+    const int row = i0 + wr * IG + i;
 #pragma unroll
     for (int jb = 0; jb < JW; ++jb) {
-      const int j = j0 + jb * 16 + r16;
-      const int pos = i * NJ + jb * 16 + r16;
+      const int j = j0 + (wq * JW + jb) * 16 + r16;
       const bool masked = (zmx[jb] == -INFINITY);
       const float inv_l = masked ? 0.f : 1.0f / lsum[i][jb];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int cb = t * MB + mb;
-        const T *gp = G + (((size_t)(b * N + rows[i]) * NB + cb) * Np + j) * 16 + 4 * g;
-        float gv[4];
-        if constexpr (BF) {
-          const uint2 w = ldg<uint2>(gp);
-          gv[0] = bflo(w.x), gv[1] = bfhi(w.x), gv[2] = bflo(w.y), gv[3] = bfhi(w.y);
-        } else {
-          const float4 w = ldg<float4>(gp);
-          gv[0] = w.x, gv[1] = w.y, gv[2] = w.z, gv[3] = w.w;
-        }
-        float ov[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float oo = masked ? (fill_nan ? __builtin_nanf("") : vmean[mb][r]) : o[i][jb][mb][r] * inv_l;
-          ov[r] = oo * gv[r];
-        }
-        T *dst = &go[pos * PITCH + t * DH + mb * 16 + 4 * g];
-        if constexpr (BF)
-          *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]));
-        else
-          *reinterpret_cast<float4 *>(dst) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-      }
-    }
-  }
-  lds_barrier();
-
-  // ---- output projection: y^T[c][pos] = Wo[c] . go[pos] + bo[c]
-  const T *Wo = reinterpret_cast<const T *>(a.Wo);
-#pragma unroll
-  for (int ob = 0; ob < NBO; ++ob) {
-    const int cbo = t * NBO + ob;
-    Frag wo[KSO];
-    const T *wrow = Wo + (size_t)(cbo * 16 + r16) * D + g * KQ;
-    if constexpr (BF) {
-#pragma unroll
-      for (int s = 0; s < KSO; ++s) wo[s] = as_bf16x8(ldg<uint4>(wrow + 8 * s));
-    } else {
-#pragma unroll
-      for (int s = 0; s < KSO; s += 4) {
-        float4 v = ldg<float4>(wrow + s);
-        wo[s] = v.x, wo[s + 1] = v.y, wo[s + 2] = v.z, wo[s + 3] = v.w;
-      }
-    }
-    f32x4 bias;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = cbo * 16 + 4 * g + r;
-      bias[r] = BF ? bf2f(reinterpret_cast<const uint16_t *>(a.bo)[c]) : reinterpret_cast<const float *>(a.bo)[c];
-    }
-#pragma unroll 1
-    for (int pb = 0; pb < IG * JW; ++pb) {
-      const int i = pb / JW, jb = pb - i * JW;
-      const T *grow = &go[(pb * 16 + r16) * PITCH + g * KQ];
-      f32x4 acc = bias;
-      if constexpr (BF) {
-#pragma unroll
-        for (int s = 0; s < KSO; ++s) acc = mfma(wo[s], as_bf16x8(*reinterpret_cast<const uint4 *>(grow + 8 * s)), acc);
-      } else {
-#pragma unroll
-        for (int s = 0; s < KSO; s += 4) {
-          const float4 v = *reinterpret_cast<const float4 *>(grow + s);
-          acc = mfma(wo[s], v.x, acc);
-          acc = mfma(wo[s + 1], v.y, acc);
-          acc = mfma(wo[s + 2], v.z, acc);
-          acc = mfma(wo[s + 3], v.w, acc);
-        }
-      }
-      const int row = i0 + i, j = j0 + jb * 16 + r16;
       if (row < N && j < N) {
-        T *dst = reinterpret_cast<T *>(a.out) + ((size_t)(b * N + row) * N + j) * D + cbo * 16 + 4 * g;
-        if constexpr (BF)
-          stg<uint2>(dst, make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])));
-        else
-          stg<float4>(dst, make_float4(acc[0], acc[1], acc[2], acc[3]));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          T *gp = G + (((size_t)(b * N + row) * NB + t * MB + mb) * Np + j) * 16 + 4 * g;
+          float gv[4];
+          if constexpr (BF) {
+            const uint2 w = ldg<uint2>(gp);
+            gv[0] = bflo(w.x), gv[1] = bfhi(w.x), gv[2] = bflo(w.y), gv[3] = bfhi(w.y);
+          } else {
+            const float4 w = ldg<float4>(gp);
+            gv[0] = w.x, gv[1] = w.y, gv[2] = w.z, gv[3] = w.w;
+          }
+          float ov[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float oo = masked ? (fill_nan ? __builtin_nanf("") : vmean[mb][r]) : o[i][jb][mb][r] * inv_l;
+            ov[r] = oo * gv[r];
+          }
+          if constexpr (BF)
+            stg<uint2>(gp, make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])));
+          else
+            stg<float4>(gp, make_float4(ov[0], ov[1], ov[2], ov[3]));
+        }
       }
     }
   }
@@ -520,23 +560,30 @@ __global__ __launch_bounds__(64 * (D / DH)) void k2_attention(K2Args a) {
 
 template <typename T, int D, int DH>
 static hipError_t launch_k2_t(const K2Args &a, hipStream_t s) {
-  hipLaunchKernelGGL((k2_attention<T, D, DH>), dim3(a.items), dim3(64 * (D / DH)), 0, s, a);
+  hipLaunchKernelGGL((k2_attention<T, D, DH>), dim3(a.items), dim3(K2Shape<T, D, DH>::NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
-int k2_items(int D, int dh, int B, int N) {
-  int IG = 4, NJ = 32;
-#define TRI_K2_SHAPE(DD, HH)                 \
-  if (D == DD && dh == HH) {                 \
-    IG = K2Shape<DD, HH>::IG;                \
-    NJ = K2Shape<DD, HH>::JW * 16;           \
+int k2_items(int dtype, int D, int dh, int B, int N) {
+  int RB = 8, QB = 64;
+#define TRI_K2_SHAPE(TT, DD, HH)  \
+  if (D == DD && dh == HH) {      \
+    RB = K2Shape<TT, DD, HH>::RB; \
+    QB = K2Shape<TT, DD, HH>::QB; \
   }
-  TRI_K2_SHAPE(128, 16)
-  TRI_K2_SHAPE(128, 32)
-  TRI_K2_SHAPE(64, 16)
-  TRI_K2_SHAPE(64, 32)
+  if (dtype == TRI_ATTN_BF16) {
+    TRI_K2_SHAPE(bf16_t, 128, 16)
+    TRI_K2_SHAPE(bf16_t, 128, 32)
+    TRI_K2_SHAPE(bf16_t, 64, 16)
+    TRI_K2_SHAPE(bf16_t, 64, 32)
+  } else {
+    TRI_K2_SHAPE(float, 128, 16)
+    TRI_K2_SHAPE(float, 128, 32)
+    TRI_K2_SHAPE(float, 64, 16)
+    TRI_K2_SHAPE(float, 64, 32)
+  }
 #undef TRI_K2_SHAPE
-  return B * ((N + IG - 1) / IG) * ((N + NJ - 1) / NJ);
+  return B * (D / dh) * ((N + RB - 1) / RB) * ((N + QB - 1) / QB);
 }
 
 hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, hipStream_t s) {

@@ -1,0 +1,155 @@
+// Kernel 3 of the triangular self-attention forward: the output projection
+// y = Wo (g * o) + bo per pair position (Kimi-K2.6 / l2_p6 transcript: the
+// last step of its forward listing and its finalize kernel; FW-GLM-5-1 /
+// l2_p6: the output kernel).
+//
+// g * o comes from kernel 2, written over the gate in the workspace as
+// [b][i][c/16][j][16]. Work unit: 64 consecutive positions (b, i, j0..j0+63);
+// persistent grid. Each wave holds the 16 rows of Wo of one output channel
+// block in registers; the tile goes through LDS once, is multiplied on the
+// matrix cores (bias as the accumulator's start), and the result goes back
+// through LDS so that every output row is written as whole 16-byte chunks.
+// The next tile is prefetched into registers while the current one computes.
+#include "device_common.h"
+#include "tri_attn_internal.h"
+
+#include <type_traits>
+
+#include "tri_attn.h"
+
+namespace tpa {
+
+template <typename T, int D>
+__global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
+  constexpr bool BF = is_bf16<T>::value;
+  constexpr int ES = BF ? 2 : 4;
+  constexpr int NB = D / 16;  // output channel blocks = waves
+  constexpr int NT = NB * 64;
+  constexpr int KQ = D / 4;
+  constexpr int KS = BF ? D / 32 : D / 4;
+  constexpr int PITCH = D + 16 / ES;
+  constexpr int TILE = kChunk;
+  constexpr int NV = 16 * ES / 16;             // 16-byte chunks of one position's channel block
+  constexpr int ROWV = D * ES / 16;            // 16-byte chunks per output row
+  constexpr int CPT = TILE * ROWV / NT;        // output chunks per thread
+  using Frag = typename std::conditional<BF, bf16x8, float>::type;
+
+  __shared__ __align__(16) T xs[TILE * PITCH];
+  __shared__ __align__(16) T ys[TILE * PITCH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int N = a.N, Np = a.Np, nch = a.nchunk;
+  const T *GO = reinterpret_cast<const T *>(a.go);
+  const T *Wo = reinterpret_cast<const T *>(a.Wo);
+
+  Frag wo[KS];
+  {
+    const T *wrow = Wo + (size_t)(wave * 16 + r16) * D + g * KQ;
+    if constexpr (BF) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) wo[s] = as_bf16x8(ldg<uint4>(wrow + 8 * s));
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; s += 4) {
+        const float4 v = ldg<float4>(wrow + s);
+        wo[s] = v.x, wo[s + 1] = v.y, wo[s + 2] = v.z, wo[s + 3] = v.w;
+      }
+    }
+  }
+  f32x4 bias;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int c = wave * 16 + 4 * g + r;
+    bias[r] = BF ? bf2f(reinterpret_cast<const uint16_t *>(a.bo)[c]) : reinterpret_cast<const float *>(a.bo)[c];
+  }
+
+  // thread (wave, lane) loads channel block `wave` of position `lane` of a tile
+  auto load_tile = [&](int tile, uint4 (&pre)[NV]) {
+    const int bi_row = tile / nch, chunk = tile - bi_row * nch;
+    const int j = chunk * TILE + lane;
+    const T *src = GO + (((size_t)bi_row * NB + wave) * Np + j) * 16;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) pre[v] = (j < N) ? ldg<uint4>(src + v * (16 / ES)) : make_uint4(0, 0, 0, 0);
+  };
+
+  int tile = blockIdx.x;
+  if (tile >= a.tiles) return;
+  uint4 pre[NV];
+  load_tile(tile, pre);
+#pragma unroll 1
+  for (; tile < a.tiles; tile += gridDim.x) {
+    const int bi_row = tile / nch, chunk = tile - bi_row * nch;
+    const int j0 = chunk * TILE;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) *reinterpret_cast<uint4 *>(&xs[lane * PITCH + wave * 16 + v * (16 / ES)]) = pre[v];
+    lds_barrier();
+    if (tile + (int)gridDim.x < a.tiles) load_tile(tile + gridDim.x, pre);
+
+#pragma unroll
+    for (int pb = 0; pb < TILE / 16; ++pb) {
+      const T *xrow = &xs[(pb * 16 + r16) * PITCH + g * KQ];
+      f32x4 acc = bias;
+      if constexpr (BF) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma(wo[s], as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s)), acc);
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; s += 4) {
+          const float4 v = *reinterpret_cast<const float4 *>(xrow + s);
+          acc = mfma(wo[s], v.x, acc);
+          acc = mfma(wo[s + 1], v.y, acc);
+          acc = mfma(wo[s + 2], v.z, acc);
+          acc = mfma(wo[s + 3], v.w, acc);
+        }
+      }
+      // y^T tile: lane (g, r16) holds channels wave*16 + 4g..4g+3 of position pb*16 + r16
+      T *dst = &ys[(pb * 16 + r16) * PITCH + wave * 16 + 4 * g];
+      if constexpr (BF)
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      else
+        *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = tid + NT * k;
+      const int pos = c / ROWV, off = c - pos * ROWV;
+      if (j0 + pos < N) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(&ys[pos * PITCH + off * (16 / ES)]);
+        stg<uint4>(reinterpret_cast<T *>(a.out) + ((size_t)bi_row * N + j0 + pos) * D + off * (16 / ES), v);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_k3_t(const K3Args &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k3_out_proj<T, D>), dim3(grid), dim3(D / 16 * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_k3(int dtype, int D, const K3Args &a, int grid, hipStream_t s) {
+  if (dtype == TRI_ATTN_BF16) {
+    if (D == 128) return launch_k3_t<bf16_t, 128>(a, grid, s);
+    if (D == 64) return launch_k3_t<bf16_t, 64>(a, grid, s);
+  } else {
+    if (D == 128) return launch_k3_t<float, 128>(a, grid, s);
+    if (D == 64) return launch_k3_t<float, 64>(a, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+int k3_blocks_per_cu(int dtype, int D) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  if (dtype == TRI_ATTN_BF16)
+    e = D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k3_out_proj<bf16_t, 128>, 512, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k3_out_proj<bf16_t, 64>, 256, 0);
+  else
+    e = D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k3_out_proj<float, 128>, 512, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k3_out_proj<float, 64>, 256, 0);
+  return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+}  // namespace tpa

@@ -15,6 +15,7 @@ struct tri_attn {
   int D, h, dh, elem;
   int device;
   int k1_grid;     // persistent grid of kernel 1 (resident workgroups)
+  int k3_grid;     // persistent grid of kernel 3
   void *wpack;     // [(4D + 16)][D] Wq; Wk; Wv; Wg; Wz; zero rows
   void *vecs;      // gamma, beta, bg, bo ([D] each), then Wo [D][D]
   size_t wpack_bytes, vecs_bytes;
@@ -101,6 +102,7 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
     return TRI_ATTN_ERR_HIP;
   }
   t->k1_grid = cus * k1_blocks_per_cu(cfg->dtype, t->D, t->dh);
+  t->k3_grid = cus * k3_blocks_per_cu(cfg->dtype, t->D);
 
   t->wpack_bytes = (size_t)(4 * D + 16) * D * e;
   t->vecs_bytes = (size_t)4 * D * e + (size_t)D * D * e;
@@ -171,13 +173,13 @@ int tri_attn_get_workspace_layout(tri_attn_t t, int B, int N, tri_attn_workspace
   return TRI_ATTN_OK;
 }
 
-// stages: 1 = projection kernel, 2 = attention kernel, 3 = both
+// stages: bit 0 = projection kernel, bit 1 = attention kernel, bit 2 = output projection
 static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
                void *ws, size_t ws_bytes, void *stream, int stages) {
   int rc = check_sizes(t, B, N);
   if (rc) return rc;
   if (B == 0 || N == 0) return TRI_ATTN_OK;
-  if (((stages & 1) && (!pair_repr || !pair_mask)) || ((stages & 2) && !out)) return TRI_ATTN_ERR_INVALID_ARG;
+  if (((stages & 1) && (!pair_repr || !pair_mask)) || ((stages & 4) && !out)) return TRI_ATTN_ERR_INVALID_ARG;
   const Layout L = make_layout(B, N, t->D, t->h, t->elem);
   if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) & 255)) return TRI_ATTN_ERR_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -202,25 +204,31 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a1.tiles = B * N * L.nchunk;
   const int grid = a1.tiles < t->k1_grid ? a1.tiles : t->k1_grid;
   if ((stages & 1) && launch_k1(t->cfg.dtype, D, t->dh, a1, grid, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
-  if (!(stages & 2)) return TRI_ATTN_OK;
 
   K2Args a2{};
   a2.q = a1.q, a2.k = a1.k, a2.vt = a1.vt, a2.g = a1.g;
   a2.zm = a1.zm, a2.zmax = a1.zmax, a2.kmax = a1.kmax;
-  a2.Wo = vp + (size_t)4 * D * e;
-  a2.bo = vp + (size_t)3 * D * e;
-  a2.out = out;
   a2.mask_fill = t->cfg.mask_fill;
   a2.shift_slack = t->cfg.shift_slack;
   a2.B = B, a2.N = N, a2.Np = L.Np, a2.nchunk = L.nchunk;
-  a2.items = k2_items(D, t->dh, B, N);
-  if (launch_k2(t->cfg.dtype, D, t->dh, a2, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
+  a2.items = k2_items(t->cfg.dtype, D, t->dh, B, N);
+  if ((stages & 2) && launch_k2(t->cfg.dtype, D, t->dh, a2, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
+
+  K3Args a3{};
+  a3.go = a1.g;
+  a3.Wo = vp + (size_t)4 * D * e;
+  a3.bo = vp + (size_t)3 * D * e;
+  a3.out = out;
+  a3.B = B, a3.N = N, a3.Np = L.Np, a3.nchunk = L.nchunk;
+  a3.tiles = a1.tiles;
+  const int grid3 = a3.tiles < t->k3_grid ? a3.tiles : t->k3_grid;
+  if ((stages & 4) && launch_k3(t->cfg.dtype, D, a3, grid3, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
   return TRI_ATTN_OK;
 }
 
 int tri_attn_forward(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
                      void *workspace, size_t ws_bytes, void *stream) {
-  return run(t, pair_repr, pair_mask, out, B, N, workspace, ws_bytes, stream, 3);
+  return run(t, pair_repr, pair_mask, out, B, N, workspace, ws_bytes, stream, 7);
 }
 
 int tri_attn_project(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, int B, int N, void *workspace,
@@ -228,8 +236,12 @@ int tri_attn_project(tri_attn_t t, const void *pair_repr, const uint8_t *pair_ma
   return run(t, pair_repr, pair_mask, nullptr, B, N, workspace, ws_bytes, stream, 1);
 }
 
-int tri_attn_attend(tri_attn_t t, void *out, int B, int N, void *workspace, size_t ws_bytes, void *stream) {
-  return run(t, nullptr, nullptr, out, B, N, workspace, ws_bytes, stream, 2);
+int tri_attn_attend(tri_attn_t t, int B, int N, void *workspace, size_t ws_bytes, void *stream) {
+  return run(t, nullptr, nullptr, nullptr, B, N, workspace, ws_bytes, stream, 2);
+}
+
+int tri_attn_output(tri_attn_t t, void *out, int B, int N, void *workspace, size_t ws_bytes, void *stream) {
+  return run(t, nullptr, nullptr, out, B, N, workspace, ws_bytes, stream, 4);
 }
 
 int tri_attn_destroy(tri_attn_t t) {

@@ -32,21 +32,30 @@ struct K1Args {
   int B, N, Np, nchunk, tiles;
 };
 
-// Kernel 2: attention core + gate + output projection.
+// Kernel 2: attention core + gate, per head; writes g * o over the gate.
 struct K2Args {
-  const void *q, *k, *vt, *g;
+  const void *q, *k, *vt;
+  void *g;
   const float *zm, *zmax, *kmax;
-  const void *Wo, *bo;
-  void *out;
   float mask_fill;  // finite (uniform rule on fully masked columns) or -inf (NaN there)
   float shift_slack;
   int B, N, Np, nchunk, items;
 };
 
+// Kernel 3: output projection of g * o (left by kernel 2 in the gate region).
+struct K3Args {
+  const void *go;  // [B][N][D/16][Np][16]
+  const void *Wo, *bo;
+  void *out;       // [B][N][N][D]
+  int B, N, Np, nchunk, tiles;
+};
+
 // Launchers: return the launch status. `dtype` is TRI_ATTN_F32 / TRI_ATTN_BF16.
 hipError_t launch_k1(int dtype, int D, int dh, const K1Args &a, int grid, hipStream_t s);
 hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, hipStream_t s);
-int k2_items(int D, int dh, int B, int N);
+hipError_t launch_k3(int dtype, int D, const K3Args &a, int grid, hipStream_t s);
+int k2_items(int dtype, int D, int dh, int B, int N);
+int k3_blocks_per_cu(int dtype, int D);  // resident workgroups of kernel 3 per CU
 int k1_blocks_per_cu(int dtype, int D, int dh);  // resident workgroups of kernel 1 per CU
 bool supported(int D, int dh);
 
