@@ -127,6 +127,8 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   T *G = reinterpret_cast<T *>(a.g);
   const float *ZM = a.zm + (size_t)(b * H + t) * N * Np;
 
+  // The per-chunk maxima are spread over the lanes (one load each, all in
+  // flight together) and reduced across lanes.
   // ---- this wave's rows: bound of |k| over the row's keys
   int rows[IG];
   float kn2[IG];
@@ -139,14 +141,18 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
     for (int mb = 0; mb < MB; ++mb) {
       const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
       float m = 0.f;
-      for (int c = 0; c < nch; ++c) m = fmaxf(m, kp[c]);
+      for (int c = lane; c < nch; c += 64) m = fmaxf(m, kp[c]);
+#pragma unroll
+      for (int x = 1; x < 64; x <<= 1) m = xor_max(m, x);
       m2 += m;
     }
     kn2[i] = m2;
   }
 
-  // ---- this wave's query columns: bias+mask maximum, last live key chunk
+  // ---- this wave's query columns: bias+mask maximum, last live key chunk.
+  // Lane (g, r16) takes chunks g, g + 4, ... of column r16.
   float zmx[JW];
+  bool colmask[JW];  // a real column whose keys are all masked
   int kend = 0;
 #pragma unroll
   for (int jb = 0; jb < JW; ++jb) {
@@ -154,26 +160,39 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
     float zx = -INFINITY;
     if (j < N) {
       const float *zp = a.zmax + ((size_t)(b * H + t) * N + j) * nch;
-      for (int c = 0; c < nch; ++c) {
+#pragma unroll 4
+      for (int c = g; c < nch; c += 4) {
         const float v = zp[c];
         zx = fmaxf(zx, v);
-        if (v > -INFINITY) kend = c + 1;
+        if (v > -INFINITY) kend = max(kend, c + 1);
       }
     }
+    zx = group4_max(zx);
     zmx[jb] = zx;
+    colmask[jb] = (j < N) && zx == -INFINITY;
+  }
+  // a column with all keys masked takes the mean of v over every key (finite
+  // fill), summed by the matrix cores during the key loop
+  bool vsum_here = false;
+  if (a.mask_fill != -INFINITY) {
+#pragma unroll
+    for (int jb = 0; jb < JW; ++jb) vsum_here |= colmask[jb];
   }
   // the workgroup steps through the keys together: its end is the max over all waves
   for (int m = 1; m < 64; m <<= 1) kend = max(kend, __shfl_xor(kend, m, 64));
   __shared__ int kend_s[NW];
+  __shared__ int vsum_s[NW];
   __shared__ int need_s;
-  if (lane == 0) kend_s[wave] = kend;
+  const bool wave_vsum = __ballot(vsum_here) != 0;
+  if (lane == 0) kend_s[wave] = kend, vsum_s[wave] = wave_vsum;
   if (threadIdx.x == 0) need_s = 0;
   lds_barrier();
+  bool need_vsum = false;
   {
     int k = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) k = max(k, kend_s[w]);
-    kend = k;
+    for (int w = 0; w < NW; ++w) k = max(k, kend_s[w]), need_vsum |= (vsum_s[w] != 0);
+    kend = need_vsum ? nch : k;
   }
   const int nsteps = __builtin_amdgcn_readfirstlane(kend) * kChunk / KT;
 
@@ -295,7 +314,12 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   f32x4 o[IG][JW][MB];
   f32x4 ol[IG][JW];    // bf16: row 0 = sum of p (ones row)
   float lacc[IG][JW];  // fp32: per-lane partial sums
+  f32x4 vs[IG][MB];    // sum of v over the keys (every column alike)
   auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < IG; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) vs[i][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < IG; ++i)
 #pragma unroll
@@ -311,6 +335,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   // constant operands: ones row for the sum, unit key slot for the shift
   const bf16x8 ones8 = (r16 == 0) ? bf16x8{one, one, one, one, one, one, one, one}
                                   : bf16x8{zero, zero, zero, zero, zero, zero, zero, zero};
+  const bf16x8 allones = bf16x8{one, one, one, one, one, one, one, one};
   const bf16x8 kunit = (g == 2) ? bf16x8{one, zero, zero, zero, zero, zero, zero, zero}
                                 : bf16x8{zero, zero, zero, zero, zero, zero, zero, zero};
   const bf16x8 kunit0 = (g == 0) ? bf16x8{one, zero, zero, zero, zero, zero, zero, zero}
@@ -346,6 +371,10 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         bf16x8 vf[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) vf[mb] = as_bf16x8(vblk[(r * VBR + mb) * 64 + lane]);
+        if (need_vsum && !max_pass) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) vs[i][mb] = mfma(vf[mb], allones, vs[i][mb]);
+        }
 #pragma unroll
         for (int jb = 0; jb < JW; ++jb) {
           f32x4 sA = mfma(kA, qf[i][jb][0], zA[jb]);
@@ -393,6 +422,12 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         f32x4 vf[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) vf[mb] = __builtin_bit_cast(f32x4, vblk[(r * VBR + mb) * 64 + lane]);
+        if (need_vsum && !max_pass) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vs[i][mb] = mfma(vf[mb][e], 1.0f, vs[i][mb]);
+        }
 #pragma unroll
         for (int jb = 0; jb < JW; ++jb) {
           f32x4 s = zA[jb];
@@ -496,39 +531,18 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   const float inv_n = 1.0f / (float)N;
 #pragma unroll
   for (int i = 0; i < IG; ++i) {
-    bool masked_any = false;
-#pragma unroll
-    for (int jb = 0; jb < JW; ++jb) masked_any |= (zmx[jb] == -INFINITY);
+    // mean of v over all N keys (padding keys hold zeros); lane (g, r16) holds
+    // channels 4g..4g+3 of each block, the layout of the output tile
     float vmean[MB][4];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vmean[mb][r] = 0.f;
-    if (__ballot(masked_any) != 0 && !fill_nan) {
-      // mean of v over all N keys (padding keys hold zeros), lane (g, u) partial over its key slots
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const T *vrow = VT + (((size_t)(b * N + rows[i]) * H + t) * DH + mb * 16 + r16) * Np;
-        float s = 0.f;
-        for (int k0 = 4 * g; k0 < Np; k0 += 16) {
-          if constexpr (BF) {
-            const uint2 w = ldg<uint2>(vrow + k0);
-            s += (bflo(w.x) + bfhi(w.x)) + (bflo(w.y) + bfhi(w.y));
-          } else {
-            const float4 w = ldg<float4>(vrow + k0);
-            s += (w.x + w.y) + (w.z + w.w);
-          }
-        }
-        s = group4_sum(s) * inv_n;  // lanes (*, u) hold mean v[u]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vmean[mb][r] = __shfl(s, 4 * g + r, 64);
-      }
-    }
+      for (int r = 0; r < 4; ++r) vmean[mb][r] = vs[i][mb][r] * inv_n;
     const int row = i0 + wr * IG + i;
 #pragma unroll
     for (int jb = 0; jb < JW; ++jb) {
       const int j = j0 + (wq * JW + jb) * 16 + r16;
-      const bool masked = (zmx[jb] == -INFINITY);
+      const bool masked = colmask[jb];
       const float inv_l = masked ? 0.f : 1.0f / lsum[i][jb];
       if (row < N && j < N) {
 #pragma unroll
