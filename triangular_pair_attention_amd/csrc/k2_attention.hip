@@ -65,7 +65,13 @@ struct K2Shape {
   static constexpr int LPW = (NBLK + NW - 1) / NW;  // loads per wave per step
   static constexpr int NBLKP = LPW * NW;            // blocks per stage (the last ones pad)
   static constexpr int NS = 3;                      // ring stages
-  static constexpr size_t LDS = (size_t)NS * NBLKP * 1024;
+  // k blocks come first in a stage. bf16, d = 16: each k block has a third
+  // half-KB of constants (the unit key slot of the lanes that carry no
+  // channels), so that every lane reads its fragment from a fixed offset.
+  static constexpr int NK = RB * KBR;
+  static constexpr int KSTR = (BF && DH == 16) ? 1536 : 1024;
+  static constexpr int STAGE = NK * KSTR + (NBLKP - NK) * 1024;  // bytes
+  static constexpr size_t LDS = (size_t)NS * STAGE;
 };
 
 template <typename T, int D, int DH>
@@ -79,12 +85,12 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   constexpr int IG = S::IG, JW = S::JW, WQ = S::WQ, NW = S::NW, RB = S::RB, QB = S::QB;
   constexpr int KT = BF ? 32 : 16;  // keys per step
   constexpr int KBR = S::KBR, VBR = S::VBR, ZBJ = S::ZBJ, NBLK = S::NBLK, LPW = S::LPW, NBLKP = S::NBLKP;
-  constexpr int NS = S::NS;
+  constexpr int NS = S::NS, NK = S::NK, KSTR = S::KSTR, STAGE = S::STAGE;
   constexpr int QS = DH / 4;  // fp32: q/k elements per lane
   using Frag = typename std::conditional<BF, bf16x8, float>::type;
   static_assert(S::LDS <= 150 * 1024, "stage ring exceeds LDS");
 
-  __shared__ __align__(16) uint4 ring[NS * NBLKP * 64];  // [NS][NBLKP][64] x 16 bytes
+  __shared__ __align__(16) uint4 ring[NS * STAGE / 16];  // NS stages of STAGE bytes
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -171,8 +177,10 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
     zmx[jb] = zx;
     colmask[jb] = (j < N) && zx == -INFINITY;
   }
-  // a column with all keys masked takes the mean of v over every key (finite
-  // fill), summed by the matrix cores during the key loop
+  // A column with all keys masked takes the mean of v over every key (finite
+  // fill). Such a column runs the key loop with its query zeroed and its bias
+  // row read as 0: every key then weighs exp2(0) = 1, the column's accumulator
+  // sums v, and the epilogue divides by N.
   bool vsum_here = false;
   if (a.mask_fill != -INFINITY) {
 #pragma unroll
@@ -232,6 +240,10 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
       }
       n2 = group4_sum(n2);
       msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : sqrtf(n2 * kn2[i]) + zmx[jb] + a.shift_slack;
+      if (need_vsum && colmask[jb]) {
+#pragma unroll
+        for (int s = 0; s < (BF ? 1 : QS); ++s) qf[i][jb][s] = Frag{};
+      }
     }
 
   auto set_shift = [&](const float (&m)[IG][JW]) {
@@ -303,23 +315,30 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   }
   const uint32_t ring_base = lds_addr(ring);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int s) {  // global -> LDS: key step s into stage s % NS
-    const uint32_t stage = ring_base + (uint32_t)((s % NS) * NBLKP * 1024);
+  uint32_t blk_lds[LPW];  // byte offset of this wave's block l within a stage
 #pragma unroll
-    for (int l = 0; l < LPW; ++l)
-      dma16_to_lds(src_ptr[l] + (size_t)s * src_step[l], stage + (uint32_t)((wave_u + NW * l) * 1024));
+  for (int l = 0; l < LPW; ++l) {
+    const int blk = wave_u + NW * l;
+    blk_lds[l] = __builtin_amdgcn_readfirstlane(blk < NK ? blk * KSTR : NK * KSTR + (blk - NK) * 1024);
+  }
+  auto issue = [&](int s) {  // global -> LDS: key step s into stage s % NS
+    const uint32_t stage = ring_base + (uint32_t)((s % NS) * STAGE);
+#pragma unroll
+    for (int l = 0; l < LPW; ++l) dma16_to_lds(src_ptr[l] + (size_t)s * src_step[l], stage + blk_lds[l]);
   };
+  if constexpr (BF && DH == 16) {
+    // the constant half of every k block: lanes 32-47 read (1, 0, ..., 0), lanes 48-63 zeros
+    for (int x = threadIdx.x; x < NS * NK * 32; x += NW * 64) {
+      const int stg = x / (NK * 32), rem = x - stg * (NK * 32), r = rem >> 5, u = rem & 31;
+      ring[(stg * STAGE + r * KSTR + 1024) / 16 + u] = make_uint4(u < 16 ? 0x3f80u : 0u, 0u, 0u, 0u);
+    }
+  }
 
   // ---- accumulators
   f32x4 o[IG][JW][MB];
   f32x4 ol[IG][JW];    // bf16: row 0 = sum of p (ones row)
   float lacc[IG][JW];  // fp32: per-lane partial sums
-  f32x4 vs[IG][MB];    // sum of v over the keys (every column alike)
   auto zero_acc = [&]() {
-#pragma unroll
-    for (int i = 0; i < IG; ++i)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) vs[i][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < IG; ++i)
 #pragma unroll
@@ -335,81 +354,87 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   // constant operands: ones row for the sum, unit key slot for the shift
   const bf16x8 ones8 = (r16 == 0) ? bf16x8{one, one, one, one, one, one, one, one}
                                   : bf16x8{zero, zero, zero, zero, zero, zero, zero, zero};
-  const bf16x8 allones = bf16x8{one, one, one, one, one, one, one, one};
-  const bf16x8 kunit = (g == 2) ? bf16x8{one, zero, zero, zero, zero, zero, zero, zero}
-                                : bf16x8{zero, zero, zero, zero, zero, zero, zero, zero};
   const bf16x8 kunit0 = (g == 0) ? bf16x8{one, zero, zero, zero, zero, zero, zero, zero}
                                  : bf16x8{zero, zero, zero, zero, zero, zero, zero, zero};
 
   // One key step from a stage of the ring (max_pass: only the running maxima).
   auto step_compute = [&](const uint4 *st, bool max_pass, float (&mx)[IG][JW]) {
     const uint4 *kblk = st;
-    const uint4 *vblk = st + RB * KBR * 64;
-    const uint4 *zblk = st + RB * (KBR + VBR) * 64;
+    const uint4 *vblk = st + NK * KSTR / 16;
+    const uint4 *zblk = vblk + RB * VBR * 64;
     if constexpr (BF) {
+      // all fragments of the step first, then the (row, query block) pairs in
+      // a software pipeline: the scores of pair n + 1 go to the matrix cores
+      // before the exponentials of pair n, so the two overlap.
+      constexpr int NP = IG * JW;
       f32x4 zA[JW], zB[JW];
 #pragma unroll
       for (int jb = 0; jb < JW; ++jb) {
         const int q = wq * JW + jb;
         zA[jb] = __builtin_bit_cast(f32x4, zblk[(q * ZBJ) * 64 + lane]);
         zB[jb] = __builtin_bit_cast(f32x4, zblk[(q * ZBJ + 1) * 64 + lane]);
+        if (need_vsum && colmask[jb]) zA[jb] = f32x4{0.f, 0.f, 0.f, 0.f}, zB[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-#pragma unroll
-      for (int i = 0; i < IG; ++i) {
+      bf16x8 kA[IG], kB[IG], vf[IG][MB];
+      auto load_row = [&](int i) {
         const int r = wr * IG + i;
-        bf16x8 kA, kB;
         if (DH == 16) {
-          kA = kunit, kB = kunit;
-          if (g < 2) {
-            kA = as_bf16x8(kblk[r * 64 + lane]);
-            kB = as_bf16x8(kblk[r * 64 + 32 + lane]);
-          }
+          const uint4 *kb = kblk + r * (KSTR / 16);
+          kA[i] = as_bf16x8(kb[lane + (lane & 32)]);
+          kB[i] = as_bf16x8(kb[32 + lane]);
         } else {
-          kA = as_bf16x8(kblk[(2 * r) * 64 + lane]);
-          kB = as_bf16x8(kblk[(2 * r + 1) * 64 + lane]);
-        }
-        bf16x8 vf[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) vf[mb] = as_bf16x8(vblk[(r * VBR + mb) * 64 + lane]);
-        if (need_vsum && !max_pass) {
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) vs[i][mb] = mfma(vf[mb], allones, vs[i][mb]);
+          kA[i] = as_bf16x8(kblk[(2 * r) * 64 + lane]);
+          kB[i] = as_bf16x8(kblk[(2 * r + 1) * 64 + lane]);
         }
 #pragma unroll
-        for (int jb = 0; jb < JW; ++jb) {
-          f32x4 sA = mfma(kA, qf[i][jb][0], zA[jb]);
-          f32x4 sB = mfma(kB, qf[i][jb][0], zB[jb]);
-          // The shift MFMA has the same shape as the score MFMA on purpose: a
-          // 16x16x16 MFMA reading, as its accumulator, the result that the
-          // 16x16x32 one wrote a few instructions before gave wrong sums on
-          // gfx950 (only where the two were closest), so only one opcode ever
-          // feeds an accumulator chain here.
-          if (DH == 32 && !max_pass) {
-            sA = mfma(kunit0, qsh[i][jb], sA);
-            sB = mfma(kunit0, qsh[i][jb], sB);
+        for (int mb = 0; mb < MB; ++mb) vf[i][mb] = as_bf16x8(vblk[(r * VBR + mb) * 64 + lane]);
+      };
+      load_row(0);
+      f32x4 sA[NP], sB[NP];
+      auto scores = [&](int n) {
+        const int i = n / JW, jb = n % JW;
+        sA[n] = mfma(kA[i], qf[i][jb][0], zA[jb]);
+        sB[n] = mfma(kB[i], qf[i][jb][0], zB[jb]);
+        // The shift MFMA has the same shape as the score MFMA on purpose: a
+        // 16x16x16 MFMA reading, as its accumulator, the result that the
+        // 16x16x32 one wrote a few instructions before gave wrong sums on
+        // gfx950 (only where the two were closest), so only one opcode ever
+        // feeds an accumulator chain here.
+        if (DH == 32 && !max_pass) {
+          sA[n] = mfma(kunit0, qsh[i][jb], sA[n]);
+          sB[n] = mfma(kunit0, qsh[i][jb], sB[n]);
+        }
+      };
+      scores(0);
+#pragma unroll
+      for (int n = 0; n < NP; ++n) {
+        const int i = n / JW, jb = n % JW;
+        if (jb == 0 && i + 1 < IG) load_row(i + 1);
+        if (n + 1 < NP) scores(n + 1);
+        if (max_pass) {
+          float m = mx[i][jb];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(sA[n][e], sB[n][e]));
+          mx[i][jb] = m;
+        } else {
+          bf16x8 p;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = (__bf16)fast_exp2(sA[n][e]);
+            p[4 + e] = (__bf16)fast_exp2(sB[n][e]);
           }
-          if (max_pass) {
-            float m = mx[i][jb];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(sA[e], sB[e]));
-            mx[i][jb] = m;
-          } else {
-            bf16x8 p;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              p[e] = (__bf16)fast_exp2(sA[e]);
-              p[4 + e] = (__bf16)fast_exp2(sB[e]);
-            }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) o[i][jb][mb] = mfma(vf[mb], p, o[i][jb][mb]);
-            ol[i][jb] = mfma(ones8, p, ol[i][jb]);
-          }
+          for (int mb = 0; mb < MB; ++mb) o[i][jb][mb] = mfma(vf[i][mb], p, o[i][jb][mb]);
+          ol[i][jb] = mfma(ones8, p, ol[i][jb]);
         }
       }
     } else {
       f32x4 zA[JW];
 #pragma unroll
-      for (int jb = 0; jb < JW; ++jb) zA[jb] = __builtin_bit_cast(f32x4, zblk[(wq * JW + jb) * 64 + lane]);
+      for (int jb = 0; jb < JW; ++jb) {
+        zA[jb] = __builtin_bit_cast(f32x4, zblk[(wq * JW + jb) * 64 + lane]);
+        if (need_vsum && colmask[jb]) zA[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int i = 0; i < IG; ++i) {
         const int r = wr * IG + i;
@@ -422,12 +447,6 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         f32x4 vf[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) vf[mb] = __builtin_bit_cast(f32x4, vblk[(r * VBR + mb) * 64 + lane]);
-        if (need_vsum && !max_pass) {
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vs[i][mb] = mfma(vf[mb][e], 1.0f, vs[i][mb]);
-        }
 #pragma unroll
         for (int jb = 0; jb < JW; ++jb) {
           f32x4 s = zA[jb];
@@ -469,7 +488,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         vmcnt_wait<0>();
       lds_barrier();
       if (s + 2 < nsteps) issue(s + 2);
-      step_compute(ring + (size_t)(s % NS) * NBLKP * 64, max_pass, mx);
+      step_compute(ring + (size_t)(s % NS) * (STAGE / 16), max_pass, mx);
     }
   };
 
@@ -531,19 +550,12 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   const float inv_n = 1.0f / (float)N;
 #pragma unroll
   for (int i = 0; i < IG; ++i) {
-    // mean of v over all N keys (padding keys hold zeros); lane (g, r16) holds
-    // channels 4g..4g+3 of each block, the layout of the output tile
-    float vmean[MB][4];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vmean[mb][r] = vs[i][mb][r] * inv_n;
     const int row = i0 + wr * IG + i;
 #pragma unroll
     for (int jb = 0; jb < JW; ++jb) {
       const int j = j0 + (wq * JW + jb) * 16 + r16;
-      const bool masked = colmask[jb];
-      const float inv_l = masked ? 0.f : 1.0f / lsum[i][jb];
+      const bool masked = colmask[jb];  // o holds the sum of v over all keys (padding keys are zero)
+      const float inv_l = masked ? inv_n : 1.0f / lsum[i][jb];
       if (row < N && j < N) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -559,7 +571,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
           float ov[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float oo = masked ? (fill_nan ? __builtin_nanf("") : vmean[mb][r]) : o[i][jb][mb][r] * inv_l;
+            const float oo = (masked && fill_nan) ? __builtin_nanf("") : o[i][jb][mb][r] * inv_l;
             ov[r] = oo * gv[r];
           }
           if constexpr (BF)
