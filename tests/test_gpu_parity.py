@@ -108,13 +108,17 @@ def test_minus_inf_fill_gives_nan_on_fully_masked_columns(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dh", [16, 32])
-def test_recovery_path_with_loose_shift(dtype, dh):
-    """A huge shift_slack makes every softmax sum underflow, so each wave takes
-    the exact-maximum recovery path; the result must not change."""
+@pytest.mark.parametrize("slack", [60.0, 400.0])
+def test_loose_shift_and_recovery_path(dtype, dh, slack):
+    """shift_slack loosens the softmax bound. At 60 the bound exceeds 64, so
+    bf16 d=32 waves apply the shift (which they skip for small bounds), while
+    the sums stay above the recovery threshold; at 400 every sum underflows
+    and each wave takes the exact-maximum recovery path. Neither may change
+    the result."""
     w = Workload("slack", 1, 48, 128, 128 // dh, dtype, ("pad", 40), seed=7)
-    log(f"shift slack {dtype} d={dh}")
-    y, ref = run_case(make_inputs(w), slack=400.0)
-    check(y, ref, dtype, "recovery")
+    log(f"shift slack {slack} {dtype} d={dh}")
+    y, ref = run_case(make_inputs(w), slack=slack)
+    check(y, ref, dtype, f"slack {slack}")
 
 
 def test_large_scores_stay_finite():

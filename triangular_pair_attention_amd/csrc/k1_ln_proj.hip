@@ -31,11 +31,13 @@
 
 namespace tpa {
 
-// TPW projections per wave; NW = 4 * NB / TPW waves per workgroup.
+// TPW projections per wave; NW = 4 * NB / TPW waves per workgroup. (Two
+// projections per wave with twice the waves would halve the register budget
+// per lane; fp32 weights then spill.)
 template <typename T, int D>
 struct K1Shape {
   static constexpr int NB = D / 16;
-  static constexpr int TPW = (!is_bf16<T>::value && D == 128) ? 2 : 4;
+  static constexpr int TPW = 4;
   static constexpr int NW = 4 * NB / TPW;
   static constexpr int THREADS = NW * 64;
 };
@@ -71,29 +73,32 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   const int N = a.N, Np = a.Np, nch = a.nchunk;
   const T *W = reinterpret_cast<const T *>(a.W);
 
-  // ---- weights into registers: lane (g, r16) holds row r16 of the block, K-range [g*KQ, g*KQ+KQ)
+  // ---- weights into registers: lane (g, r16) holds row r16 of the block, K-range [g*KQ, g*KQ+KQ).
+  // Loaded after the first tile's pair_repr loads are issued, so that the
+  // LayerNorm of the first tile waits on its own data only.
   Frag wf[TPW][KS];
+  auto load_weights = [&]() {
 #pragma unroll
-  for (int p = 0; p < TPW; ++p) {
-    const T *wrow = W + (size_t)(((type0 + p) * NB + cb) * 16 + r16) * D + g * KQ;
-    if constexpr (BF) {
+    for (int p = 0; p < TPW; ++p) {
+      const T *wrow = W + (size_t)(((type0 + p) * NB + cb) * 16 + r16) * D + g * KQ;
+      if constexpr (BF) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) wf[p][s] = as_bf16x8(ldg<uint4>(wrow + 8 * s));
-    } else {
+        for (int s = 0; s < KS; ++s) wf[p][s] = as_bf16x8(ldg<uint4>(wrow + 8 * s));
+      } else {
 #pragma unroll
-      for (int s = 0; s < KS; s += 4) {
-        const float4 v = ldg<float4>(wrow + s);
-        wf[p][s] = v.x, wf[p][s + 1] = v.y, wf[p][s + 2] = v.z, wf[p][s + 3] = v.w;
+        for (int s = 0; s < KS; s += 4) {
+          const float4 v = ldg<float4>(wrow + s);
+          wf[p][s] = v.x, wf[p][s + 1] = v.y, wf[p][s + 2] = v.z, wf[p][s + 3] = v.w;
+        }
       }
     }
-  }
-  for (int c = tid; c < 3 * D; c += NT) {
-    const int which = c / D, cc = c - which * D;
-    const void *src = which == 0 ? a.gamma : (which == 1 ? a.beta : a.bg);
-    vec_s[which][cc] = BF ? bf2f(reinterpret_cast<const uint16_t *>(src)[cc]) : reinterpret_cast<const float *>(src)[cc];
-  }
-  for (int e = tid; e < 16 * D; e += NT) wz_s[(e / D) * PITCH + e % D] = W[(size_t)4 * D * D + e];
-  lds_barrier();
+    for (int c = tid; c < 3 * D; c += NT) {
+      const int which = c / D, cc = c - which * D;
+      const void *src = which == 0 ? a.gamma : (which == 1 ? a.beta : a.bg);
+      vec_s[which][cc] = BF ? bf2f(reinterpret_cast<const uint16_t *>(src)[cc]) : reinterpret_cast<const float *>(src)[cc];
+    }
+    for (int e = tid; e < 16 * D; e += NT) wz_s[(e / D) * PITCH + e % D] = W[(size_t)4 * D * D + e];
+  };
 
   // ---- LayerNorm thread mapping: TPP threads per position, EPT channels each
   const int lpos = tid / TPP, lpart = tid % TPP;
@@ -304,6 +309,8 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     uint32_t mA, mB = 0;
     load_tile(tile, preA, mA);
     if (tile + G < a.tiles) load_tile(tile + G, preB, mB);
+    load_weights();
+    lds_barrier();
 #pragma unroll 1
     for (; tile < a.tiles; tile += 2 * G) {
       layer_norm_to_lds(tile, preA, mA, 0);
@@ -317,15 +324,18 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
       compute(tile + G, 1);
     }
   } else {
-    // fp32 is matrix-core-bound and short of registers: no cross-tile prefetch
+    // fp32: the next tile is prefetched one ahead
     uint4 pre[NV];
     uint32_t mpre;
     int buf = 0;
+    load_tile(tile, pre, mpre);
+    load_weights();
+    lds_barrier();
 #pragma unroll 1
     for (; tile < a.tiles; tile += G) {
-      load_tile(tile, pre, mpre);
       layer_norm_to_lds(tile, pre, mpre, buf);
       lds_barrier();
+      if (tile + G < a.tiles) load_tile(tile + G, pre, mpre);
       compute(tile, buf);
       buf ^= 1;
     }

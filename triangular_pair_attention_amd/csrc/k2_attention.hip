@@ -263,6 +263,20 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
     }
   };
   set_shift(msh);
+  // bf16, d = 32: the shift costs two more MFMAs per score tile. Where every
+  // bound of the wave is at most 64, exp2 of a score cannot overflow (2^64 per
+  // key, sums far below the fp32 range) and the wave goes without it; scores
+  // far below their bound only risk a tiny sum, which the recovery below
+  // catches either way.
+  bool shift_on = true;
+  if constexpr (BF && DH == 32) {
+    bool big = false;
+#pragma unroll
+    for (int i = 0; i < IG; ++i)
+#pragma unroll
+      for (int jb = 0; jb < JW; ++jb) big |= !(msh[i][jb] <= 64.f);
+    shift_on = __ballot(big) != 0;
+  }
 
   // ---- loader: this wave fills blocks wave + NW*l of each stage; each lane
   // keeps the byte address of its 16 bytes at key step 0 and the per-step stride.
@@ -400,7 +414,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         // 16x16x32 one wrote a few instructions before gave wrong sums on
         // gfx950 (only where the two were closest), so only one opcode ever
         // feeds an accumulator chain here.
-        if (DH == 32 && !max_pass) {
+        if (DH == 32 && !max_pass && shift_on) {
           sA[n] = mfma(kunit0, qsh[i][jb], sA[n]);
           sB[n] = mfma(kunit0, qsh[i][jb], sB[n]);
         }
@@ -539,6 +553,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : m;
       }
     set_shift(msh);
+    shift_on = true;
     zero_acc();
     lds_barrier();  // every wave is done with the ring before it is refilled
     key_loop(false, dummy);
