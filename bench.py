@@ -39,7 +39,7 @@ KERNEL_SOURCES = {
     "k2_attention": "triangular_pair_attention_amd/csrc/k2_attention.hip",
     "k3_out_proj": "triangular_pair_attention_amd/csrc/k3_out_proj.hip",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def source_hash(kernel: str) -> str:
@@ -81,16 +81,27 @@ def roofline_of(kernel, w, m, ms):
 
 
 def stored_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    """HBM bytes per launch from the committed rocprofv3 counter runs (the
+    table in profiles/hbm_traffic.md), if they were taken on the current
+    kernel source; else None. Table row:
+    | workload | kernel | source sha256[:16] | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch scale | write scale |"""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)[workload][kernel]
-    except (OSError, KeyError, ValueError):
+            lines = f.read().splitlines()
+    except OSError:
         return None
-    if rec.get("source_sha256") != source_hash(kernel):
-        return None
-    return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
+    for line in lines:
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) != 7 or cells[0] != workload or cells[1] != kernel:
+            continue
+        if cells[2] != source_hash(kernel):
+            return None
+        try:
+            fetch, write, fs, ws = (float(c) for c in cells[3:7])
+        except ValueError:
+            return None
+        return fetch * 1024 * fs + write * 1024 * ws
+    return None
 
 
 def cpu_baseline(inp, w, seconds):
