@@ -3,7 +3,7 @@
  * self-attention forward.
  *
  * The operation is the one the POPCORNBENCH l2_p6 transcripts work on
- * ("Kimi-K2.6 / l2_p6": its 18-step forward listing and its layer list;
+ * ("Kimi-K2.6 / l2_p6": its forward listing and its layer list;
  * "FW-GLM-5-1 / l2_p6": the module's forward as restated while debugging).
  * For a pair representation P of shape (B, N, N, D), a pair mask M of shape
  * (B, N, N), h heads of size d = D / h:
@@ -106,7 +106,7 @@ int tri_attn_destroy(tri_attn_t h);
 const char *tri_attn_strerror(int code);
 
 /* ---------------------------------------------------------------------------
- * Stage access (tests and tools): the first of the two kernels alone, and
+ * Stage access (tests and tools): each of the three kernels alone, and
  * where it leaves its results in the workspace.
  * ------------------------------------------------------------------------ */
 

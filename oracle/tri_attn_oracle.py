@@ -14,7 +14,7 @@ transcripts of the POPCORNBENCH kernel benchmark):
   ``view(B*N, N, h, d).transpose(1, 2)``, the pair bias broadcast over rows
   through ``unsqueeze(1)``, the mask broadcast ``(B,1,1,N,N)``, softmax over
   the key axis, the ``transpose(1, 2).reshape(B, N, N, D)`` merge).
-* "Kimi-K2.6 / l2_p6" transcript: the 18-step forward listing, the layer list
+* "Kimi-K2.6 / l2_p6" transcript: the forward listing, the layer list
   (query/key/value/bias_proj without bias, gate and out_proj with bias,
   ``head_dim = pair_dim // num_heads``), eval-mode dropout, and the kernels'
   LayerNorm (biased variance, eps = 1e-5).

@@ -1,7 +1,8 @@
 // Kernel 1 of the triangular self-attention forward: LayerNorm of the pair
 // representation and ONE fused projection GEMM producing q | k | v | gate |
-// pair bias (Kimi-K2.6 / l2_p6 transcript: steps 1-7 of its forward listing
-// and its layer list; FW-GLM-5-1 / l2_p6: the LayerNorm and linear kernels).
+// pair bias (Kimi-K2.6 / l2_p6 transcript: the LayerNorm and projection steps
+// of its forward listing and its layer list; FW-GLM-5-1 / l2_p6: the
+// LayerNorm and linear kernels).
 //
 // Work unit: a tile of 64 consecutive pair positions (b, i, j0..j0+63) of one
 // row. A persistent grid walks the tiles; each workgroup keeps the packed

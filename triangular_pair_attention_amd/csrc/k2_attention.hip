@@ -1,9 +1,10 @@
 // Kernel 2 of the triangular self-attention forward: for one head, rows i of
 // a row block attend over the key columns k of their own row, query columns j
 // of a query block, with the shared pair bias and mask; softmax over k; the
-// value sum; the gate multiply (Kimi-K2.6 / l2_p6 transcript: steps 8-17 of
-// its forward listing and its attention kernel; FW-GLM-5-1 / l2_p6: the
-// fused attention kernel). The output projection is kernel 3.
+// value sum; the gate multiply (Kimi-K2.6 / l2_p6 transcript: the score,
+// softmax, value and gate steps of its forward listing and its attention
+// kernel; FW-GLM-5-1 / l2_p6: the fused attention kernel). The output
+// projection is kernel 3.
 //
 // Workgroup = (b, head t, RB rows i, QB query columns j); wave (wr, wq) takes
 // IG rows x JW*16 queries. The (B, N, h, N, N) scores are never stored.
