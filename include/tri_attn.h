@@ -121,9 +121,11 @@ const char *tri_attn_strerror(int code);
  *             and k < N, -inf elsewhere.
  *   zmax    : [B][h][N][Np/64] float32: max of zm over each 64-key chunk.
  *   kmax    : [B][N][D/16][Np/64] float32: max over each 64-column chunk of
- *             the squared norm of k over one 16-channel block. */
+ *             the squared norm of k over one 16-channel block.
+ *   vsum    : [B][N][D][Np/64] float32: sum of v over each 64-column chunk
+ *             (for the uniform weights of fully masked query columns). */
 typedef struct {
-  size_t q, k, vt, g, zm, zmax, kmax;
+  size_t q, k, vt, g, zm, zmax, kmax, vsum;
   size_t total;
   int padded_n;
 } tri_attn_workspace_layout;

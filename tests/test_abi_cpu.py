@@ -31,10 +31,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    # config: 3 ints + 3 floats; weights: 10 pointers; layout: 8 size_t + int (padded)
+    # config: 3 ints + 3 floats; weights: 10 pointers; layout: 9 size_t + int (padded)
     assert ctypes.sizeof(B.tri_attn_config) == 24
     assert ctypes.sizeof(B.tri_attn_weights) == 10 * ctypes.sizeof(ctypes.c_void_p)
-    assert ctypes.sizeof(B.tri_attn_workspace_layout) == 9 * 8
+    assert ctypes.sizeof(B.tri_attn_workspace_layout) == 10 * 8
 
 
 def test_strerror():

@@ -155,6 +155,7 @@ def test_projection_stage(dtype, shape):
         zm = f(lay.zm, B_ * h * N * Np, torch.float32).reshape(B_, h, N, Np)
         zmax = f(lay.zmax, B_ * h * N * (Np // 64), torch.float32).reshape(B_, h, N, Np // 64)
         kmax = f(lay.kmax, B_ * N * (D // 16) * (Np // 64), torch.float32).reshape(B_, N, D // 16, Np // 64)
+        vsum = f(lay.vsum, B_ * N * D * (Np // 64), torch.float32).reshape(B_, N, D, Np // 64)
     finally:
         g.close()
     q = q.reshape(B_, N, N, D)
@@ -180,6 +181,11 @@ def test_projection_stage(dtype, shape):
     kn2 = np.zeros((B_, N, D // 16, Np))  # |k|^2 over each 16-channel block, per column
     kn2[..., :N] = (rk.reshape(B_, N, N, D // 16, 16) ** 2).sum(-1).transpose(0, 1, 3, 2)
     np.testing.assert_allclose(kmax, kn2.reshape(B_, N, D // 16, Np // 64, 64).max(-1), rtol=2 * rtol, atol=atol)
+    # per-chunk sums of v over the key columns (zero beyond N)
+    vs = np.zeros((B_, N, D, Np))
+    vs[..., :N] = O.merge_heads(cap["v"]).reshape(B_, N, N, D).transpose(0, 1, 3, 2)
+    vs = vs.reshape(B_, N, D, Np // 64, 64).sum(-1)
+    np.testing.assert_allclose(vsum, vs, rtol=rtol, atol=atol * 64)
 
 
 # ------------------------------------------------------------------ ABI behaviour on the GPU

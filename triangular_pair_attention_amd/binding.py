@@ -46,7 +46,7 @@ class tri_attn_weights(ctypes.Structure):
 
 
 class tri_attn_workspace_layout(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_size_t) for name in ("q", "k", "vt", "g", "zm", "zmax", "kmax", "total")] + [
+    _fields_ = [(name, ctypes.c_size_t) for name in ("q", "k", "vt", "g", "zm", "zmax", "kmax", "vsum", "total")] + [
         ("padded_n", ctypes.c_int)
     ]
 

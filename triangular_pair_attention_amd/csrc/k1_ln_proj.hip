@@ -22,7 +22,8 @@
 //     per head [b][i][t][u][j]; the pair bias z*log2(e) with the mask folded
 //     in (-inf where masked) as [b][t][i][j]; per-64-key-chunk maxima of that
 //     tile and of the squared norm of k over each 16-channel block, which
-//     kernel 2 uses to bound the softmax shift and to skip masked key chunks.
+//     kernel 2 uses to bound the softmax shift and to skip masked key chunks;
+//     per-chunk sums of v, for the uniform weights of fully masked columns.
 #include "device_common.h"
 #include "tri_attn_internal.h"
 
@@ -190,6 +191,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     const int b = bi_row / N, i = bi_row - b * N;
     const int j0 = chunk * TILE;
     float kn_run = 0.f;  // running max over positions of |k|^2 over this channel block
+    float v_run = 0.f;   // running sum of v over this lane's positions
     float z_run = -INFINITY;
     const bool zwave = (wave == NW - 1);
 
@@ -231,6 +233,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
           const int ch = cb * 16 + r16, th = ch / DH, uu = ch - th * DH;
           T *dst = reinterpret_cast<T *>(a.vt) + ((((size_t)bi_row * H + th) * DH + uu) * Np + j0 + pb * 16 + 4 * g);
           store4(dst, c[0], c[1], c[2], c[3]);
+          v_run += (c[0] + c[1]) + (c[2] + c[3]);  // positions j >= N hold v = 0
         } else if (type == 0) {
           T *dst = reinterpret_cast<T *>(a.q) + ((((size_t)bi_row * NB + cb) * Np + jcol) * 16 + 4 * g);
           store4(dst, c[0] * a.qscale, c[1] * a.qscale, c[2] * a.qscale, c[3] * a.qscale);
@@ -278,6 +281,11 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
           stg<float4>(dst, make_float4(z[0], z[1], z[2], z[3]));
         }
       }
+    }
+    // per-chunk sums of v (a fixed summation order: deterministic)
+    if (TYPE0 <= 2 && TYPE0 + TPW > 2) {
+      const float sv = group4_sum(v_run);
+      if (g == 0) a.vsum[((size_t)bi_row * D + cb * 16 + r16) * nch + chunk] = sv;
     }
     // per-chunk maxima
     if (TYPE0 <= 1 && TYPE0 + TPW > 1) {

@@ -33,9 +33,10 @@
 //
 // Mask: zm = -inf where masked, so masked keys get weight exactly 0. A query
 // column whose keys are all masked (max zm = -inf) gets the rule of the
-// finite fill value: uniform weights over all N keys, i.e. the mean of v; or
-// NaN when the fill is -inf. Key chunks of 64 beyond the last live chunk of
-// the workgroup's columns are skipped.
+// finite fill value: uniform weights over all N keys, i.e. the mean of v
+// (from kernel 1's per-chunk sums of v); or NaN when the fill is -inf. Key
+// chunks of 64 beyond the last live chunk of the workgroup's columns are
+// skipped.
 //
 // Output: o / l times the gate, written over the gate in the workspace
 // ([b][i][c/16][j][16]); kernel 3 reads it from there.
@@ -65,7 +66,8 @@ struct K2Shape {
   static constexpr int NBLK = RB * (KBR + VBR) + (QB / 16) * ZBJ;
   static constexpr int LPW = (NBLK + NW - 1) / NW;  // loads per wave per step
   static constexpr int NBLKP = LPW * NW;            // blocks per stage (the last ones pad)
-  static constexpr int NS = 3;                      // ring stages
+  // ring stages: NS - 1 key steps in flight (a fourth stage measured no faster)
+  static constexpr int NS = 3;
   // k blocks come first in a stage. bf16, d = 16: each k block has a third
   // half-KB of constants (the unit key slot of the lanes that carry no
   // channels), so that every lane reads its fragment from a fixed offset.
@@ -92,6 +94,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   static_assert(S::LDS <= 150 * 1024, "stage ring exceeds LDS");
 
   __shared__ __align__(16) uint4 ring[NS * STAGE / 16];  // NS stages of STAGE bytes
+  static_assert(S::LDS + RB * DH * 4 <= 150 * 1024, "LDS budget");
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -178,30 +181,32 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
     zmx[jb] = zx;
     colmask[jb] = (j < N) && zx == -INFINITY;
   }
-  // A column with all keys masked takes the mean of v over every key (finite
-  // fill). Such a column runs the key loop with its query zeroed and its bias
-  // row read as 0: every key then weighs exp2(0) = 1, the column's accumulator
-  // sums v, and the epilogue divides by N.
-  bool vsum_here = false;
-  if (a.mask_fill != -INFINITY) {
-#pragma unroll
-    for (int jb = 0; jb < JW; ++jb) vsum_here |= colmask[jb];
+  // Sum of v over all keys of each (row, channel) of the workgroup, from
+  // kernel 1's per-chunk sums: the uniform weights of a fully masked column
+  // (finite fill). One thread per (row, channel), loads issued with the
+  // other setup loads.
+  __shared__ __align__(16) float vsum_s[RB * DH];
+  for (int x = threadIdx.x; x < RB * DH; x += NW * 64) {
+    const int r = x / DH, ch = x - r * DH;
+    const float *p = a.vsum + ((size_t)(b * N + min(i0 + r, N - 1)) * D + t * DH + ch) * nch;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    int c = 0;
+    for (; c + 4 <= nch; c += 4) s0 += p[c], s1 += p[c + 1], s2 += p[c + 2], s3 += p[c + 3];
+    for (; c < nch; ++c) s0 += p[c];
+    vsum_s[x] = (s0 + s1) + (s2 + s3);
   }
   // the workgroup steps through the keys together: its end is the max over all waves
   for (int m = 1; m < 64; m <<= 1) kend = max(kend, __shfl_xor(kend, m, 64));
   __shared__ int kend_s[NW];
-  __shared__ int vsum_s[NW];
   __shared__ int need_s;
-  const bool wave_vsum = __ballot(vsum_here) != 0;
-  if (lane == 0) kend_s[wave] = kend, vsum_s[wave] = wave_vsum;
+  if (lane == 0) kend_s[wave] = kend;
   if (threadIdx.x == 0) need_s = 0;
   lds_barrier();
-  bool need_vsum = false;
   {
     int k = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) k = max(k, kend_s[w]), need_vsum |= (vsum_s[w] != 0);
-    kend = need_vsum ? nch : k;
+    for (int w = 0; w < NW; ++w) k = max(k, kend_s[w]);
+    kend = k;
   }
   const int nsteps = __builtin_amdgcn_readfirstlane(kend) * kChunk / KT;
 
@@ -241,10 +246,6 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
       }
       n2 = group4_sum(n2);
       msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : sqrtf(n2 * kn2[i]) + zmx[jb] + a.shift_slack;
-      if (need_vsum && colmask[jb]) {
-#pragma unroll
-        for (int s = 0; s < (BF ? 1 : QS); ++s) qf[i][jb][s] = Frag{};
-      }
     }
 
   auto set_shift = [&](const float (&m)[IG][JW]) {
@@ -388,7 +389,6 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         const int q = wq * JW + jb;
         zA[jb] = __builtin_bit_cast(f32x4, zblk[(q * ZBJ) * 64 + lane]);
         zB[jb] = __builtin_bit_cast(f32x4, zblk[(q * ZBJ + 1) * 64 + lane]);
-        if (need_vsum && colmask[jb]) zA[jb] = f32x4{0.f, 0.f, 0.f, 0.f}, zB[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       bf16x8 kA[IG], kB[IG], vf[IG][MB];
       auto load_row = [&](int i) {
@@ -448,7 +448,6 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
       for (int jb = 0; jb < JW; ++jb) {
         zA[jb] = __builtin_bit_cast(f32x4, zblk[(wq * JW + jb) * 64 + lane]);
-        if (need_vsum && colmask[jb]) zA[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int i = 0; i < IG; ++i) {
@@ -492,17 +491,24 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   // via vmcnt, everyone's via the barrier, which also retires every wave's
   // reads of the stage that the next issue overwrites), then step s + 2 is
   // issued and step s computed.
+  constexpr int LA = NS - 1;  // steps in flight
+  static_assert(LA >= 1 && LA <= 3, "");
   auto key_loop = [&](bool max_pass, float (&mx)[IG][JW]) {
-    if (nsteps > 0) issue(0);
-    if (nsteps > 1) issue(1);
+#pragma unroll
+    for (int s = 0; s < LA; ++s)
+      if (s < nsteps) issue(s);
 #pragma unroll 1
     for (int s = 0; s < nsteps; ++s) {
-      if (s + 1 < nsteps)
+      // step s is complete once at most (steps issued after it) * LPW loads are outstanding
+      const int after = min(LA - 1, nsteps - 1 - s);
+      if (after >= 2)
+        vmcnt_wait<2 * LPW>();
+      else if (after == 1)
         vmcnt_wait<LPW>();
       else
         vmcnt_wait<0>();
       lds_barrier();
-      if (s + 2 < nsteps) issue(s + 2);
+      if (s + LA < nsteps) issue(s + LA);
       step_compute(ring + (size_t)(s % NS) * (STAGE / 16), max_pass, mx);
     }
   };
@@ -567,11 +573,20 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
   for (int i = 0; i < IG; ++i) {
     const int row = i0 + wr * IG + i;
+    // Uniform weights of a fully masked column (finite fill): the mean of v
+    // over all N keys (padding keys are zero). Lane (g, r16) needs channels
+    // 4g..4g+3 of each of the head's 16-channel blocks.
+    float vmean[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const float4 m4 = *reinterpret_cast<const float4 *>(&vsum_s[(wr * IG + i) * DH + mb * 16 + 4 * g]);
+      vmean[mb][0] = m4.x * inv_n, vmean[mb][1] = m4.y * inv_n, vmean[mb][2] = m4.z * inv_n, vmean[mb][3] = m4.w * inv_n;
+    }
 #pragma unroll
     for (int jb = 0; jb < JW; ++jb) {
       const int j = j0 + (wq * JW + jb) * 16 + r16;
-      const bool masked = colmask[jb];  // o holds the sum of v over all keys (padding keys are zero)
-      const float inv_l = masked ? inv_n : 1.0f / lsum[i][jb];
+      const bool masked = colmask[jb];
+      const float inv_l = masked ? 0.f : 1.0f / lsum[i][jb];
       if (row < N && j < N) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -587,7 +602,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
           float ov[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float oo = (masked && fill_nan) ? __builtin_nanf("") : o[i][jb][mb][r] * inv_l;
+            const float oo = masked ? (fill_nan ? __builtin_nanf("") : vmean[mb][r]) : o[i][jb][mb][r] * inv_l;
             ov[r] = oo * gv[r];
           }
           if constexpr (BF)

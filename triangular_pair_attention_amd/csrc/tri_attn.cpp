@@ -38,6 +38,7 @@ Layout make_layout(int B, int N, int D, int h, int elem) {
   L.zm = off, off = align256(off + (size_t)B * h * N * L.Np * 4);
   L.zmax = off, off = align256(off + (size_t)B * h * N * L.nchunk * 4);
   L.kmax = off, off = align256(off + (size_t)B * N * (D / 16) * L.nchunk * 4);
+  L.vsum = off, off = align256(off + (size_t)B * N * D * L.nchunk * 4);
   L.total = off;
   return L;
 }
@@ -167,7 +168,7 @@ int tri_attn_get_workspace_layout(tri_attn_t t, int B, int N, tri_attn_workspace
   if (B == 0 || N == 0) return TRI_ATTN_OK;
   const Layout L = make_layout(B, N, t->D, t->h, t->elem);
   out->q = L.q, out->k = L.k, out->vt = L.vt, out->g = L.g;
-  out->zm = L.zm, out->zmax = L.zmax, out->kmax = L.kmax;
+  out->zm = L.zm, out->zmax = L.zmax, out->kmax = L.kmax, out->vsum = L.vsum;
   out->total = L.total;
   out->padded_n = L.Np;
   return TRI_ATTN_OK;
@@ -198,6 +199,7 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a1.zm = reinterpret_cast<float *>(w + L.zm);
   a1.zmax = reinterpret_cast<float *>(w + L.zmax);
   a1.kmax = reinterpret_cast<float *>(w + L.kmax);
+  a1.vsum = reinterpret_cast<float *>(w + L.vsum);
   a1.eps = t->cfg.ln_eps;
   a1.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->dh));
   a1.B = B, a1.N = N, a1.Np = L.Np, a1.nchunk = L.nchunk;
@@ -207,7 +209,7 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
 
   K2Args a2{};
   a2.q = a1.q, a2.k = a1.k, a2.vt = a1.vt, a2.g = a1.g;
-  a2.zm = a1.zm, a2.zmax = a1.zmax, a2.kmax = a1.kmax;
+  a2.zm = a1.zm, a2.zmax = a1.zmax, a2.kmax = a1.kmax, a2.vsum = a1.vsum;
   a2.mask_fill = t->cfg.mask_fill;
   a2.shift_slack = t->cfg.shift_slack;
   a2.B = B, a2.N = N, a2.Np = L.Np, a2.nchunk = L.nchunk;

@@ -12,7 +12,7 @@ constexpr int kChunk = 64;  // key chunk of the per-chunk maxima; also K1's posi
 
 // Workspace regions (byte offsets); see tri_attn_workspace_layout in the header.
 struct Layout {
-  size_t q, k, vt, g, zm, zmax, kmax, total;
+  size_t q, k, vt, g, zm, zmax, kmax, vsum, total;
   int Np;      // N rounded up to kChunk
   int nchunk;  // Np / kChunk
 };
@@ -26,7 +26,7 @@ struct K1Args {
   const void *W;          // packed [(4D + 16)][D]: Wq; Wk; Wv; Wg; Wz; zero rows
   const void *gamma, *beta, *bg;  // [D]
   void *q, *k, *vt, *g;
-  float *zm, *zmax, *kmax;
+  float *zm, *zmax, *kmax, *vsum;
   float eps;
   float qscale;  // log2(e) / sqrt(d)
   int B, N, Np, nchunk, tiles;
@@ -36,7 +36,7 @@ struct K1Args {
 struct K2Args {
   const void *q, *k, *vt;
   void *g;
-  const float *zm, *zmax, *kmax;
+  const float *zm, *zmax, *kmax, *vsum;
   float mask_fill;  // finite (uniform rule on fully masked columns) or -inf (NaN there)
   float shift_slack;
   int B, N, Np, nchunk, items;
