@@ -14,8 +14,9 @@
 //     position; the normalised rows go to LDS in the operand type. bf16 tiles
 //     prefetch pair_repr and the mask two tiles ahead.
 //  2. Wave w owns channel block w % NB of its TPW projections, so every wave
-//     has the same MFMA and epilogue work (the pair-bias block, whose weight
-//     sits in LDS, is the only extra: on the last wave).
+//     has the same MFMA and epilogue work; the pair-bias block (its weight
+//     sits in LDS) is the only extra, one 16-position block on each of the
+//     first four waves (one per SIMD).
 //  3. Epilogues write directly in the layouts kernel 2 reads:
 //     q (pre-scaled by log2(e)/sqrt(d)), k, gate (sigmoid(+bias)) as
 //     [b][i][c/16][j][16] (one 512-byte burst per 16x16 tile); v transposed
@@ -67,6 +68,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   __shared__ uint8_t mask_s[2][TILE];           // the tile's mask bytes (0 also for j >= N)
   __shared__ float vec_s[3][D];                 // gamma, beta, gate bias (fp32)
   __shared__ __align__(16) T wz_s[16 * PITCH];  // pair-bias weight block (rows >= h are zero)
+  __shared__ float zpart_s[TILE / 16][16];      // per-block maxima of the pair bias of a tile
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -193,7 +195,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     float kn_run = 0.f;  // running max over positions of |k|^2 over this channel block
     float v_run = 0.f;   // running sum of v over this lane's positions
     float z_run = -INFINITY;
-    const bool zwave = (wave == NW - 1);
+    static_assert(NW >= TILE / 16, "");
 
 #pragma unroll 1
     for (int pb = 0; pb < TILE / 16; ++pb) {
@@ -250,8 +252,9 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
                  fast_rcp(1.f + fast_exp2(-(c[3] + bgv.w) * kLog2e)));
         }
       }
-      if (zwave) {
-        // pair bias: rows = positions, column r16 = head
+      if (wave == pb) {
+        // pair bias of this 16-position block, on wave pb (spread over the
+        // SIMDs): rows = positions, column r16 = head
         const T *zrow = &wz_s[r16 * PITCH + g * KQ];
         f32x4 accz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -292,9 +295,17 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
       const float m = row16_max(kn_run);
       if (lane == 0) a.kmax[((size_t)bi_row * NB + cb) * nch + chunk] = m;
     }
-    if (zwave) {
+    // the chunk maximum of the bias combines the blocks of waves 0..3 through LDS
+    if (wave < TILE / 16) {
       const float m = group4_max(z_run);
-      if (g == 0 && r16 < H) a.zmax[((size_t)(b * H + r16) * N + i) * nch + chunk] = m;
+      if (g == 0) zpart_s[wave][r16] = m;
+    }
+    lds_barrier();
+    if (wave == 0 && lane < H) {
+      float m = zpart_s[0][lane];
+#pragma unroll
+      for (int q = 1; q < TILE / 16; ++q) m = fmaxf(m, zpart_s[q][lane]);
+      a.zmax[((size_t)(b * H + lane) * N + i) * nch + chunk] = m;
     }
   };
 
