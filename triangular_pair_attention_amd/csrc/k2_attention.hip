@@ -53,10 +53,12 @@ namespace tpa {
 template <typename T, int D, int DH>
 struct K2Shape {
   static constexpr bool BF = is_bf16<T>::value;
-  static constexpr int IG = (BF && DH == 16) ? 4 : 2;
-  static constexpr int JW = 2;
+  // fp32 runs at sizes where one workgroup per CU would leave the CUs idle
+  // on latency: one row per wave and small blocks, so two fit on a CU.
+  static constexpr int IG = BF ? ((DH == 16) ? 4 : 2) : 1;
+  static constexpr int JW = (!BF && DH == 16) ? 1 : 2;
   static constexpr int WR = (BF && DH == 32) ? 4 : 2;
-  static constexpr int WQ = BF ? ((DH == 16) ? 4 : 2) : ((DH == 16) ? 1 : 2);
+  static constexpr int WQ = BF ? ((DH == 16) ? 4 : 2) : 2;
   static constexpr int NW = WR * WQ;
   static constexpr int RB = WR * IG;       // rows per workgroup
   static constexpr int QB = WQ * JW * 16;  // query columns per workgroup
