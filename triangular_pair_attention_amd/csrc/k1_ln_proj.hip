@@ -82,20 +82,28 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   // LayerNorm of the first tile waits on its own data only.
   Frag wf[TPW][KS];
   auto load_weights = [&]() {
+    // issued in the order the MFMAs consume them (contraction step outer), so
+    // the first products start while later weights are still arriving
+    if constexpr (BF) {
 #pragma unroll
-    for (int p = 0; p < TPW; ++p) {
-      const T *wrow = W + (size_t)(((type0 + p) * NB + cb) * 16 + r16) * D + g * KQ;
-      if constexpr (BF) {
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) wf[p][s] = as_bf16x8(ldg<uint4>(wrow + 8 * s));
-      } else {
+        for (int p = 0; p < TPW; ++p)
+          wf[p][s] = as_bf16x8(ldg<uint4>(W + (size_t)(((type0 + p) * NB + cb) * 16 + r16) * D + g * KQ + 8 * s));
+    } else {
 #pragma unroll
-        for (int s = 0; s < KS; s += 4) {
-          const float4 v = ldg<float4>(wrow + s);
+      for (int s = 0; s < KS; s += 4)
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          const float4 v = ldg<float4>(W + (size_t)(((type0 + p) * NB + cb) * 16 + r16) * D + g * KQ + s);
           wf[p][s] = v.x, wf[p][s + 1] = v.y, wf[p][s + 2] = v.z, wf[p][s + 3] = v.w;
         }
-      }
     }
+  };
+  // LayerNorm affine parameters, gate bias and the pair-bias weight block into
+  // LDS. Issued before the weight loads: loads complete in order, and these
+  // small ones are waited for at once.
+  auto load_vecs = [&]() {
     for (int c = tid; c < 3 * D; c += NT) {
       const int which = c / D, cc = c - which * D;
       const void *src = which == 0 ? a.gamma : (which == 1 ? a.beta : a.bg);
@@ -329,6 +337,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     uint32_t mA, mB = 0;
     load_tile(tile, preA, mA);
     if (tile + G < a.tiles) load_tile(tile + G, preB, mB);
+    load_vecs();
     load_weights();
     lds_barrier();
 #pragma unroll 1
@@ -349,6 +358,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     uint32_t mpre;
     int buf = 0;
     load_tile(tile, pre, mpre);
+    load_vecs();
     load_weights();
     lds_barrier();
 #pragma unroll 1
