@@ -68,6 +68,19 @@ def test_workload5_sampled_rows():
     check(y, ref, w.dtype, w.name + " sampled")
 
 
+@pytest.mark.parametrize("dtype,h", [("bf16", 8), ("bf16", 4), ("f32", 4)])
+def test_large_n_sampled_rows(dtype, h):
+    """N = 1040 (17 key chunks, the last one ragged): larger than any
+    workload, so 64-bit offsets, many key steps and the chunk bookkeeping are
+    exercised; compared on sampled rows."""
+    w = Workload("largeN", 1, 1040, 128, h, dtype, ("pad", 1000), seed=21)
+    log(f"large N {dtype} h={h}: sampled rows")
+    inp = make_inputs(w)
+    rows = [(0, i) for i in (0, 517, 999, 1000, 1039)]
+    y, ref = run_case(inp, rows=rows)
+    check(y, ref, dtype, f"large N {dtype} h={h}")
+
+
 # ------------------------------------------------------------------ small and ragged shapes
 SHAPES = [
     (1, 1, 64, 4), (2, 3, 64, 2), (2, 17, 64, 4), (1, 33, 128, 4), (1, 65, 128, 8),
