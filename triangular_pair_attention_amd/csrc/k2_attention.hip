@@ -55,8 +55,10 @@ struct K2Shape {
   static constexpr bool BF = is_bf16<T>::value;
   // fp32 runs at sizes where one workgroup per CU would leave the CUs idle
   // on latency: one row per wave and small blocks, so two fit on a CU.
-  static constexpr int IG = BF ? ((DH == 16) ? 4 : 2) : 1;
-  static constexpr int JW = (!BF && DH == 16) ? 1 : 2;
+  // bf16, d = 32: one row per wave and four query blocks, so a row's k and v
+  // serve 128 query columns (the feed per score is what limits this shape).
+  static constexpr int IG = BF ? ((DH == 16) ? 4 : 1) : 1;
+  static constexpr int JW = BF ? ((DH == 16) ? 2 : 4) : ((DH == 16) ? 1 : 2);
   static constexpr int WR = (BF && DH == 32) ? 4 : 2;
   static constexpr int WQ = BF ? ((DH == 16) ? 4 : 2) : 2;
   static constexpr int NW = WR * WQ;
@@ -216,7 +218,6 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   // bf16: lane (g, r16) holds q'[j = r16][8g..8g+7] (d = 16: groups 0-1 real, group 2 slot 0 = -m);
   // fp32: lane (g, r16) holds q'[j][g*d/4 .. +d/4).
   Frag qf[IG][JW][BF ? 1 : QS];
-  bf16x8 qsh[IG][JW];  // bf16, d = 32: B operand of the shift MFMA
   float msh[IG][JW];
 #pragma unroll
   for (int i = 0; i < IG; ++i)
@@ -258,11 +259,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         for (int jb = 0; jb < JW; ++jb) {
           const __bf16 nm = (__bf16)(-m[i][jb]);
           const __bf16 z = (__bf16)0.f;
-          if (DH == 16) {
-            if (g == 2) qf[i][jb][0] = bf16x8{nm, z, z, z, z, z, z, z};
-          } else {
-            qsh[i][jb] = (g == 0) ? bf16x8{nm, z, z, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
-          }
+          if (DH == 16 && g == 2) qf[i][jb][0] = bf16x8{nm, z, z, z, z, z, z, z};
         }
     }
   };
@@ -418,8 +415,11 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         // gfx950 (only where the two were closest), so only one opcode ever
         // feeds an accumulator chain here.
         if (DH == 32 && !max_pass && shift_on) {
-          sA[n] = mfma(kunit0, qsh[i][jb], sA[n]);
-          sB[n] = mfma(kunit0, qsh[i][jb], sB[n]);
+          // B operand: -m in row 0 of lane group 0 (built here: it is rarely needed)
+          const __bf16 nm = (__bf16)(-msh[i][jb]), z = (__bf16)0.f;
+          const bf16x8 qsh = (g == 0) ? bf16x8{nm, z, z, z, z, z, z, z} : bf16x8{z, z, z, z, z, z, z, z};
+          sA[n] = mfma(kunit0, qsh, sA[n]);
+          sB[n] = mfma(kunit0, qsh, sB[n]);
         }
       };
       scores(0);
