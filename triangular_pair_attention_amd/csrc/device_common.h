@@ -98,7 +98,11 @@ __device__ __forceinline__ void vmcnt_wait() {
 // lds_base + 16*l (lds_base is the same for the whole wave). Issued through
 // inline assembly so that the compiler does not hold later LDS reads of other
 // ring stages behind it; the caller tracks completion with vmcnt_wait (vector
-// memory operations complete in issue order for vmcnt).
+// memory operations complete in issue order for vmcnt). The assembly sets
+// M0, a register the compiler reserves and does not let an asm statement
+// declare as clobbered; these kernels make no other use of M0 (no indexed
+// register access, no message or GDS instructions), which a host-side test
+// checks on the generated code.
 __device__ __forceinline__ void dma16_to_lds(const void *gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base)
                : "memory");

@@ -8,7 +8,8 @@
 // row. A persistent grid walks the tiles; each workgroup keeps the packed
 // weight [Wq; Wk; Wv; Wg] in registers for its whole life (each wave holds
 // one 16-channel block of TPW projections), so the weight is read from L2
-// once per workgroup, not once per tile.
+// once per workgroup, not once per tile, and is stored in fragment order
+// (one contiguous kilobyte per wave load).
 //
 //  1. LayerNorm (fp32 statistics, two-pass in registers), TPP lanes per
 //     position; the normalised rows go to LDS in the operand type. bf16 tiles
@@ -45,7 +46,9 @@ struct K1Shape {
   static constexpr int THREADS = NW * 64;
 };
 
-template <typename T, int D, int DH>
+// ONE: the grid has one tile per workgroup (a straight path with no prefetch
+// and no tile loop); otherwise a persistent loop over tiles.
+template <typename T, int D, int DH, bool ONE>
 __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a) {
   constexpr bool BF = is_bf16<T>::value;
   constexpr int ES = BF ? 2 : 4;           // element bytes
@@ -79,37 +82,55 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
 
   // ---- weights into registers: lane (g, r16) holds row r16 of the block, K-range [g*KQ, g*KQ+KQ).
   // Loaded after the first tile's pair_repr loads are issued, so that the
-  // LayerNorm of the first tile waits on its own data only.
+  // LayerNorm of the first tile waits on its own data only. The weights are
+  // stored in fragment order: each load of a wave reads 1 KB contiguously.
+  constexpr int NVW = D * ES / 64;  // 16-byte pieces per lane per block
+  static_assert(NVW == (BF ? KS : KS / 4), "");
   Frag wf[TPW][KS];
   auto load_weights = [&]() {
+    const char *wsrc = reinterpret_cast<const char *>(a.Wf) + (size_t)lane * 16;
+    auto piece = [&](int p, int v) {
+      return ldg<uint4>(wsrc + ((size_t)((type0 + p) * NB + cb) * NVW + v) * 1024);
+    };
     // issued in the order the MFMAs consume them (contraction step outer), so
     // the first products start while later weights are still arriving
-    if constexpr (BF) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+    for (int v = 0; v < NVW; ++v)
 #pragma unroll
-        for (int p = 0; p < TPW; ++p)
-          wf[p][s] = as_bf16x8(ldg<uint4>(W + (size_t)(((type0 + p) * NB + cb) * 16 + r16) * D + g * KQ + 8 * s));
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; s += 4)
-#pragma unroll
-        for (int p = 0; p < TPW; ++p) {
-          const float4 v = ldg<float4>(W + (size_t)(((type0 + p) * NB + cb) * 16 + r16) * D + g * KQ + s);
-          wf[p][s] = v.x, wf[p][s + 1] = v.y, wf[p][s + 2] = v.z, wf[p][s + 3] = v.w;
+      for (int p = 0; p < TPW; ++p) {
+        const uint4 u = piece(p, v);
+        if constexpr (BF) {
+          wf[p][v] = as_bf16x8(u);
+        } else {
+          wf[p][4 * v] = __uint_as_float(u.x), wf[p][4 * v + 1] = __uint_as_float(u.y);
+          wf[p][4 * v + 2] = __uint_as_float(u.z), wf[p][4 * v + 3] = __uint_as_float(u.w);
         }
-    }
+      }
   };
-  // LayerNorm affine parameters, gate bias and the pair-bias weight block into
-  // LDS. Issued before the weight loads: loads complete in order, and these
-  // small ones are waited for at once.
-  auto load_vecs = [&]() {
-    for (int c = tid; c < 3 * D; c += NT) {
-      const int which = c / D, cc = c - which * D;
-      const void *src = which == 0 ? a.gamma : (which == 1 ? a.beta : a.bg);
-      vec_s[which][cc] = BF ? bf2f(reinterpret_cast<const uint16_t *>(src)[cc]) : reinterpret_cast<const float *>(src)[cc];
+  // LayerNorm affine parameters, gate bias and the pair-bias weight block,
+  // staged through LDS: one element of the three vectors and one 16-byte
+  // vector of the block per thread. issue_params() starts the loads (their
+  // pointer is chosen per wave, so no load waits on another), and
+  // commit_params() writes them to LDS once they have arrived.
+  constexpr int WZV = 16 * D * ES / 16;  // 16-byte vectors of the pair-bias block
+  static_assert(3 * D <= NT && WZV <= NT, "one parameter load per thread");
+  const int pwhich = __builtin_amdgcn_readfirstlane(tid / D);  // 0 gamma, 1 beta, 2 gate bias (D % 64 == 0)
+  float pv = 0.f;
+  uint4 wzv = make_uint4(0, 0, 0, 0);
+  auto issue_params = [&]() {
+    if (pwhich < 3) {
+      const void *src = pwhich == 0 ? a.gamma : (pwhich == 1 ? a.beta : a.bg);
+      pv = BF ? bf2f(reinterpret_cast<const uint16_t *>(src)[tid - pwhich * D])
+              : reinterpret_cast<const float *>(src)[tid - pwhich * D];
     }
-    for (int e = tid; e < 16 * D; e += NT) wz_s[(e / D) * PITCH + e % D] = W[(size_t)4 * D * D + e];
+    if (tid < WZV) wzv = ldg<uint4>(reinterpret_cast<const char *>(W + (size_t)4 * D * D) + 16 * tid);
+  };
+  auto commit_params = [&]() {
+    if (pwhich < 3) vec_s[pwhich][tid - pwhich * D] = pv;
+    if (tid < WZV) {
+      const int e = tid * (16 / ES);  // first element of this vector; rows are whole vectors
+      *reinterpret_cast<uint4 *>(&wz_s[(e / D) * PITCH + e % D]) = wzv;
+    }
   };
 
   // ---- LayerNorm thread mapping: TPP threads per position, EPT channels each
@@ -195,8 +216,13 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   };
 
   // One tile with this wave's projections starting at TYPE0 (compile time).
-  auto compute_tile = [&](auto type0_c, int tile, int buf) {
+  // PEEL: the first 16-position block is emitted as its own straight-line
+  // copy, so that on a workgroup's first tile each product waits only for its
+  // own weight registers while later ones are still arriving (inside a loop
+  // the compiler waits for all outstanding loads before entering it).
+  auto compute_tile = [&](auto type0_c, auto peel_c, int tile, int buf) __attribute__((always_inline)) {
     constexpr int TYPE0 = decltype(type0_c)::value;
+    constexpr bool PEEL = decltype(peel_c)::value;
     const int bi_row = tile / nch, chunk = tile - bi_row * nch;
     const int b = bi_row / N, i = bi_row - b * N;
     const int j0 = chunk * TILE;
@@ -205,8 +231,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     float z_run = -INFINITY;
     static_assert(NW >= TILE / 16, "");
 
-#pragma unroll 1
-    for (int pb = 0; pb < TILE / 16; ++pb) {
+    auto block = [&](int pb) __attribute__((always_inline)) {
       // x fragments: lane (g, r16) = position pb*16 + r16, K-range [g*KQ, g*KQ+KQ)
       const T *xrow = &xs[buf][(pb * 16 + r16) * PITCH + g * KQ];
       f32x4 acc[TPW];
@@ -292,7 +317,15 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
           stg<float4>(dst, make_float4(z[0], z[1], z[2], z[3]));
         }
       }
+    };
+    int pb0 = 0;
+    if constexpr (PEEL) {
+      block(0);
+      pb0 = 1;
     }
+#pragma unroll 1
+    for (int pb = pb0; pb < TILE / 16; ++pb) block(pb);
+
     // per-chunk sums of v (a fixed summation order: deterministic)
     if (TYPE0 <= 2 && TYPE0 + TPW > 2) {
       const float sv = group4_sum(v_run);
@@ -317,56 +350,80 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     }
   };
 
-  auto compute = [&](int tile, int buf) {
+  auto compute = [&](auto peel_c, int tile, int buf) __attribute__((always_inline)) {
     if constexpr (TPW == 4) {
-      compute_tile(std::integral_constant<int, 0>{}, tile, buf);
+      compute_tile(std::integral_constant<int, 0>{}, peel_c, tile, buf);
     } else {
       if (type0 == 0)
-        compute_tile(std::integral_constant<int, 0>{}, tile, buf);
+        compute_tile(std::integral_constant<int, 0>{}, peel_c, tile, buf);
       else
-        compute_tile(std::integral_constant<int, 2>{}, tile, buf);
+        compute_tile(std::integral_constant<int, 2>{}, peel_c, tile, buf);
     }
   };
+  const std::true_type first{};
+  const std::false_type later{};
 
   int tile = blockIdx.x;
   if (tile >= a.tiles) return;
   const int G = gridDim.x;
-  if constexpr (BF) {
-    // bf16 is HBM-bound: pair_repr and the mask are prefetched two tiles ahead
+  if constexpr (ONE) {
+    // the weight loads go out between the parameter loads and their LDS
+    // writes, and the first block is peeled: products start as their own
+    // weights arrive
+    uint4 pre[NV];
+    uint32_t mpre;
+    load_tile(tile, pre, mpre);
+    issue_params();
+    load_weights();
+    commit_params();
+    lds_barrier();
+    layer_norm_to_lds(tile, pre, mpre, 0);
+    lds_barrier();
+    compute(first, tile, 0);
+  } else if constexpr (BF) {
+    // bf16 is HBM-bound: pair_repr and the mask are prefetched two tiles
+    // ahead, alternately into A and B
     uint4 preA[NV], preB[NV];
     uint32_t mA, mB = 0;
     load_tile(tile, preA, mA);
     if (tile + G < a.tiles) load_tile(tile + G, preB, mB);
-    load_vecs();
+    issue_params();
+    commit_params();
     load_weights();
     lds_barrier();
+    layer_norm_to_lds(tile, preA, mA, 0);
+    lds_barrier();
+    if (tile + 2 * G < a.tiles) load_tile(tile + 2 * G, preA, mA);
+    compute(first, tile, 0);
 #pragma unroll 1
-    for (; tile < a.tiles; tile += 2 * G) {
-      layer_norm_to_lds(tile, preA, mA, 0);
+    for (tile += G; tile < a.tiles; tile += 2 * G) {
+      layer_norm_to_lds(tile, preB, mB, 1);
       lds_barrier();
-      if (tile + 2 * G < a.tiles) load_tile(tile + 2 * G, preA, mA);
-      compute(tile, 0);
+      if (tile + 2 * G < a.tiles) load_tile(tile + 2 * G, preB, mB);
+      compute(later, tile, 1);
       if (tile + G >= a.tiles) break;
-      layer_norm_to_lds(tile + G, preB, mB, 1);
+      layer_norm_to_lds(tile + G, preA, mA, 0);
       lds_barrier();
-      if (tile + 3 * G < a.tiles) load_tile(tile + 3 * G, preB, mB);
-      compute(tile + G, 1);
+      if (tile + 3 * G < a.tiles) load_tile(tile + 3 * G, preA, mA);
+      compute(later, tile + G, 0);
     }
   } else {
-    // fp32: the next tile is prefetched one ahead
+    // fp32: the next tile is prefetched one ahead (no peel: the loop's
+    // registers are full)
     uint4 pre[NV];
     uint32_t mpre;
-    int buf = 0;
     load_tile(tile, pre, mpre);
-    load_vecs();
+    issue_params();
+    commit_params();
     load_weights();
     lds_barrier();
+    int buf = 0;
 #pragma unroll 1
     for (; tile < a.tiles; tile += G) {
       layer_norm_to_lds(tile, pre, mpre, buf);
       lds_barrier();
       if (tile + G < a.tiles) load_tile(tile + G, pre, mpre);
-      compute(tile, buf);
+      compute(later, tile, buf);
       buf ^= 1;
     }
   }
@@ -374,7 +431,10 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
 
 template <typename T, int D, int DH>
 static hipError_t launch_k1_t(const K1Args &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k1_ln_proj<T, D, DH>), dim3(grid), dim3(K1Shape<T, D>::THREADS), 0, s, a);
+  if (a.tiles <= grid)
+    hipLaunchKernelGGL((k1_ln_proj<T, D, DH, true>), dim3(a.tiles), dim3(K1Shape<T, D>::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((k1_ln_proj<T, D, DH, false>), dim3(grid), dim3(K1Shape<T, D>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -400,7 +460,7 @@ int k1_blocks_per_cu(int dtype, int D, int dh) {
   int n = 0;
 #define TRI_K1_OCC(TT, DD, HH)                                                                                    \
   if (D == DD && dh == HH &&                                                                                      \
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k1_ln_proj<TT, DD, HH>, K1Shape<TT, DD>::THREADS, 0) !=    \
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k1_ln_proj<TT, DD, HH, false>, K1Shape<TT, DD>::THREADS, 0) != \
           hipSuccess)                                                                                             \
     n = 1;
   if (dtype == TRI_ATTN_BF16) {

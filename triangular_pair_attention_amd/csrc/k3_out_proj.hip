@@ -6,7 +6,7 @@
 // g * o comes from kernel 2, written over the gate in the workspace as
 // [b][i][c/16][j][16]. Work unit: 64 consecutive positions (b, i, j0..j0+63);
 // persistent grid. Each wave holds the 16 rows of Wo of one output channel
-// block in registers; the tile goes through LDS once, is multiplied on the
+// block in registers (read from a copy in fragment order); the tile goes through LDS once, is multiplied on the
 // matrix cores (bias as the accumulator's start), and the result goes back
 // through LDS so that every output row is written as whole 16-byte chunks.
 // The next tile is prefetched into registers while the current one computes.
@@ -41,19 +41,22 @@ __global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
   const int g = lane >> 4, r16 = lane & 15;
   const int N = a.N, Np = a.Np, nch = a.nchunk;
   const T *GO = reinterpret_cast<const T *>(a.go);
-  const T *Wo = reinterpret_cast<const T *>(a.Wo);
 
+  // Wo rows of this wave's block, stored in fragment order (each load of the
+  // wave reads 1 KB contiguously): lane (g, r16) holds row wave*16 + r16,
+  // K-range [g*KQ, g*KQ+KQ)
+  constexpr int NVW = D * ES / 64;
   Frag wo[KS];
   {
-    const T *wrow = Wo + (size_t)(wave * 16 + r16) * D + g * KQ;
-    if constexpr (BF) {
+    const char *wsrc = reinterpret_cast<const char *>(a.Wof) + ((size_t)wave * NVW * 64 + lane) * 16;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) wo[s] = as_bf16x8(ldg<uint4>(wrow + 8 * s));
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; s += 4) {
-        const float4 v = ldg<float4>(wrow + s);
-        wo[s] = v.x, wo[s + 1] = v.y, wo[s + 2] = v.z, wo[s + 3] = v.w;
+    for (int v = 0; v < NVW; ++v) {
+      const uint4 u = ldg<uint4>(wsrc + (size_t)v * 1024);
+      if constexpr (BF) {
+        wo[v] = as_bf16x8(u);
+      } else {
+        wo[4 * v] = __uint_as_float(u.x), wo[4 * v + 1] = __uint_as_float(u.y);
+        wo[4 * v + 2] = __uint_as_float(u.z), wo[4 * v + 3] = __uint_as_float(u.w);
       }
     }
   }

@@ -18,7 +18,8 @@ struct tri_attn {
   int k3_grid;     // persistent grid of kernel 3
   void *wpack;     // [(4D + 16)][D] Wq; Wk; Wv; Wg; Wz; zero rows
   void *vecs;      // gamma, beta, bg, bo ([D] each), then Wo [D][D]
-  size_t wpack_bytes, vecs_bytes;
+  void *wfrag;     // Wq; Wk; Wv; Wg, then Wo, in fragment order
+  size_t wpack_bytes, vecs_bytes, wfrag_bytes;
 };
 
 namespace tpa {
@@ -116,6 +117,13 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
     delete t;
     return TRI_ATTN_ERR_OOM;
   }
+  t->wfrag_bytes = (size_t)5 * D * D * e;
+  if (hipMalloc(&t->wfrag, t->wfrag_bytes) != hipSuccess) {
+    (void)hipFree(t->wpack);
+    (void)hipFree(t->vecs);
+    delete t;
+    return TRI_ATTN_ERR_OOM;
+  }
   char *wp = static_cast<char *>(t->wpack);
   char *vp = static_cast<char *>(t->vecs);
   const size_t mat = (size_t)D * D * e, vec = (size_t)D * e;
@@ -130,11 +138,14 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
   ok = ok && hipMemcpyAsync(vp + 2 * vec, w->b_gate, vec, hipMemcpyDefault, s) == hipSuccess;
   ok = ok && hipMemcpyAsync(vp + 3 * vec, w->b_out, vec, hipMemcpyDefault, s) == hipSuccess;
   ok = ok && hipMemcpyAsync(vp + 4 * vec, w->w_out, mat, hipMemcpyDefault, s) == hipSuccess;
+  ok = ok && launch_pack_frags(e, D, wp, t->wfrag, 4 * D / 16, s) == hipSuccess;
+  ok = ok && launch_pack_frags(e, D, vp + 4 * vec, static_cast<char *>(t->wfrag) + 4 * mat, D / 16, s) == hipSuccess;
   ok = ok && hipStreamSynchronize(s) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
     (void)hipFree(t->wpack);
     (void)hipFree(t->vecs);
+    (void)hipFree(t->wfrag);
     delete t;
     return TRI_ATTN_ERR_HIP;
   }
@@ -192,6 +203,7 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a1.P = pair_repr;
   a1.mask = pair_mask;
   a1.W = t->wpack;
+  a1.Wf = t->wfrag;
   a1.gamma = vp;
   a1.beta = vp + (size_t)D * e;
   a1.bg = vp + (size_t)2 * D * e;
@@ -218,7 +230,7 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
 
   K3Args a3{};
   a3.go = a1.g;
-  a3.Wo = vp + (size_t)4 * D * e;
+  a3.Wof = static_cast<const char *>(t->wfrag) + (size_t)4 * D * D * e;
   a3.bo = vp + (size_t)3 * D * e;
   a3.out = out;
   a3.B = B, a3.N = N, a3.Np = L.Np, a3.nchunk = L.nchunk;
@@ -252,6 +264,7 @@ int tri_attn_destroy(tri_attn_t t) {
   if (hipDeviceSynchronize() != hipSuccess) rc = TRI_ATTN_ERR_HIP;
   if (hipFree(t->wpack) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
   if (hipFree(t->vecs) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
+  if (hipFree(t->wfrag) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
   delete t;
   return rc;
 }

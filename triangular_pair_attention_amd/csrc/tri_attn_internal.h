@@ -1,4 +1,4 @@
-// Internal declarations shared by the host library and the two kernels.
+// Internal declarations shared by the host library and the kernels.
 // Not part of the public ABI (include/tri_attn.h is).
 #pragma once
 
@@ -24,6 +24,7 @@ struct K1Args {
   const void *P;          // [B][N][N][D]
   const uint8_t *mask;    // [B][N][N]
   const void *W;          // packed [(4D + 16)][D]: Wq; Wk; Wv; Wg; Wz; zero rows
+  const void *Wf;         // Wq; Wk; Wv; Wg in fragment order (pack_weights.hip)
   const void *gamma, *beta, *bg;  // [D]
   void *q, *k, *vt, *g;
   float *zm, *zmax, *kmax, *vsum;
@@ -45,7 +46,8 @@ struct K2Args {
 // Kernel 3: output projection of g * o (left by kernel 2 in the gate region).
 struct K3Args {
   const void *go;  // [B][N][D/16][Np][16]
-  const void *Wo, *bo;
+  const void *Wof;  // Wo in fragment order (pack_weights.hip)
+  const void *bo;
   void *out;       // [B][N][N][D]
   int B, N, Np, nchunk, tiles;
 };
@@ -54,6 +56,8 @@ struct K3Args {
 hipError_t launch_k1(int dtype, int D, int dh, const K1Args &a, int grid, hipStream_t s);
 hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, hipStream_t s);
 hipError_t launch_k3(int dtype, int D, const K3Args &a, int grid, hipStream_t s);
+// Copies the row-major [16 * nblocks][D] matrix `rows` into fragment order.
+hipError_t launch_pack_frags(int elem_bytes, int D, const void *rows, void *frags, int nblocks, hipStream_t s);
 int k2_items(int dtype, int D, int dh, int B, int N);
 int k3_blocks_per_cu(int dtype, int D);  // resident workgroups of kernel 3 per CU
 int k1_blocks_per_cu(int dtype, int D, int dh);  // resident workgroups of kernel 1 per CU
