@@ -1,5 +1,6 @@
 // Calibration microbenchmarks for the roofline ceilings on gfx950: matrix-core
-// rates of the MFMA shapes the kernels use, the transcendental (v_exp_f32) and
+// rates of the MFMA shapes the kernels use (with fixed and with changing
+// operands), the transcendental (v_exp_f32) and
 // plain FMA VALU rates, and a streaming HBM copy. Every kernel runs a fixed,
 // bounded loop on registers (no memory traffic) except the copy.
 //
@@ -35,6 +36,54 @@ __global__ __launch_bounds__(256) void mfma_bf16_32(float *out, float seed) {
   for (int it = 0; it < ITERS; ++it)
 #pragma unroll
     for (int i = 0; i < CHAINS; ++i) c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[i], 0, 0, 0);
+  float s = 0;
+  for (int i = 0; i < CHAINS; ++i) s += c[i][0] + c[i][1] + c[i][2] + c[i][3];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// The same products with operands that change from one instruction to the
+// next (random mantissas, eight register sets cycled), as in a real GEMM: the
+// matrix cores' sustained rate depends on the data they switch.
+__device__ __forceinline__ uint32_t xorshift(uint32_t &x) {
+  x ^= x << 13;
+  x ^= x >> 17;
+  x ^= x << 5;
+  return x;
+}
+__device__ __forceinline__ float rand_unit(uint32_t &x) {  // uniform in [-0.5, 0.5) with a full mantissa
+  return __uint_as_float((xorshift(x) & 0x007fffffu) | 0x3f800000u) - 1.5f;
+}
+
+__global__ __launch_bounds__(256) void mfma_bf16_32_rand(float *out, float seed) {
+  uint32_t x = (threadIdx.x + 1) * 0x9e3779b9u ^ __float_as_uint(seed);
+  bf16x8 a[4], b[4];
+  for (int k = 0; k < 4; ++k)
+    for (int e = 0; e < 8; ++e) a[k][e] = (__bf16)rand_unit(x), b[k][e] = (__bf16)rand_unit(x);
+  f32x4 c[CHAINS];
+  for (int i = 0; i < CHAINS; ++i) c[i] = f32x4{0, 0, 0, 0};
+  for (int it = 0; it < ITERS; it += 4)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < CHAINS; ++i)
+        c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[(u + i) & 3], b[(u + 3 * i + 1) & 3], c[i], 0, 0, 0);
+  float s = 0;
+  for (int i = 0; i < CHAINS; ++i) s += c[i][0] + c[i][1] + c[i][2] + c[i][3];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void mfma_f32_4_rand(float *out, float seed) {
+  uint32_t x = (threadIdx.x + 1) * 0x9e3779b9u ^ __float_as_uint(seed);
+  float a[8], b[8];
+  for (int k = 0; k < 8; ++k) a[k] = rand_unit(x), b[k] = rand_unit(x);
+  f32x4 c[CHAINS];
+  for (int i = 0; i < CHAINS; ++i) c[i] = f32x4{0, 0, 0, 0};
+  for (int it = 0; it < ITERS; it += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < CHAINS; ++i)
+        c[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(u + i) & 7], b[(u + 3 * i + 1) & 7], c[i], 0, 0, 0);
   float s = 0;
   for (int i = 0; i < CHAINS; ++i) s += c[i][0] + c[i][1] + c[i][2] + c[i][3];
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
@@ -143,6 +192,8 @@ int main() {
   const double t_bf32 = time_kernel(mfma_bf16_32, grid, out) * 1e-3;
   const double t_bf16 = time_kernel(mfma_bf16_16, grid, out) * 1e-3;
   const double t_f32 = time_kernel(mfma_f32_4, grid, out) * 1e-3;
+  const double t_bf32r = time_kernel(mfma_bf16_32_rand, grid, out) * 1e-3;
+  const double t_f32r = time_kernel(mfma_f32_4_rand, grid, out) * 1e-3;
   const double t_exp = time_kernel(valu_exp, grid, out) * 1e-3;
   const double t_fma = time_kernel(valu_fma, grid, out) * 1e-3;
   const double t_mix = time_kernel(valu_exp_fma, grid, out) * 1e-3;
@@ -170,10 +221,12 @@ int main() {
 
   printf("{\"cus\": %d, \"clock_mhz\": %.0f, "
          "\"mfma_bf16_16x16x32_TFLOPs\": %.1f, \"mfma_bf16_16x16x16_TFLOPs\": %.1f, "
-         "\"mfma_f32_16x16x4_TFLOPs\": %.1f, \"v_exp_f32_Gops\": %.1f, \"v_fma_f32_Gops\": %.1f, "
+         "\"mfma_f32_16x16x4_TFLOPs\": %.1f, \"mfma_bf16_16x16x32_random_TFLOPs\": %.1f, "
+         "\"mfma_f32_16x16x4_random_TFLOPs\": %.1f, \"v_exp_f32_Gops\": %.1f, \"v_fma_f32_Gops\": %.1f, "
          "\"exp_plus_3fma_Gexp\": %.1f, \"copy_GBps\": %.1f}\n",
          cus, clk_khz / 1000.0, waves * per_wave * 16384 / t_bf32 / 1e12, waves * per_wave * 8192 / t_bf16 / 1e12,
-         waves * per_wave * 2048 / t_f32 / 1e12, lanes / t_exp / 1e9, lanes / t_fma / 1e9, lanes / t_mix / 1e9,
+         waves * per_wave * 2048 / t_f32 / 1e12, waves * per_wave * 16384 / t_bf32r / 1e12,
+         waves * per_wave * 2048 / t_f32r / 1e12, lanes / t_exp / 1e9, lanes / t_fma / 1e9, lanes / t_mix / 1e9,
          copy_GBps);
   CHECK(hipFree(out));
   CHECK(hipFree(a));
