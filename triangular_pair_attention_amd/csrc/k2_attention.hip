@@ -141,84 +141,14 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   T *G = reinterpret_cast<T *>(a.g);
   const float *ZM = a.zm + (size_t)(b * H + t) * N * Np;
 
-  // The per-chunk maxima are spread over the lanes (one load each, all in
-  // flight together) and reduced across lanes.
-  // ---- this wave's rows: bound of |k| over the row's keys
-  int rows[IG];
-  float kn2[IG];
-#pragma unroll
-  for (int i = 0; i < IG; ++i) {
-    rows[i] = min(i0 + wr * IG + i, N - 1);
-    // |k|^2 <= sum over the head's 16-channel blocks of each block's chunk maxima
-    float m2 = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
-      float m = 0.f;
-      for (int c = lane; c < nch; c += 64) m = fmaxf(m, kp[c]);
-#pragma unroll
-      for (int x = 1; x < 64; x <<= 1) m = xor_max(m, x);
-      m2 += m;
-    }
-    kn2[i] = m2;
-  }
-
-  // ---- this wave's query columns: bias+mask maximum, last live key chunk.
-  // Lane (g, r16) takes chunks g, g + 4, ... of column r16.
-  float zmx[JW];
-  bool colmask[JW];  // a real column whose keys are all masked
-  int kend = 0;
-#pragma unroll
-  for (int jb = 0; jb < JW; ++jb) {
-    const int j = j0 + (wq * JW + jb) * 16 + r16;
-    float zx = -INFINITY;
-    if (j < N) {
-      const float *zp = a.zmax + ((size_t)(b * H + t) * N + j) * nch;
-#pragma unroll 4
-      for (int c = g; c < nch; c += 4) {
-        const float v = zp[c];
-        zx = fmaxf(zx, v);
-        if (v > -INFINITY) kend = max(kend, c + 1);
-      }
-    }
-    zx = group4_max(zx);
-    zmx[jb] = zx;
-    colmask[jb] = (j < N) && zx == -INFINITY;
-  }
-  // Sum of v over all keys of each (row, channel) of the workgroup, from
-  // kernel 1's per-chunk sums: the uniform weights of a fully masked column
-  // (finite fill). One thread per (row, channel), loads issued with the
-  // other setup loads.
-  __shared__ __align__(16) float vsum_s[RB * DH];
-  for (int x = threadIdx.x; x < RB * DH; x += NW * 64) {
-    const int r = x / DH, ch = x - r * DH;
-    const float *p = a.vsum + ((size_t)(b * N + min(i0 + r, N - 1)) * D + t * DH + ch) * nch;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    int c = 0;
-    for (; c + 4 <= nch; c += 4) s0 += p[c], s1 += p[c + 1], s2 += p[c + 2], s3 += p[c + 3];
-    for (; c < nch; ++c) s0 += p[c];
-    vsum_s[x] = (s0 + s1) + (s2 + s3);
-  }
-  // the workgroup steps through the keys together: its end is the max over all waves
-  for (int m = 1; m < 64; m <<= 1) kend = max(kend, __shfl_xor(kend, m, 64));
-  __shared__ int kend_s[NW];
-  __shared__ int need_s;
-  if (lane == 0) kend_s[wave] = kend;
-  if (threadIdx.x == 0) need_s = 0;
-  lds_barrier();
-  {
-    int k = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) k = max(k, kend_s[w]);
-    kend = k;
-  }
-  const int nsteps = __builtin_amdgcn_readfirstlane(kend) * kChunk / KT;
-
-  // ---- query fragments and their norms; the shift
+  // ---- query fragments (loads issued first; their norms are taken after the
+  // setup loads below have also been issued)
   // bf16: lane (g, r16) holds q'[j = r16][8g..8g+7] (d = 16: groups 0-1 real, group 2 slot 0 = -m);
   // fp32: lane (g, r16) holds q'[j][g*d/4 .. +d/4).
+  int rows[IG];
+#pragma unroll
+  for (int i = 0; i < IG; ++i) rows[i] = min(i0 + wr * IG + i, N - 1);
   Frag qf[IG][JW][BF ? 1 : QS];
-  float msh[IG][JW];
 #pragma unroll
   for (int i = 0; i < IG; ++i)
 #pragma unroll
@@ -226,16 +156,10 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
       const int j = min(j0 + (wq * JW + jb) * 16 + r16, Np - 1);
       const size_t rowbase = (size_t)(b * N + rows[i]) * NB;
       const int cb = (DH == 16) ? t : 2 * t + (g >> 1);
-      float n2 = 0.f;
       if constexpr (BF) {
         uint4 raw = ldg<uint4>(Q + ((rowbase + cb) * Np + j) * 16 + 8 * (g & 1));
         if (DH == 16 && g >= 2) raw = make_uint4(0, 0, 0, 0);
         qf[i][jb][0] = as_bf16x8(raw);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (float)qf[i][jb][0][e];
-          n2 += x * x;
-        }
       } else {
         const int off = (DH == 16) ? 4 * g : 8 * (g & 1);
         const float *src = reinterpret_cast<const float *>(Q) + ((rowbase + cb) * Np + j) * 16 + off;
@@ -244,39 +168,26 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
           const float4 v = ldg<float4>(src + s);
           qf[i][jb][s] = v.x, qf[i][jb][s + 1] = v.y, qf[i][jb][s + 2] = v.z, qf[i][jb][s + 3] = v.w;
         }
-#pragma unroll
-        for (int s = 0; s < QS; ++s) n2 += qf[i][jb][s] * qf[i][jb][s];
       }
-      n2 = group4_sum(n2);
-      msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : sqrtf(n2 * kn2[i]) + zmx[jb] + a.shift_slack;
     }
 
-  auto set_shift = [&](const float (&m)[IG][JW]) {
-    if constexpr (BF) {
-#pragma unroll
-      for (int i = 0; i < IG; ++i)
-#pragma unroll
-        for (int jb = 0; jb < JW; ++jb) {
-          const __bf16 nm = (__bf16)(-m[i][jb]);
-          const __bf16 z = (__bf16)0.f;
-          if (DH == 16 && g == 2) qf[i][jb][0] = bf16x8{nm, z, z, z, z, z, z, z};
-        }
-    }
-  };
-  set_shift(msh);
-  // bf16, d = 32: the shift costs two more MFMAs per score tile. Where every
-  // bound of the wave is at most 64, exp2 of a score cannot overflow (2^64 per
-  // key, sums far below the fp32 range) and the wave goes without it; scores
-  // far below their bound only risk a tiny sum, which the recovery below
-  // catches either way.
-  bool shift_on = true;
-  if constexpr (BF && DH == 32) {
-    bool big = false;
+  // ---- the gate of this wave's outputs, loaded now and used in the
+  // epilogue, so its round trip is hidden behind the key loop (bf16 d = 16
+  // has no registers to spare and loads it in the epilogue). Addresses are
+  // clamped into the tensor; values of rows or columns past N are not used.
+  constexpr bool GPRE = !(BF && DH == 16);
+  using GVec = typename std::conditional<BF, uint2, float4>::type;
+  GVec gpre[GPRE ? IG : 1][GPRE ? JW : 1][GPRE ? MB : 1];
+  if constexpr (GPRE) {
 #pragma unroll
     for (int i = 0; i < IG; ++i)
 #pragma unroll
-      for (int jb = 0; jb < JW; ++jb) big |= !(msh[i][jb] <= 64.f);
-    shift_on = __ballot(big) != 0;
+      for (int jb = 0; jb < JW; ++jb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int jc = min(j0 + (wq * JW + jb) * 16 + r16, N - 1);
+          gpre[i][jb][mb] = ldg<GVec>(G + (((size_t)(b * N + rows[i]) * NB + t * MB + mb) * Np + jc) * 16 + 4 * g);
+        }
   }
 
   // ---- loader: this wave fills blocks wave + NW*l of each stage; each lane
@@ -341,6 +252,156 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
     for (int l = 0; l < LPW; ++l) dma16_to_lds(src_ptr[l] + (size_t)s * src_step[l], stage + blk_lds[l]);
   };
+  // The first LA key steps go out now, before the setup loads: every key
+  // step below Np / KT (>= LA) addresses padded, in-bounds rows, so they are
+  // issued before the number of live steps is known; steps past that number
+  // are waited for and ignored.
+  constexpr int LA = NS - 1;  // steps in flight
+  static_assert(LA >= 1 && LA <= 3, "");
+#pragma unroll
+  for (int s = 0; s < LA; ++s) issue(s);
+
+  // The per-chunk maxima are spread over the lanes and reduced across lanes.
+  // The first round of every one of these loads is issued before any of them
+  // is used (one round trip); rows longer than that first round (more than 64
+  // key chunks for |k|, 4 for the bias) continue in loops.
+  // |k|^2 <= sum over the head's 16-channel blocks of each block's chunk maxima;
+  // lane l takes chunks l, l + 64, ... of each row's block.
+  // Bias+mask maximum and last live key chunk of this wave's query columns:
+  // lane (g, r16) takes chunks g, g + 4, ... of column r16.
+  float kmx[IG][MB];
+#pragma unroll
+  for (int i = 0; i < IG; ++i)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
+      kmx[i][mb] = lane < nch ? kp[lane] : 0.f;
+    }
+  float zfirst[JW];
+#pragma unroll
+  for (int jb = 0; jb < JW; ++jb) {
+    const int j = j0 + (wq * JW + jb) * 16 + r16;
+    zfirst[jb] = (j < N && g < nch) ? a.zmax[((size_t)(b * H + t) * N + j) * nch + g] : -INFINITY;
+  }
+  // Sum of v over all keys of each (row, channel) of the workgroup, from
+  // kernel 1's per-chunk sums: the uniform weights of a fully masked column
+  // (finite fill). One thread per (row, channel), loads issued with the
+  // other setup loads.
+  __shared__ __align__(16) float vsum_s[RB * DH];
+  for (int x = threadIdx.x; x < RB * DH; x += NW * 64) {
+    const int r = x / DH, ch = x - r * DH;
+    const float *p = a.vsum + ((size_t)(b * N + min(i0 + r, N - 1)) * D + t * DH + ch) * nch;
+    // four independent loads per round (guarded, not a dependent tail loop)
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    for (int c = 0; c < nch; c += 4) {
+      const float v0 = p[c];
+      const float v1 = c + 1 < nch ? p[c + 1] : 0.f;
+      const float v2 = c + 2 < nch ? p[c + 2] : 0.f;
+      const float v3 = c + 3 < nch ? p[c + 3] : 0.f;
+      s0 += v0, s1 += v1, s2 += v2, s3 += v3;
+    }
+    vsum_s[x] = (s0 + s1) + (s2 + s3);
+  }
+  float kn2[IG];
+#pragma unroll
+  for (int i = 0; i < IG; ++i) {
+    float m2 = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
+      float m = kmx[i][mb];
+      for (int c = lane + 64; c < nch; c += 64) m = fmaxf(m, kp[c]);
+#pragma unroll
+      for (int x = 1; x < 64; x <<= 1) m = xor_max(m, x);
+      m2 += m;
+    }
+    kn2[i] = m2;
+  }
+  float zmx[JW];
+  bool colmask[JW];  // a real column whose keys are all masked
+  int kend = 0;
+#pragma unroll
+  for (int jb = 0; jb < JW; ++jb) {
+    const int j = j0 + (wq * JW + jb) * 16 + r16;
+    float zx = zfirst[jb];
+    if (zx > -INFINITY) kend = max(kend, g + 1);
+    if (j < N) {
+      const float *zp = a.zmax + ((size_t)(b * H + t) * N + j) * nch;
+      for (int c = g + 4; c < nch; c += 4) {
+        const float v = zp[c];
+        zx = fmaxf(zx, v);
+        if (v > -INFINITY) kend = max(kend, c + 1);
+      }
+    }
+    zx = group4_max(zx);
+    zmx[jb] = zx;
+    colmask[jb] = (j < N) && zx == -INFINITY;
+  }
+  // the workgroup steps through the keys together: its end is the max over all waves
+  for (int m = 1; m < 64; m <<= 1) kend = max(kend, __shfl_xor(kend, m, 64));
+  __shared__ int kend_s[NW];
+  __shared__ int need_s;
+  if (lane == 0) kend_s[wave] = kend;
+  if (threadIdx.x == 0) need_s = 0;
+  lds_barrier();
+  {
+    int k = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) k = max(k, kend_s[w]);
+    kend = k;
+  }
+  const int nsteps = __builtin_amdgcn_readfirstlane(kend) * kChunk / KT;
+
+  // ---- query norms and the shift
+  float msh[IG][JW];
+#pragma unroll
+  for (int i = 0; i < IG; ++i)
+#pragma unroll
+    for (int jb = 0; jb < JW; ++jb) {
+      float n2 = 0.f;
+      if constexpr (BF) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)qf[i][jb][0][e];
+          n2 += x * x;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < QS; ++s) n2 += qf[i][jb][s] * qf[i][jb][s];
+      }
+      n2 = group4_sum(n2);
+      msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : sqrtf(n2 * kn2[i]) + zmx[jb] + a.shift_slack;
+    }
+
+
+  auto set_shift = [&](const float (&m)[IG][JW]) {
+    if constexpr (BF) {
+#pragma unroll
+      for (int i = 0; i < IG; ++i)
+#pragma unroll
+        for (int jb = 0; jb < JW; ++jb) {
+          const __bf16 nm = (__bf16)(-m[i][jb]);
+          const __bf16 z = (__bf16)0.f;
+          if (DH == 16 && g == 2) qf[i][jb][0] = bf16x8{nm, z, z, z, z, z, z, z};
+        }
+    }
+  };
+  set_shift(msh);
+  // bf16, d = 32: the shift costs two more MFMAs per score tile. Where every
+  // bound of the wave is at most 64, exp2 of a score cannot overflow (2^64 per
+  // key, sums far below the fp32 range) and the wave goes without it; scores
+  // far below their bound only risk a tiny sum, which the recovery below
+  // catches either way.
+  bool shift_on = true;
+  if constexpr (BF && DH == 32) {
+    bool big = false;
+#pragma unroll
+    for (int i = 0; i < IG; ++i)
+#pragma unroll
+      for (int jb = 0; jb < JW; ++jb) big |= !(msh[i][jb] <= 64.f);
+    shift_on = __ballot(big) != 0;
+  }
+
   if constexpr (BF && DH == 16) {
     // the constant half of every k block: lanes 32-47 read (1, 0, ..., 0), lanes 48-63 zeros
     for (int x = threadIdx.x; x < NS * NK * 32; x += NW * 64) {
@@ -492,13 +553,13 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   // The key loop over the ring: stage s is waited for (this wave's own loads
   // via vmcnt, everyone's via the barrier, which also retires every wave's
   // reads of the stage that the next issue overwrites), then step s + 2 is
-  // issued and step s computed.
-  constexpr int LA = NS - 1;  // steps in flight
-  static_assert(LA >= 1 && LA <= 3, "");
-  auto key_loop = [&](bool max_pass, float (&mx)[IG][JW]) {
+  // issued and step s computed. `issued`: the first LA steps are already out.
+  auto key_loop = [&](bool max_pass, float (&mx)[IG][JW], bool issued) {
+    if (!issued) {
 #pragma unroll
-    for (int s = 0; s < LA; ++s)
-      if (s < nsteps) issue(s);
+      for (int s = 0; s < LA; ++s)
+        if (s < nsteps) issue(s);
+    }
 #pragma unroll 1
     for (int s = 0; s < nsteps; ++s) {
       // step s is complete once at most (steps issued after it) * LPW loads are outstanding
@@ -530,7 +591,8 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 
   float dummy[IG][JW];
   zero_acc();
-  key_loop(false, dummy);
+  key_loop(false, dummy, true);
+  vmcnt_wait<0>();  // early steps past the live ones, if any, have landed
   row_sums();
 
   // ---- recovery: exact maximum where the bound was too loose. The decision is
@@ -553,7 +615,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         msh[i][jb] = 0.f;
       }
     set_shift(msh);  // no shift during the max pass
-    key_loop(true, mx);
+    key_loop(true, mx, false);
 #pragma unroll
     for (int i = 0; i < IG; ++i)
 #pragma unroll
@@ -565,7 +627,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
     shift_on = true;
     zero_acc();
     lds_barrier();  // every wave is done with the ring before it is refilled
-    key_loop(false, dummy);
+    key_loop(false, dummy, false);
     row_sums();
   }
 
@@ -594,13 +656,15 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         for (int mb = 0; mb < MB; ++mb) {
           T *gp = G + (((size_t)(b * N + row) * NB + t * MB + mb) * Np + j) * 16 + 4 * g;
           float gv[4];
-          if constexpr (BF) {
-            const uint2 w = ldg<uint2>(gp);
+          GVec w;
+          if constexpr (GPRE)
+            w = gpre[i][jb][mb];
+          else
+            w = ldg<GVec>(gp);
+          if constexpr (BF)
             gv[0] = bflo(w.x), gv[1] = bfhi(w.x), gv[2] = bflo(w.y), gv[3] = bfhi(w.y);
-          } else {
-            const float4 w = ldg<float4>(gp);
+          else
             gv[0] = w.x, gv[1] = w.y, gv[2] = w.z, gv[3] = w.w;
-          }
           float ov[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
