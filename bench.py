@@ -34,6 +34,14 @@ PEAK = {  # MI355X published dense peaks
     "mfma_f32_TFLOPs": 157.3,
     "mfma_bf16_TFLOPs": 2500.0,
 }
+# Rates measured on one MI355X by triangular_pair_attention_amd/calib/calib.hip
+# (tri_attn_calib): the attention kernel's exponentials and matrix-core work
+# do not overlap, so its floor is the sum of the two at these rates.
+CALIB = {
+    "v_exp_f32_Gops": 13224.7,
+    "mfma_bf16_random_TFLOPs": 1655.4,
+    "mfma_f32_random_TFLOPs": 148.2,
+}
 KERNEL_SOURCES = {
     "k1_ln_proj": "triangular_pair_attention_amd/csrc/k1_ln_proj.hip",
     "k2_attention": "triangular_pair_attention_amd/csrc/k2_attention.hip",
@@ -77,6 +85,23 @@ def roofline_of(kernel, w, m, ms):
     else:
         r = {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": mfma, "unit": "TFLOP/s"}
     r["frac"] = r["achieved"] / r["peak"]
+    return r
+
+
+def attention_floor(w, m, ms, mask=None):
+    """Kernel 2 against its binding floor: the exponentials (one per score,
+    B*h*N^3) plus the matrix-core work at the calibrated rates, serially.
+    With a mask, also the TFLOP/s on the valid (j, k) score pairs only."""
+    B, N, h = w.B, w.N, w.h
+    exps = B * h * N ** 3
+    mfma = CALIB["mfma_f32_random_TFLOPs"] if w.dtype == "f32" else CALIB["mfma_bf16_random_TFLOPs"]
+    t_exp = exps / (CALIB["v_exp_f32_Gops"] * 1e9)
+    t_mfma = m["k2_attention"]["flops"] / (mfma * 1e12)
+    r = {"exps": exps, "exp_Gops": exps / (ms * 1e-3) / 1e9, "floor_ms": (t_exp + t_mfma) * 1e3,
+         "frac_of_floor": (t_exp + t_mfma) * 1e3 / ms}
+    if mask is not None:
+        valid = int((mask != 0).sum())  # (b, j, k) pairs, each scored for all N rows i
+        r["valid_tflops"] = 4 * N * w.D * valid / (ms * 1e-3) / 1e12
     return r
 
 
@@ -259,6 +284,7 @@ def main():
         "tflops": tflops,
         "kernels_ms": ms_k,
         "kernels_roofline": {k: roofline_of(k, w, m, v) for k, v in ms_k.items()},
+        "attention_floor": attention_floor(w, m, ms_k2, inp["pair_mask"]),
         "wall_s_timed": wall,
         "roofline": roof,
     }

@@ -74,3 +74,19 @@ def test_committed_traffic_table_parses():
                 float(cells[3]), float(cells[4]), float(cells[5]), float(cells[6])
                 rows += 1
     assert rows >= 6
+
+
+def test_attention_floor():
+    import numpy as np
+    w = WORKLOADS[5]
+    m = bench.work_model(w)
+    exps = 4 * 8 * 512 ** 3
+    t_floor = exps / (bench.CALIB["v_exp_f32_Gops"] * 1e9) + m["k2_attention"]["flops"] / (
+        bench.CALIB["mfma_bf16_random_TFLOPs"] * 1e12)
+    mask = np.zeros((4, 512, 512), np.uint8)
+    mask[:, :100, :200] = 1
+    r = bench.attention_floor(w, m, 1.0, mask)
+    assert r["exps"] == exps
+    assert r["floor_ms"] == pytest.approx(t_floor * 1e3)
+    assert r["frac_of_floor"] == pytest.approx(t_floor * 1e3 / 1.0)
+    assert r["valid_tflops"] == pytest.approx(4 * 512 * 128 * (4 * 100 * 200) / 1e-3 / 1e12)

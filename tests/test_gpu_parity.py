@@ -146,8 +146,13 @@ def test_large_scores_stay_finite():
 
 
 # ------------------------------------------------------------------ stage parity of kernel 1
+# Up to one 64-position tile per resident workgroup, kernel 1 runs its straight
+# one-tile instantiation; more tiles (the last three shapes: 900, 900 and 1500
+# tiles, ragged last chunks) take the persistent loop with its prefetch.
 @pytest.mark.parametrize("dtype,shape", [("f32", (2, 40, 64, 4)), ("bf16", (1, 70, 128, 4)),
-                                         ("bf16", (1, 66, 128, 8)), ("f32", (1, 64, 128, 4))])
+                                         ("bf16", (1, 66, 128, 8)), ("f32", (1, 64, 128, 4)),
+                                         ("f32", (2, 150, 64, 4)), ("bf16", (2, 150, 128, 8)),
+                                         ("f32", (1, 300, 128, 4))])
 def test_projection_stage(dtype, shape):
     B_, N, D, h = shape
     d = D // h
