@@ -216,10 +216,11 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   };
 
   // One tile with this wave's projections starting at TYPE0 (compile time).
-  // PEEL: the first 16-position block is emitted as its own straight-line
-  // copy, so that on a workgroup's first tile each product waits only for its
-  // own weight registers while later ones are still arriving (inside a loop
-  // the compiler waits for all outstanding loads before entering it).
+  // PEEL (fp32): the first 16-position block is emitted as its own
+  // straight-line copy, so that on a workgroup's first tile each product waits
+  // only for its own weight registers while later ones are still arriving
+  // (inside a loop the compiler waits for all outstanding loads before
+  // entering it). bf16 tiles are straight-line code throughout.
   auto compute_tile = [&](auto type0_c, auto peel_c, int tile, int buf) __attribute__((always_inline)) {
     constexpr int TYPE0 = decltype(type0_c)::value;
     constexpr bool PEEL = decltype(peel_c)::value;
@@ -231,10 +232,9 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     float z_run = -INFINITY;
     static_assert(NW >= TILE / 16, "");
 
-    auto block = [&](int pb) __attribute__((always_inline)) {
+    auto products = [&](int pb, f32x4 (&acc)[TPW]) __attribute__((always_inline)) {
       // x fragments: lane (g, r16) = position pb*16 + r16, K-range [g*KQ, g*KQ+KQ)
       const T *xrow = &xs[buf][(pb * 16 + r16) * PITCH + g * KQ];
-      f32x4 acc[TPW];
 #pragma unroll
       for (int p = 0; p < TPW; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
       constexpr int KC = BF ? 1 : 4;
@@ -257,7 +257,9 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
               acc[p] = mfma(wf[p][s0 + s], xf[s], acc[p]);  // q, k, gate: rows = channels
           }
       }
-
+    };
+    auto epilogue = [&](int pb, const f32x4 (&acc)[TPW]) __attribute__((always_inline)) {
+      const T *xrow = &xs[buf][(pb * 16 + r16) * PITCH + g * KQ];  // for the pair-bias block
       const int jcol = j0 + pb * 16 + r16;  // position of this lane's column (q/k/gate tiles)
 #pragma unroll
       for (int p = 0; p < TPW; ++p) {
@@ -318,13 +320,37 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
         }
       }
     };
-    int pb0 = 0;
-    if constexpr (PEEL) {
-      block(0);
-      pb0 = 1;
-    }
+    static_assert(TILE / 16 == 4, "four 16-position blocks per tile");
+    if constexpr (BF) {
+      // software pipeline over the four blocks: the products of block pb + 1
+      // go to the matrix cores before the epilogue of block pb, which then
+      // finds its results ready (straight-line code, so the first tile's
+      // products also wait only for their own weights)
+      f32x4 accA[TPW], accB[TPW];
+      products(0, accA);
+      products(1, accB);
+      epilogue(0, accA);
+      products(2, accA);
+      epilogue(1, accB);
+      products(3, accB);
+      epilogue(2, accA);
+      epilogue(3, accB);
+    } else {
+      // fp32 has no registers for a second set of accumulators
+      int pb0 = 0;
+      if constexpr (PEEL) {
+        f32x4 acc[TPW];
+        products(0, acc);
+        epilogue(0, acc);
+        pb0 = 1;
+      }
 #pragma unroll 1
-    for (int pb = pb0; pb < TILE / 16; ++pb) block(pb);
+      for (int pb = pb0; pb < TILE / 16; ++pb) {
+        f32x4 acc[TPW];
+        products(pb, acc);
+        epilogue(pb, acc);
+      }
+    }
 
     // per-chunk sums of v (a fixed summation order: deterministic)
     if (TYPE0 <= 2 && TYPE0 + TPW > 2) {
