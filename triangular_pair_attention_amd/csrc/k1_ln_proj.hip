@@ -73,7 +73,8 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   __shared__ __align__(16) T wz_s[16 * PITCH];  // pair-bias weight block (rows >= h are zero)
   __shared__ float zpart_s[TILE / 16][16];      // per-block maxima of the pair bias of a tile
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar block and base arithmetic
   const int g = lane >> 4, r16 = lane & 15;
   const int cb = wave % NB;             // this wave's channel block in each of its projections
   const int type0 = (wave / NB) * TPW;  // first projection of this wave (0 q, 1 k, 2 v, 3 gate)
@@ -208,7 +209,10 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     }
   };
 
-  auto store4 = [&](T *dst, float v0, float v1, float v2, float v3) {
+  // four consecutive elements at element offset `off` from a uniform base: the
+  // offset stays a 32-bit byte offset, so the store adds it to the scalar base
+  auto store4 = [&](T *base, uint32_t off, float v0, float v1, float v2, float v3) {
+    char *dst = reinterpret_cast<char *>(base) + off * (uint32_t)ES;
     if constexpr (BF)
       stg<uint2>(dst, make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)));
     else
@@ -232,11 +236,24 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     float z_run = -INFINITY;
     static_assert(NW >= TILE / 16, "");
 
+    // gate bias of this lane's four channels (cb*16 + 4g .. +3): the gate
+    // accumulators start from it
+    f32x4 bg4 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (TYPE0 <= 3 && TYPE0 + TPW > 3) {
+      const float4 v = *reinterpret_cast<const float4 *>(&vec_s[2][cb * 16 + 4 * g]);
+      bg4 = f32x4{v.x, v.y, v.z, v.w};
+    }
+    // store bases of this tile (uniform); lanes add 32-bit offsets
+    T *const qbase = reinterpret_cast<T *>(a.q) + ((size_t)bi_row * NB + cb) * Np * 16;
+    T *const kbase = reinterpret_cast<T *>(a.k) + ((size_t)bi_row * NB + cb) * Np * 16;
+    T *const gbase = reinterpret_cast<T *>(a.g) + ((size_t)bi_row * NB + cb) * Np * 16;
+    T *const vbase = reinterpret_cast<T *>(a.vt) + (size_t)bi_row * D * Np;
+
     auto products = [&](int pb, f32x4 (&acc)[TPW]) __attribute__((always_inline)) {
       // x fragments: lane (g, r16) = position pb*16 + r16, K-range [g*KQ, g*KQ+KQ)
       const T *xrow = &xs[buf][(pb * 16 + r16) * PITCH + g * KQ];
 #pragma unroll
-      for (int p = 0; p < TPW; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int p = 0; p < TPW; ++p) acc[p] = (TYPE0 + p == 3) ? bg4 : f32x4{0.f, 0.f, 0.f, 0.f};  // gate: + bg
       constexpr int KC = BF ? 1 : 4;
 #pragma unroll
       for (int s0 = 0; s0 < KS; s0 += KC) {
@@ -265,26 +282,21 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
       for (int p = 0; p < TPW; ++p) {
         const int type = TYPE0 + p;
         const f32x4 c = acc[p];
+        const uint32_t toff = (uint32_t)(jcol * 16 + 4 * g);  // q/k/gate tiles: [b][i][c/16][j][16]
         if (type == 2) {
-          // v^T per head: lane (g, r16) holds channel r16 of positions 4g..4g+3
-          const int ch = cb * 16 + r16, th = ch / DH, uu = ch - th * DH;
-          T *dst = reinterpret_cast<T *>(a.vt) + ((((size_t)bi_row * H + th) * DH + uu) * Np + j0 + pb * 16 + 4 * g);
-          store4(dst, c[0], c[1], c[2], c[3]);
+          // v^T per head, [b][i][t][u][j] (t * DH + u = channel): lane (g, r16)
+          // holds channel cb*16 + r16 of positions 4g..4g+3
+          store4(vbase, (uint32_t)((cb * 16 + r16) * Np + j0 + pb * 16 + 4 * g), c[0], c[1], c[2], c[3]);
           v_run += (c[0] + c[1]) + (c[2] + c[3]);  // positions j >= N hold v = 0
         } else if (type == 0) {
-          T *dst = reinterpret_cast<T *>(a.q) + ((((size_t)bi_row * NB + cb) * Np + jcol) * 16 + 4 * g);
-          store4(dst, c[0] * a.qscale, c[1] * a.qscale, c[2] * a.qscale, c[3] * a.qscale);
+          store4(qbase, toff, c[0] * a.qscale, c[1] * a.qscale, c[2] * a.qscale, c[3] * a.qscale);
         } else if (type == 1) {
-          T *dst = reinterpret_cast<T *>(a.k) + ((((size_t)bi_row * NB + cb) * Np + jcol) * 16 + 4 * g);
-          store4(dst, c[0], c[1], c[2], c[3]);
+          store4(kbase, toff, c[0], c[1], c[2], c[3]);
           kn_run = fmaxf(kn_run, group4_sum(c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3]));
         } else {
-          const float4 bgv = *reinterpret_cast<const float4 *>(&vec_s[2][cb * 16 + 4 * g]);
-          T *dst = reinterpret_cast<T *>(a.g) + ((((size_t)bi_row * NB + cb) * Np + jcol) * 16 + 4 * g);
-          store4(dst, fast_rcp(1.f + fast_exp2(-(c[0] + bgv.x) * kLog2e)),
-                 fast_rcp(1.f + fast_exp2(-(c[1] + bgv.y) * kLog2e)),
-                 fast_rcp(1.f + fast_exp2(-(c[2] + bgv.z) * kLog2e)),
-                 fast_rcp(1.f + fast_exp2(-(c[3] + bgv.w) * kLog2e)));
+          // sigmoid of (Wg x + bg): the bias is already in the accumulator
+          store4(gbase, toff, fast_rcp(1.f + fast_exp2(-c[0] * kLog2e)), fast_rcp(1.f + fast_exp2(-c[1] * kLog2e)),
+                 fast_rcp(1.f + fast_exp2(-c[2] * kLog2e)), fast_rcp(1.f + fast_exp2(-c[3] * kLog2e)));
         }
       }
       if (wave == pb) {
