@@ -277,11 +277,16 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
       const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
       kmx[i][mb] = lane < nch ? kp[lane] : 0.f;
     }
-  float zfirst[JW];
+  // bias chunk maxima: chunks g, g + 4, g + 8, g + 12 of each column in the
+  // first round (every key chunk of N <= 1024)
+  constexpr int ZR = 4;
+  float zfirst[JW][ZR];
 #pragma unroll
   for (int jb = 0; jb < JW; ++jb) {
     const int j = j0 + (wq * JW + jb) * 16 + r16;
-    zfirst[jb] = (j < N && g < nch) ? a.zmax[((size_t)(b * H + t) * N + j) * nch + g] : -INFINITY;
+    const float *zp = a.zmax + ((size_t)(b * H + t) * N + min(j, N - 1)) * nch;
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) zfirst[jb][u] = (j < N && g + 4 * u < nch) ? zp[g + 4 * u] : -INFINITY;
   }
   // Sum of v over all keys of each (row, channel) of the workgroup, from
   // kernel 1's per-chunk sums: the uniform weights of a fully masked column
@@ -291,16 +296,16 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   for (int x = threadIdx.x; x < RB * DH; x += NW * 64) {
     const int r = x / DH, ch = x - r * DH;
     const float *p = a.vsum + ((size_t)(b * N + min(i0 + r, N - 1)) * D + t * DH + ch) * nch;
-    // four independent loads per round (guarded, not a dependent tail loop)
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    for (int c = 0; c < nch; c += 4) {
-      const float v0 = p[c];
-      const float v1 = c + 1 < nch ? p[c + 1] : 0.f;
-      const float v2 = c + 2 < nch ? p[c + 2] : 0.f;
-      const float v3 = c + 3 < nch ? p[c + 3] : 0.f;
-      s0 += v0, s1 += v1, s2 += v2, s3 += v3;
+    // eight independent guarded loads per round (every key chunk of N <= 512
+    // in the first round), summed in a fixed order
+    float sv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sv[u] = u < nch ? p[u] : 0.f;
+    for (int c = 8; c < nch; c += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sv[u] += c + u < nch ? p[c + u] : 0.f;
     }
-    vsum_s[x] = (s0 + s1) + (s2 + s3);
+    vsum_s[x] = ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
   }
   float kn2[IG];
 #pragma unroll
@@ -323,11 +328,15 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
   for (int jb = 0; jb < JW; ++jb) {
     const int j = j0 + (wq * JW + jb) * 16 + r16;
-    float zx = zfirst[jb];
-    if (zx > -INFINITY) kend = max(kend, g + 1);
+    float zx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) {
+      zx = fmaxf(zx, zfirst[jb][u]);
+      if (zfirst[jb][u] > -INFINITY) kend = max(kend, g + 4 * u + 1);
+    }
     if (j < N) {
       const float *zp = a.zmax + ((size_t)(b * H + t) * N + j) * nch;
-      for (int c = g + 4; c < nch; c += 4) {
+      for (int c = g + 4 * ZR; c < nch; c += 4) {
         const float v = zp[c];
         zx = fmaxf(zx, v);
         if (v > -INFINITY) kend = max(kend, c + 1);
