@@ -100,27 +100,35 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   __shared__ __align__(16) uint4 ring[NS * STAGE / 16];  // NS stages of STAGE bytes
   static_assert(S::LDS + RB * DH * 4 <= 150 * 1024, "LDS budget");
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
+  // lane, g and r16 are re-declared opaque to the compiler after every item's
+  // key loop (see below), so address arithmetic of the next item is not
+  // hoisted out of the item loop and kept live across the key loop
+  int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int g = lane >> 4, r16 = lane & 15;
   const int wr = wave / WQ, wq = wave - wr * WQ;
   const int N = a.N, Np = a.Np, nch = a.nchunk;
 
-  // ---- work item, XCD-aware. Workgroup w runs on XCD w % 8; each XCD takes a
-  // contiguous range of the linear order below, in which consecutive items of
-  // one (b, t) form super-tiles of SI row blocks x SJ query blocks, so the
-  // concurrently running workgroups of an XCD share k/v (same rows) and zm
-  // (same query columns) through its L2.
+  // ---- persistent workgroups. Virtual workgroup v (this workgroup's index,
+  // then + G, + 2G, ...) maps to a work item XCD-aware: v runs on XCD v % 8
+  // (G is a multiple of 8); each XCD takes a contiguous range of the linear
+  // order below, in which consecutive items of one (b, t) form super-tiles of
+  // SI row blocks x SJ query blocks, so the concurrently running workgroups
+  // of an XCD share k/v (same rows) and zm (same query columns) through its L2.
   const int nRB = (N + RB - 1) / RB, nQB = (N + QB - 1) / QB;
-  int lin = blockIdx.x;
-  {
+  const int per_bt = nRB * nQB;
+  const int G8 = gridDim.x;
+  struct Item {
+    int b, t, i0, j0;
+  };
+  auto coords = [&](int v) {
+    int lin = v;
     const int w8 = (a.items / 8) * 8;
     if (lin < w8) lin = (lin & 7) * (w8 / 8) + (lin >> 3);
-  }
-  const int per_bt = nRB * nQB;
-  const int bt = lin / per_bt;
-  const int b = bt / H, t = bt - b * H;
-  int rbk, qbk;
-  {
+    const int bt = lin / per_bt;
+    Item it;
+    it.b = bt / H;
+    it.t = bt - it.b * H;
     const int SJ = nQB < 8 ? nQB : 8;
     const int SI = 32 / SJ;
     const int rem = lin - bt * per_bt;
@@ -130,55 +138,60 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
     const int jrs = (r2 / (si * SJ)) * SJ;
     const int sj = min(SJ, nQB - jrs);
     const int r3 = r2 - jrs * si;
-    rbk = igs + r3 / sj;
-    qbk = jrs + r3 % sj;
-  }
-  const int i0 = rbk * RB, j0 = qbk * QB;
+    it.i0 = (igs + r3 / sj) * RB;
+    it.j0 = (jrs + r3 % sj) * QB;
+    return it;
+  };
 
   const T *Q = reinterpret_cast<const T *>(a.q);
   const T *K = reinterpret_cast<const T *>(a.k);
   const T *VT = reinterpret_cast<const T *>(a.vt);
   T *G = reinterpret_cast<T *>(a.g);
-  const float *ZM = a.zm + (size_t)(b * H + t) * N * Np;
 
-  // ---- query fragments (loads issued first; their norms are taken after the
-  // setup loads below have also been issued)
+  // ---- the item in flight: coordinates and everything derived from them
+  int b = 0, t = 0, i0 = 0, j0 = 0;
+  const float *ZM = a.zm;
+  int rows[IG];
+  auto set_item = [&](const Item &it) {
+    b = it.b, t = it.t, i0 = it.i0, j0 = it.j0;
+    ZM = a.zm + (size_t)(b * H + t) * N * Np;
+#pragma unroll
+    for (int i = 0; i < IG; ++i) rows[i] = min(i0 + wr * IG + i, N - 1);
+  };
+
+  // query fragments
   // bf16: lane (g, r16) holds q'[j = r16][8g..8g+7] (d = 16: groups 0-1 real, group 2 slot 0 = -m);
   // fp32: lane (g, r16) holds q'[j][g*d/4 .. +d/4).
-  int rows[IG];
-#pragma unroll
-  for (int i = 0; i < IG; ++i) rows[i] = min(i0 + wr * IG + i, N - 1);
   Frag qf[IG][JW][BF ? 1 : QS];
+  auto load_q = [&]() {
 #pragma unroll
-  for (int i = 0; i < IG; ++i)
+    for (int i = 0; i < IG; ++i)
 #pragma unroll
-    for (int jb = 0; jb < JW; ++jb) {
-      const int j = min(j0 + (wq * JW + jb) * 16 + r16, Np - 1);
-      const size_t rowbase = (size_t)(b * N + rows[i]) * NB;
-      const int cb = (DH == 16) ? t : 2 * t + (g >> 1);
-      if constexpr (BF) {
-        uint4 raw = ldg<uint4>(Q + ((rowbase + cb) * Np + j) * 16 + 8 * (g & 1));
-        if (DH == 16 && g >= 2) raw = make_uint4(0, 0, 0, 0);
-        qf[i][jb][0] = as_bf16x8(raw);
-      } else {
-        const int off = (DH == 16) ? 4 * g : 8 * (g & 1);
-        const float *src = reinterpret_cast<const float *>(Q) + ((rowbase + cb) * Np + j) * 16 + off;
+      for (int jb = 0; jb < JW; ++jb) {
+        const int j = min(j0 + (wq * JW + jb) * 16 + r16, Np - 1);
+        const size_t rowbase = (size_t)(b * N + rows[i]) * NB;
+        const int cb = (DH == 16) ? t : 2 * t + (g >> 1);
+        if constexpr (BF) {
+          uint4 raw = ldg<uint4>(Q + ((rowbase + cb) * Np + j) * 16 + 8 * (g & 1));
+          if (DH == 16 && g >= 2) raw = make_uint4(0, 0, 0, 0);
+          qf[i][jb][0] = as_bf16x8(raw);
+        } else {
+          const int off = (DH == 16) ? 4 * g : 8 * (g & 1);
+          const float *src = reinterpret_cast<const float *>(Q) + ((rowbase + cb) * Np + j) * 16 + off;
 #pragma unroll
-        for (int s = 0; s < QS; s += 4) {
-          const float4 v = ldg<float4>(src + s);
-          qf[i][jb][s] = v.x, qf[i][jb][s + 1] = v.y, qf[i][jb][s + 2] = v.z, qf[i][jb][s + 3] = v.w;
+          for (int s = 0; s < QS; s += 4) {
+            const float4 v = ldg<float4>(src + s);
+            qf[i][jb][s] = v.x, qf[i][jb][s + 1] = v.y, qf[i][jb][s + 2] = v.z, qf[i][jb][s + 3] = v.w;
+          }
         }
       }
-    }
+  };
 
-  // ---- the gate of this wave's outputs, loaded now and used in the
-  // epilogue, so its round trip is hidden behind the key loop (bf16 d = 16
-  // has no registers to spare and loads it in the epilogue). Addresses are
-  // clamped into the tensor; values of rows or columns past N are not used.
-  constexpr bool GPRE = !(BF && DH == 16);
+  // the gate of this wave's outputs (addresses clamped into the tensor; values
+  // of rows or columns past N are not used)
   using GVec = typename std::conditional<BF, uint2, float4>::type;
-  GVec gpre[GPRE ? IG : 1][GPRE ? JW : 1][GPRE ? MB : 1];
-  if constexpr (GPRE) {
+  GVec gate[IG][JW][MB];
+  auto load_gate = [&]() {
 #pragma unroll
     for (int i = 0; i < IG; ++i)
 #pragma unroll
@@ -186,59 +199,61 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int jc = min(j0 + (wq * JW + jb) * 16 + r16, N - 1);
-          gpre[i][jb][mb] = ldg<GVec>(G + (((size_t)(b * N + rows[i]) * NB + t * MB + mb) * Np + jc) * 16 + 4 * g);
+          gate[i][jb][mb] = ldg<GVec>(G + (((size_t)(b * N + rows[i]) * NB + t * MB + mb) * Np + jc) * 16 + 4 * g);
         }
-  }
+  };
 
   // ---- loader: this wave fills blocks wave + NW*l of each stage; each lane
   // keeps the byte address of its 16 bytes at key step 0 and the per-step stride.
   const char *src_ptr[LPW];
   int src_step[LPW];
+  auto set_loader = [&]() {
 #pragma unroll
-  for (int l = 0; l < LPW; ++l) {
-    int blk = wave + NW * l;
-    if (blk >= NBLK) blk = 0;  // padding block: a harmless duplicate of block 0
-    const char *p;
-    int step;
-    if (blk < RB * KBR) {
-      const int r = blk / KBR, kp = blk - r * KBR;
-      const int row = min(i0 + r, N - 1);
-      const size_t rowbase = (size_t)(b * N + row) * NB;
-      if constexpr (BF) {
-        if (DH == 16) {
-          // lanes 0-31: key tile A (keys 8(rho/4)+rho%4), lanes 32-63: tile B (+4); 16 channels in two halves
-          const int half = lane >> 5, gg = (lane >> 4) & 1, rho = lane & 15;
-          const int key = 4 * half + 8 * (rho >> 2) + (rho & 3);
-          p = reinterpret_cast<const char *>(K + ((rowbase + t) * Np + key) * 16 + 8 * gg);
+    for (int l = 0; l < LPW; ++l) {
+      int blk = wave + NW * l;
+      if (blk >= NBLK) blk = 0;  // padding block: a harmless duplicate of block 0
+      const char *p;
+      int step;
+      if (blk < RB * KBR) {
+        const int r = blk / KBR, kp = blk - r * KBR;
+        const int row = min(i0 + r, N - 1);
+        const size_t rowbase = (size_t)(b * N + row) * NB;
+        if constexpr (BF) {
+          if (DH == 16) {
+            // lanes 0-31: key tile A (keys 8(rho/4)+rho%4), lanes 32-63: tile B (+4); 16 channels in two halves
+            const int half = lane >> 5, gg = (lane >> 4) & 1, rho = lane & 15;
+            const int key = 4 * half + 8 * (rho >> 2) + (rho & 3);
+            p = reinterpret_cast<const char *>(K + ((rowbase + t) * Np + key) * 16 + 8 * gg);
+          } else {
+            const int key = 4 * kp + 8 * (r16 >> 2) + (r16 & 3);
+            p = reinterpret_cast<const char *>(K + ((rowbase + 2 * t + (g >> 1)) * Np + key) * 16 + 8 * (g & 1));
+          }
         } else {
-          const int key = 4 * kp + 8 * (r16 >> 2) + (r16 & 3);
-          p = reinterpret_cast<const char *>(K + ((rowbase + 2 * t + (g >> 1)) * Np + key) * 16 + 8 * (g & 1));
+          if (DH == 16)
+            p = reinterpret_cast<const char *>(K + ((rowbase + t) * Np + r16) * 16 + 4 * g);
+          else
+            p = reinterpret_cast<const char *>(K + ((rowbase + 2 * t + (g >> 1)) * Np + r16) * 16 + 8 * (g & 1) +
+                                               4 * kp);
         }
+        step = KT * 16 * ES;
+      } else if (blk < RB * (KBR + VBR)) {
+        const int v = blk - RB * KBR;
+        const int r = v / VBR, mb = v - r * VBR;
+        const int row = min(i0 + r, N - 1);
+        p = reinterpret_cast<const char *>(VT + (((size_t)(b * N + row) * H + t) * DH + mb * 16 + r16) * Np +
+                                           (BF ? 8 : 4) * g);
+        step = KT * ES;
       } else {
-        if (DH == 16)
-          p = reinterpret_cast<const char *>(K + ((rowbase + t) * Np + r16) * 16 + 4 * g);
-        else
-          p = reinterpret_cast<const char *>(K + ((rowbase + 2 * t + (g >> 1)) * Np + r16) * 16 + 8 * (g & 1) +
-                                             4 * kp);
+        const int z = blk - RB * (KBR + VBR);
+        const int jb = z / ZBJ, zp = z - jb * ZBJ;
+        const int jrow = min(j0 + jb * 16 + r16, N - 1);
+        p = reinterpret_cast<const char *>(ZM + (size_t)jrow * Np + (BF ? 8 : 4) * g + 4 * zp);
+        step = KT * 4;
       }
-      step = KT * 16 * ES;
-    } else if (blk < RB * (KBR + VBR)) {
-      const int v = blk - RB * KBR;
-      const int r = v / VBR, mb = v - r * VBR;
-      const int row = min(i0 + r, N - 1);
-      p = reinterpret_cast<const char *>(VT + (((size_t)(b * N + row) * H + t) * DH + mb * 16 + r16) * Np +
-                                         (BF ? 8 : 4) * g);
-      step = KT * ES;
-    } else {
-      const int z = blk - RB * (KBR + VBR);
-      const int jb = z / ZBJ, zp = z - jb * ZBJ;
-      const int jrow = min(j0 + jb * 16 + r16, N - 1);
-      p = reinterpret_cast<const char *>(ZM + (size_t)jrow * Np + (BF ? 8 : 4) * g + 4 * zp);
-      step = KT * 4;
+      src_ptr[l] = p;
+      src_step[l] = step;
     }
-    src_ptr[l] = p;
-    src_step[l] = step;
-  }
+  };
   const uint32_t ring_base = lds_addr(ring);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t blk_lds[LPW];  // byte offset of this wave's block l within a stage
@@ -252,137 +267,62 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
     for (int l = 0; l < LPW; ++l) dma16_to_lds(src_ptr[l] + (size_t)s * src_step[l], stage + blk_lds[l]);
   };
-  // The first LA key steps go out now, before the setup loads: every key
+  // An item's first LA key steps go out before its setup is done: every key
   // step below Np / KT (>= LA) addresses padded, in-bounds rows, so they are
   // issued before the number of live steps is known; steps past that number
   // are waited for and ignored.
   constexpr int LA = NS - 1;  // steps in flight
   static_assert(LA >= 1 && LA <= 3, "");
-#pragma unroll
-  for (int s = 0; s < LA; ++s) issue(s);
 
-  // The per-chunk maxima are spread over the lanes and reduced across lanes.
-  // The first round of every one of these loads is issued before any of them
-  // is used (one round trip); rows longer than that first round (more than 64
-  // key chunks for |k|, 4 for the bias) continue in loops.
-  // |k|^2 <= sum over the head's 16-channel blocks of each block's chunk maxima;
-  // lane l takes chunks l, l + 64, ... of each row's block.
+  // ---- setup loads. The per-chunk maxima are spread over the lanes and
+  // reduced across lanes; the first round of every one of these loads is
+  // issued before any of them is used (one round trip); rows longer than
+  // that first round (more than 64 key chunks for |k|, 16 for the bias, 8
+  // for the v sums) continue in loops.
+  // |k|^2 <= sum over the head's 16-channel blocks of each block's chunk
+  // maxima: lane l takes chunks l, l + 64, ... of each row's block.
   // Bias+mask maximum and last live key chunk of this wave's query columns:
   // lane (g, r16) takes chunks g, g + 4, ... of column r16.
-  float kmx[IG][MB];
-#pragma unroll
-  for (int i = 0; i < IG; ++i)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
-      kmx[i][mb] = lane < nch ? kp[lane] : 0.f;
-    }
-  // bias chunk maxima: chunks g, g + 4, g + 8, g + 12 of each column in the
-  // first round (every key chunk of N <= 1024)
-  constexpr int ZR = 4;
-  float zfirst[JW][ZR];
-#pragma unroll
-  for (int jb = 0; jb < JW; ++jb) {
-    const int j = j0 + (wq * JW + jb) * 16 + r16;
-    const float *zp = a.zmax + ((size_t)(b * H + t) * N + min(j, N - 1)) * nch;
-#pragma unroll
-    for (int u = 0; u < ZR; ++u) zfirst[jb][u] = (j < N && g + 4 * u < nch) ? zp[g + 4 * u] : -INFINITY;
-  }
   // Sum of v over all keys of each (row, channel) of the workgroup, from
-  // kernel 1's per-chunk sums: the uniform weights of a fully masked column
-  // (finite fill). One thread per (row, channel), loads issued with the
-  // other setup loads.
-  __shared__ __align__(16) float vsum_s[RB * DH];
-  for (int x = threadIdx.x; x < RB * DH; x += NW * 64) {
-    const int r = x / DH, ch = x - r * DH;
-    const float *p = a.vsum + ((size_t)(b * N + min(i0 + r, N - 1)) * D + t * DH + ch) * nch;
-    // eight independent guarded loads per round (every key chunk of N <= 512
-    // in the first round), summed in a fixed order
-    float sv[8];
+  // kernel 1's per-chunk sums (the uniform weights of a fully masked column,
+  // finite fill): one thread per (row, channel).
+  constexpr int ZR = 4;
+  float kmx[IG][MB], zfirst[JW][ZR], sv[8];
+  auto load_setup = [&]() {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sv[u] = u < nch ? p[u] : 0.f;
-    for (int c = 8; c < nch; c += 8) {
+    for (int i = 0; i < IG; ++i)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sv[u] += c + u < nch ? p[c + u] : 0.f;
-    }
-    vsum_s[x] = ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
-  }
-  float kn2[IG];
-#pragma unroll
-  for (int i = 0; i < IG; ++i) {
-    float m2 = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
-      float m = kmx[i][mb];
-      for (int c = lane + 64; c < nch; c += 64) m = fmaxf(m, kp[c]);
-#pragma unroll
-      for (int x = 1; x < 64; x <<= 1) m = xor_max(m, x);
-      m2 += m;
-    }
-    kn2[i] = m2;
-  }
-  float zmx[JW];
-  bool colmask[JW];  // a real column whose keys are all masked
-  int kend = 0;
-#pragma unroll
-  for (int jb = 0; jb < JW; ++jb) {
-    const int j = j0 + (wq * JW + jb) * 16 + r16;
-    float zx = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < ZR; ++u) {
-      zx = fmaxf(zx, zfirst[jb][u]);
-      if (zfirst[jb][u] > -INFINITY) kend = max(kend, g + 4 * u + 1);
-    }
-    if (j < N) {
-      const float *zp = a.zmax + ((size_t)(b * H + t) * N + j) * nch;
-      for (int c = g + 4 * ZR; c < nch; c += 4) {
-        const float v = zp[c];
-        zx = fmaxf(zx, v);
-        if (v > -INFINITY) kend = max(kend, c + 1);
+      for (int mb = 0; mb < MB; ++mb) {
+        const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
+        kmx[i][mb] = lane < nch ? kp[lane] : 0.f;
       }
-    }
-    zx = group4_max(zx);
-    zmx[jb] = zx;
-    colmask[jb] = (j < N) && zx == -INFINITY;
-  }
-  // the workgroup steps through the keys together: its end is the max over all waves
-  for (int m = 1; m < 64; m <<= 1) kend = max(kend, __shfl_xor(kend, m, 64));
-  __shared__ int kend_s[NW];
-  __shared__ int need_s;
-  if (lane == 0) kend_s[wave] = kend;
-  if (threadIdx.x == 0) need_s = 0;
-  lds_barrier();
-  {
-    int k = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) k = max(k, kend_s[w]);
-    kend = k;
-  }
-  const int nsteps = __builtin_amdgcn_readfirstlane(kend) * kChunk / KT;
-
-  // ---- query norms and the shift
-  float msh[IG][JW];
-#pragma unroll
-  for (int i = 0; i < IG; ++i)
 #pragma unroll
     for (int jb = 0; jb < JW; ++jb) {
-      float n2 = 0.f;
-      if constexpr (BF) {
+      const int j = j0 + (wq * JW + jb) * 16 + r16;
+      const float *zp = a.zmax + ((size_t)(b * H + t) * N + min(j, N - 1)) * nch;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (float)qf[i][jb][0][e];
-          n2 += x * x;
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < QS; ++s) n2 += qf[i][jb][s] * qf[i][jb][s];
-      }
-      n2 = group4_sum(n2);
-      msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : sqrtf(n2 * kn2[i]) + zmx[jb] + a.shift_slack;
+      for (int u = 0; u < ZR; ++u) zfirst[jb][u] = (j < N && g + 4 * u < nch) ? zp[g + 4 * u] : -INFINITY;
     }
+    static_assert(RB * DH <= NW * 64, "one (row, channel) v sum per thread");
+    const int x = threadIdx.x;
+    if (x < RB * DH) {
+      const int r = x / DH, ch = x - r * DH;
+      const float *p = a.vsum + ((size_t)(b * N + min(i0 + r, N - 1)) * D + t * DH + ch) * nch;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sv[u] = u < nch ? p[u] : 0.f;
+    }
+  };
 
-
+  // ---- setup: per-item LDS state is double-buffered by item parity, so the
+  // next item's setup can run before the current item's epilogue
+  __shared__ __align__(16) float vsum_s[2][RB * DH];
+  __shared__ int kend_s[NW];
+  __shared__ int need_s[2];
+  float kn2[IG], zmx[JW];
+  bool colmask[JW];  // a real column whose keys are all masked
+  float msh[IG][JW];
+  int nsteps = 0;
+  bool shift_on = true;
   auto set_shift = [&](const float (&m)[IG][JW]) {
     if constexpr (BF) {
 #pragma unroll
@@ -395,21 +335,105 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         }
     }
   };
-  set_shift(msh);
-  // bf16, d = 32: the shift costs two more MFMAs per score tile. Where every
-  // bound of the wave is at most 64, exp2 of a score cannot overflow (2^64 per
-  // key, sums far below the fp32 range) and the wave goes without it; scores
-  // far below their bound only risk a tiny sum, which the recovery below
-  // catches either way.
-  bool shift_on = true;
-  if constexpr (BF && DH == 32) {
-    bool big = false;
+  auto setup = [&](int buf) {
+    {
+      const int x = threadIdx.x;
+      if (x < RB * DH) {
+        const int r = x / DH, ch = x - r * DH;
+        const float *p = a.vsum + ((size_t)(b * N + min(i0 + r, N - 1)) * D + t * DH + ch) * nch;
+        float s8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s8[u] = sv[u];
+        for (int c = 8; c < nch; c += 8) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) s8[u] += c + u < nch ? p[c + u] : 0.f;
+        }
+        // a fixed summation order: deterministic
+        vsum_s[buf][x] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < IG; ++i) {
+      float m2 = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
+        float m = kmx[i][mb];
+        for (int c = lane + 64; c < nch; c += 64) m = fmaxf(m, kp[c]);
+#pragma unroll
+        for (int x = 1; x < 64; x <<= 1) m = xor_max(m, x);
+        m2 += m;
+      }
+      kn2[i] = m2;
+    }
+    int kend = 0;
+#pragma unroll
+    for (int jb = 0; jb < JW; ++jb) {
+      const int j = j0 + (wq * JW + jb) * 16 + r16;
+      float zx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < ZR; ++u) {
+        zx = fmaxf(zx, zfirst[jb][u]);
+        if (zfirst[jb][u] > -INFINITY) kend = max(kend, g + 4 * u + 1);
+      }
+      if (j < N) {
+        const float *zp = a.zmax + ((size_t)(b * H + t) * N + j) * nch;
+        for (int c = g + 4 * ZR; c < nch; c += 4) {
+          const float v = zp[c];
+          zx = fmaxf(zx, v);
+          if (v > -INFINITY) kend = max(kend, c + 1);
+        }
+      }
+      zx = group4_max(zx);
+      zmx[jb] = zx;
+      colmask[jb] = (j < N) && zx == -INFINITY;
+    }
+    // the workgroup steps through the keys together: its end is the max over all waves
+    for (int m = 1; m < 64; m <<= 1) kend = max(kend, __shfl_xor(kend, m, 64));
+    if (lane == 0) kend_s[wave] = kend;
+    if (threadIdx.x == 0) need_s[buf] = 0;
+    lds_barrier();
+    {
+      int k = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) k = max(k, kend_s[w]);
+      nsteps = __builtin_amdgcn_readfirstlane(k) * kChunk / KT;
+    }
+    // query norms and the shift
 #pragma unroll
     for (int i = 0; i < IG; ++i)
 #pragma unroll
-      for (int jb = 0; jb < JW; ++jb) big |= !(msh[i][jb] <= 64.f);
-    shift_on = __ballot(big) != 0;
-  }
+      for (int jb = 0; jb < JW; ++jb) {
+        float n2 = 0.f;
+        if constexpr (BF) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = (float)qf[i][jb][0][e];
+            n2 += x * x;
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < QS; ++s) n2 += qf[i][jb][s] * qf[i][jb][s];
+        }
+        n2 = group4_sum(n2);
+        msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : sqrtf(n2 * kn2[i]) + zmx[jb] + a.shift_slack;
+      }
+    set_shift(msh);
+    // bf16, d = 32: the shift costs two more MFMAs per score tile. Where every
+    // bound of the wave is at most 64, exp2 of a score cannot overflow (2^64
+    // per key, sums far below the fp32 range) and the wave goes without it;
+    // scores far below their bound only risk a tiny sum, which the recovery
+    // below catches either way.
+    shift_on = true;
+    if constexpr (BF && DH == 32) {
+      bool big = false;
+#pragma unroll
+      for (int i = 0; i < IG; ++i)
+#pragma unroll
+        for (int jb = 0; jb < JW; ++jb) big |= !(msh[i][jb] <= 64.f);
+      shift_on = __ballot(big) != 0;
+    }
+  };
 
   if constexpr (BF && DH == 16) {
     // the constant half of every k block: lanes 32-47 read (1, 0, ..., 0), lanes 48-63 zeros
@@ -598,101 +622,146 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
       }
   };
 
-  float dummy[IG][JW];
-  zero_acc();
-  key_loop(false, dummy, true);
-  vmcnt_wait<0>();  // early steps past the live ones, if any, have landed
-  row_sums();
 
-  // ---- recovery: exact maximum where the bound was too loose. The decision is
-  // workgroup-wide: every wave runs the key loop and its barriers together.
-  bool need = false;
-#pragma unroll
-  for (int i = 0; i < IG; ++i)
-#pragma unroll
-    for (int jb = 0; jb < JW; ++jb)
-      if (zmx[jb] > -INFINITY && !(lsum[i][jb] >= 0x1p-64f)) need = true;
-  if (__ballot(need) != 0 && lane == 0) need_s = 1;
-  lds_barrier();  // also: every wave is done with the ring
-  if (need_s) {
-    float mx[IG][JW];
-#pragma unroll
-    for (int i = 0; i < IG; ++i)
-#pragma unroll
-      for (int jb = 0; jb < JW; ++jb) {
-        mx[i][jb] = -INFINITY;
-        msh[i][jb] = 0.f;
-      }
-    set_shift(msh);  // no shift during the max pass
-    key_loop(true, mx, false);
-#pragma unroll
-    for (int i = 0; i < IG; ++i)
-#pragma unroll
-      for (int jb = 0; jb < JW; ++jb) {
-        const float m = group4_max(mx[i][jb]);
-        msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : m;
-      }
-    set_shift(msh);
-    shift_on = true;
-    zero_acc();
-    lds_barrier();  // every wave is done with the ring before it is refilled
-    key_loop(false, dummy, false);
-    row_sums();
-  }
-
-  // ---- normalise, fully masked columns, gate; write over the gate
+  // ---- normalise, fully masked columns, gate; write over the gate. `it`,
+  // `cm` and vsum_s[buf] belong to the finished item (the next item's setup
+  // may have run already).
   const bool fill_nan = (a.mask_fill == -INFINITY);
   const float inv_n = 1.0f / (float)N;
+  auto epilogue = [&](const Item &it, const bool (&cm)[JW], int buf) {
 #pragma unroll
-  for (int i = 0; i < IG; ++i) {
-    const int row = i0 + wr * IG + i;
-    // Uniform weights of a fully masked column (finite fill): the mean of v
-    // over all N keys (padding keys are zero). Lane (g, r16) needs channels
-    // 4g..4g+3 of each of the head's 16-channel blocks.
-    float vmean[MB][4];
+    for (int i = 0; i < IG; ++i) {
+      const int row = it.i0 + wr * IG + i;
+      // Uniform weights of a fully masked column (finite fill): the mean of v
+      // over all N keys (padding keys are zero). Lane (g, r16) needs channels
+      // 4g..4g+3 of each of the head's 16-channel blocks.
+      float vmean[MB][4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const float4 m4 = *reinterpret_cast<const float4 *>(&vsum_s[(wr * IG + i) * DH + mb * 16 + 4 * g]);
-      vmean[mb][0] = m4.x * inv_n, vmean[mb][1] = m4.y * inv_n, vmean[mb][2] = m4.z * inv_n, vmean[mb][3] = m4.w * inv_n;
-    }
+      for (int mb = 0; mb < MB; ++mb) {
+        const float4 m4 = *reinterpret_cast<const float4 *>(&vsum_s[buf][(wr * IG + i) * DH + mb * 16 + 4 * g]);
+        vmean[mb][0] = m4.x * inv_n, vmean[mb][1] = m4.y * inv_n, vmean[mb][2] = m4.z * inv_n, vmean[mb][3] = m4.w * inv_n;
+      }
 #pragma unroll
-    for (int jb = 0; jb < JW; ++jb) {
-      const int j = j0 + (wq * JW + jb) * 16 + r16;
-      const bool masked = colmask[jb];
-      const float inv_l = masked ? 0.f : 1.0f / lsum[i][jb];
-      if (row < N && j < N) {
+      for (int jb = 0; jb < JW; ++jb) {
+        const int j = it.j0 + (wq * JW + jb) * 16 + r16;
+        const bool masked = cm[jb];
+        const float inv_l = masked ? 0.f : 1.0f / lsum[i][jb];
+        if (row < N && j < N) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          T *gp = G + (((size_t)(b * N + row) * NB + t * MB + mb) * Np + j) * 16 + 4 * g;
-          float gv[4];
-          GVec w;
-          if constexpr (GPRE)
-            w = gpre[i][jb][mb];
-          else
-            w = ldg<GVec>(gp);
-          if constexpr (BF)
-            gv[0] = bflo(w.x), gv[1] = bfhi(w.x), gv[2] = bflo(w.y), gv[3] = bfhi(w.y);
-          else
-            gv[0] = w.x, gv[1] = w.y, gv[2] = w.z, gv[3] = w.w;
-          float ov[4];
+          for (int mb = 0; mb < MB; ++mb) {
+            T *gp = G + (((size_t)(it.b * N + row) * NB + it.t * MB + mb) * Np + j) * 16 + 4 * g;
+            const GVec w = gate[i][jb][mb];
+            float gv[4];
+            if constexpr (BF)
+              gv[0] = bflo(w.x), gv[1] = bfhi(w.x), gv[2] = bflo(w.y), gv[3] = bfhi(w.y);
+            else
+              gv[0] = w.x, gv[1] = w.y, gv[2] = w.z, gv[3] = w.w;
+            float ov[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float oo = masked ? (fill_nan ? __builtin_nanf("") : vmean[mb][r]) : o[i][jb][mb][r] * inv_l;
-            ov[r] = oo * gv[r];
+            for (int r = 0; r < 4; ++r) {
+              const float oo = masked ? (fill_nan ? __builtin_nanf("") : vmean[mb][r]) : o[i][jb][mb][r] * inv_l;
+              ov[r] = oo * gv[r];
+            }
+            if constexpr (BF)
+              stg<uint2>(gp, make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])));
+            else
+              stg<float4>(gp, make_float4(ov[0], ov[1], ov[2], ov[3]));
           }
-          if constexpr (BF)
-            stg<uint2>(gp, make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])));
-          else
-            stg<float4>(gp, make_float4(ov[0], ov[1], ov[2], ov[3]));
         }
       }
     }
+  };
+
+  // ---- the first item
+  int v = blockIdx.x;
+  if (v >= a.items) return;
+  Item cur = coords(v);
+  set_item(cur);
+  load_setup();
+  load_q();
+  set_loader();
+#pragma unroll
+  for (int s = 0; s < LA; ++s) issue(s);
+  int buf = 0;
+  setup(buf);
+
+  float dummy[IG][JW];
+#pragma unroll 1
+  for (;;) {
+    zero_acc();
+    key_loop(false, dummy, true);
+    vmcnt_wait<0>();  // early steps past the live ones, if any, have landed
+    row_sums();
+
+    // ---- recovery: exact maximum where the bound was too loose. The
+    // decision is workgroup-wide: every wave runs the key loop and its
+    // barriers together.
+    bool need = false;
+#pragma unroll
+    for (int i = 0; i < IG; ++i)
+#pragma unroll
+      for (int jb = 0; jb < JW; ++jb)
+        if (zmx[jb] > -INFINITY && !(lsum[i][jb] >= 0x1p-64f)) need = true;
+    if (__ballot(need) != 0 && lane == 0) need_s[buf] = 1;
+    lds_barrier();  // also: every wave is done with the ring
+    if (need_s[buf]) {
+      float mx[IG][JW];
+#pragma unroll
+      for (int i = 0; i < IG; ++i)
+#pragma unroll
+        for (int jb = 0; jb < JW; ++jb) {
+          mx[i][jb] = -INFINITY;
+          msh[i][jb] = 0.f;
+        }
+      set_shift(msh);  // no shift during the max pass
+      key_loop(true, mx, false);
+#pragma unroll
+      for (int i = 0; i < IG; ++i)
+#pragma unroll
+        for (int jb = 0; jb < JW; ++jb) {
+          const float m = group4_max(mx[i][jb]);
+          msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : m;
+        }
+      set_shift(msh);
+      shift_on = true;
+      zero_acc();
+      lds_barrier();  // every wave is done with the ring before it is refilled
+      key_loop(false, dummy, false);
+      row_sums();
+      vmcnt_wait<0>();
+      lds_barrier();  // every wave is done with the ring
+    }
+
+    // ---- this item's gate, then the next item's setup loads, query
+    // fragments and first key steps (the ring is free): their round trips
+    // overlap the next item's setup and this item's epilogue
+    asm volatile("" : "+v"(lane), "+v"(g), "+v"(r16));
+    load_gate();
+    bool cm[JW];
+#pragma unroll
+    for (int jb = 0; jb < JW; ++jb) cm[jb] = colmask[jb];
+    const Item done = cur;
+    v += G8;
+    const bool more = v < a.items;
+    if (more) {
+      cur = coords(v);
+      set_item(cur);
+      load_setup();
+      load_q();
+      set_loader();
+#pragma unroll
+      for (int s = 0; s < LA; ++s) issue(s);
+      setup(buf ^ 1);
+    }
+    epilogue(done, cm, buf);
+    if (!more) break;
+    buf ^= 1;
   }
 }
 
 template <typename T, int D, int DH>
-static hipError_t launch_k2_t(const K2Args &a, hipStream_t s) {
-  hipLaunchKernelGGL((k2_attention<T, D, DH>), dim3(a.items), dim3(K2Shape<T, D, DH>::NW * 64), 0, s, a);
+static hipError_t launch_k2_t(const K2Args &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k2_attention<T, D, DH>), dim3(grid), dim3(K2Shape<T, D, DH>::NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -718,9 +787,9 @@ int k2_items(int dtype, int D, int dh, int B, int N) {
   return B * (D / dh) * ((N + RB - 1) / RB) * ((N + QB - 1) / QB);
 }
 
-hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, hipStream_t s) {
+hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, int grid, hipStream_t s) {
 #define TRI_K2_CASE(TT, DD, HH) \
-  if (D == DD && dh == HH) return launch_k2_t<TT, DD, HH>(a, s);
+  if (D == DD && dh == HH) return launch_k2_t<TT, DD, HH>(a, grid, s);
   if (dtype == TRI_ATTN_BF16) {
     TRI_K2_CASE(bf16_t, 128, 16)
     TRI_K2_CASE(bf16_t, 128, 32)
@@ -734,6 +803,32 @@ hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, hipStream_t s) {
   }
 #undef TRI_K2_CASE
   return hipErrorInvalidValue;
+}
+
+}  // namespace tpa
+
+namespace tpa {
+
+int k2_blocks_per_cu(int dtype, int D, int dh) {
+  int n = 0;
+#define TRI_K2_OCC(TT, DD, HH)                                                                                   \
+  if (D == DD && dh == HH &&                                                                                     \
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k2_attention<TT, DD, HH>, K2Shape<TT, DD, HH>::NW * 64, 0) != \
+          hipSuccess)                                                                                            \
+    n = 1;
+  if (dtype == TRI_ATTN_BF16) {
+    TRI_K2_OCC(bf16_t, 128, 16)
+    TRI_K2_OCC(bf16_t, 128, 32)
+    TRI_K2_OCC(bf16_t, 64, 16)
+    TRI_K2_OCC(bf16_t, 64, 32)
+  } else {
+    TRI_K2_OCC(float, 128, 16)
+    TRI_K2_OCC(float, 128, 32)
+    TRI_K2_OCC(float, 64, 16)
+    TRI_K2_OCC(float, 64, 32)
+  }
+#undef TRI_K2_OCC
+  return n > 0 ? n : 1;
 }
 
 }  // namespace tpa

@@ -15,6 +15,7 @@ struct tri_attn {
   int D, h, dh, elem;
   int device;
   int k1_grid;     // persistent grid of kernel 1 (resident workgroups)
+  int k2_grid;     // persistent grid of kernel 2
   int k3_grid;     // persistent grid of kernel 3
   void *wpack;     // [(4D + 16)][D] Wq; Wk; Wv; Wg; Wz; zero rows
   void *vecs;      // gamma, beta, bg, bo ([D] each), then Wo [D][D]
@@ -104,6 +105,7 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
     return TRI_ATTN_ERR_HIP;
   }
   t->k1_grid = cus * k1_blocks_per_cu(cfg->dtype, t->D, t->dh);
+  t->k2_grid = cus * k2_blocks_per_cu(cfg->dtype, t->D, t->dh);
   t->k3_grid = cus * k3_blocks_per_cu(cfg->dtype, t->D);
 
   t->wpack_bytes = (size_t)(4 * D + 16) * D * e;
@@ -226,7 +228,11 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a2.shift_slack = t->cfg.shift_slack;
   a2.B = B, a2.N = N, a2.Np = L.Np, a2.nchunk = L.nchunk;
   a2.items = k2_items(t->cfg.dtype, D, t->dh, B, N);
-  if ((stages & 2) && launch_k2(t->cfg.dtype, D, t->dh, a2, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
+  // persistent workgroups; with more items than that, a multiple of 8 so that
+  // each keeps its XCD from item to item
+  int grid2 = a2.items;
+  if (grid2 > t->k2_grid) grid2 = t->k2_grid >= 8 ? t->k2_grid / 8 * 8 : t->k2_grid;
+  if ((stages & 2) && launch_k2(t->cfg.dtype, D, t->dh, a2, grid2, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
 
   K3Args a3{};
   a3.go = a1.g;

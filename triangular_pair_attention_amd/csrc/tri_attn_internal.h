@@ -54,11 +54,13 @@ struct K3Args {
 
 // Launchers: return the launch status. `dtype` is TRI_ATTN_F32 / TRI_ATTN_BF16.
 hipError_t launch_k1(int dtype, int D, int dh, const K1Args &a, int grid, hipStream_t s);
-hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, hipStream_t s);
+// grid: persistent workgroups (a multiple of 8 when smaller than a.items)
+hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, int grid, hipStream_t s);
 hipError_t launch_k3(int dtype, int D, const K3Args &a, int grid, hipStream_t s);
 // Copies the row-major [16 * nblocks][D] matrix `rows` into fragment order.
 hipError_t launch_pack_frags(int elem_bytes, int D, const void *rows, void *frags, int nblocks, hipStream_t s);
 int k2_items(int dtype, int D, int dh, int B, int N);
+int k2_blocks_per_cu(int dtype, int D, int dh);  // resident workgroups of kernel 2 per CU
 int k3_blocks_per_cu(int dtype, int D);  // resident workgroups of kernel 3 per CU
 int k1_blocks_per_cu(int dtype, int D, int dh);  // resident workgroups of kernel 1 per CU
 bool supported(int D, int dh);
