@@ -119,11 +119,13 @@ const char *tri_attn_strerror(int code);
  *             zero for j >= N.
  *   zm      : [B][h][N][Np] float32: z[b,t,j,k] * log2(e) where M[b,j,k] != 0
  *             and k < N, -inf elsewhere.
- *   zmax    : [B][h][N][Np/64] float32: max of zm over each 64-key chunk.
+ *   zmax    : [B][h][Np/64][N] float32: max of zm[b,t,j,:] over each 64-key
+ *             chunk (chunk-major: consecutive j are adjacent).
  *   kmax    : [B][N][D/16][Np/64] float32: max over each 64-column chunk of
  *             the squared norm of k over one 16-channel block.
- *   vsum    : [B][N][D][Np/64] float32: sum of v over each 64-column chunk
- *             (for the uniform weights of fully masked query columns). */
+ *   vsum    : [B][N][Np/64][D] float32: sum of v over each 64-column chunk
+ *             (for the uniform weights of fully masked query columns;
+ *             chunk-major: consecutive channels are adjacent). */
 typedef struct {
   size_t q, k, vt, g, zm, zmax, kmax, vsum;
   size_t total;

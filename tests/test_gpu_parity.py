@@ -171,9 +171,9 @@ def test_projection_stage(dtype, shape):
         gg = f(lay.g, B_ * N * D * Np).reshape(B_, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4)
         vt = f(lay.vt, B_ * N * D * Np).reshape(B_, N, h, d, Np)[..., :N]
         zm = f(lay.zm, B_ * h * N * Np, torch.float32).reshape(B_, h, N, Np)
-        zmax = f(lay.zmax, B_ * h * N * (Np // 64), torch.float32).reshape(B_, h, N, Np // 64)
+        zmax = f(lay.zmax, B_ * h * N * (Np // 64), torch.float32).reshape(B_, h, Np // 64, N).transpose(0, 1, 3, 2)
         kmax = f(lay.kmax, B_ * N * (D // 16) * (Np // 64), torch.float32).reshape(B_, N, D // 16, Np // 64)
-        vsum = f(lay.vsum, B_ * N * D * (Np // 64), torch.float32).reshape(B_, N, D, Np // 64)
+        vsum = f(lay.vsum, B_ * N * D * (Np // 64), torch.float32).reshape(B_, N, Np // 64, D).transpose(0, 1, 3, 2)
     finally:
         g.close()
     q = q.reshape(B_, N, N, D)

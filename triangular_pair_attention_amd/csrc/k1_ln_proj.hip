@@ -367,7 +367,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     // per-chunk sums of v (a fixed summation order: deterministic)
     if (TYPE0 <= 2 && TYPE0 + TPW > 2) {
       const float sv = group4_sum(v_run);
-      if (g == 0) a.vsum[((size_t)bi_row * D + cb * 16 + r16) * nch + chunk] = sv;
+      if (g == 0) a.vsum[((size_t)bi_row * nch + chunk) * D + cb * 16 + r16] = sv;
     }
     // per-chunk maxima
     if (TYPE0 <= 1 && TYPE0 + TPW > 1) {
@@ -384,7 +384,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
       float m = zpart_s[0][lane];
 #pragma unroll
       for (int q = 1; q < TILE / 16; ++q) m = fmaxf(m, zpart_s[q][lane]);
-      a.zmax[((size_t)(b * H + lane) * N + i) * nch + chunk] = m;
+      a.zmax[((size_t)(b * H + lane) * nch + chunk) * N + i] = m;
     }
   };
 

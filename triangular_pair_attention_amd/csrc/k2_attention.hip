@@ -299,17 +299,19 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
     for (int jb = 0; jb < JW; ++jb) {
       const int j = j0 + (wq * JW + jb) * 16 + r16;
-      const float *zp = a.zmax + ((size_t)(b * H + t) * N + min(j, N - 1)) * nch;
+      // [b][t][chunk][j]: the 16 lanes of a lane group read 16 consecutive columns
+      const float *zp = a.zmax + (size_t)(b * H + t) * nch * N + min(j, N - 1);
 #pragma unroll
-      for (int u = 0; u < ZR; ++u) zfirst[jb][u] = (j < N && g + 4 * u < nch) ? zp[g + 4 * u] : -INFINITY;
+      for (int u = 0; u < ZR; ++u) zfirst[jb][u] = (j < N && g + 4 * u < nch) ? zp[(size_t)(g + 4 * u) * N] : -INFINITY;
     }
     static_assert(RB * DH <= NW * 64, "one (row, channel) v sum per thread");
     const int x = threadIdx.x;
     if (x < RB * DH) {
       const int r = x / DH, ch = x - r * DH;
-      const float *p = a.vsum + ((size_t)(b * N + min(i0 + r, N - 1)) * D + t * DH + ch) * nch;
+      // [b][i][chunk][channel]: consecutive threads read consecutive channels
+      const float *p = a.vsum + (size_t)(b * N + min(i0 + r, N - 1)) * nch * D + t * DH + ch;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sv[u] = u < nch ? p[u] : 0.f;
+      for (int u = 0; u < 8; ++u) sv[u] = u < nch ? p[(size_t)u * D] : 0.f;
     }
   };
 
@@ -340,13 +342,13 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
       const int x = threadIdx.x;
       if (x < RB * DH) {
         const int r = x / DH, ch = x - r * DH;
-        const float *p = a.vsum + ((size_t)(b * N + min(i0 + r, N - 1)) * D + t * DH + ch) * nch;
+        const float *p = a.vsum + (size_t)(b * N + min(i0 + r, N - 1)) * nch * D + t * DH + ch;
         float s8[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) s8[u] = sv[u];
         for (int c = 8; c < nch; c += 8) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) s8[u] += c + u < nch ? p[c + u] : 0.f;
+          for (int u = 0; u < 8; ++u) s8[u] += c + u < nch ? p[(size_t)(c + u) * D] : 0.f;
         }
         // a fixed summation order: deterministic
         vsum_s[buf][x] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
@@ -377,9 +379,9 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         if (zfirst[jb][u] > -INFINITY) kend = max(kend, g + 4 * u + 1);
       }
       if (j < N) {
-        const float *zp = a.zmax + ((size_t)(b * H + t) * N + j) * nch;
+        const float *zp = a.zmax + (size_t)(b * H + t) * nch * N + j;
         for (int c = g + 4 * ZR; c < nch; c += 4) {
-          const float v = zp[c];
+          const float v = zp[(size_t)c * N];
           zx = fmaxf(zx, v);
           if (v > -INFINITY) kend = max(kend, c + 1);
         }
