@@ -134,6 +134,20 @@ def test_loose_shift_and_recovery_path(dtype, dh, slack):
     check(y, ref, dtype, f"slack {slack}")
 
 
+@pytest.mark.parametrize("dtype,dh", [("bf16", 16), ("bf16", 32), ("f32", 32)])
+def test_recovery_on_every_item_of_persistent_workgroups(dtype, dh):
+    """N = 300 gives more attention work items than resident workgroups
+    (900 to 3000), so each workgroup runs several items back to back, with
+    its per-item state double-buffered; slack 400 sends every item through
+    the exact-maximum recovery path."""
+    w = Workload("slack300", 1, 300, 128, 128 // dh, dtype, ("pad", 290), seed=11)
+    log(f"persistent recovery {dtype} d={dh}")
+    inp = make_inputs(w)
+    rows = [(0, i) for i in (0, 1, 7, 8, 150, 151, 289, 290, 299)]
+    y, ref = run_case(inp, slack=400.0, rows=rows)
+    check(y, ref, dtype, f"persistent recovery {dtype} d={dh}")
+
+
 def test_large_scores_stay_finite():
     """Scaled-up query weights make the scores large (peaked softmax)."""
     w = Workload("peaked", 1, 40, 64, 4, "f32", ("bernoulli", 0.8), seed=8)
