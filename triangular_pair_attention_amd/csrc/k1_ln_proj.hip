@@ -17,7 +17,11 @@
 //  2. Wave w owns channel block w % NB of its TPW projections, so every wave
 //     has the same MFMA and epilogue work; the pair-bias block (its weight
 //     sits in LDS) is the only extra, one 16-position block on each of the
-//     first four waves (one per SIMD).
+//     first four waves (one per SIMD). In bf16 the four 16-position blocks
+//     of a tile run as a software pipeline (the products of block pb + 1
+//     are issued before the epilogue of block pb). A grid with one tile per
+//     workgroup uses its own instantiation without a tile loop, whose first
+//     products wait only for their own weights.
 //  3. Epilogues write directly in the layouts kernel 2 reads:
 //     q (pre-scaled by log2(e)/sqrt(d)), k, gate (sigmoid(+bias)) as
 //     [b][i][c/16][j][16] (one 512-byte burst per 16x16 tile); v transposed

@@ -6,8 +6,13 @@
 // kernel; FW-GLM-5-1 / l2_p6: the fused attention kernel). The output
 // projection is kernel 3.
 //
-// Workgroup = (b, head t, RB rows i, QB query columns j); wave (wr, wq) takes
+// Work item = (b, head t, RB rows i, QB query columns j); wave (wr, wq) takes
 // IG rows x JW*16 queries. The (B, N, h, N, N) scores are never stored.
+// Workgroups are persistent (as many as are resident) and loop over items:
+// after an item's key loop, the next item's setup loads, query fragments and
+// first key steps go out together with this item's gate, and the next item's
+// setup runs while they arrive, followed by this item's epilogue, so the CU
+// is not left idle on the round trips at the start and end of an item.
 //
 // Key tiles through LDS. Per key step (KT keys) the workgroup needs k and v
 // of its RB rows and the bias+mask tile zm of its QB query columns. Every
@@ -28,8 +33,8 @@
 // accumulator starts from the zm tile and the row sum comes from a row of
 // ones in the PV MFMA: the VALU work per score is one exp2 and half a bf16
 // conversion. If a column's sum falls below 2^-64 (only with a pathological
-// bound, or the shift_slack test knob) the wave recomputes with the exact
-// maximum (a max pass, then the loop again).
+// bound, or the shift_slack test knob) the workgroup recomputes that item
+// with the exact maximum (a max pass, then the loop again).
 //
 // Mask: zm = -inf where masked, so masked keys get weight exactly 0. A query
 // column whose keys are all masked (max zm = -inf) gets the rule of the
