@@ -90,3 +90,11 @@ def test_attention_floor():
     assert r["floor_ms"] == pytest.approx(t_floor * 1e3)
     assert r["frac_of_floor"] == pytest.approx(t_floor * 1e3 / 1.0)
     assert r["valid_tflops"] == pytest.approx(4 * 512 * 128 * (4 * 100 * 200) / 1e-3 / 1e12)
+
+
+def test_source_hash_ignores_comments():
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n/* block\ncomment */\n"
+    same = "int f(int x) { return x + 1; }  // other words\n"
+    other = "int f(int x) { return x + 2; }\n"
+    assert bench._code_only(code) == bench._code_only(same)
+    assert bench._code_only(code) != bench._code_only(other)
