@@ -148,6 +148,20 @@ def test_recovery_on_every_item_of_persistent_workgroups(dtype, dh):
     check(y, ref, dtype, f"persistent recovery {dtype} d={dh}")
 
 
+@pytest.mark.parametrize("dtype,h", [("bf16", 4), ("bf16", 2), ("f32", 2)])
+def test_d64_two_batches_sampled_rows(dtype, h):
+    """D = 64 at N = 300, two batches with their own padding length (a range
+    like the largest workload's): more attention items than resident
+    workgroups and more projection tiles than workgroups, so the persistent
+    attention loop and kernel 1's tile loop both run, with ragged chunks."""
+    w = Workload("d64", 2, 300, 64, h, dtype, ("pad_range", 200, 300), seed=12)
+    log(f"D=64 two batches {dtype} h={h}")
+    inp = make_inputs(w)
+    rows = [(0, 0), (0, 5), (0, 199), (0, 250), (1, 3), (1, 150), (1, 298), (1, 299)]
+    y, ref = run_case(inp, rows=rows)
+    check(y, ref, dtype, f"D=64 two batches {dtype} h={h}")
+
+
 def test_large_scores_stay_finite():
     """Scaled-up query weights make the scores large (peaked softmax)."""
     w = Workload("peaked", 1, 40, 64, 4, "f32", ("bernoulli", 0.8), seed=8)
