@@ -215,6 +215,7 @@ def test_projection_stage(dtype, shape):
     rz = np.where(M[:, None] != 0, cap["z"] * LOG2E, -np.inf)  # (b, t, j, k)
     atol, rtol = (1e-4, 1e-4) if dtype == "f32" else (2e-2, 1e-2)
     for name, got, ref in (("q", q, rq), ("k", k, rk), ("g", gg, rg), ("v", vt, rv.transpose(0, 1, 2, 4, 3))):
+        log(f"  {name}: max abs err {np.abs(got - ref).max():.3e}, max |ref| {np.abs(ref).max():.3f}")
         np.testing.assert_allclose(got, ref, rtol=rtol, atol=atol, err_msg=name)
     fin = np.isfinite(rz)
     assert (np.isfinite(zm[..., :N]) == fin).all()

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "lib", "libtri_attn.so")
 CALIB = os.path.join(PKG, "lib", "tri_attn_calib")
-SOURCES = ("tri_attn.cpp", "pack_weights.hip", "k1_ln_proj.hip", "k2_attention.hip", "k3_out_proj.hip")
+SOURCES = ("tri_attn.cpp", "pack_weights.hip", "k1_ln_proj.hip", "k1_split.hip", "k2_attention.hip",
+           "k3_out_proj.hip")
 ARCH = "gfx950"
 
 FLAGS = [

@@ -57,6 +57,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
+// Three-way bf16 split of two floats: a = a1 + a2 + a3 exactly (likewise b),
+// with a1 = bf16(a), a2 = bf16(a - a1), a3 = a - a1 - a2 (each rounded to
+// nearest even). a - a1 is exact in float32 and has at most 16 significant
+// bits, so a2 keeps its top 8 and a3 the rest exactly. Returned as packed
+// pairs (low half a, high half b) of the first, second and third parts.
+__device__ __forceinline__ void split3(float a, float b, uint32_t &p1, uint32_t &p2, uint32_t &p3) {
+  p1 = pack_bf16x2(a, b);
+  const float ra = a - bflo(p1), rb = b - bfhi(p1);
+  p2 = pack_bf16x2(ra, rb);
+  p3 = pack_bf16x2(ra - bflo(p2), rb - bfhi(p2));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
 

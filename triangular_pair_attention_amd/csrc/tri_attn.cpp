@@ -20,7 +20,8 @@ struct tri_attn {
   void *wpack;     // [(4D + 16)][D] Wq; Wk; Wv; Wg; Wz; zero rows
   void *vecs;      // gamma, beta, bg, bo ([D] each), then Wo [D][D]
   void *wfrag;     // Wq; Wk; Wv; Wg, then Wo, in fragment order
-  size_t wpack_bytes, vecs_bytes, wfrag_bytes;
+  void *wsplit;    // float32 handles: the same five matrices as three bf16 planes in fragment order
+  size_t wpack_bytes, vecs_bytes, wfrag_bytes, wsplit_plane;
 };
 
 namespace tpa {
@@ -104,7 +105,8 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
     delete t;
     return TRI_ATTN_ERR_HIP;
   }
-  t->k1_grid = cus * k1_blocks_per_cu(cfg->dtype, t->D, t->dh);
+  t->k1_grid = cus * (cfg->dtype == TRI_ATTN_F32 ? k1_split_blocks_per_cu(t->D, t->dh)
+                                                 : k1_blocks_per_cu(cfg->dtype, t->D, t->dh));
   t->k2_grid = cus * k2_blocks_per_cu(cfg->dtype, t->D, t->dh);
   t->k3_grid = cus * k3_blocks_per_cu(cfg->dtype, t->D);
 
@@ -126,6 +128,14 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
     delete t;
     return TRI_ATTN_ERR_OOM;
   }
+  t->wsplit_plane = (size_t)5 * D * D * 2;
+  if (cfg->dtype == TRI_ATTN_F32 && hipMalloc(&t->wsplit, 3 * t->wsplit_plane) != hipSuccess) {
+    (void)hipFree(t->wpack);
+    (void)hipFree(t->vecs);
+    (void)hipFree(t->wfrag);
+    delete t;
+    return TRI_ATTN_ERR_OOM;
+  }
   char *wp = static_cast<char *>(t->wpack);
   char *vp = static_cast<char *>(t->vecs);
   const size_t mat = (size_t)D * D * e, vec = (size_t)D * e;
@@ -142,12 +152,18 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
   ok = ok && hipMemcpyAsync(vp + 4 * vec, w->w_out, mat, hipMemcpyDefault, s) == hipSuccess;
   ok = ok && launch_pack_frags(e, D, wp, t->wfrag, 4 * D / 16, s) == hipSuccess;
   ok = ok && launch_pack_frags(e, D, vp + 4 * vec, static_cast<char *>(t->wfrag) + 4 * mat, D / 16, s) == hipSuccess;
+  if (t->wsplit) {
+    ok = ok && launch_pack_frags_split3(D, wp, t->wsplit, t->wsplit_plane, 4 * D / 16, s) == hipSuccess;
+    ok = ok && launch_pack_frags_split3(D, vp + 4 * vec, static_cast<char *>(t->wsplit) + (size_t)4 * D * D * 2,
+                                        t->wsplit_plane, D / 16, s) == hipSuccess;
+  }
   ok = ok && hipStreamSynchronize(s) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
     (void)hipFree(t->wpack);
     (void)hipFree(t->vecs);
     (void)hipFree(t->wfrag);
+    if (t->wsplit) (void)hipFree(t->wsplit);
     delete t;
     return TRI_ATTN_ERR_HIP;
   }
@@ -206,6 +222,8 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a1.mask = pair_mask;
   a1.W = t->wpack;
   a1.Wf = t->wfrag;
+  a1.Ws = t->wsplit;
+  a1.ws_plane = t->wsplit_plane;
   a1.gamma = vp;
   a1.beta = vp + (size_t)D * e;
   a1.bg = vp + (size_t)2 * D * e;
@@ -218,8 +236,21 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a1.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->dh));
   a1.B = B, a1.N = N, a1.Np = L.Np, a1.nchunk = L.nchunk;
   a1.tiles = B * N * L.nchunk;
-  const int grid = a1.tiles < t->k1_grid ? a1.tiles : t->k1_grid;
-  if ((stages & 1) && launch_k1(t->cfg.dtype, D, t->dh, a1, grid, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
+  if (stages & 1) {
+    hipError_t e1;
+    if (t->cfg.dtype == TRI_ATTN_F32) {
+      // two workgroups per tile (one per half of the projections); a multiple
+      // of 8 per half when the tiles fill the device, so a tile's two halves
+      // share an XCD
+      int half = t->k1_grid / 2;
+      if (half >= 8) half = half / 8 * 8;
+      if (half < 1) half = 1;
+      e1 = launch_k1_split(D, t->dh, a1, 2 * (a1.tiles < half ? a1.tiles : half), s);
+    } else {
+      e1 = launch_k1(t->cfg.dtype, D, t->dh, a1, a1.tiles < t->k1_grid ? a1.tiles : t->k1_grid, s);
+    }
+    if (e1 != hipSuccess) return TRI_ATTN_ERR_HIP;
+  }
 
   K2Args a2{};
   a2.q = a1.q, a2.k = a1.k, a2.vt = a1.vt, a2.g = a1.g;
@@ -271,6 +302,7 @@ int tri_attn_destroy(tri_attn_t t) {
   if (hipFree(t->wpack) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
   if (hipFree(t->vecs) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
   if (hipFree(t->wfrag) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
+  if (t->wsplit && hipFree(t->wsplit) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
   delete t;
   return rc;
 }

@@ -25,6 +25,8 @@ struct K1Args {
   const uint8_t *mask;    // [B][N][N]
   const void *W;          // packed [(4D + 16)][D]: Wq; Wk; Wv; Wg; Wz; zero rows
   const void *Wf;         // Wq; Wk; Wv; Wg in fragment order (pack_weights.hip)
+  const void *Ws;         // float32 handles: Wq; Wk; Wv; Wg; Wo as three bf16 planes in fragment order
+  size_t ws_plane;        // bytes from one plane of Ws to the next
   const void *gamma, *beta, *bg;  // [D]
   void *q, *k, *vt, *g;
   float *zm, *zmax, *kmax, *vsum;
@@ -59,10 +61,17 @@ hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, int grid, hipStr
 hipError_t launch_k3(int dtype, int D, const K3Args &a, int grid, hipStream_t s);
 // Copies the row-major [16 * nblocks][D] matrix `rows` into fragment order.
 hipError_t launch_pack_frags(int elem_bytes, int D, const void *rows, void *frags, int nblocks, hipStream_t s);
+// Splits the float32 rows into three bf16 planes (plane_bytes apart), each in bf16 fragment order.
+hipError_t launch_pack_frags_split3(int D, const void *rows, void *frags, size_t plane_bytes, int nblocks,
+                                    hipStream_t s);
 int k2_items(int dtype, int D, int dh, int B, int N);
 int k2_blocks_per_cu(int dtype, int D, int dh);  // resident workgroups of kernel 2 per CU
 int k3_blocks_per_cu(int dtype, int D);  // resident workgroups of kernel 3 per CU
 int k1_blocks_per_cu(int dtype, int D, int dh);  // resident workgroups of kernel 1 per CU
+// Float32 kernel 1 (split products): grid = 2 x workgroups per half (each
+// workgroup computes one half of the projections).
+hipError_t launch_k1_split(int D, int dh, const K1Args &a, int grid, hipStream_t s);
+int k1_split_blocks_per_cu(int D, int dh);
 bool supported(int D, int dh);
 
 }  // namespace tpa
