@@ -48,6 +48,11 @@ KERNEL_SOURCES = {
     "k2_attention": "triangular_pair_attention_amd/csrc/k2_attention.hip",
     "k3_out_proj": "triangular_pair_attention_amd/csrc/k3_out_proj.hip",
 }
+# float32 tensors run kernel 1 from its own source (split products)
+F32_SOURCES = {"k1_ln_proj": "triangular_pair_attention_amd/csrc/k1_split.hip"}
+# float32 kernels whose products run as six bf16 products each (three-way split
+# operands): their matrix-core ceiling is the bf16 peak / 6
+SPLIT_KERNELS = ("k1_ln_proj", "k3_out_proj")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
@@ -59,10 +64,14 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def source_hash(kernel: str) -> str:
+def kernel_source(kernel: str, dtype: str = "bf16") -> str:
+    return F32_SOURCES.get(kernel, KERNEL_SOURCES[kernel]) if dtype == "f32" else KERNEL_SOURCES[kernel]
+
+
+def source_hash(kernel: str, dtype: str = "bf16") -> str:
     """sha256 (first 16 hex digits) of the kernel's code and device_common.h."""
     h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES[kernel], "triangular_pair_attention_amd/csrc/device_common.h"):
+    for rel in (kernel_source(kernel, dtype), "triangular_pair_attention_amd/csrc/device_common.h"):
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -95,6 +104,11 @@ def roofline_of(kernel, w, m, ms):
     else:
         r = {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": mfma, "unit": "TFLOP/s"}
     r["frac"] = r["achieved"] / r["peak"]
+    if w.dtype == "f32" and kernel in SPLIT_KERNELS and r["bound"] == "mfma":
+        # the matrix cores run six bf16 products per float32 product
+        ceil = PEAK["mfma_bf16_TFLOPs"] / 6
+        r["split_products"] = {"bf16_products_per_f32_product": 6, "ceiling": ceil,
+                               "frac_of_ceiling": r["achieved"] / ceil}
     return r
 
 
@@ -115,7 +129,7 @@ def attention_floor(w, m, ms, mask=None):
     return r
 
 
-def stored_traffic(workload: str, kernel: str):
+def stored_traffic(workload: str, kernel: str, dtype: str = "bf16"):
     """HBM bytes per launch from the committed rocprofv3 counter runs (the
     table in profiles/hbm_traffic.md), if they were taken on the current
     kernel source; else None. Table row:
@@ -129,7 +143,7 @@ def stored_traffic(workload: str, kernel: str):
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
         if len(cells) != 7 or cells[0] != workload or cells[1] != kernel:
             continue
-        if cells[2] != source_hash(kernel):
+        if cells[2] != source_hash(kernel, dtype):
             return None
         try:
             fetch, write, fs, ws = (float(c) for c in cells[3:7])
@@ -272,7 +286,7 @@ def main():
     ms_k = {"k1_ln_proj": ms_k1, "k2_attention": ms_k2, "k3_out_proj": ms_k3}
     dom = max(ms_k, key=ms_k.get)
     roof = roofline_of(dom, w, m, ms_k[dom])
-    roof["traffic"] = stored_traffic(w.name, dom)
+    roof["traffic"] = stored_traffic(w.name, dom, w.dtype)
     roof["kernel"] = dom
     roof["kernel_ms"] = ms_k[dom]
 

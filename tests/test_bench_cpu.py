@@ -49,6 +49,22 @@ def test_bound_selection():
     assert r["frac"] == pytest.approx(r["achieved"] / 157.3)
 
 
+def test_split_products_ceiling():
+    # float32 kernels 1 and 3 run six bf16 products per float32 product
+    m2 = bench.work_model(WORKLOADS[2])
+    r = bench.roofline_of("k3_out_proj", WORKLOADS[2], m2, 0.01)
+    assert r["split_products"]["ceiling"] == pytest.approx(2500.0 / 6)
+    assert r["split_products"]["frac_of_ceiling"] == pytest.approx(r["achieved"] / (2500.0 / 6))
+    assert "split_products" not in bench.roofline_of("k2_attention", WORKLOADS[2], m2, 0.01)
+    assert "split_products" not in bench.roofline_of("k2_attention", WORKLOADS[5], bench.work_model(WORKLOADS[5]), 1.0)
+
+
+def test_float32_kernel1_source():
+    assert bench.kernel_source("k1_ln_proj", "f32").endswith("k1_split.hip")
+    assert bench.kernel_source("k1_ln_proj", "bf16").endswith("k1_ln_proj.hip")
+    assert bench.source_hash("k1_ln_proj", "f32") != bench.source_hash("k1_ln_proj", "bf16")
+
+
 def test_traffic_table_is_used_only_for_the_current_source(tmp_path, monkeypatch):
     k = "k1_ln_proj"
     good = bench.source_hash(k)

@@ -1,4 +1,5 @@
-// Kernel 1 of the triangular self-attention forward: LayerNorm of the pair
+// Kernel 1 of the triangular self-attention forward for bf16 tensors
+// (float32 tensors use k1_split.hip): LayerNorm of the pair
 // representation and ONE fused projection GEMM producing q | k | v | gate |
 // pair bias (Kimi-K2.6 / l2_p6 transcript: the LayerNorm and projection steps
 // of its forward listing and its layer list; FW-GLM-5-1 / l2_p6: the
@@ -17,7 +18,7 @@
 //  2. Wave w owns channel block w % NB of its TPW projections, so every wave
 //     has the same MFMA and epilogue work; the pair-bias block (its weight
 //     sits in LDS) is the only extra, one 16-position block on each of the
-//     first four waves (one per SIMD). In bf16 the four 16-position blocks
+//     first four waves (one per SIMD). The four 16-position blocks
 //     of a tile run as a software pipeline (the products of block pb + 1
 //     are issued before the epilogue of block pb). A grid with one tile per
 //     workgroup uses its own instantiation without a tile loop, whose first
@@ -39,10 +40,8 @@
 
 namespace tpa {
 
-// TPW projections per wave; NW = 4 * NB / TPW waves per workgroup. (Two
-// projections per wave with twice the waves would halve the register budget
-// per lane; fp32 weights then spill.)
-template <typename T, int D>
+// TPW projections per wave; NW = 4 * NB / TPW waves per workgroup.
+template <int D>
 struct K1Shape {
   static constexpr int NB = D / 16;
   static constexpr int TPW = 4;
@@ -52,23 +51,23 @@ struct K1Shape {
 
 // ONE: the grid has one tile per workgroup (a straight path with no prefetch
 // and no tile loop); otherwise a persistent loop over tiles.
-template <typename T, int D, int DH, bool ONE>
-__global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a) {
-  constexpr bool BF = is_bf16<T>::value;
-  constexpr int ES = BF ? 2 : 4;           // element bytes
+template <int D, int DH, bool ONE>
+__global__ __launch_bounds__((K1Shape<D>::THREADS)) void k1_ln_proj(K1Args a) {
+  using T = bf16_t;
+  constexpr int ES = 2;                    // element bytes
   constexpr int H = D / DH;                // heads
-  constexpr int NB = K1Shape<T, D>::NB;    // 16-channel blocks per projection
-  constexpr int TPW = K1Shape<T, D>::TPW;  // projections per wave
-  constexpr int NW = K1Shape<T, D>::NW;
-  constexpr int NT = K1Shape<T, D>::THREADS;
+  constexpr int NB = K1Shape<D>::NB;       // 16-channel blocks per projection
+  constexpr int TPW = K1Shape<D>::TPW;     // projections per wave
+  constexpr int NW = K1Shape<D>::NW;
+  constexpr int NT = K1Shape<D>::THREADS;
   constexpr int KQ = D / 4;                // K-dim elements per lane (lane group g owns [g*KQ, g*KQ+KQ))
-  constexpr int KS = BF ? D / 32 : D / 4;  // MFMA steps over K = D
+  constexpr int KS = D / 32;               // MFMA steps over K = D
   constexpr int PITCH = D + 16 / ES;       // LDS row pitch (elements), 16-byte pad against bank conflicts
   constexpr int TPP = NT / 64;             // LayerNorm threads per position
   constexpr int EPT = D / TPP;             // LayerNorm elements per thread
   constexpr int NV = EPT * ES / 16;        // 16-byte loads per thread per tile
   constexpr int TILE = kChunk;
-  using Frag = typename std::conditional<BF, bf16x8, float>::type;
+  using Frag = bf16x8;
   static_assert(NV >= 1 && EPT % 8 == 0, "");
 
   __shared__ __align__(16) T xs[2][TILE * PITCH];
@@ -90,7 +89,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   // LayerNorm of the first tile waits on its own data only. The weights are
   // stored in fragment order: each load of a wave reads 1 KB contiguously.
   constexpr int NVW = D * ES / 64;  // 16-byte pieces per lane per block
-  static_assert(NVW == (BF ? KS : KS / 4), "");
+  static_assert(NVW == KS, "");
   Frag wf[TPW][KS];
   auto load_weights = [&]() {
     const char *wsrc = reinterpret_cast<const char *>(a.Wf) + (size_t)lane * 16;
@@ -103,13 +102,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     for (int v = 0; v < NVW; ++v)
 #pragma unroll
       for (int p = 0; p < TPW; ++p) {
-        const uint4 u = piece(p, v);
-        if constexpr (BF) {
-          wf[p][v] = as_bf16x8(u);
-        } else {
-          wf[p][4 * v] = __uint_as_float(u.x), wf[p][4 * v + 1] = __uint_as_float(u.y);
-          wf[p][4 * v + 2] = __uint_as_float(u.z), wf[p][4 * v + 3] = __uint_as_float(u.w);
-        }
+        wf[p][v] = as_bf16x8(piece(p, v));
       }
   };
   // LayerNorm affine parameters, gate bias and the pair-bias weight block,
@@ -125,8 +118,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   auto issue_params = [&]() {
     if (pwhich < 3) {
       const void *src = pwhich == 0 ? a.gamma : (pwhich == 1 ? a.beta : a.bg);
-      pv = BF ? bf2f(reinterpret_cast<const uint16_t *>(src)[tid - pwhich * D])
-              : reinterpret_cast<const float *>(src)[tid - pwhich * D];
+      pv = bf2f(reinterpret_cast<const uint16_t *>(src)[tid - pwhich * D]);
     }
     if (tid < WZV) wzv = ldg<uint4>(reinterpret_cast<const char *>(W + (size_t)4 * D * D) + 16 * tid);
   };
@@ -162,12 +154,7 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     float v[EPT];
     const uint32_t *w32 = reinterpret_cast<const uint32_t *>(pre);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      if constexpr (BF)
-        v[e] = (e & 1) ? bfhi(w32[e >> 1]) : bflo(w32[e >> 1]);
-      else
-        v[e] = __uint_as_float(w32[e]);
-    }
+    for (int e = 0; e < EPT; ++e) v[e] = (e & 1) ? bfhi(w32[e >> 1]) : bflo(w32[e >> 1]);
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) s += v[e];
@@ -188,28 +175,16 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     const float *gam = &vec_s[0][lpart * EPT];
     const float *bet = &vec_s[1][lpart * EPT];
     T *dst = &xs[buf][lpos * PITCH + lpart * EPT];
-    if constexpr (BF) {
 #pragma unroll
-      for (int e = 0; e < EPT; e += 8) {
-        uint32_t p4[4];
+    for (int e = 0; e < EPT; e += 8) {
+      uint32_t p4[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = e + 2 * u;
-          p4[u] = pack_bf16x2((v[c] - mean) * scale * gam[c] + bet[c] * bmul,
-                              (v[c + 1] - mean) * scale * gam[c + 1] + bet[c + 1] * bmul);
-        }
-        *reinterpret_cast<uint4 *>(dst + e) = make_uint4(p4[0], p4[1], p4[2], p4[3]);
+      for (int u = 0; u < 4; ++u) {
+        const int c = e + 2 * u;
+        p4[u] = pack_bf16x2((v[c] - mean) * scale * gam[c] + bet[c] * bmul,
+                            (v[c + 1] - mean) * scale * gam[c + 1] + bet[c + 1] * bmul);
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPT; e += 4) {
-        float4 o;
-        o.x = (v[e] - mean) * scale * gam[e] + bet[e] * bmul;
-        o.y = (v[e + 1] - mean) * scale * gam[e + 1] + bet[e + 1] * bmul;
-        o.z = (v[e + 2] - mean) * scale * gam[e + 2] + bet[e + 2] * bmul;
-        o.w = (v[e + 3] - mean) * scale * gam[e + 3] + bet[e + 3] * bmul;
-        *reinterpret_cast<float4 *>(dst + e) = o;
-      }
+      *reinterpret_cast<uint4 *>(dst + e) = make_uint4(p4[0], p4[1], p4[2], p4[3]);
     }
   };
 
@@ -217,21 +192,16 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
   // offset stays a 32-bit byte offset, so the store adds it to the scalar base
   auto store4 = [&](T *base, uint32_t off, float v0, float v1, float v2, float v3) {
     char *dst = reinterpret_cast<char *>(base) + off * (uint32_t)ES;
-    if constexpr (BF)
-      stg<uint2>(dst, make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)));
-    else
-      stg<float4>(dst, make_float4(v0, v1, v2, v3));
+    stg<uint2>(dst, make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)));
   };
 
   // One tile with this wave's projections starting at TYPE0 (compile time).
-  // PEEL (fp32): the first 16-position block is emitted as its own
-  // straight-line copy, so that on a workgroup's first tile each product waits
-  // only for its own weight registers while later ones are still arriving
-  // (inside a loop the compiler waits for all outstanding loads before
-  // entering it). bf16 tiles are straight-line code throughout.
-  auto compute_tile = [&](auto type0_c, auto peel_c, int tile, int buf) __attribute__((always_inline)) {
+  // Straight-line code throughout, so on a workgroup's first tile each
+  // product waits only for its own weight registers while later ones are
+  // still arriving (inside a loop the compiler waits for all outstanding loads
+  // before entering it).
+  auto compute_tile = [&](auto type0_c, int tile, int buf) __attribute__((always_inline)) {
     constexpr int TYPE0 = decltype(type0_c)::value;
-    constexpr bool PEEL = decltype(peel_c)::value;
     const int bi_row = tile / nch, chunk = tile - bi_row * nch;
     const int b = bi_row / N, i = bi_row - b * N;
     const int j0 = chunk * TILE;
@@ -258,25 +228,16 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
       const T *xrow = &xs[buf][(pb * 16 + r16) * PITCH + g * KQ];
 #pragma unroll
       for (int p = 0; p < TPW; ++p) acc[p] = (TYPE0 + p == 3) ? bg4 : f32x4{0.f, 0.f, 0.f, 0.f};  // gate: + bg
-      constexpr int KC = BF ? 1 : 4;
 #pragma unroll
-      for (int s0 = 0; s0 < KS; s0 += KC) {
-        Frag xf[KC];
-        if constexpr (BF) {
-          xf[0] = as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s0));
-        } else {
-          const float4 v = *reinterpret_cast<const float4 *>(xrow + s0);
-          xf[0] = v.x, xf[1] = v.y, xf[2] = v.z, xf[3] = v.w;
+      for (int s0 = 0; s0 < KS; ++s0) {
+        const Frag xf = as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s0));
+#pragma unroll
+        for (int p = 0; p < TPW; ++p) {
+          if (TYPE0 + p == 2)
+            acc[p] = mfma(xf, wf[p][s0], acc[p]);  // v: rows = positions
+          else
+            acc[p] = mfma(wf[p][s0], xf, acc[p]);  // q, k, gate: rows = channels
         }
-#pragma unroll
-        for (int s = 0; s < KC; ++s)
-#pragma unroll
-          for (int p = 0; p < TPW; ++p) {
-            if (TYPE0 + p == 2)
-              acc[p] = mfma(xf[s], wf[p][s0 + s], acc[p]);  // v: rows = positions
-            else
-              acc[p] = mfma(wf[p][s0 + s], xf[s], acc[p]);  // q, k, gate: rows = channels
-          }
       }
     };
     auto epilogue = [&](int pb, const f32x4 (&acc)[TPW]) __attribute__((always_inline)) {
@@ -309,19 +270,9 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
         const T *zrow = &wz_s[r16 * PITCH + g * KQ];
         f32x4 accz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s0 = 0; s0 < KS; s0 += (BF ? 1 : 4)) {
-          if constexpr (BF) {
-            accz = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s0)),
-                        as_bf16x8(*reinterpret_cast<const uint4 *>(zrow + 8 * s0)), accz);
-          } else {
-            const float4 v = *reinterpret_cast<const float4 *>(xrow + s0);
-            const float4 u = *reinterpret_cast<const float4 *>(zrow + s0);
-            accz = mfma(v.x, u.x, accz);
-            accz = mfma(v.y, u.y, accz);
-            accz = mfma(v.z, u.z, accz);
-            accz = mfma(v.w, u.w, accz);
-          }
-        }
+        for (int s0 = 0; s0 < KS; ++s0)
+          accz = mfma(as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s0)),
+                      as_bf16x8(*reinterpret_cast<const uint4 *>(zrow + 8 * s0)), accz);
         if (r16 < H) {
           const int jb = j0 + pb * 16 + 4 * g;
           float z[4];
@@ -337,36 +288,18 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
       }
     };
     static_assert(TILE / 16 == 4, "four 16-position blocks per tile");
-    if constexpr (BF) {
-      // software pipeline over the four blocks: the products of block pb + 1
-      // go to the matrix cores before the epilogue of block pb, which then
-      // finds its results ready (straight-line code, so the first tile's
-      // products also wait only for their own weights)
-      f32x4 accA[TPW], accB[TPW];
-      products(0, accA);
-      products(1, accB);
-      epilogue(0, accA);
-      products(2, accA);
-      epilogue(1, accB);
-      products(3, accB);
-      epilogue(2, accA);
-      epilogue(3, accB);
-    } else {
-      // fp32 has no registers for a second set of accumulators
-      int pb0 = 0;
-      if constexpr (PEEL) {
-        f32x4 acc[TPW];
-        products(0, acc);
-        epilogue(0, acc);
-        pb0 = 1;
-      }
-#pragma unroll 1
-      for (int pb = pb0; pb < TILE / 16; ++pb) {
-        f32x4 acc[TPW];
-        products(pb, acc);
-        epilogue(pb, acc);
-      }
-    }
+    // software pipeline over the four blocks: the products of block pb + 1
+    // go to the matrix cores before the epilogue of block pb, which then
+    // finds its results ready
+    f32x4 accA[TPW], accB[TPW];
+    products(0, accA);
+    products(1, accB);
+    epilogue(0, accA);
+    products(2, accA);
+    epilogue(1, accB);
+    products(3, accB);
+    epilogue(2, accA);
+    epilogue(3, accB);
 
     // per-chunk sums of v (a fixed summation order: deterministic)
     if (TYPE0 <= 2 && TYPE0 + TPW > 2) {
@@ -392,26 +325,23 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     }
   };
 
-  auto compute = [&](auto peel_c, int tile, int buf) __attribute__((always_inline)) {
+  auto compute = [&](int tile, int buf) __attribute__((always_inline)) {
     if constexpr (TPW == 4) {
-      compute_tile(std::integral_constant<int, 0>{}, peel_c, tile, buf);
+      compute_tile(std::integral_constant<int, 0>{}, tile, buf);
     } else {
       if (type0 == 0)
-        compute_tile(std::integral_constant<int, 0>{}, peel_c, tile, buf);
+        compute_tile(std::integral_constant<int, 0>{}, tile, buf);
       else
-        compute_tile(std::integral_constant<int, 2>{}, peel_c, tile, buf);
+        compute_tile(std::integral_constant<int, 2>{}, tile, buf);
     }
   };
-  const std::true_type first{};
-  const std::false_type later{};
 
   int tile = blockIdx.x;
   if (tile >= a.tiles) return;
   const int G = gridDim.x;
   if constexpr (ONE) {
     // the weight loads go out between the parameter loads and their LDS
-    // writes, and the first block is peeled: products start as their own
-    // weights arrive
+    // writes: products start as their own weights arrive
     uint4 pre[NV];
     uint32_t mpre;
     load_tile(tile, pre, mpre);
@@ -421,10 +351,10 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     lds_barrier();
     layer_norm_to_lds(tile, pre, mpre, 0);
     lds_barrier();
-    compute(first, tile, 0);
-  } else if constexpr (BF) {
-    // bf16 is HBM-bound: pair_repr and the mask are prefetched two tiles
-    // ahead, alternately into A and B
+    compute(tile, 0);
+  } else {
+    // HBM-bound: pair_repr and the mask are prefetched two tiles ahead,
+    // alternately into A and B
     uint4 preA[NV], preB[NV];
     uint32_t mA, mB = 0;
     load_tile(tile, preA, mA);
@@ -436,86 +366,55 @@ __global__ __launch_bounds__((K1Shape<T, D>::THREADS)) void k1_ln_proj(K1Args a)
     layer_norm_to_lds(tile, preA, mA, 0);
     lds_barrier();
     if (tile + 2 * G < a.tiles) load_tile(tile + 2 * G, preA, mA);
-    compute(first, tile, 0);
+    compute(tile, 0);
 #pragma unroll 1
     for (tile += G; tile < a.tiles; tile += 2 * G) {
       layer_norm_to_lds(tile, preB, mB, 1);
       lds_barrier();
       if (tile + 2 * G < a.tiles) load_tile(tile + 2 * G, preB, mB);
-      compute(later, tile, 1);
+      compute(tile, 1);
       if (tile + G >= a.tiles) break;
       layer_norm_to_lds(tile + G, preA, mA, 0);
       lds_barrier();
       if (tile + 3 * G < a.tiles) load_tile(tile + 3 * G, preA, mA);
-      compute(later, tile + G, 0);
-    }
-  } else {
-    // fp32: the next tile is prefetched one ahead (no peel: the loop's
-    // registers are full)
-    uint4 pre[NV];
-    uint32_t mpre;
-    load_tile(tile, pre, mpre);
-    issue_params();
-    commit_params();
-    load_weights();
-    lds_barrier();
-    int buf = 0;
-#pragma unroll 1
-    for (; tile < a.tiles; tile += G) {
-      layer_norm_to_lds(tile, pre, mpre, buf);
-      lds_barrier();
-      if (tile + G < a.tiles) load_tile(tile + G, pre, mpre);
-      compute(later, tile, buf);
-      buf ^= 1;
+      compute(tile + G, 0);
     }
   }
 }
 
-template <typename T, int D, int DH>
+template <int D, int DH>
 static hipError_t launch_k1_t(const K1Args &a, int grid, hipStream_t s) {
   if (a.tiles <= grid)
-    hipLaunchKernelGGL((k1_ln_proj<T, D, DH, true>), dim3(a.tiles), dim3(K1Shape<T, D>::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k1_ln_proj<D, DH, true>), dim3(a.tiles), dim3(K1Shape<D>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((k1_ln_proj<T, D, DH, false>), dim3(grid), dim3(K1Shape<T, D>::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k1_ln_proj<D, DH, false>), dim3(grid), dim3(K1Shape<D>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_k1(int dtype, int D, int dh, const K1Args &a, int grid, hipStream_t s) {
-#define TRI_K1_CASE(TT, DD, HH) \
-  if (D == DD && dh == HH) return launch_k1_t<TT, DD, HH>(a, grid, s);
-  if (dtype == TRI_ATTN_BF16) {
-    TRI_K1_CASE(bf16_t, 128, 16)
-    TRI_K1_CASE(bf16_t, 128, 32)
-    TRI_K1_CASE(bf16_t, 64, 16)
-    TRI_K1_CASE(bf16_t, 64, 32)
-  } else {
-    TRI_K1_CASE(float, 128, 16)
-    TRI_K1_CASE(float, 128, 32)
-    TRI_K1_CASE(float, 64, 16)
-    TRI_K1_CASE(float, 64, 32)
-  }
+  if (dtype != TRI_ATTN_BF16) return hipErrorInvalidValue;  // float32: launch_k1_split
+#define TRI_K1_CASE(DD, HH) \
+  if (D == DD && dh == HH) return launch_k1_t<DD, HH>(a, grid, s);
+  TRI_K1_CASE(128, 16)
+  TRI_K1_CASE(128, 32)
+  TRI_K1_CASE(64, 16)
+  TRI_K1_CASE(64, 32)
 #undef TRI_K1_CASE
   return hipErrorInvalidValue;
 }
 
 int k1_blocks_per_cu(int dtype, int D, int dh) {
   int n = 0;
-#define TRI_K1_OCC(TT, DD, HH)                                                                                    \
-  if (D == DD && dh == HH &&                                                                                      \
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k1_ln_proj<TT, DD, HH, false>, K1Shape<TT, DD>::THREADS, 0) != \
-          hipSuccess)                                                                                             \
+  if (dtype != TRI_ATTN_BF16) return 1;
+#define TRI_K1_OCC(DD, HH)                                                                                    \
+  if (D == DD && dh == HH &&                                                                                  \
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k1_ln_proj<DD, HH, false>, K1Shape<DD>::THREADS, 0) != \
+          hipSuccess)                                                                                         \
     n = 1;
-  if (dtype == TRI_ATTN_BF16) {
-    TRI_K1_OCC(bf16_t, 128, 16)
-    TRI_K1_OCC(bf16_t, 128, 32)
-    TRI_K1_OCC(bf16_t, 64, 16)
-    TRI_K1_OCC(bf16_t, 64, 32)
-  } else {
-    TRI_K1_OCC(float, 128, 16)
-    TRI_K1_OCC(float, 128, 32)
-    TRI_K1_OCC(float, 64, 16)
-    TRI_K1_OCC(float, 64, 32)
-  }
+  TRI_K1_OCC(128, 16)
+  TRI_K1_OCC(128, 32)
+  TRI_K1_OCC(64, 16)
+  TRI_K1_OCC(64, 32)
 #undef TRI_K1_OCC
   return n > 0 ? n : 1;
 }

@@ -10,6 +10,12 @@
 // matrix cores (bias as the accumulator's start), and the result goes back
 // through LDS so that every output row is written as whole 16-byte chunks.
 // The next tile is prefetched into registers while the current one computes.
+//
+// Float32 tensors use the bf16 matrix cores with three-way split operands
+// (six exact bf16 products per float32 product, float32 accumulation; see
+// kernel 1's split products): Wo comes from its three-plane copy, and the
+// tile is split once, by the thread that loads it, into three bf16 planes in
+// LDS.
 #include "device_common.h"
 #include "tri_attn_internal.h"
 
@@ -26,15 +32,16 @@ __global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
   constexpr int NB = D / 16;  // output channel blocks = waves
   constexpr int NT = NB * 64;
   constexpr int KQ = D / 4;
-  constexpr int KS = BF ? D / 32 : D / 4;
-  constexpr int PITCH = D + 16 / ES;
+  constexpr int KS = D / 32;                   // MFMA steps over K = D
+  constexpr int PARTS = BF ? 1 : 3;            // bf16 parts per operand
+  constexpr int PITCH = D + 16 / ES;           // output staging row pitch (elements of T)
+  constexpr int XPITCH = D + 8;                // operand row pitch (bf16 elements)
   constexpr int TILE = kChunk;
   constexpr int NV = 16 * ES / 16;             // 16-byte chunks of one position's channel block
   constexpr int ROWV = D * ES / 16;            // 16-byte chunks per output row
   constexpr int CPT = TILE * ROWV / NT;        // output chunks per thread
-  using Frag = typename std::conditional<BF, bf16x8, float>::type;
 
-  __shared__ __align__(16) T xs[TILE * PITCH];
+  __shared__ __align__(16) uint16_t xs[PARTS][TILE * XPITCH];
   __shared__ __align__(16) T ys[TILE * PITCH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -44,21 +51,14 @@ __global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
 
   // Wo rows of this wave's block, stored in fragment order (each load of the
   // wave reads 1 KB contiguously): lane (g, r16) holds row wave*16 + r16,
-  // K-range [g*KQ, g*KQ+KQ)
-  constexpr int NVW = D * ES / 64;
-  Frag wo[KS];
+  // K-range [g*KQ, g*KQ+KQ), in PARTS bf16 planes
+  bf16x8 wo[KS][PARTS];
   {
-    const char *wsrc = reinterpret_cast<const char *>(a.Wof) + ((size_t)wave * NVW * 64 + lane) * 16;
+    const char *wsrc = reinterpret_cast<const char *>(a.Wof) + ((size_t)wave * KS * 64 + lane) * 16;
 #pragma unroll
-    for (int v = 0; v < NVW; ++v) {
-      const uint4 u = ldg<uint4>(wsrc + (size_t)v * 1024);
-      if constexpr (BF) {
-        wo[v] = as_bf16x8(u);
-      } else {
-        wo[4 * v] = __uint_as_float(u.x), wo[4 * v + 1] = __uint_as_float(u.y);
-        wo[4 * v + 2] = __uint_as_float(u.z), wo[4 * v + 3] = __uint_as_float(u.w);
-      }
-    }
+    for (int v = 0; v < KS; ++v)
+#pragma unroll
+      for (int q = 0; q < PARTS; ++q) wo[v][q] = as_bf16x8(ldg<uint4>(wsrc + q * a.wo_plane + (size_t)v * 1024));
   }
   f32x4 bias;
 #pragma unroll
@@ -84,27 +84,49 @@ __global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
   for (; tile < a.tiles; tile += gridDim.x) {
     const int bi_row = tile / nch, chunk = tile - bi_row * nch;
     const int j0 = chunk * TILE;
+    if constexpr (BF) {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) *reinterpret_cast<uint4 *>(&xs[lane * PITCH + wave * 16 + v * (16 / ES)]) = pre[v];
+      for (int v = 0; v < NV; ++v) *reinterpret_cast<uint4 *>(&xs[0][lane * XPITCH + wave * 16 + v * 8]) = pre[v];
+    } else {
+      // this position's 16 channels, split into three bf16 parts
+      const float *f = reinterpret_cast<const float *>(pre);
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        uint32_t p1[4], p2[4], p3[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) split3(f[8 * h8 + 2 * u], f[8 * h8 + 2 * u + 1], p1[u], p2[u], p3[u]);
+        const int o = lane * XPITCH + wave * 16 + 8 * h8;
+        *reinterpret_cast<uint4 *>(&xs[0][o]) = make_uint4(p1[0], p1[1], p1[2], p1[3]);
+        *reinterpret_cast<uint4 *>(&xs[PARTS - 2][o]) = make_uint4(p2[0], p2[1], p2[2], p2[3]);
+        *reinterpret_cast<uint4 *>(&xs[PARTS - 1][o]) = make_uint4(p3[0], p3[1], p3[2], p3[3]);
+      }
+    }
     lds_barrier();
     if (tile + (int)gridDim.x < a.tiles) load_tile(tile + gridDim.x, pre);
 
 #pragma unroll
     for (int pb = 0; pb < TILE / 16; ++pb) {
-      const T *xrow = &xs[(pb * 16 + r16) * PITCH + g * KQ];
+      const int xo = (pb * 16 + r16) * XPITCH + g * KQ;
+      auto xf = [&](int q, int s) { return as_bf16x8(*reinterpret_cast<const uint4 *>(&xs[q][xo + 8 * s])); };
       f32x4 acc = bias;
       if constexpr (BF) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma(wo[s], as_bf16x8(*reinterpret_cast<const uint4 *>(xrow + 8 * s)), acc);
+        for (int s = 0; s < KS; ++s) acc = mfma(wo[s][0], xf(0, s), acc);
       } else {
+        // (weight part, tile part): small terms (3,1) (2,2) (1,3) into acc1,
+        // large terms (2,1) (1,2) (1,1) into acc
+        f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; s += 4) {
-          const float4 v = *reinterpret_cast<const float4 *>(xrow + s);
-          acc = mfma(wo[s], v.x, acc);
-          acc = mfma(wo[s + 1], v.y, acc);
-          acc = mfma(wo[s + 2], v.z, acc);
-          acc = mfma(wo[s + 3], v.w, acc);
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 x1 = xf(0, s), x2 = xf(PARTS - 2, s), x3 = xf(PARTS - 1, s);
+          acc1 = mfma(wo[s][PARTS - 1], x1, acc1);
+          acc = mfma(wo[s][PARTS - 2], x1, acc);
+          acc1 = mfma(wo[s][PARTS - 2], x2, acc1);
+          acc = mfma(wo[s][0], x2, acc);
+          acc1 = mfma(wo[s][0], x3, acc1);
+          acc = mfma(wo[s][0], x1, acc);
         }
+        acc += acc1;
       }
       // y^T tile: lane (g, r16) holds channels wave*16 + 4g..4g+3 of position pb*16 + r16
       T *dst = &ys[(pb * 16 + r16) * PITCH + wave * 16 + 4 * g];

@@ -267,7 +267,12 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
 
   K3Args a3{};
   a3.go = a1.g;
-  a3.Wof = static_cast<const char *>(t->wfrag) + (size_t)4 * D * D * e;
+  if (t->wsplit) {
+    a3.Wof = static_cast<const char *>(t->wsplit) + (size_t)4 * D * D * 2;
+    a3.wo_plane = t->wsplit_plane;
+  } else {
+    a3.Wof = static_cast<const char *>(t->wfrag) + (size_t)4 * D * D * e;
+  }
   a3.bo = vp + (size_t)3 * D * e;
   a3.out = out;
   a3.B = B, a3.N = N, a3.Np = L.Np, a3.nchunk = L.nchunk;

@@ -48,7 +48,8 @@ struct K2Args {
 // Kernel 3: output projection of g * o (left by kernel 2 in the gate region).
 struct K3Args {
   const void *go;  // [B][N][D/16][Np][16]
-  const void *Wof;  // Wo in fragment order (pack_weights.hip)
+  const void *Wof;  // Wo in fragment order (pack_weights.hip); float32 handles: its first split plane
+  size_t wo_plane;  // float32 handles: bytes from one split plane of Wo to the next
   const void *bo;
   void *out;       // [B][N][N][D]
   int B, N, Np, nchunk, tiles;
