@@ -213,7 +213,9 @@ def test_projection_stage(dtype, shape):
     rg = cap["g"].reshape(B_, N, N, D)
     M = inp["pair_mask"]
     rz = np.where(M[:, None] != 0, cap["z"] * LOG2E, -np.inf)  # (b, t, j, k)
-    atol, rtol = (1e-4, 1e-4) if dtype == "f32" else (2e-2, 1e-2)
+    # float32: the products run as six exact bf16 products of split operands;
+    # the bound is float32-level (measured errors are about 1e-6)
+    atol, rtol = (1e-5, 1e-5) if dtype == "f32" else (2e-2, 1e-2)
     for name, got, ref in (("q", q, rq), ("k", k, rk), ("g", gg, rg), ("v", vt, rv.transpose(0, 1, 2, 4, 3))):
         log(f"  {name}: max abs err {np.abs(got - ref).max():.3e}, max |ref| {np.abs(ref).max():.3f}")
         np.testing.assert_allclose(got, ref, rtol=rtol, atol=atol, err_msg=name)

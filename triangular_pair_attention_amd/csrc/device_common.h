@@ -86,6 +86,24 @@ __device__ __forceinline__ void stg(void *p, V v) {
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
 
+// Sum over each aligned group of W lanes (W = 4 or 8: lanes Wk .. Wk+W-1),
+// every lane getting its group's sum, with DPP lane moves on the VALU instead
+// of round trips through the LDS crossbar: swap neighbours (quad_perm
+// 1,0,3,2), swap pairs (quad_perm 2,3,0,1) and, for 8, add the other quad
+// (row_half_mirror: lane i of the 8 reads lane 7 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(W == 4 || W == 8, "groups of 4 or 8 lanes");
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  if constexpr (W == 8) v += dpp_mov<0x141>(v);
+  return v;
+}
+
 // Sum / max over the four lanes that share l % 16 (lane groups l / 16).
 __device__ __forceinline__ float group4_sum(float v) { return xor_sum(xor_sum(v, 16), 32); }
 __device__ __forceinline__ float group4_max(float v) { return xor_max(xor_max(v, 16), 32); }

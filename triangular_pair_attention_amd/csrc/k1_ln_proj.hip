@@ -158,8 +158,7 @@ __global__ __launch_bounds__((K1Shape<D>::THREADS)) void k1_ln_proj(K1Args a) {
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) s += v[e];
-#pragma unroll
-    for (int m = 1; m < TPP; m <<= 1) s = xor_sum(s, m);
+    s = group_sum<TPP>(s);
     const float mean = s * (1.0f / D);
     float q = 0.f;
 #pragma unroll
@@ -167,8 +166,7 @@ __global__ __launch_bounds__((K1Shape<D>::THREADS)) void k1_ln_proj(K1Args a) {
       const float dv = v[e] - mean;
       q += dv * dv;
     }
-#pragma unroll
-    for (int m = 1; m < TPP; m <<= 1) q = xor_sum(q, m);
+    q = group_sum<TPP>(q);
     const float rstd = rsqrtf(q * (1.0f / D) + a.eps);
     const float scale = (j < N) ? rstd : 0.f;  // padding positions (j >= N) become zero rows
     const float bmul = (j < N) ? 1.f : 0.f;

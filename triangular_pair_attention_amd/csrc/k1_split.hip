@@ -24,8 +24,9 @@
 // the grid allows it, so the second read of the tile's pair_repr hits L2.
 //
 //  1. LayerNorm (fp32 statistics, two-pass in registers), 8 lanes per
-//     position; the normalised row goes to LDS as its three bf16 parts. The
-//     next tile's pair_repr and mask are prefetched during this tile's products.
+//     position; the normalised row goes to LDS as its three bf16 parts. A
+//     workgroup's first two tiles are normalised together before their
+//     products; later tiles' pair_repr and mask are prefetched one ahead.
 //  2. Products: six MFMAs per step into two accumulators per projection (the
 //     three small terms, then the three large), so consecutive MFMAs are
 //     independent; the four 16-position blocks run as a software pipeline.
@@ -71,7 +72,8 @@ __global__ __launch_bounds__(512) void k1_ln_proj_split(K1Args a) {
   __shared__ uint8_t mask_s[2][TILE];                 // the tile's mask bytes (0 also for j >= N)
   __shared__ float vec_s[3][D];                       // gamma, beta, gate bias
   __shared__ __align__(16) uint16_t wz_s[3][16 * PITCH];  // pair-bias weight block, three parts (rows >= h zero)
-  __shared__ float zpart_s[TILE / 16][16];            // per-block maxima of the pair bias of a tile
+  __shared__ float zpart_s[2][TILE / 16][16];         // per-block maxima of the pair bias of a tile (per buffer:
+                                                      // a workgroup's first two tiles have no barrier between them)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,8 +156,7 @@ __global__ __launch_bounds__(512) void k1_ln_proj_split(K1Args a) {
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) s += v[e];
-#pragma unroll
-    for (int m = 1; m < TPP; m <<= 1) s = xor_sum(s, m);
+    s = group_sum<TPP>(s);
     const float mean = s * (1.0f / D);
     float q = 0.f;
 #pragma unroll
@@ -163,8 +164,7 @@ __global__ __launch_bounds__(512) void k1_ln_proj_split(K1Args a) {
       const float dv = v[e] - mean;
       q += dv * dv;
     }
-#pragma unroll
-    for (int m = 1; m < TPP; m <<= 1) q = xor_sum(q, m);
+    q = group_sum<TPP>(q);
     const float rstd = rsqrtf(q * (1.0f / D) + a.eps);
     const float scale = (j < N) ? rstd : 0.f;  // padding positions (j >= N) become zero rows
     const float bmul = (j < N) ? 1.f : 0.f;
@@ -332,13 +332,13 @@ __global__ __launch_bounds__(512) void k1_ln_proj_split(K1Args a) {
     if constexpr (HALF0) {
       if (wave < TILE / 16) {
         const float m = group4_max(z_run);
-        if (g == 0) zpart_s[wave][r16] = m;
+        if (g == 0) zpart_s[buf][wave][r16] = m;
       }
       lds_barrier();
       if (wave == 0 && lane < H) {
-        float m = zpart_s[0][lane];
+        float m = zpart_s[buf][0][lane];
 #pragma unroll
-        for (int q = 1; q < TILE / 16; ++q) m = fmaxf(m, zpart_s[q][lane]);
+        for (int q = 1; q < TILE / 16; ++q) m = fmaxf(m, zpart_s[buf][q][lane]);
         a.zmax[((size_t)(b * H + lane) * nch + chunk) * N + i] = m;
       }
     }
@@ -364,24 +364,36 @@ __global__ __launch_bounds__(512) void k1_ln_proj_split(K1Args a) {
 
   int tile = slot;
   if (tile >= a.tiles) return;  // uniform over the workgroup
-  float4 pre[NV];
-  uint32_t mpre;
-  // the first tile's pair_repr goes out first, then the small parameters, then
-  // the weights: LayerNorm waits only for its own data
+  const bool two = tile + GH < a.tiles;
+  float4 pre[NV], pre2[NV];
+  uint32_t mpre, mpre2 = 0;
+  // the first two tiles' pair_repr go out first, then the small parameters,
+  // then the weights: LayerNorm waits only for its own data
   load_tile(tile, pre, mpre);
+  if (two) load_tile(tile + GH, pre2, mpre2);
   issue_params();
   load_weights();
   commit_params();
   lds_barrier();
-  // first tile in straight-line code, so that its products wait only for
-  // their own weights (a loop would wait for every outstanding load first)
+  // the first two tiles in straight-line code, both normalised before any
+  // product: their eight 16-position blocks run with no barrier between the
+  // tiles (one wave's late finish of the first tile holds no one up), and the
+  // products wait only for their own weights (a loop would wait for every
+  // outstanding load first)
   layer_norm_to_lds(tile, pre, mpre, 0);
+  if (two) layer_norm_to_lds(tile + GH, pre2, mpre2, 1);
   lds_barrier();
-  if (tile + GH < a.tiles) load_tile(tile + GH, pre, mpre);
+  if (tile + 2 * GH < a.tiles) load_tile(tile + 2 * GH, pre, mpre);
   compute(tile, 0);
-  int buf = 1;
+  if (!two) return;
+  compute(tile + GH, 1);
+  if (tile + 2 * GH >= a.tiles) return;
+  // both buffers were read by the two tiles above: every wave must be done
+  // with them before the loop overwrites buffer 0
+  lds_barrier();
+  int buf = 0;
 #pragma unroll 1
-  for (tile += GH; tile < a.tiles; tile += GH) {
+  for (tile += 2 * GH; tile < a.tiles; tile += GH) {
     layer_norm_to_lds(tile, pre, mpre, buf);
     lds_barrier();
     if (tile + GH < a.tiles) load_tile(tile + GH, pre, mpre);
