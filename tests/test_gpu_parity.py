@@ -237,6 +237,40 @@ def test_projection_stage(dtype, shape):
     np.testing.assert_allclose(vsum, vs, rtol=rtol, atol=atol * 64)
 
 
+def test_float32_split_products_scale():
+    """float32 projections run as six exact bf16 products of split operands:
+    their error must stay at float32 level relative to the values' scale,
+    here with pair_repr offset by 3e4 (spread 1e4) and weights scaled by 1e3
+    and 1e-3."""
+    B_, N, D, h = 1, 70, 128, 4
+    inp = make_inputs(Workload("scale", B_, N, D, h, "f32", ("bernoulli", 0.8), seed=12))
+    inp["pair_repr"] = (inp["pair_repr"] * 1e4 + 3e4).astype(np.float32)
+    inp["w_key"] = (inp["w_key"] * 1e3).astype(np.float32)
+    inp["w_value"] = (inp["w_value"] * 1e-3).astype(np.float32)
+    inp["w_out"] = (inp["w_out"] * 1e3).astype(np.float32)
+    inp["b_out"] = (inp["b_out"] * 1e3).astype(np.float32)
+    log("float32 split products at scale")
+    g = Gpu(inp)
+    try:
+        lay = g.project()
+        Np = lay.padded_n
+        f = lambda off, n: g.region(off, n, torch.float32).cpu().numpy().astype(np.float64)  # noqa: E731
+        k = f(lay.k, B_ * N * D * Np).reshape(B_, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4)
+        vt = f(lay.vt, B_ * N * D * Np).reshape(B_, N, h, D // h, Np)[..., :N]
+        y = y_numpy(g.forward())
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+    cap = {}
+    ref = O.forward(inp, capture=cap)
+    rk = O.merge_heads(cap["k"]).reshape(B_, N, N, D)
+    rv = cap["v"].reshape(B_, N, h, N, D // h).transpose(0, 1, 2, 4, 3)
+    for name, got, want, bound in (("k", k.reshape(B_, N, N, D), rk, 1e-5), ("v", vt, rv, 1e-5), ("y", y, ref, 1e-5)):
+        rel = float(np.abs(got - want).max() / np.abs(want).max())
+        log(f"  {name}: max |ref| {np.abs(want).max():.3e}, max abs err / max |ref| {rel:.2e}")
+        assert rel <= bound, f"{name}: relative error {rel} > {bound}"
+
+
 # ------------------------------------------------------------------ ABI behaviour on the GPU
 def test_deterministic_and_stream():
     inp = make_inputs(WORKLOADS[3].replace(N=96))
