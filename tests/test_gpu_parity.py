@@ -287,6 +287,40 @@ def test_deterministic_and_stream():
         g.close()
 
 
+@pytest.mark.parametrize("k", [2, 3])
+def test_forward_captured_in_hip_graph(k):
+    """The forward enqueues kernels only (no memsets, no allocation), so it can
+    be captured in a HIP graph; every replay, with eager work of the library
+    between replays, must equal the eager forward bit for bit."""
+    w = WORKLOADS[k]
+    inp = make_inputs(w)
+    log(f"HIP graph capture {w.name}")
+    g = Gpu(inp)
+    try:
+        eager = g.forward().clone()
+        torch.cuda.synchronize()
+        out = torch.empty_like(g.P)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            g.forward(out=out, stream=side)  # warm-up on a side stream before capture
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            g.forward(out=out, stream=torch.cuda.current_stream())
+        for r in range(4):
+            out.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"replay {r} differs from the eager forward"
+            other = g.forward()  # eager work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(other, eager)
+        del graph
+    finally:
+        g.close()
+
+
 def test_empty_and_error_paths():
     inp = make_inputs(Workload("err", 1, 20, 64, 4, "f32", ("bernoulli", 0.8), 3))
     log("error paths")
