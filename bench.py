@@ -277,6 +277,25 @@ def main():
     ms_k2 = timed(k2, args.steps)
     ms_k3 = timed(k3, args.steps)
     torch.cuda.synchronize()
+    # the same forward replayed from a captured HIP graph (a serving loop's
+    # launch path), for comparison; `value` stays the direct forward call
+    ms_graph = None
+    try:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            B.tri_attn_forward(h, P, M, out, w.B, w.N, ws, nws, side)
+        stream.wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            B.tri_attn_forward(h, P, M, out, w.B, w.N, ws, nws, torch.cuda.current_stream(dev))
+        for _ in range(args.warmup):
+            graph.replay()
+        ms_graph = timed(graph.replay, args.steps)
+        del graph
+    except RuntimeError as e:  # capture unsupported: report no graph timing
+        print(f"bench.py: graph timing skipped ({e})", file=sys.stderr)
+    torch.cuda.synchronize()
     B.tri_attn_destroy(h)
 
     m = work_model(w)
@@ -306,6 +325,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "h": w.h, "d": w.d,
                    "mask": list(w.mask), "seed": w.seed, "parallelism": "none (1 GPU)"},
         "tflops": tflops,
+        "ms_per_step_graph_replay": ms_graph,
         "kernels_ms": ms_k,
         "kernels_roofline": {k: roofline_of(k, w, m, v) for k, v in ms_k.items()},
         "attention_floor": attention_floor(w, m, ms_k2, inp["pair_mask"]),
