@@ -168,6 +168,13 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   // bf16: lane (g, r16) holds q'[j = r16][8g..8g+7] (d = 16: groups 0-1 real, group 2 slot 0 = -m);
   // fp32: lane (g, r16) holds q'[j][g*d/4 .. +d/4).
   Frag qf[IG][JW][BF ? 1 : QS];
+  // fp32, d = 32: the scores run as six bf16 products of three-way split
+  // operands (float32 accuracy; kernel 1's split products): each lane
+  // already holds channels 8g..8g+7 of one query and of one key, the bf16
+  // 16x16x32 fragment layout. The queries are split once per item (below,
+  // in setup), the keys per step.
+  constexpr bool SPLITQK = !BF && DH == 32;
+  bf16x8 qsp[IG][JW][SPLITQK ? 3 : 1];
   auto load_q = [&]() {
 #pragma unroll
     for (int i = 0; i < IG; ++i)
@@ -426,6 +433,19 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : sqrtf(n2 * kn2[i]) + zmx[jb] + a.shift_slack;
       }
     set_shift(msh);
+    if constexpr (SPLITQK) {
+#pragma unroll
+      for (int i = 0; i < IG; ++i)
+#pragma unroll
+        for (int jb = 0; jb < JW; ++jb) {
+          uint32_t p1[4], p2[4], p3[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) split3(qf[i][jb][2 * u], qf[i][jb][2 * u + 1], p1[u], p2[u], p3[u]);
+          qsp[i][jb][0] = as_bf16x8(make_uint4(p1[0], p1[1], p1[2], p1[3]));
+          qsp[i][jb][1] = as_bf16x8(make_uint4(p2[0], p2[1], p2[2], p2[3]));
+          qsp[i][jb][2] = as_bf16x8(make_uint4(p3[0], p3[1], p3[2], p3[3]));
+        }
+    }
     // bf16, d = 32: the shift costs two more MFMAs per score tile. Where every
     // bound of the wave is at most 64, exp2 of a score cannot overflow (2^64
     // per key, sums far below the fp32 range) and the wave goes without it;
@@ -564,11 +584,32 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         f32x4 vf[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) vf[mb] = __builtin_bit_cast(f32x4, vblk[(r * VBR + mb) * 64 + lane]);
+        bf16x8 ks[SPLITQK ? 3 : 1];
+        if constexpr (SPLITQK) {
+          uint32_t p1[4], p2[4], p3[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) split3(kf[2 * u], kf[2 * u + 1], p1[u], p2[u], p3[u]);
+          ks[0] = as_bf16x8(make_uint4(p1[0], p1[1], p1[2], p1[3]));
+          ks[1] = as_bf16x8(make_uint4(p2[0], p2[1], p2[2], p2[3]));
+          ks[2] = as_bf16x8(make_uint4(p3[0], p3[1], p3[2], p3[3]));
+        }
 #pragma unroll
         for (int jb = 0; jb < JW; ++jb) {
           f32x4 s = zA[jb];
+          if constexpr (SPLITQK) {
+            // (key part, query part): small terms (3,1) (2,2) (1,3), then large (2,1) (1,2) (1,1)
+            f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
+            s1 = mfma(ks[2], qsp[i][jb][0], s1);
+            s = mfma(ks[1], qsp[i][jb][0], s);
+            s1 = mfma(ks[1], qsp[i][jb][1], s1);
+            s = mfma(ks[0], qsp[i][jb][1], s);
+            s1 = mfma(ks[0], qsp[i][jb][2], s1);
+            s = mfma(ks[0], qsp[i][jb][0], s);
+            s += s1;
+          } else {
 #pragma unroll
-          for (int ss = 0; ss < QS; ++ss) s = mfma(kf[ss], qf[i][jb][ss], s);
+            for (int ss = 0; ss < QS; ++ss) s = mfma(kf[ss], qf[i][jb][ss], s);
+          }
           if (max_pass) {
             float m = mx[i][jb];
 #pragma unroll
