@@ -7,8 +7,10 @@
 // [b][i][c/16][j][16]. Work unit: 64 consecutive positions (b, i, j0..j0+63);
 // persistent grid. Each wave holds the 16 rows of Wo of one output channel
 // block in registers (read from a copy in fragment order); the tile goes through LDS once, is multiplied on the
-// matrix cores (bias as the accumulator's start), and the result goes back
-// through LDS so that every output row is written as whole 16-byte chunks.
+// matrix cores (bias as the accumulator's start), and the bf16 result goes
+// back through LDS so that every output row is written as whole 16-byte
+// chunks (float32 results are 16 contiguous bytes per lane already and are
+// stored straight from the accumulators).
 // The next tile is prefetched into registers while the current one computes.
 //
 // Float32 tensors use the bf16 matrix cores with three-way split operands
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
   constexpr int CPT = TILE * ROWV / NT;        // output chunks per thread
 
   __shared__ __align__(16) uint16_t xs[PARTS][TILE * XPITCH];
-  __shared__ __align__(16) T ys[TILE * PITCH];
+  __shared__ __align__(16) T ys[BF ? TILE * PITCH : 1];  // bf16: output staging
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -129,20 +131,31 @@ __global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
         acc += acc1;
       }
       // y^T tile: lane (g, r16) holds channels wave*16 + 4g..4g+3 of position pb*16 + r16
-      T *dst = &ys[(pb * 16 + r16) * PITCH + wave * 16 + 4 * g];
-      if constexpr (BF)
+      if constexpr (BF) {
+        T *dst = &ys[(pb * 16 + r16) * PITCH + wave * 16 + 4 * g];
         *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
-      else
-        *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      } else {
+        // float32: 16 contiguous bytes per lane, stored at once, so the
+        // stores of block pb overlap the products of block pb + 1
+        const int j = j0 + pb * 16 + r16;
+        if (j < N)
+          stg<float4>(reinterpret_cast<float *>(a.out) + ((size_t)bi_row * N + j) * D + wave * 16 + 4 * g,
+                      make_float4(acc[0], acc[1], acc[2], acc[3]));
+      }
     }
+    // every wave is done with xs before the next tile overwrites it (and, for
+    // bf16, the staged output tile is complete)
     lds_barrier();
+    if constexpr (BF) {
+      // whole 16-byte chunks of each output row
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int c = tid + NT * k;
-      const int pos = c / ROWV, off = c - pos * ROWV;
-      if (j0 + pos < N) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(&ys[pos * PITCH + off * (16 / ES)]);
-        stg<uint4>(reinterpret_cast<T *>(a.out) + ((size_t)bi_row * N + j0 + pos) * D + off * (16 / ES), v);
+      for (int k = 0; k < CPT; ++k) {
+        const int c = tid + NT * k;
+        const int pos = c / ROWV, off = c - pos * ROWV;
+        if (j0 + pos < N) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(&ys[pos * PITCH + off * (16 / ES)]);
+          stg<uint4>(reinterpret_cast<T *>(a.out) + ((size_t)bi_row * N + j0 + pos) * D + off * (16 / ES), v);
+        }
       }
     }
   }
