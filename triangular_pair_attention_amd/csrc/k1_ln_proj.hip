@@ -75,6 +75,10 @@ __global__ __launch_bounds__((K1Shape<D>::THREADS)) void k1_ln_proj(K1Args a) {
   __shared__ float vec_s[3][D];                 // gamma, beta, gate bias (fp32)
   __shared__ __align__(16) T wz_s[16 * PITCH];  // pair-bias weight block (rows >= h are zero)
   __shared__ float zpart_s[TILE / 16][16];      // per-block maxima of the pair bias of a tile
+  // this wave's v^T block of a tile (16 channels x 64 positions), written out
+  // as whole 128-byte channel rows instead of 16 pieces of 32 bytes per block
+  constexpr int VPITCH = TILE + 8;
+  __shared__ __align__(16) uint16_t vst_s[NW][16 * VPITCH];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar block and base arithmetic
@@ -248,8 +252,10 @@ __global__ __launch_bounds__((K1Shape<D>::THREADS)) void k1_ln_proj(K1Args a) {
         const uint32_t toff = (uint32_t)(jcol * 16 + 4 * g);  // q/k/gate tiles: [b][i][c/16][j][16]
         if (type == 2) {
           // v^T per head, [b][i][t][u][j] (t * DH + u = channel): lane (g, r16)
-          // holds channel cb*16 + r16 of positions 4g..4g+3
-          store4(vbase, (uint32_t)((cb * 16 + r16) * Np + j0 + pb * 16 + 4 * g), c[0], c[1], c[2], c[3]);
+          // holds channel cb*16 + r16 of positions 4g..4g+3; staged in LDS
+          // and stored after the tile's four blocks
+          *reinterpret_cast<uint2 *>(&vst_s[wave][r16 * VPITCH + pb * 16 + 4 * g]) =
+              make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
           v_run += (c[0] + c[1]) + (c[2] + c[3]);  // positions j >= N hold v = 0
         } else if (type == 0) {
           store4(qbase, toff, c[0] * a.qscale, c[1] * a.qscale, c[2] * a.qscale, c[3] * a.qscale);
@@ -299,6 +305,16 @@ __global__ __launch_bounds__((K1Shape<D>::THREADS)) void k1_ln_proj(K1Args a) {
     epilogue(2, accA);
     epilogue(3, accB);
 
+    if constexpr (TYPE0 <= 2 && TYPE0 + TPW > 2) {
+      // v^T rows of this wave's channel block: 128 contiguous bytes per
+      // channel, 16 per lane (each wave reads back only what it wrote)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int piece = lane + 64 * hh, row = piece >> 3, col = (piece & 7) * 8;
+        const uint4 v = *reinterpret_cast<const uint4 *>(&vst_s[wave][row * VPITCH + col]);
+        stg<uint4>(reinterpret_cast<char *>(vbase) + ((size_t)(cb * 16 + row) * Np + j0 + col) * ES, v);
+      }
+    }
     // per-chunk sums of v (a fixed summation order: deterministic)
     if (TYPE0 <= 2 && TYPE0 + TPW > 2) {
       const float sv = group4_sum(v_run);
