@@ -101,6 +101,30 @@ def test_small_ragged(shape, dtype, mask):
     check(y, ref, dtype, f"{shape} {dtype} {mask}")
 
 
+def _random_case(n):
+    """Seeded random configuration n: batch 1-3, N 1-200, D 64 or 128, head
+    size 16 or 32, either dtype, Bernoulli or padding mask, -1e9 fill."""
+    rng = np.random.default_rng(5000 + n)
+    B_ = int(rng.integers(1, 4))
+    N = int(rng.integers(1, 201))
+    D = int(rng.choice([64, 128]))
+    h = D // int(rng.choice([16, 32]))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    if rng.random() < 0.5:
+        mask = ("bernoulli", float(rng.uniform(0.5, 0.95)))
+    else:
+        mask = ("pad", int(rng.integers(1, N + 1)))
+    return Workload(f"random{n}", B_, N, D, h, dtype, mask, seed=6000 + n)
+
+
+@pytest.mark.parametrize("n", range(16))
+def test_random_shapes(n):
+    w = _random_case(n)
+    log(f"random case {n}: B={w.B} N={w.N} D={w.D} h={w.h} {w.dtype} {w.mask}")
+    y, ref = run_case(make_inputs(w))
+    check(y, ref, w.dtype, w.name)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_all_keys_masked(dtype):
     """Mask all zero: every query column is fully masked -> mean of v over all N keys."""

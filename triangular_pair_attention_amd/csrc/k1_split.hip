@@ -12,7 +12,7 @@
 // accurate as a float32 GEMM (the six-product scheme of Henry, Tang and
 // Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype For
 // Higher-Precision Computations", ARITH 2019). A 16x16x32 block of work takes
-// six bf16 16x16x32 MFMAs instead of eight float32 16x16x4 ones: about 2.5x
+// six bf16 16x16x32 MFMAs instead of eight float32 16x16x4 ones: about 2.4x
 // fewer matrix-core cycles at the rates gfx950 runs them.
 //
 // Work item: a tile of 64 consecutive positions (b, i, j0..j0+63) of one row
