@@ -93,9 +93,11 @@ def work_model(w):
     }
 
 
-def roofline_of(kernel, w, m, ms):
+def roofline_of(kernel, w, m, ms, mask=None):
     """The bound of one kernel: HBM where its arithmetic intensity is below the
-    ridge of its dtype's matrix-core peak, else the matrix cores."""
+    ridge of its dtype's matrix-core peak, else the matrix cores. For the
+    attention kernel with a mask, also the rate and fraction on the valid
+    (j, k) score pairs only (the work that must be computed)."""
     mfma = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
     ridge = mfma * 1e12 / (PEAK["hbm_GBps"] * 1e9)
     fl, by = m[kernel]["flops"], m[kernel]["bytes"]
@@ -104,6 +106,10 @@ def roofline_of(kernel, w, m, ms):
     else:
         r = {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": mfma, "unit": "TFLOP/s"}
     r["frac"] = r["achieved"] / r["peak"]
+    if kernel == "k2_attention" and mask is not None:
+        valid = int((mask != 0).sum())  # (b, j, k) pairs, each scored for all N rows i
+        r["achieved_valid_pairs"] = 4 * w.N * w.D * valid / (ms * 1e-3) / 1e12
+        r["frac_valid_pairs"] = r["achieved_valid_pairs"] / r["peak"]
     if w.dtype == "f32" and kernel in SPLIT_KERNELS and r["bound"] == "mfma":
         # the matrix cores run six bf16 products per float32 product
         ceil = PEAK["mfma_bf16_TFLOPs"] / 6
@@ -304,7 +310,7 @@ def main():
     tflops = total_flops / (ms_fwd * 1e-3) / 1e12
     ms_k = {"k1_ln_proj": ms_k1, "k2_attention": ms_k2, "k3_out_proj": ms_k3}
     dom = max(ms_k, key=ms_k.get)
-    roof = roofline_of(dom, w, m, ms_k[dom])
+    roof = roofline_of(dom, w, m, ms_k[dom], inp["pair_mask"])
     roof["traffic"] = stored_traffic(w.name, dom, w.dtype)
     roof["kernel"] = dom
     roof["kernel_ms"] = ms_k[dom]
@@ -327,7 +333,7 @@ def main():
         "tflops": tflops,
         "ms_per_step_graph_replay": ms_graph,
         "kernels_ms": ms_k,
-        "kernels_roofline": {k: roofline_of(k, w, m, v) for k, v in ms_k.items()},
+        "kernels_roofline": {k: roofline_of(k, w, m, v, inp["pair_mask"]) for k, v in ms_k.items()},
         "attention_floor": attention_floor(w, m, ms_k2, inp["pair_mask"]),
         "wall_s_timed": wall,
         "roofline": roof,

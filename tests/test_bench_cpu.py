@@ -49,6 +49,18 @@ def test_bound_selection():
     assert r["frac"] == pytest.approx(r["achieved"] / 157.3)
 
 
+def test_attention_roofline_on_valid_pairs():
+    import numpy as np
+    w = WORKLOADS[5]
+    m = bench.work_model(w)
+    mask = np.zeros((4, 512, 512), np.uint8)
+    mask[:, :100, :200] = 1
+    r = bench.roofline_of("k2_attention", w, m, 1.0, mask)
+    assert r["achieved_valid_pairs"] == pytest.approx(4 * 512 * 128 * (4 * 100 * 200) / 1e-3 / 1e12)
+    assert r["frac_valid_pairs"] == pytest.approx(r["achieved_valid_pairs"] / 2500.0)
+    assert "achieved_valid_pairs" not in bench.roofline_of("k1_ln_proj", w, m, 1.0, mask)
+
+
 def test_split_products_ceiling():
     # float32 kernels 1 and 3 run six bf16 products per float32 product
     m2 = bench.work_model(WORKLOADS[2])
