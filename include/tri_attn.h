@@ -39,7 +39,7 @@ typedef struct tri_attn *tri_attn_t; /* opaque handle */
  * q/k/v/gate/bias weights, and the output projection) run on the bf16 matrix
  * cores with each float32 operand split exactly into three bf16 parts and
  * six of the nine part products summed in float32 (relative error per
- * product below 2^-24, as for a float32 product); so do the attention scores
+ * product at most about 2^-23, float32 level); so do the attention scores
  * q.k for head size 32, while the probability-value products (and head size
  * 16's scores) are float32 matrix-core products. TRI_ATTN_BF16: the
  * matrix-core operands are

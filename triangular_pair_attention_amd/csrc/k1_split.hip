@@ -7,7 +7,7 @@
 // Split products. Each float32 operand is written as three bf16 numbers,
 // a = a1 + a2 + a3 exactly (split3 in device_common.h). The product a*b is
 // summed as the six terms a_i*b_j with i + j <= 4; the three dropped terms are
-// of order 2^-24 |a b| and below, and every kept term is an exact bf16 x bf16
+// at most 2^-24 |a b| each, and every kept term is an exact bf16 x bf16
 // product accumulated in float32 by the matrix cores, so the result is as
 // accurate as a float32 GEMM (the six-product scheme of Henry, Tang and
 // Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype For
