@@ -43,6 +43,10 @@
 // chunks of 64 beyond the last live chunk of the workgroup's columns are
 // skipped.
 //
+// Float32: the scores of head size 32 are six bf16 products of three-way
+// split operands (float32 accuracy at fewer matrix-core cycles); the
+// probability-value products are float32 MFMAs.
+//
 // Output: o / l times the gate, written over the gate in the workspace
 // ([b][i][c/16][j][16]); kernel 3 reads it from there.
 #include "device_common.h"
