@@ -159,11 +159,15 @@ def stored_traffic(workload: str, kernel: str, dtype: str = "bf16"):
     return None
 
 
-def cpu_baseline(inp, w, seconds):
+def cpu_baseline(inp, w, seconds, ending_node=False):
     """The oracle as it stands on the host cores: all N rows of batch 0 (with
-    that batch's LayerNorm and pair bias), repeated until `seconds` elapse."""
+    that batch's LayerNorm and pair bias), repeated until `seconds` elapse
+    (ending-node: all N columns of batch 0)."""
     import numpy as np  # noqa: F401
-    from oracle.tri_attn_oracle import forward_rows
+    from oracle.tri_attn_oracle import forward_ending_cols, forward_rows
+
+    if ending_node:
+        forward_rows = forward_ending_cols  # noqa: F811 (same work, the other residue axis)
 
     try:
         from threadpoolctl import threadpool_info
@@ -186,7 +190,8 @@ def cpu_baseline(inp, w, seconds):
         "unit": "pair-positions/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"{done} x all {w.N} rows of batch 0 of {w.name} ({pos} pair positions, "
+        "sample": f"{done} x all {w.N} {'columns' if ending_node else 'rows'} of batch 0 of {w.name} "
+                  f"({pos} pair positions, "
                   f"{el:.1f} s, float64 numpy, BLAS threads = {cores})",
     }
 
@@ -211,6 +216,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--ending-node", action="store_true",
+                    help="the ending-node variant (attention along the other residue axis)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -237,7 +244,8 @@ def main():
     M = torch.from_numpy(inp["pair_mask"]).to(dev).contiguous()
     out = torch.empty_like(P)
     stream = torch.cuda.current_stream(dev)
-    cfg = B.tri_attn_config(w.D, w.h, B.TRI_ATTN_F32 if w.dtype == "f32" else B.TRI_ATTN_BF16, 1e-5, -1e9, 0.0)
+    cfg = B.tri_attn_config(w.D, w.h, B.TRI_ATTN_F32 if w.dtype == "f32" else B.TRI_ATTN_BF16, 1e-5, -1e9, 0.0,
+                            int(args.ending_node))
     h = B.tri_attn_create(cfg, weights, stream)
     nws = B.tri_attn_workspace_size(h, w.B, w.N)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
@@ -328,8 +336,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "N": w.N, "D": w.D, "h": w.h, "d": w.d,
-                   "mask": list(w.mask), "seed": w.seed, "parallelism": "none (1 GPU)"},
+        "config": {"workload": w.name + ("_ending_node" if args.ending_node else ""), "B": w.B, "N": w.N,
+                   "D": w.D, "h": w.h, "d": w.d, "mask": list(w.mask), "seed": w.seed,
+                   "variant": "ending-node" if args.ending_node else "starting-node",
+                   "parallelism": "none (1 GPU)"},
         "tflops": tflops,
         "ms_per_step_graph_replay": ms_graph,
         "kernels_ms": ms_k,
@@ -339,7 +349,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds, args.ending_node)
     print(json.dumps(result), flush=True)
 
 

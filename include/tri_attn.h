@@ -70,6 +70,17 @@ typedef struct {
    * softmax shift, which pushes the kernel into its exact-maximum recovery
    * path. Results are unchanged. */
   float shift_slack;
+  /* 0: starting-node attention, the variant the transcripts work through
+   * (each pair row i attends along its columns: scores q[i,j].k[i,k] plus the
+   * bias z[j,k], mask M[j,k]). 1: ending-node attention, the counterpart
+   * along the other residue axis: the starting-node computation applied to
+   * the transposed pair representation and mask, transposed back, i.e.
+   * y[i,j] from scores q[i,j].k[k,j] plus the bias z[k,i] (from the
+   * LayerNorm output at position (k,i)), mask M[k,i], values v[k,j]. The
+   * transcripts name only the starting-node variant; this reading of its
+   * counterpart swaps the two residue axes throughout. Same workspace, same
+   * cost. Any other value: TRI_ATTN_ERR_INVALID_ARG. */
+  int ending_node;
 } tri_attn_config;
 
 /* Parameters in nn.LayerNorm / nn.Linear layouts (weight = (out, in)),

@@ -32,6 +32,13 @@ u channel within a head, d = D / h):
   (7) o[b,i,j,t*d+u]= sum_k a[b,i,t,j,k] v[b,i,t,k,u]
   (8) y[b,i,j]      = Wo (g[b,i,j] * o[b,i,j]) + bo
 
+Ending-node counterpart (``forward_ending``): the transcripts name only the
+starting-node variant; its counterpart along the other residue axis is read
+here as the same computation on the transposed pair representation and mask,
+transposed back. In index notation: s[b,t,i,j,k] = q[b,i,j] . k[b,k,j] /
+sqrt(d) + z_t(x[b,k,i]), FILL where mask[b,k,i] == 0, softmax over k,
+o[b,i,j] = sum_k a v[b,k,j], y[b,i,j] = Wo (g[b,i,j] * o[b,i,j]) + bo.
+
 Readings of points the pages leave open (each is listed with its reason in
 the design notes): FILL defaults to -1e9, so a query column whose keys are
 all masked gets uniform weights over all N keys; FILL = -inf reproduces the
@@ -257,6 +264,26 @@ def forward_rows(
         for key, vals in per_row.items():
             capture[key] = np.stack(vals)
     return out
+
+
+def _transposed(inp: dict) -> dict:
+    t = dict(inp)
+    t["pair_repr"] = np.ascontiguousarray(np.swapaxes(np.asarray(inp["pair_repr"]), 1, 2))
+    t["pair_mask"] = np.ascontiguousarray(np.swapaxes(np.asarray(inp["pair_mask"]), 1, 2))
+    return t
+
+
+def forward_ending(inp: dict, fill: float = MASK_FILL, eps: float = LN_EPS) -> np.ndarray:
+    """Ending-node forward, y (B, N, N, D) in float64: the starting-node
+    forward of the pair representation and mask with both residue axes
+    swapped, swapped back (see the module notes for the index form)."""
+    return np.swapaxes(forward(_transposed(inp), fill=fill, eps=eps), 1, 2)
+
+
+def forward_ending_cols(inp: dict, cols: Sequence[Tuple[int, int]], fill: float = MASK_FILL,
+                        eps: float = LN_EPS) -> np.ndarray:
+    """Ending-node y[b, :, j] for the listed columns (b, j): (len(cols), N, D)."""
+    return forward_rows(_transposed(inp), cols, fill=fill, eps=eps)
 
 
 def flops(B: int, N: int, D: int, h: int) -> dict:

@@ -24,7 +24,7 @@ def log(msg):
 class Gpu:
     """One library handle built from seeded inputs (numpy dict from workloads)."""
 
-    def __init__(self, inp, fill=-1e9, slack=0.0, device="cuda"):
+    def __init__(self, inp, fill=-1e9, slack=0.0, device="cuda", ending=False):
         self.inp = inp
         self.dt = torch_dtype(inp["dtype"])
         self.dev = torch.device(device)
@@ -35,7 +35,8 @@ class Gpu:
         self.P = torch.from_numpy(P).to(self.dev).to(self.dt).contiguous()
         self.M = torch.from_numpy(inp["pair_mask"]).to(self.dev).contiguous()
         code = B.TRI_ATTN_F32 if inp["dtype"] == "f32" else B.TRI_ATTN_BF16
-        self.cfg = B.tri_attn_config(self.D, self.h, code, 1e-5, fill if math.isfinite(fill) else -math.inf, slack)
+        self.cfg = B.tri_attn_config(self.D, self.h, code, 1e-5, fill if math.isfinite(fill) else -math.inf, slack,
+                                     int(ending))
         self.handle = B.tri_attn_create(self.cfg, self.w, torch.cuda.current_stream())
         self.ws_bytes = B.tri_attn_workspace_size(self.handle, self.B, self.N)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.dev)

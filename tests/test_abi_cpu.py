@@ -30,11 +30,33 @@ def test_library_exports_every_declared_symbol():
     assert set(B.declared_functions()) <= exported
 
 
-def test_struct_layouts_match_header():
-    # config: 3 ints + 3 floats; weights: 10 pointers; layout: 9 size_t + int (padded)
-    assert ctypes.sizeof(B.tri_attn_config) == 24
-    assert ctypes.sizeof(B.tri_attn_weights) == 10 * ctypes.sizeof(ctypes.c_void_p)
-    assert ctypes.sizeof(B.tri_attn_workspace_layout) == 10 * 8
+def test_struct_layouts_match_header(tmp_path):
+    """Sizes and field offsets of the binding's structs equal what a C
+    compiler makes of include/tri_attn.h."""
+    import shutil
+
+    structs = (("tri_attn_config", B.tri_attn_config), ("tri_attn_weights", B.tri_attn_weights),
+               ("tri_attn_workspace_layout", B.tri_attn_workspace_layout))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tri_attn.h"', "int main(void) {"]
+    for cname, cls in structs:
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    include = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-I", include, str(src), "-o", str(exe)], check=True, capture_output=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    for cname, cls in structs:
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert int(got[f"{cname}.{fname}"]) == getattr(cls, fname).offset, f"{cname}.{fname}"
 
 
 def test_strerror():
@@ -63,6 +85,8 @@ def _create_rc(**kw):
     (dict(mask_fill=-1.0), B.TRI_ATTN_ERR_INVALID_ARG),              # not a masking value
     (dict(mask_fill=math.nan), B.TRI_ATTN_ERR_INVALID_ARG),
     (dict(shift_slack=-1.0), B.TRI_ATTN_ERR_INVALID_ARG),
+    (dict(ending_node=2), B.TRI_ATTN_ERR_INVALID_ARG),               # 0 or 1 only
+    (dict(ending_node=-1), B.TRI_ATTN_ERR_INVALID_ARG),
     (dict(pair_dim=96, num_heads=3), B.TRI_ATTN_ERR_UNSUPPORTED),     # d = 32 but D = 96
     (dict(pair_dim=128, num_heads=2), B.TRI_ATTN_ERR_UNSUPPORTED),    # d = 64
     (dict(pair_dim=256, num_heads=8), B.TRI_ATTN_ERR_UNSUPPORTED),    # D = 256

@@ -297,6 +297,44 @@ def test_float32_split_products_scale():
         assert rel <= bound, f"{name}: relative error {rel} > {bound}"
 
 
+# ------------------------------------------------------------------ ending-node variant
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,mask", [((2, 40, 64, 4), ("bernoulli", 0.8)), ((1, 130, 128, 4), ("pad", 100)),
+                                        ((1, 150, 128, 8), ("bernoulli", 0.7)), ((2, 33, 64, 2), ("pad", 20))],
+                         ids=["B2N40", "N130pad", "N150h8", "B2N33d32"])
+def test_ending_node(shape, mask, dtype):
+    """Ending-node attention (the other residue axis) against the oracle's
+    ending-node forward, element by element."""
+    B_, N, D, h = shape
+    inp = make_inputs(Workload("ending", B_, N, D, h, dtype, mask, seed=40 + N))
+    log(f"ending node {shape} {dtype} {mask}")
+    g = Gpu(inp, ending=True)
+    try:
+        y = y_numpy(g.forward())
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+    check(y, O.forward_ending(inp), dtype, f"ending {shape} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ending_node_large_sampled_columns(dtype):
+    """N = 300 (persistent loops in every kernel), compared on sampled output
+    columns y[b, :, j]."""
+    w = Workload("ending_large", 1, 300, 128, 4, dtype, ("pad", 270), seed=77)
+    inp = make_inputs(w)
+    log(f"ending node N=300 {dtype}")
+    g = Gpu(inp, ending=True)
+    try:
+        y = y_numpy(g.forward())
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+    cols = [(0, 0), (0, 131), (0, 269), (0, 270), (0, 299)]
+    got = np.stack([y[b, :, j] for b, j in cols])
+    check(got, O.forward_ending_cols(inp, cols), dtype, f"ending N=300 {dtype} sampled columns")
+
+
 # ------------------------------------------------------------------ ABI behaviour on the GPU
 def test_deterministic_and_stream():
     inp = make_inputs(WORKLOADS[3].replace(N=96))

@@ -110,6 +110,51 @@ def brute_force(inp, fill=O.MASK_FILL):
     return y
 
 
+def brute_force_ending(inp, fill=O.MASK_FILL):
+    """Ending-node per-element formula with Python loops (tiny shapes only):
+    position (i, j) attends over k with q[i,j].k[k,j]/sqrt(d) + Wz[t].x[k,i],
+    FILL where mask[k,i] == 0, values v[k,j]."""
+    P = np.asarray(inp["pair_repr"], dtype=np.float64)
+    M = np.asarray(inp["pair_mask"])
+    B, N, _, D = P.shape
+    h = inp["num_heads"]
+    d = D // h
+    W = {k: np.asarray(inp[k], dtype=np.float64) for k in WEIGHTS}
+    x = np.zeros_like(P)
+    for b, i, j in itertools.product(range(B), range(N), range(N)):
+        mu = sum(P[b, i, j, c] for c in range(D)) / D
+        var = sum((P[b, i, j, c] - mu) ** 2 for c in range(D)) / D
+        for c in range(D):
+            x[b, i, j, c] = (P[b, i, j, c] - mu) / math.sqrt(var + O.LN_EPS) * W["ln_weight"][c] + W["ln_bias"][c]
+
+    def dot(wrow, vec):
+        return sum(wrow[e] * vec[e] for e in range(D))
+
+    y = np.zeros_like(P)
+    for b, i, j in itertools.product(range(B), range(N), range(N)):
+        q = [dot(W["w_query"][c], x[b, i, j]) for c in range(D)]
+        g = [1.0 / (1.0 + math.exp(-(dot(W["w_gate"][c], x[b, i, j]) + W["b_gate"][c]))) for c in range(D)]
+        kk = [[dot(W["w_key"][c], x[b, k_, j]) for c in range(D)] for k_ in range(N)]
+        v = [[dot(W["w_value"][c], x[b, k_, j]) for c in range(D)] for k_ in range(N)]
+        o = [0.0] * D
+        for t in range(h):
+            s = []
+            for k_ in range(N):
+                if M[b, k_, i] == 0:
+                    s.append(fill)
+                    continue
+                qk = sum(q[t * d + u] * kk[k_][t * d + u] for u in range(d)) / math.sqrt(d)
+                s.append(qk + dot(W["w_bias_proj"][t], x[b, k_, i]))
+            mx = max(s)
+            e = [math.exp(sv - mx) for sv in s]
+            tot = sum(e)
+            for u in range(d):
+                o[t * d + u] = sum(e[k_] / tot * v[k_][t * d + u] for k_ in range(N))
+        for c in range(D):
+            y[b, i, j, c] = sum(W["w_out"][c][e] * g[e] * o[e] for e in range(D)) + W["b_out"][c]
+    return y
+
+
 # ================================================================== library special cases
 def test_layer_norm_matches_torch():
     inp = small(B=2, N=4, D=16)
@@ -163,6 +208,28 @@ def test_sdpa_textbook_case_no_bias_no_mask():
 
 
 # ================================================================== brute force
+@pytest.mark.parametrize("fill", [O.MASK_FILL, -1e4])
+@pytest.mark.parametrize("shape,mask", [((1, 3, 4, 2), ("bernoulli", 0.6)),
+                                        ((2, 3, 6, 3), ("pad", 2)),
+                                        ((1, 4, 4, 1), ("bernoulli", 0.5))])
+def test_brute_force_tiny_ending_node(shape, mask, fill):
+    B, N, D, h = shape
+    inp = small(B=B, N=N, D=D, h=h, mask=mask, seed=5 + D)
+    np.testing.assert_allclose(O.forward_ending(inp, fill=fill), brute_force_ending(inp, fill=fill), rtol=0,
+                               atol=1e-12)
+
+
+def test_ending_node_columns_and_difference():
+    """forward_ending_cols gives columns of forward_ending; on a generic input
+    the ending-node output differs from the starting-node one."""
+    inp = small(B=2, N=5, D=8, h=2, mask=("bernoulli", 0.7), seed=21)
+    y = O.forward_ending(inp)
+    cols = [(0, 1), (1, 4)]
+    np.testing.assert_allclose(O.forward_ending_cols(inp, cols), np.stack([y[b, :, j] for b, j in cols]),
+                               rtol=0, atol=1e-13)
+    assert np.abs(y - O.forward(inp)).max() > 1e-3
+
+
 @pytest.mark.parametrize("fill", [O.MASK_FILL, -1e4])
 @pytest.mark.parametrize("shape,mask", [((1, 3, 4, 2), ("bernoulli", 0.6)),
                                         ((2, 3, 6, 3), ("pad", 2)),

@@ -38,6 +38,7 @@ class tri_attn_config(ctypes.Structure):
         ("ln_eps", ctypes.c_float),
         ("mask_fill", ctypes.c_float),
         ("shift_slack", ctypes.c_float),
+        ("ending_node", ctypes.c_int),
     ]
 
 

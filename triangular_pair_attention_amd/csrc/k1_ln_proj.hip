@@ -140,9 +140,12 @@ __global__ __launch_bounds__((K1Shape<D>::THREADS)) void k1_ln_proj(K1Args a) {
   auto load_tile = [&](int tile, uint4 (&pre)[NV], uint32_t &mpre) {
     const int bi_row = tile / nch, chunk = tile - bi_row * nch;
     const int j = chunk * TILE + lpos;
-    mpre = (j < N && lpart == 0) ? a.mask[(size_t)bi_row * N + j] : 0u;
+    // element (b, i, j) of pair_repr and the mask; ending-node reads (b, j, i)
+    const int bb = bi_row / N;
+    const size_t at = a.transposed ? ((size_t)bb * N + j) * N + (bi_row - bb * N) : (size_t)bi_row * N + j;
+    mpre = (j < N && lpart == 0) ? a.mask[at] : 0u;
     if (j < N) {
-      const char *src = reinterpret_cast<const char *>(a.P) + ((size_t)bi_row * N + j) * D * ES + lpart * EPT * ES;
+      const char *src = reinterpret_cast<const char *>(a.P) + at * D * ES + lpart * EPT * ES;
 #pragma unroll
       for (int v = 0; v < NV; ++v) pre[v] = ldg<uint4>(src + 16 * v);
     } else {

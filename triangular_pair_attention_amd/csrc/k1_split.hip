@@ -137,9 +137,12 @@ __global__ __launch_bounds__(512) void k1_ln_proj_split(K1Args a) {
   auto load_tile = [&](int tile, float4 (&pre)[NV], uint32_t &mpre) {
     const int bi_row = tile / nch, chunk = tile - bi_row * nch;
     const int j = chunk * TILE + lpos;
-    mpre = (j < N && lpart == 0) ? a.mask[(size_t)bi_row * N + j] : 0u;
+    // element (b, i, j) of pair_repr and the mask; ending-node reads (b, j, i)
+    const int bb = bi_row / N;
+    const size_t at = a.transposed ? ((size_t)bb * N + j) * N + (bi_row - bb * N) : (size_t)bi_row * N + j;
+    mpre = (j < N && lpart == 0) ? a.mask[at] : 0u;
     if (j < N) {
-      const float *src = reinterpret_cast<const float *>(a.P) + ((size_t)bi_row * N + j) * D + lpart * EPT;
+      const float *src = reinterpret_cast<const float *>(a.P) + at * D + lpart * EPT;
 #pragma unroll
       for (int v = 0; v < NV; ++v) pre[v] = ldg<float4>(src + 4 * v);
     } else {

@@ -78,6 +78,12 @@ __global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
     for (int v = 0; v < NV; ++v) pre[v] = (j < N) ? ldg<uint4>(src + v * (16 / ES)) : make_uint4(0, 0, 0, 0);
   };
 
+  // output element (b, i, j); ending-node writes (b, j, i)
+  auto out_at = [&](int bi_row, int j) -> size_t {
+    const int bb = bi_row / N;
+    return a.transposed ? ((size_t)bb * N + j) * N + (bi_row - bb * N) : (size_t)bi_row * N + j;
+  };
+
   int tile = blockIdx.x;
   if (tile >= a.tiles) return;
   uint4 pre[NV];
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
         // stores of block pb overlap the products of block pb + 1
         const int j = j0 + pb * 16 + r16;
         if (j < N)
-          stg<float4>(reinterpret_cast<float *>(a.out) + ((size_t)bi_row * N + j) * D + wave * 16 + 4 * g,
+          stg<float4>(reinterpret_cast<float *>(a.out) + out_at(bi_row, j) * D + wave * 16 + 4 * g,
                       make_float4(acc[0], acc[1], acc[2], acc[3]));
       }
     }
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(D / 16 * 64) void k3_out_proj(K3Args a) {
         const int pos = c / ROWV, off = c - pos * ROWV;
         if (j0 + pos < N) {
           const uint4 v = *reinterpret_cast<const uint4 *>(&ys[pos * PITCH + off * (16 / ES)]);
-          stg<uint4>(reinterpret_cast<T *>(a.out) + ((size_t)bi_row * N + j0 + pos) * D + off * (16 / ES), v);
+          stg<uint4>(reinterpret_cast<T *>(a.out) + out_at(bi_row, j0 + pos) * D + off * (16 / ES), v);
         }
       }
     }

@@ -73,6 +73,7 @@ static int check_config(const tri_attn_config *cfg) {
   const float f = cfg->mask_fill;
   if (std::isnan(f) || !(f == -INFINITY || (std::isfinite(f) && f <= -1e4f))) return TRI_ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(cfg->shift_slack) || cfg->shift_slack < 0.f) return TRI_ATTN_ERR_INVALID_ARG;
+  if (cfg->ending_node != 0 && cfg->ending_node != 1) return TRI_ATTN_ERR_INVALID_ARG;
   if (!supported(cfg->pair_dim, cfg->pair_dim / cfg->num_heads)) return TRI_ATTN_ERR_UNSUPPORTED;
   return TRI_ATTN_OK;
 }
@@ -235,6 +236,7 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a1.eps = t->cfg.ln_eps;
   a1.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->dh));
   a1.B = B, a1.N = N, a1.Np = L.Np, a1.nchunk = L.nchunk;
+  a1.transposed = t->cfg.ending_node;
   a1.tiles = B * N * L.nchunk;
   if (stages & 1) {
     hipError_t e1;
@@ -276,6 +278,7 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a3.bo = vp + (size_t)3 * D * e;
   a3.out = out;
   a3.B = B, a3.N = N, a3.Np = L.Np, a3.nchunk = L.nchunk;
+  a3.transposed = t->cfg.ending_node;
   a3.tiles = a1.tiles;
   const int grid3 = a3.tiles < t->k3_grid ? a3.tiles : t->k3_grid;
   if ((stages & 4) && launch_k3(t->cfg.dtype, D, a3, grid3, s) != hipSuccess) return TRI_ATTN_ERR_HIP;

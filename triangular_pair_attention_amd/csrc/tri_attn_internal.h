@@ -33,6 +33,7 @@ struct K1Args {
   float eps;
   float qscale;  // log2(e) / sqrt(d)
   int B, N, Np, nchunk, tiles;
+  int transposed;  // ending-node: position (b, i, j) reads pair_repr[b][j][i] and mask[b][j][i]
 };
 
 // Kernel 2: attention core + gate, per head; writes g * o over the gate.
@@ -53,6 +54,7 @@ struct K3Args {
   const void *bo;
   void *out;       // [B][N][N][D]
   int B, N, Np, nchunk, tiles;
+  int transposed;  // ending-node: position (b, i, j) is written to out[b][j][i]
 };
 
 // Launchers: return the launch status. `dtype` is TRI_ATTN_F32 / TRI_ATTN_BF16.
