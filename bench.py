@@ -185,7 +185,7 @@ def cpu_baseline(inp, w, seconds, ending_node=False):
         if el >= seconds:
             break
     pos = done * w.N * w.N
-    return {
+    result = {
         "value": pos / el,
         "unit": "pair-positions/s",
         "cores": int(cores),
@@ -194,6 +194,29 @@ def cpu_baseline(inp, w, seconds, ending_node=False):
                   f"({pos} pair positions, "
                   f"{el:.1f} s, float64 numpy, BLAS threads = {cores})",
     }
+    # the same oracle on one thread, for a few seconds (all rows where a pass
+    # is short, else the first 32 rows with their batch's full pair bias)
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return result
+    sub = rows if w.N <= 256 else rows[:32]
+    done1 = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            forward_rows(inp, sub)
+            done1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= max(1.0, seconds / 3):
+                break
+    pos1 = done1 * len(sub) * w.N
+    result["single_thread"] = {
+        "value": pos1 / el1, "unit": "pair-positions/s", "cores": 1,
+        "sample": f"{done1} x {len(sub)} {'columns' if ending_node else 'rows'} of batch 0 ({pos1} pair positions, "
+                  f"{el1:.1f} s)",
+    }
+    return result
 
 
 def copy_probe(mib: int = 256, reps: int = 5):
