@@ -15,7 +15,7 @@ import pytest
 
 from triangular_pair_attention_amd import build as B
 
-KERNELS = tuple(f for f in B.SOURCES if f.endswith(".hip"))
+KERNELS = tuple(u for u in B.units() if u[0].endswith(".hip"))
 
 
 def _hipcc():
@@ -25,16 +25,17 @@ def _hipcc():
         return None
 
 
-@pytest.fixture(scope="module", params=KERNELS)
+@pytest.fixture(scope="module", params=KERNELS, ids=lambda u: u[1])
 def asm(request, tmp_path_factory):
     cc = _hipcc()
     if cc is None:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / (request.param + ".s")
+    src, name, extra = request.param
+    out = tmp_path_factory.mktemp("asm") / (name + ".s")
     flags = [f for f in B.FLAGS if f != "-fPIC"]
-    cmd = [cc, *flags, "--cuda-device-only", "-S", os.path.join(B.CSRC, request.param), "-o", str(out)]
+    cmd = [cc, *flags, *extra, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True, timeout=300)
-    return request.param, out.read_text().splitlines()
+    return name, out.read_text().splitlines()
 
 
 def _instructions(lines):

@@ -817,6 +817,32 @@ static hipError_t launch_k2_t(const K2Args &a, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// bf16 with head size 16 is compiled in a unit of its own (this source with
+// TPA_K2_BF16_D16 defined), built with LLVM's max-memory-clause instruction
+// scheduler: its key loop measured 3% faster that way, the other shapes
+// slower. Each kernel instantiation lives in exactly one unit.
+hipError_t launch_k2_bf16_d16(int D, const K2Args &a, int grid, hipStream_t s);
+int k2_blocks_per_cu_bf16_d16(int D);
+
+#ifdef TPA_K2_BF16_D16
+hipError_t launch_k2_bf16_d16(int D, const K2Args &a, int grid, hipStream_t s) {
+  if (D == 128) return launch_k2_t<bf16_t, 128, 16>(a, grid, s);
+  if (D == 64) return launch_k2_t<bf16_t, 64, 16>(a, grid, s);
+  return hipErrorInvalidValue;
+}
+
+int k2_blocks_per_cu_bf16_d16(int D) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  if (D == 128)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k2_attention<bf16_t, 128, 16>,
+                                                     K2Shape<bf16_t, 128, 16>::NW * 64, 0);
+  else if (D == 64)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k2_attention<bf16_t, 64, 16>,
+                                                     K2Shape<bf16_t, 64, 16>::NW * 64, 0);
+  return (e == hipSuccess && n > 0) ? n : 1;
+}
+#else
 int k2_items(int dtype, int D, int dh, int B, int N) {
   int RB = 8, QB = 64;
 #define TRI_K2_SHAPE(TT, DD, HH)  \
@@ -843,9 +869,8 @@ hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, int grid, hipStr
 #define TRI_K2_CASE(TT, DD, HH) \
   if (D == DD && dh == HH) return launch_k2_t<TT, DD, HH>(a, grid, s);
   if (dtype == TRI_ATTN_BF16) {
-    TRI_K2_CASE(bf16_t, 128, 16)
+    if (dh == 16) return launch_k2_bf16_d16(D, a, grid, s);
     TRI_K2_CASE(bf16_t, 128, 32)
-    TRI_K2_CASE(bf16_t, 64, 16)
     TRI_K2_CASE(bf16_t, 64, 32)
   } else {
     TRI_K2_CASE(float, 128, 16)
@@ -857,11 +882,8 @@ hipError_t launch_k2(int dtype, int D, int dh, const K2Args &a, int grid, hipStr
   return hipErrorInvalidValue;
 }
 
-}  // namespace tpa
-
-namespace tpa {
-
 int k2_blocks_per_cu(int dtype, int D, int dh) {
+  if (dtype == TRI_ATTN_BF16 && dh == 16) return k2_blocks_per_cu_bf16_d16(D);
   int n = 0;
 #define TRI_K2_OCC(TT, DD, HH)                                                                                   \
   if (D == DD && dh == HH &&                                                                                     \
@@ -869,9 +891,7 @@ int k2_blocks_per_cu(int dtype, int D, int dh) {
           hipSuccess)                                                                                            \
     n = 1;
   if (dtype == TRI_ATTN_BF16) {
-    TRI_K2_OCC(bf16_t, 128, 16)
     TRI_K2_OCC(bf16_t, 128, 32)
-    TRI_K2_OCC(bf16_t, 64, 16)
     TRI_K2_OCC(bf16_t, 64, 32)
   } else {
     TRI_K2_OCC(float, 128, 16)
@@ -882,5 +902,6 @@ int k2_blocks_per_cu(int dtype, int D, int dh) {
 #undef TRI_K2_OCC
   return n > 0 ? n : 1;
 }
+#endif
 
 }  // namespace tpa
