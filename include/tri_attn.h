@@ -133,6 +133,11 @@ const char *tri_attn_strerror(int code);
  *             of row (b, i) is at [b][i][c/16][j][c%16]. q is pre-scaled by
  *             log2(e)/sqrt(d); g is after the sigmoid (the attention stage
  *             overwrites it with g * o). Columns j >= N hold q = k = 0.
+ *             Exception: float32 handles with d = 32 store k as its three
+ *             bf16 parts, k = k1 + k2 + k3 exactly (round to nearest even
+ *             at each step), [B][N][h][3][Np/16][4][16][8] bf16: channel
+ *             8G + e of head t, key column 16s + r, part p is at
+ *             [b][i][t][p][s][G][r][e].
  *   vt      : [B][N][h][d][Np] config dtype (value, transposed per head),
  *             zero for j >= N.
  *   zm      : [B][h][N][Np] float32: z[b,t,j,k] * log2(e) where M[b,j,k] != 0

@@ -54,6 +54,20 @@ class Gpu:
         torch.cuda.synchronize()
         return B.tri_attn_get_workspace_layout(self.handle, self.B, self.N)
 
+    def k_region(self, lay):
+        """k from the workspace as float64 [B, N, N(key), D]: float32 handles
+        with d = 32 hold it as three bf16 parts [b][i][t][p][s][G][r][e]
+        (channel 8G + e of head t, key 16s + r), summed here exactly."""
+        Bn, N, D, h, Np = self.B, self.N, self.D, self.h, lay.padded_n
+        if self.inp["dtype"] == "f32" and D // h == 32:
+            raw = self.region(lay.k, Bn * N * D * Np * 3, torch.int16).cpu().numpy().astype(np.uint16)
+            parts = (raw.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            parts = parts.reshape(Bn, N, h, 3, Np // 16, 4, 16, 8).sum(3)  # b i t s G r e
+            k = parts.transpose(0, 1, 3, 5, 2, 4, 6).reshape(Bn, N, Np, D)  # b i (s r) (t G e)
+            return k[:, :, :N]
+        k = self.region(lay.k, Bn * N * D * Np, self.dt).float().cpu().numpy().astype(np.float64)
+        return k.reshape(Bn, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4).reshape(Bn, N, N, D)
+
     def region(self, off, count, dtype):
         elem = torch.tensor([], dtype=dtype).element_size()
         return self.ws[off:off + count * elem].view(dtype)

@@ -221,7 +221,7 @@ def test_projection_stage(dtype, shape):
         dt = g.dt
         f = lambda off, n, t=dt: g.region(off, n, t).float().cpu().numpy().astype(np.float64)  # noqa: E731
         q = f(lay.q, B_ * N * D * Np).reshape(B_, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4)
-        k = f(lay.k, B_ * N * D * Np).reshape(B_, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4)
+        k = g.k_region(lay)
         gg = f(lay.g, B_ * N * D * Np).reshape(B_, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4)
         vt = f(lay.vt, B_ * N * D * Np).reshape(B_, N, h, d, Np)[..., :N]
         zm = f(lay.zm, B_ * h * N * Np, torch.float32).reshape(B_, h, N, Np)
@@ -281,7 +281,7 @@ def test_float32_split_products_scale():
         lay = g.project()
         Np = lay.padded_n
         f = lambda off, n: g.region(off, n, torch.float32).cpu().numpy().astype(np.float64)  # noqa: E731
-        k = f(lay.k, B_ * N * D * Np).reshape(B_, N, D // 16, Np, 16)[:, :, :, :N].transpose(0, 1, 3, 2, 4)
+        k = g.k_region(lay)
         vt = f(lay.vt, B_ * N * D * Np).reshape(B_, N, h, D // h, Np)[..., :N]
         y = y_numpy(g.forward())
         torch.cuda.synchronize()

@@ -31,7 +31,9 @@
 //     three small terms, then the three large), so consecutive MFMAs are
 //     independent; the four 16-position blocks run as a software pipeline.
 //  3. Epilogues as in the bf16 kernel: q pre-scaled by log2(e)/sqrt(d), k,
-//     gate = sigmoid(+bias) as [b][i][c/16][j][16]; v transposed per head
+//     gate = sigmoid(+bias) as [b][i][c/16][j][16] (with d = 32, k instead
+//     as its three bf16 parts in kernel 2's fragment order, so that kernel 2
+//     does not split every key it loads); v transposed per head
 //     [b][i][t][u][j]; the pair bias z*log2(e) with the mask folded in as
 //     [b][t][i][j]; per-64-key-chunk maxima of the bias and of |k|^2 per
 //     16-channel block, and per-chunk sums of v.
@@ -55,6 +57,7 @@ struct K1SplitShape {
 template <int D, int DH>
 __global__ __launch_bounds__(512) void k1_ln_proj_split(K1Args a) {
   constexpr int H = D / DH;
+  constexpr bool KSPLIT = DH == 32;  // k is stored pre-split for kernel 2's split score products
   constexpr int NB = K1SplitShape<D>::NB;
   constexpr int TPW = K1SplitShape<D>::TPW;
   constexpr int NT = K1SplitShape<D>::THREADS;
@@ -213,6 +216,7 @@ __global__ __launch_bounds__(512) void k1_ln_proj_split(K1Args a) {
     }
     float *const qbase = reinterpret_cast<float *>(a.q) + ((size_t)bi_row * NB + cb) * Np * 16;
     float *const kbase = reinterpret_cast<float *>(a.k) + ((size_t)bi_row * NB + cb) * Np * 16;
+    char *const ksp = reinterpret_cast<char *>(a.k) + ((size_t)bi_row * H + (cb >> 1)) * 3 * Np * 64;
     float *const gbase = reinterpret_cast<float *>(a.g) + ((size_t)bi_row * NB + cb) * Np * 16;
     float *const vbase = reinterpret_cast<float *>(a.vt) + (size_t)bi_row * D * Np;
 
@@ -264,7 +268,21 @@ __global__ __launch_bounds__(512) void k1_ln_proj_split(K1Args a) {
         } else if (type == 0) {
           store4(qbase, toff, c[0] * a.qscale, c[1] * a.qscale, c[2] * a.qscale, c[3] * a.qscale);
         } else if (type == 1) {
-          store4(kbase, toff, c[0], c[1], c[2], c[3]);
+          if constexpr (KSPLIT) {
+            // k as three bf16 parts, 1 KB per (row, head, part, 16 keys):
+            // lane (G, r) of that block holds channels 8G..8G+7 of key r of
+            // the head; this lane's four channels are half of one such slot,
+            // and the wave's 64 lanes fill 512 contiguous bytes
+            uint32_t p1[2], p2[2], p3[2];
+            split3(c[0], c[1], p1[0], p2[0], p3[0]);
+            split3(c[2], c[3], p1[1], p2[1], p3[1]);
+            char *dst = ksp + (size_t)(jcol >> 4) * 1024 + ((2 * (cb & 1) + (g >> 1)) * 16 + r16) * 16 + (g & 1) * 8;
+            stg<uint2>(dst, make_uint2(p1[0], p1[1]));
+            stg<uint2>(dst + (size_t)Np * 64, make_uint2(p2[0], p2[1]));
+            stg<uint2>(dst + (size_t)Np * 128, make_uint2(p3[0], p3[1]));
+          } else {
+            store4(kbase, toff, c[0], c[1], c[2], c[3]);
+          }
           kn_run = fmaxf(kn_run, group4_sum(c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3]));
         } else {
           // sigmoid of (Wg x + bg): the bias is already in the accumulator

@@ -73,7 +73,8 @@ struct K2Shape {
   static constexpr int NW = WR * WQ;
   static constexpr int RB = WR * IG;       // rows per workgroup
   static constexpr int QB = WQ * JW * 16;  // query columns per workgroup
-  static constexpr int KBR = (DH == 16) ? 1 : 2;  // k blocks per row and key step
+  // k blocks per row and key step (float32, d = 32: the three bf16 parts)
+  static constexpr int KBR = (DH == 16) ? 1 : (BF ? 2 : 3);
   static constexpr int VBR = DH / 16;             // v blocks per row and key step
   static constexpr int ZBJ = BF ? 2 : 1;          // zm blocks per 16 queries and key step
   static constexpr int NBLK = RB * (KBR + VBR) + (QB / 16) * ZBJ;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   // operands (float32 accuracy; kernel 1's split products): each lane
   // already holds channels 8g..8g+7 of one query and of one key, the bf16
   // 16x16x32 fragment layout. The queries are split once per item (below,
-  // in setup), the keys per step.
+  // in setup); kernel 1 stores the keys already split.
   constexpr bool SPLITQK = !BF && DH == 32;
   bf16x8 qsp[IG][JW][SPLITQK ? 3 : 1];
   auto load_q = [&]() {
@@ -247,9 +248,9 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         } else {
           if (DH == 16)
             p = reinterpret_cast<const char *>(K + ((rowbase + t) * Np + r16) * 16 + 4 * g);
-          else
-            p = reinterpret_cast<const char *>(K + ((rowbase + 2 * t + (g >> 1)) * Np + r16) * 16 + 8 * (g & 1) +
-                                               4 * kp);
+          else  // part kp of k, as kernel 1 stores it: 1 KB per 16 keys in fragment order
+            p = reinterpret_cast<const char *>(K) + ((((size_t)(b * N + row) * H + t) * 3 + kp) * (Np / 16)) * 1024 +
+                lane * 16;
         }
         step = KT * 16 * ES;
       } else if (blk < RB * (KBR + VBR)) {
@@ -579,24 +580,22 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
       for (int i = 0; i < IG; ++i) {
         const int r = wr * IG + i;
-        float kf[QS];
+        float kf[SPLITQK ? 1 : QS];
+        bf16x8 ks[SPLITQK ? 3 : 1];
+        if constexpr (SPLITQK) {
+          // the key's three bf16 parts, split by kernel 1
 #pragma unroll
-        for (int kp = 0; kp < KBR; ++kp) {
-          const float4 v = __builtin_bit_cast(float4, kblk[(r * KBR + kp) * 64 + lane]);
-          kf[4 * kp] = v.x, kf[4 * kp + 1] = v.y, kf[4 * kp + 2] = v.z, kf[4 * kp + 3] = v.w;
+          for (int kp = 0; kp < 3; ++kp) ks[kp] = as_bf16x8(kblk[(r * KBR + kp) * 64 + lane]);
+        } else {
+#pragma unroll
+          for (int kp = 0; kp < KBR; ++kp) {
+            const float4 v = __builtin_bit_cast(float4, kblk[(r * KBR + kp) * 64 + lane]);
+            kf[4 * kp] = v.x, kf[4 * kp + 1] = v.y, kf[4 * kp + 2] = v.z, kf[4 * kp + 3] = v.w;
+          }
         }
         f32x4 vf[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) vf[mb] = __builtin_bit_cast(f32x4, vblk[(r * VBR + mb) * 64 + lane]);
-        bf16x8 ks[SPLITQK ? 3 : 1];
-        if constexpr (SPLITQK) {
-          uint32_t p1[4], p2[4], p3[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) split3(kf[2 * u], kf[2 * u + 1], p1[u], p2[u], p3[u]);
-          ks[0] = as_bf16x8(make_uint4(p1[0], p1[1], p1[2], p1[3]));
-          ks[1] = as_bf16x8(make_uint4(p2[0], p2[1], p2[2], p2[3]));
-          ks[2] = as_bf16x8(make_uint4(p3[0], p3[1], p3[2], p3[3]));
-        }
 #pragma unroll
         for (int jb = 0; jb < JW; ++jb) {
           f32x4 s = zA[jb];

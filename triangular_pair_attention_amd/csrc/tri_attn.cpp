@@ -35,7 +35,8 @@ Layout make_layout(int B, int N, int D, int h, int elem) {
   const size_t proj = (size_t)B * N * D * L.Np * elem;  // [B][N][D/16][Np][16] (and v^T)
   size_t off = 0;
   L.q = off, off = align256(off + proj);
-  L.k = off, off = align256(off + proj);
+  // float32 with d = 32: k as three bf16 parts (6 bytes per element)
+  L.k = off, off = align256(off + ((elem == 4 && D / h == 32) ? proj / 4 * 6 : proj));
   L.vt = off, off = align256(off + proj);
   L.g = off, off = align256(off + proj);
   L.zm = off, off = align256(off + (size_t)B * h * N * L.Np * 4);
