@@ -68,6 +68,43 @@ def test_workload5_sampled_rows():
     check(y, ref, w.dtype, w.name + " sampled")
 
 
+def gpu_y32(inp):
+    g = Gpu(inp)
+    try:
+        y = g.forward().float().cpu().numpy()
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+    return y
+
+
+@pytest.mark.parametrize("k", [5, 4, 2])
+def test_full_size_permutation_equivariance(k):
+    """Every output at full size, through a property of the method: one
+    permutation pi of all residue axes with a permutation sigma of the batch,
+    P'[b,i,j] = P[sigma(b),pi(i),pi(j)] and M'[b,j,k] = M[sigma(b),pi(j),pi(k)],
+    gives y'[b,i,j] = y[sigma(b),pi(i),pi(j)] (exact for the oracle; its own
+    tests check that). Both GPU results lie within the tolerance of the
+    oracle's, so they may differ by at most twice the tolerance. The permuted
+    mask scatters the padding, so the permuted run skips no key chunk while
+    the plain one does."""
+    w = WORKLOADS[k]
+    log(f"workload {w.name}: permutation equivariance at full size")
+    inp = make_inputs(w)
+    rng = np.random.default_rng(7)
+    pi, sg = rng.permutation(w.N), rng.permutation(w.B)
+    perm = dict(inp)
+    for name in ("pair_repr", "pair_mask"):
+        perm[name] = np.ascontiguousarray(inp[name][sg][:, pi][:, :, pi])
+    y = gpu_y32(inp)
+    y2 = gpu_y32(perm)
+    want = y[sg][:, pi][:, :, pi]
+    assert (np.isfinite(y2) == np.isfinite(want)).all()
+    diff = float(np.abs(y2 - want).max())
+    log(f"  max |y' - permuted y| {diff:.3e}, max |y| {np.abs(y).max():.3f}")
+    assert diff <= 2 * TOL[w.dtype]
+
+
 @pytest.mark.parametrize("dtype,h", [("bf16", 8), ("bf16", 4), ("f32", 4)])
 def test_large_n_sampled_rows(dtype, h):
     """N = 1040 (17 key chunks, the last one ragged): larger than any
@@ -79,6 +116,29 @@ def test_large_n_sampled_rows(dtype, h):
     rows = [(0, i) for i in (0, 517, 999, 1000, 1039)]
     y, ref = run_case(inp, rows=rows)
     check(y, ref, dtype, f"large N {dtype} h={h}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_workspace_past_4gib_sampled_rows(dtype):
+    """N = 2048, d = 32: the workspace exceeds 4 GiB (bf16 about 4.1 GB,
+    float32 9.7 GB with the split keys), so region offsets past 2^32 bytes
+    are exercised in every kernel; compared on sampled rows, including the
+    last valid row, the first padded one and the last one."""
+    w = Workload("ws4g", 1, 2048, 128, 4, dtype, ("pad", 2000), seed=23)
+    log(f"workspace past 4 GiB {dtype}: sampled rows")
+    inp = make_inputs(w)
+    rows = [(0, i) for i in (0, 1023, 1999, 2000, 2047)]
+    g = Gpu(inp)
+    try:
+        log(f"  workspace {g.ws_bytes / 2**30:.2f} GiB")
+        assert g.ws_bytes > 2**32
+        y = g.forward()
+        ys = torch.stack([y[b, i] for b, i in rows]).float().cpu().numpy().astype(np.float64)
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+    ref = O.forward_rows(inp, rows)
+    check(ys, ref, dtype, f"workspace past 4 GiB {dtype}")
 
 
 # ------------------------------------------------------------------ small and ragged shapes
