@@ -177,7 +177,7 @@ def _random_case(n):
     return Workload(f"random{n}", B_, N, D, h, dtype, mask, seed=6000 + n)
 
 
-@pytest.mark.parametrize("n", range(16))
+@pytest.mark.parametrize("n", range(48))
 def test_random_shapes(n):
     w = _random_case(n)
     log(f"random case {n}: B={w.B} N={w.N} D={w.D} h={w.h} {w.dtype} {w.mask}")
