@@ -117,6 +117,27 @@ int tri_attn_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
 int tri_attn_forward(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
                      void *workspace, size_t ws_bytes, void *stream);
 
+/* Training-mode forward (arguments as tri_attn_forward, same workspace):
+ * dropout on the attention weights after the softmax over keys and before
+ * their product with v (FW-GLM-5-1 / l2_p6 transcript, the restated forward;
+ * Kimi-K2.6 / l2_p6, the module's dropout layer). Key k of query column j,
+ * head t, row (b, i) is kept iff word (k mod 4) of Philox4x32-10 (Salmon,
+ * Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+ * SC 2011) at counter (k / 4, j, (b*N + i)*h + t, offset) and key
+ * (seed & 0xFFFFFFFF, seed >> 32) is >= thr = min(round(dropout_rate * 2^32),
+ * 2^32 - 1); kept weights are scaled by 2^32 / (2^32 - thr). The softmax is
+ * normalised over the undropped weights.
+ *   lse : DEVICE pointer, [B][N][h][N] float32, written with
+ *         ln sum_k exp(s[b,i,t,j,k]) over the masked scores (fill included:
+ *         a fully masked column has fill + ln N); may be NULL.
+ * dropout_rate in [0, 1), else TRI_ATTN_ERR_INVALID_ARG; rate 0 gives the
+ * inference output. Ending-node handles: TRI_ATTN_ERR_UNSUPPORTED. The
+ * attention step is a plain kernel (one lane per query column), several
+ * times slower than the inference one. */
+int tri_attn_forward_train(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, void *out, float *lse,
+                           int B, int N, double dropout_rate, uint64_t seed, uint32_t offset, void *workspace,
+                           size_t ws_bytes, void *stream);
+
 /* Free everything the handle owns (synchronises the device). NULL is a no-op. */
 int tri_attn_destroy(tri_attn_t h);
 

@@ -17,7 +17,7 @@ def test_header_declares_the_abi():
     names = B.declared_functions()
     for n in ("tri_attn_create", "tri_attn_workspace_size", "tri_attn_forward", "tri_attn_destroy",
               "tri_attn_strerror", "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend",
-              "tri_attn_output"):
+              "tri_attn_output", "tri_attn_forward_train"):
         assert n in names
 
 
@@ -116,6 +116,8 @@ def test_null_handle_paths():
     assert B.raw_call("tri_attn_project", None, 1, 1, 1, 8, 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
     assert B.raw_call("tri_attn_attend", None, 1, 8, 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
     assert B.raw_call("tri_attn_output", None, 1, 1, 8, 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
+    assert B.raw_call("tri_attn_forward_train", None, 1, 1, 1, None, 1, 8, ctypes.c_double(0.1), ctypes.c_uint64(1),
+                      ctypes.c_uint32(0), 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
     lay = B.tri_attn_workspace_layout()
     assert B.raw_call("tri_attn_get_workspace_layout", None, 1, 8, ctypes.byref(lay)) == B.TRI_ATTN_ERR_INVALID_ARG
     assert B.raw_call("tri_attn_destroy", None) == B.TRI_ATTN_OK

@@ -1,0 +1,108 @@
+"""GPU parity of the training-mode forward (tri_attn_forward_train) with the
+training oracle: the same dropout decisions (integers, compared through the
+outputs they select), y within the inference tolerances, and the saved
+log-sum-exp."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, Gpu, log, max_err, y_numpy
+from oracle import tri_attn_oracle as O
+from oracle import tri_attn_train_oracle as TO
+from triangular_pair_attention_amd import binding as B
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"f32": 1e-4, "bf16": 5e-2}  # on columns with a valid key (|lse| of order 10)
+
+
+def run_train(inp, rate, seed, offset, fill=O.MASK_FILL):
+    g = Gpu(inp, fill=fill)
+    try:
+        h = g.h
+        lse = torch.empty((g.B, g.N, h, g.N), dtype=torch.float32, device=g.dev)
+        out = torch.empty_like(g.P)
+        B.tri_attn_forward_train(g.handle, g.P, g.M, out, lse, g.B, g.N, rate, seed, offset, g.ws, g.ws_bytes,
+                                 torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return y_numpy(out), lse.double().cpu().numpy(), y_numpy(g.forward())
+    finally:
+        g.close()
+
+
+def check_train(inp, rate, seed, offset, what, fill=O.MASK_FILL):
+    dtype = inp["dtype"]
+    y, lse, y_inf = run_train(inp, rate, seed, offset, fill)
+    ref, ref_lse = TO.forward_train(inp, rate, seed, offset, fill=fill)
+    fin = np.isfinite(ref)
+    assert (np.isfinite(y) == fin).all(), f"{what}: NaN pattern of y differs"
+    err, idx = max_err(np.where(fin, y, 0), np.where(fin, ref, 0))
+    log(f"{what}: y max abs err {err:.3e} at {idx}")
+    assert err <= TOL[dtype], f"{what}: y error {err}"
+    live = np.asarray(inp["pair_mask"]).any(-1)  # (b, j): the column has a valid key
+    live = np.broadcast_to(live[:, None, None, :], ref_lse.shape)
+    lerr = float(np.abs(lse - ref_lse)[live].max()) if live.any() else 0.0
+    log(f"{what}: lse max abs err {lerr:.3e} on columns with a valid key")
+    assert lerr <= LSE_TOL[dtype]
+    dead = ~live
+    if dead.any():
+        if math.isfinite(fill):
+            np.testing.assert_allclose(lse[dead], ref_lse[dead], rtol=1e-6)
+        else:
+            assert np.isnan(lse[dead]).all()
+    return y, y_inf
+
+
+SHAPES = [((2, 40, 64, 4), ("bernoulli", 0.8)), ((1, 70, 128, 4), ("pad", 50)),
+          ((1, 66, 128, 8), ("pad", 60)), ((2, 37, 128, 4), ("bernoulli", 0.6)), ((1, 5, 64, 2), ("pad", 3))]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,mask", SHAPES, ids=lambda s: str(s))
+@pytest.mark.parametrize("rate", [0.0, 0.3])
+def test_train_small(shape, mask, dtype, rate):
+    Bn, N, D, h = shape
+    inp = make_inputs(Workload("train", Bn, N, D, h, dtype, mask, seed=71))
+    y, y_inf = check_train(inp, rate, seed=2**33 + 5, offset=7, what=f"train {dtype} {shape} {mask} rate {rate}")
+    if rate == 0.0:
+        # no weight dropped: the inference forward's output, within both tolerances
+        assert np.abs(y - y_inf)[np.isfinite(y)].max() <= 2 * TOL[dtype]
+
+
+@pytest.mark.parametrize("k", [2, 3])
+def test_train_workload(k):
+    w = WORKLOADS[k]
+    log(f"train {w.name}")
+    check_train(make_inputs(w), 0.15, seed=12345, offset=0, what=f"train {w.name}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_train_minus_inf_fill(dtype):
+    inp = make_inputs(Workload("train", 1, 20, 64, 4, dtype, ("pad", 14), seed=72))
+    check_train(inp, 0.25, seed=3, offset=1, what=f"train -inf fill {dtype}", fill=-math.inf)
+
+
+def test_train_argument_errors():
+    inp = make_inputs(Workload("train", 1, 8, 64, 4, "f32", ("ones",), seed=73))
+    g = Gpu(inp)
+    try:
+        out = torch.empty_like(g.P)
+        for bad in (1.0, -0.1, float("nan")):
+            rc = B.raw_call("tri_attn_forward_train", g.handle, g.P.data_ptr(), g.M.data_ptr(), out.data_ptr(), None,
+                            g.B, g.N, B.ctypes.c_double(bad), B.ctypes.c_uint64(1), B.ctypes.c_uint32(0),
+                            g.ws.data_ptr(), g.ws_bytes, None)
+            assert rc == B.TRI_ATTN_ERR_INVALID_ARG
+    finally:
+        g.close()
+    e = Gpu(inp, ending=True)
+    try:
+        out = torch.empty_like(e.P)
+        rc = B.raw_call("tri_attn_forward_train", e.handle, e.P.data_ptr(), e.M.data_ptr(), out.data_ptr(), None,
+                        e.B, e.N, B.ctypes.c_double(0.1), B.ctypes.c_uint64(1), B.ctypes.c_uint32(0),
+                        e.ws.data_ptr(), e.ws_bytes, None)
+        assert rc == B.TRI_ATTN_ERR_UNSUPPORTED
+    finally:
+        e.close()

@@ -1,0 +1,174 @@
+// Training-mode attention core: kernel 2's step with dropout on the attention
+// weights and the row log-sum-exp saved (FW-GLM-5-1 / l2_p6 transcript, the
+// forward as restated: dropout right after the softmax over keys, before the
+// product with v; Kimi-K2.6 / l2_p6: the module's dropout layer).
+//
+// Dropout decision of key k for query column j, head t, row (b, i): word
+// k mod 4 of Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011) at counter (k / 4, j,
+// (b*N + i)*h + t, offset) and key (seed low word, seed high word); the
+// weight is kept iff that word >= thr and kept weights are scaled by
+// 2^32 / (2^32 - thr), which keeps the expectation exact. The row sums that
+// normalise the softmax use the undropped weights.
+//
+// Reads kernel 1's workspace (q pre-scaled by log2(e)/sqrt(d), the bias+mask
+// tile in the log2 domain), writes g * o over the gate like kernel 2 (kernel 3
+// then projects it), and lse[b][i][t][j] = ln sum_k exp(s), s the masked
+// scores. A fully masked column (finite fill) has uniform weights 1/N over
+// all N keys before dropout and lse = fill + ln N; with fill = -inf it gets
+// NaN, as the definition does.
+//
+// One wave per (b, i, t, 64 query columns), one lane per column, a running
+// maximum over the keys in float32. Plain and unoptimised: each lane forms
+// its own scores with FMAs and draws its own numbers (one generator call per
+// four keys); every lane of a wave reads the same key and value, so those
+// loads are broadcasts.
+#include "device_common.h"
+#include "tri_attn.h"
+#include "tri_attn_internal.h"
+
+namespace tpa {
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_elem(const void *p, size_t i) {
+  if constexpr (is_bf16<T>::value)
+    return bf2f(reinterpret_cast<const uint16_t *>(p)[i]);
+  else
+    return reinterpret_cast<const float *>(p)[i];
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(64) void k2_train(K2Args a, K2TrainArgs tr) {
+  constexpr bool BF = is_bf16<T>::value;
+  constexpr bool KSPLIT = !BF && DH == 32;  // k stored as three bf16 parts (kernel 1)
+  const int N = a.N, Np = a.Np, nch = a.nchunk;
+  const int H = tr.h, NB = tr.h * DH / 16;
+  int blk = blockIdx.x;
+  const int chunk = blk % nch;
+  blk /= nch;
+  const int t = blk % H;
+  const int row = blk / H;  // b * N + i
+  const int b = row / N;
+  const int j = chunk * 64 + (int)threadIdx.x;
+  if (j >= N) return;  // no barriers or LDS in this kernel
+
+  float q[DH];
+#pragma unroll
+  for (int u = 0; u < DH; ++u)
+    q[u] = ld_elem<T>(a.q, (((size_t)row * NB + t * (DH / 16) + u / 16) * Np + j) * 16 + u % 16);
+  const float *zrow = a.zm + ((size_t)(b * H + t) * N + j) * Np;
+  auto key_at = [&](int k, float (&kv)[DH]) {
+    if constexpr (KSPLIT) {
+      const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + ((size_t)row * H + t) * 3 * Np * 32 +
+                           (size_t)(k >> 4) * 512 + (k & 15) * 8;
+#pragma unroll
+      for (int u = 0; u < DH; ++u) {
+        const size_t o = (size_t)(u >> 3) * 128 + (u & 7);
+        kv[u] = bf2f(kp[o]) + bf2f(kp[o + (size_t)Np * 32]) + bf2f(kp[o + (size_t)Np * 64]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < DH; ++u)
+        kv[u] = ld_elem<T>(a.k, (((size_t)row * NB + t * (DH / 16) + u / 16) * Np + k) * 16 + u % 16);
+    }
+  };
+  const size_t vbase = ((size_t)row * H + t) * DH * Np;  // v^T [b][i][t][u][k]
+  const uint32_t ctr2 = (uint32_t)(row * H + t);
+
+  float m = -INFINITY, l = 0.f, o[DH];
+#pragma unroll
+  for (int u = 0; u < DH; ++u) o[u] = 0.f;
+  uint4 w = make_uint4(0, 0, 0, 0);
+  for (int k = 0; k < N; ++k) {
+    if ((k & 3) == 0) w = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, ctr2, tr.offset), tr.seed_lo,
+                                        tr.seed_hi);
+    const float z = zrow[k];
+    if (z == -INFINITY) continue;  // masked key: weight exactly 0
+    float kv[DH];
+    key_at(k, kv);
+    float s = z;
+#pragma unroll
+    for (int u = 0; u < DH; ++u) s = fmaf(q[u], kv[u], s);
+    if (s > m) {
+      const float c = exp2f(m - s);  // 0 for the first live key
+      l *= c;
+#pragma unroll
+      for (int u = 0; u < DH; ++u) o[u] *= c;
+      m = s;
+    }
+    const float p = exp2f(s - m);
+    l += p;
+    const uint32_t word = (k & 3) == 0 ? w.x : (k & 3) == 1 ? w.y : (k & 3) == 2 ? w.z : w.w;
+    if (word >= tr.thr) {
+#pragma unroll
+      for (int u = 0; u < DH; ++u) o[u] = fmaf(p, ld_elem<T>(a.vt, vbase + (size_t)u * Np + k), o[u]);
+    }
+  }
+  float inv, lse;
+  if (m == -INFINITY) {
+    // every key masked: uniform weights over all N keys before dropout
+    if (a.mask_fill == -INFINITY) {
+      inv = NAN;
+      lse = NAN;
+    } else {
+      for (int k = 0; k < N; ++k) {
+        if ((k & 3) == 0) w = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, ctr2, tr.offset),
+                                            tr.seed_lo, tr.seed_hi);
+        const uint32_t word = (k & 3) == 0 ? w.x : (k & 3) == 1 ? w.y : (k & 3) == 2 ? w.z : w.w;
+        if (word >= tr.thr) {
+#pragma unroll
+          for (int u = 0; u < DH; ++u) o[u] += ld_elem<T>(a.vt, vbase + (size_t)u * Np + k);
+        }
+      }
+      inv = tr.scale / (float)N;
+      lse = a.mask_fill + logf((float)N);
+    }
+  } else {
+    inv = tr.scale / l;
+    lse = (m + log2f(l)) * 0.69314718055994531f;
+  }
+  if (tr.lse) tr.lse[((size_t)row * H + t) * N + j] = lse;
+  // g * o over the gate: [b][i][c/16][j][16]
+#pragma unroll
+  for (int u = 0; u < DH; ++u) {
+    const size_t gi = (((size_t)row * NB + t * (DH / 16) + u / 16) * Np + j) * 16 + u % 16;
+    const float val = ld_elem<T>(a.g, gi) * (o[u] * inv);
+    if constexpr (BF)
+      reinterpret_cast<uint16_t *>(a.g)[gi] = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
+    else
+      reinterpret_cast<float *>(a.g)[gi] = val;
+  }
+}
+
+template <typename T, int DH>
+static hipError_t launch_t(const K2Args &a, const K2TrainArgs &tr, hipStream_t s) {
+  const long long blocks = (long long)a.B * a.N * tr.h * a.nchunk;
+  if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k2_train<T, DH>), dim3((unsigned)blocks), dim3(64), 0, s, a, tr);
+  return hipGetLastError();
+}
+
+hipError_t launch_k2_train(int dtype, int dh, const K2Args &a, const K2TrainArgs &tr, hipStream_t s) {
+  if (dtype == TRI_ATTN_BF16) {
+    if (dh == 16) return launch_t<bf16_t, 16>(a, tr, s);
+    if (dh == 32) return launch_t<bf16_t, 32>(a, tr, s);
+  } else {
+    if (dh == 16) return launch_t<float, 16>(a, tr, s);
+    if (dh == 32) return launch_t<float, 32>(a, tr, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tpa

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -207,7 +208,7 @@ int tri_attn_get_workspace_layout(tri_attn_t t, int B, int N, tri_attn_workspace
 
 // stages: bit 0 = projection kernel, bit 1 = attention kernel, bit 2 = output projection
 static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
-               void *ws, size_t ws_bytes, void *stream, int stages) {
+               void *ws, size_t ws_bytes, void *stream, int stages, const K2TrainArgs *train = nullptr) {
   int rc = check_sizes(t, B, N);
   if (rc) return rc;
   if (B == 0 || N == 0) return TRI_ATTN_OK;
@@ -266,7 +267,11 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   // each keeps its XCD from item to item
   int grid2 = a2.items;
   if (grid2 > t->k2_grid) grid2 = t->k2_grid >= 8 ? t->k2_grid / 8 * 8 : t->k2_grid;
-  if ((stages & 2) && launch_k2(t->cfg.dtype, D, t->dh, a2, grid2, s) != hipSuccess) return TRI_ATTN_ERR_HIP;
+  if (stages & 2) {
+    const hipError_t e2 = train ? launch_k2_train(t->cfg.dtype, t->dh, a2, *train, s)
+                                : launch_k2(t->cfg.dtype, D, t->dh, a2, grid2, s);
+    if (e2 != hipSuccess) return TRI_ATTN_ERR_HIP;
+  }
 
   K3Args a3{};
   a3.go = a1.g;
@@ -289,6 +294,24 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
 int tri_attn_forward(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
                      void *workspace, size_t ws_bytes, void *stream) {
   return run(t, pair_repr, pair_mask, out, B, N, workspace, ws_bytes, stream, 7);
+}
+
+int tri_attn_forward_train(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, float *lse,
+                           int B, int N, double dropout_rate, uint64_t seed, uint32_t offset, void *workspace,
+                           size_t ws_bytes, void *stream) {
+  if (!t) return TRI_ATTN_ERR_INVALID_ARG;
+  if (!(dropout_rate >= 0.0 && dropout_rate < 1.0)) return TRI_ATTN_ERR_INVALID_ARG;
+  if (t->cfg.ending_node) return TRI_ATTN_ERR_UNSUPPORTED;
+  K2TrainArgs tr{};
+  const double thr = std::min(std::nearbyint(dropout_rate * 4294967296.0), 4294967295.0);
+  tr.thr = (uint32_t)thr;
+  tr.scale = (float)(4294967296.0 / (4294967296.0 - thr));
+  tr.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  tr.seed_hi = (uint32_t)(seed >> 32);
+  tr.offset = offset;
+  tr.lse = lse;
+  tr.h = t->h;
+  return run(t, pair_repr, pair_mask, out, B, N, workspace, ws_bytes, stream, 7, &tr);
 }
 
 int tri_attn_project(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, int B, int N, void *workspace,

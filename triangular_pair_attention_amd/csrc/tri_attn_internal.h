@@ -46,6 +46,15 @@ struct K2Args {
   int B, N, Np, nchunk, items;
 };
 
+// Training-mode attention (k2_train.hip): dropout and the saved log-sum-exp.
+struct K2TrainArgs {
+  float *lse;        // [B][N][h][N] float32 or null
+  uint32_t thr;      // keep iff the generator's word >= thr
+  float scale;       // 2^32 / (2^32 - thr)
+  uint32_t seed_lo, seed_hi, offset;
+  int h;
+};
+
 // Kernel 3: output projection of g * o (left by kernel 2 in the gate region).
 struct K3Args {
   const void *go;  // [B][N][D/16][Np][16]
@@ -56,6 +65,8 @@ struct K3Args {
   int B, N, Np, nchunk, tiles;
   int transposed;  // ending-node: position (b, i, j) is written to out[b][j][i]
 };
+
+hipError_t launch_k2_train(int dtype, int dh, const K2Args &a, const K2TrainArgs &tr, hipStream_t s);
 
 // Launchers: return the launch status. `dtype` is TRI_ATTN_F32 / TRI_ATTN_BF16.
 hipError_t launch_k1(int dtype, int D, int dh, const K1Args &a, int grid, hipStream_t s);
