@@ -34,6 +34,7 @@ PEAK = {  # MI355X published dense peaks
     "hbm_GBps": 8000.0,
     "mfma_f32_TFLOPs": 157.3,
     "mfma_bf16_TFLOPs": 2500.0,
+    "valu_f32_TFLOPs": 157.3,  # fp32 vector FMA (packed), 256 CUs at 2.4 GHz
 }
 # Rates measured on one MI355X by triangular_pair_attention_amd/calib/calib.hip
 # (tri_attn_calib): the attention kernel's exponentials and matrix-core work
@@ -238,6 +239,7 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", action="store_true", help="skip timing the training-mode forward")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--ending-node", action="store_true",
                     help="the ending-node variant (attention along the other residue axis)")
@@ -333,6 +335,27 @@ def main():
     except RuntimeError as e:  # capture unsupported: report no graph timing
         print(f"bench.py: graph timing skipped ({e})", file=sys.stderr)
     torch.cuda.synchronize()
+    # the training-mode forward (dropout 0.1, log-sum-exp saved) on the same
+    # workload, for comparison; `value` stays the inference forward
+    train = None
+    if not args.ending_node and not args.no_train:
+        lse = torch.empty((w.B, w.N, w.h, w.N), dtype=torch.float32, device=dev)
+
+        def trn():
+            B.tri_attn_forward_train(h, P, M, out, lse, w.B, w.N, 0.1, 12345, 0, ws, nws, stream)
+
+        for _ in range(3):
+            trn()
+        ms_train = timed(trn, max(1, args.steps // 5))
+        # its attention step (a plain FMA kernel): the forward less kernels 1 and 3 timed alone
+        ms_att = max(ms_train - ms_k1 - ms_k3, 1e-6)
+        att_flops = 4.0 * w.B * w.N ** 3 * w.D  # q.k and a'.v, dense
+        train = {"dropout_rate": 0.1, "ms_per_step": ms_train, "ratio_to_inference": ms_train / ms_fwd,
+                 "attention_ms_est": ms_att,
+                 "attention_alu": {"bound": "alu", "achieved": att_flops / (ms_att * 1e-3) / 1e12,
+                                   "peak": PEAK["valu_f32_TFLOPs"], "unit": "TFLOP/s",
+                                   "frac": att_flops / (ms_att * 1e-3) / 1e12 / PEAK["valu_f32_TFLOPs"]}}
+    torch.cuda.synchronize()
     B.tri_attn_destroy(h)
 
     m = work_model(w)
@@ -370,6 +393,7 @@ def main():
         "attention_floor": attention_floor(w, m, ms_k2, inp["pair_mask"]),
         "wall_s_timed": wall,
         "roofline": roof,
+        "train": train,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds, args.ending_node)
