@@ -132,8 +132,8 @@ int tri_attn_forward(tri_attn_t h, const void *pair_repr, const uint8_t *pair_ma
  *         a fully masked column has fill + ln N); may be NULL.
  * dropout_rate in [0, 1), else TRI_ATTN_ERR_INVALID_ARG; rate 0 gives the
  * inference output. Ending-node handles: TRI_ATTN_ERR_UNSUPPORTED. The
- * attention step is a plain kernel (one lane per query column), several
- * times slower than the inference one. */
+ * attention step is a plain kernel (one lane per query column, key tiles in
+ * LDS), several times slower than the inference one. */
 int tri_attn_forward_train(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, void *out, float *lse,
                            int B, int N, double dropout_rate, uint64_t seed, uint32_t offset, void *workspace,
                            size_t ws_bytes, void *stream);

@@ -18,11 +18,12 @@
 // all N keys before dropout and lse = fill + ln N; with fill = -inf it gets
 // NaN, as the definition does.
 //
-// One wave per (b, i, t, 64 query columns), one lane per column, a running
-// maximum over the keys in float32. Plain and unoptimised: each lane forms
+// One workgroup per (b, i, t, 256 query columns), one lane per column, a
+// running maximum over the keys in float32. Tiles of 64 keys of k and v go
+// through LDS (every lane reads the same key: broadcasts); each lane forms
 // its own scores with FMAs and draws its own numbers (one generator call per
-// four keys); every lane of a wave reads the same key and value, so those
-// loads are broadcasts.
+// four keys). A column with no valid key is known from kernel 1's per-chunk
+// bias maxima, so its uniform-weight sum runs in the same loop.
 #include "device_common.h"
 #include "tri_attn.h"
 #include "tri_attn_internal.h"
@@ -50,40 +51,35 @@ __device__ __forceinline__ float ld_elem(const void *p, size_t i) {
 }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(64) void k2_train(K2Args a, K2TrainArgs tr) {
+__global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
   constexpr bool BF = is_bf16<T>::value;
   constexpr bool KSPLIT = !BF && DH == 32;  // k stored as three bf16 parts (kernel 1)
+  constexpr int KT = 64;                    // keys per LDS tile
+  constexpr int QW = 256;                   // query columns per workgroup
+  __shared__ float ks[KT][DH];              // k of the tile's keys (read as broadcasts)
+  __shared__ float vs[DH][KT];              // v^T of the tile's keys
   const int N = a.N, Np = a.Np, nch = a.nchunk;
   const int H = tr.h, NB = tr.h * DH / 16;
+  const int nq = (N + QW - 1) / QW;
   int blk = blockIdx.x;
-  const int chunk = blk % nch;
-  blk /= nch;
+  const int qc = blk % nq;
+  blk /= nq;
   const int t = blk % H;
   const int row = blk / H;  // b * N + i
   const int b = row / N;
-  const int j = chunk * 64 + (int)threadIdx.x;
-  if (j >= N) return;  // no barriers or LDS in this kernel
+  const int tid = threadIdx.x;
+  const int j = qc * QW + tid;
+  const bool active = j < N;  // every thread stays for the barriers
+  const int jc = active ? j : N - 1;
 
   float q[DH];
 #pragma unroll
   for (int u = 0; u < DH; ++u)
-    q[u] = ld_elem<T>(a.q, (((size_t)row * NB + t * (DH / 16) + u / 16) * Np + j) * 16 + u % 16);
-  const float *zrow = a.zm + ((size_t)(b * H + t) * N + j) * Np;
-  auto key_at = [&](int k, float (&kv)[DH]) {
-    if constexpr (KSPLIT) {
-      const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + ((size_t)row * H + t) * 3 * Np * 32 +
-                           (size_t)(k >> 4) * 512 + (k & 15) * 8;
-#pragma unroll
-      for (int u = 0; u < DH; ++u) {
-        const size_t o = (size_t)(u >> 3) * 128 + (u & 7);
-        kv[u] = bf2f(kp[o]) + bf2f(kp[o + (size_t)Np * 32]) + bf2f(kp[o + (size_t)Np * 64]);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < DH; ++u)
-        kv[u] = ld_elem<T>(a.k, (((size_t)row * NB + t * (DH / 16) + u / 16) * Np + k) * 16 + u % 16);
-    }
-  };
+    q[u] = ld_elem<T>(a.q, (((size_t)row * NB + t * (DH / 16) + u / 16) * Np + jc) * 16 + u % 16);
+  const float *zrow = a.zm + ((size_t)(b * H + t) * N + jc) * Np;
+  // a column with no valid key (finite fill): uniform weights over all N keys
+  bool dead = true;
+  for (int c = 0; c < nch; ++c) dead = dead && a.zmax[((size_t)(b * H + t) * nch + c) * N + jc] == -INFINITY;
   const size_t vbase = ((size_t)row * H + t) * DH * Np;  // v^T [b][i][t][u][k]
   const uint32_t ctr2 = (uint32_t)(row * H + t);
 
@@ -91,47 +87,71 @@ __global__ __launch_bounds__(64) void k2_train(K2Args a, K2TrainArgs tr) {
 #pragma unroll
   for (int u = 0; u < DH; ++u) o[u] = 0.f;
   uint4 w = make_uint4(0, 0, 0, 0);
-  for (int k = 0; k < N; ++k) {
-    if ((k & 3) == 0) w = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, ctr2, tr.offset), tr.seed_lo,
-                                        tr.seed_hi);
-    const float z = zrow[k];
-    if (z == -INFINITY) continue;  // masked key: weight exactly 0
-    float kv[DH];
-    key_at(k, kv);
-    float s = z;
-#pragma unroll
-    for (int u = 0; u < DH; ++u) s = fmaf(q[u], kv[u], s);
-    if (s > m) {
-      const float c = exp2f(m - s);  // 0 for the first live key
-      l *= c;
-#pragma unroll
-      for (int u = 0; u < DH; ++u) o[u] *= c;
-      m = s;
+  for (int k0 = 0; k0 < N; k0 += KT) {
+    // stage the tile (keys past N as zeros)
+    for (int e = tid; e < KT * DH; e += QW) {
+      const int kk = e / DH, u = e - kk * DH, k = k0 + kk;
+      float kv = 0.f;
+      if (k < N) {
+        if constexpr (KSPLIT) {
+          const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k) + ((size_t)row * H + t) * 3 * Np * 32 +
+                               (size_t)(k >> 4) * 512 + (k & 15) * 8 + (size_t)(u >> 3) * 128 + (u & 7);
+          kv = bf2f(kp[0]) + bf2f(kp[(size_t)Np * 32]) + bf2f(kp[(size_t)Np * 64]);
+        } else {
+          kv = ld_elem<T>(a.k, (((size_t)row * NB + t * (DH / 16) + u / 16) * Np + k) * 16 + u % 16);
+        }
+      }
+      ks[kk][u] = kv;
     }
-    const float p = exp2f(s - m);
-    l += p;
-    const uint32_t word = (k & 3) == 0 ? w.x : (k & 3) == 1 ? w.y : (k & 3) == 2 ? w.z : w.w;
-    if (word >= tr.thr) {
-#pragma unroll
-      for (int u = 0; u < DH; ++u) o[u] = fmaf(p, ld_elem<T>(a.vt, vbase + (size_t)u * Np + k), o[u]);
+    for (int e = tid; e < KT * DH; e += QW) {
+      const int u = e / KT, kk = e - u * KT, k = k0 + kk;
+      vs[u][kk] = k < N ? ld_elem<T>(a.vt, vbase + (size_t)u * Np + k) : 0.f;
     }
+    __syncthreads();
+    const int kn = min(KT, N - k0);
+    if (active) {
+      for (int kk = 0; kk < kn; ++kk) {
+        const int k = k0 + kk;
+        if ((k & 3) == 0)
+          w = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, ctr2, tr.offset), tr.seed_lo, tr.seed_hi);
+        const uint32_t word = (k & 3) == 0 ? w.x : (k & 3) == 1 ? w.y : (k & 3) == 2 ? w.z : w.w;
+        const bool keep = word >= tr.thr;
+        if (dead) {
+          if (keep) {
+#pragma unroll
+            for (int u = 0; u < DH; ++u) o[u] += vs[u][kk];
+          }
+          continue;
+        }
+        const float z = zrow[k];
+        if (z == -INFINITY) continue;  // masked key: weight exactly 0
+        float s = z;
+#pragma unroll
+        for (int u = 0; u < DH; ++u) s = fmaf(q[u], ks[kk][u], s);
+        if (s > m) {
+          const float c = exp2f(m - s);  // 0 for the first live key
+          l *= c;
+#pragma unroll
+          for (int u = 0; u < DH; ++u) o[u] *= c;
+          m = s;
+        }
+        const float p = exp2f(s - m);
+        l += p;
+        if (keep) {
+#pragma unroll
+          for (int u = 0; u < DH; ++u) o[u] = fmaf(p, vs[u][kk], o[u]);
+        }
+      }
+    }
+    __syncthreads();  // every lane is done with the tile before it is refilled
   }
+  if (!active) return;  // past the last barrier
   float inv, lse;
-  if (m == -INFINITY) {
-    // every key masked: uniform weights over all N keys before dropout
+  if (dead) {
     if (a.mask_fill == -INFINITY) {
       inv = NAN;
       lse = NAN;
     } else {
-      for (int k = 0; k < N; ++k) {
-        if ((k & 3) == 0) w = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, ctr2, tr.offset),
-                                            tr.seed_lo, tr.seed_hi);
-        const uint32_t word = (k & 3) == 0 ? w.x : (k & 3) == 1 ? w.y : (k & 3) == 2 ? w.z : w.w;
-        if (word >= tr.thr) {
-#pragma unroll
-          for (int u = 0; u < DH; ++u) o[u] += ld_elem<T>(a.vt, vbase + (size_t)u * Np + k);
-        }
-      }
       inv = tr.scale / (float)N;
       lse = a.mask_fill + logf((float)N);
     }
@@ -154,9 +174,9 @@ __global__ __launch_bounds__(64) void k2_train(K2Args a, K2TrainArgs tr) {
 
 template <typename T, int DH>
 static hipError_t launch_t(const K2Args &a, const K2TrainArgs &tr, hipStream_t s) {
-  const long long blocks = (long long)a.B * a.N * tr.h * a.nchunk;
+  const long long blocks = (long long)a.B * a.N * tr.h * ((a.N + 255) / 256);
   if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k2_train<T, DH>), dim3((unsigned)blocks), dim3(64), 0, s, a, tr);
+  hipLaunchKernelGGL((k2_train<T, DH>), dim3((unsigned)blocks), dim3(256), 0, s, a, tr);
   return hipGetLastError();
 }
 
