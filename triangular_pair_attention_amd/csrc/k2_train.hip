@@ -87,6 +87,7 @@ __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
 #pragma unroll
   for (int u = 0; u < DH; ++u) o[u] = 0.f;
   uint4 w = make_uint4(0, 0, 0, 0);
+  float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);  // bias of the current four keys (rows run to Np)
   for (int k0 = 0; k0 < N; k0 += KT) {
     // stage the tile (keys past N as zeros)
     for (int e = tid; e < KT * DH; e += QW) {
@@ -112,8 +113,10 @@ __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
     if (active) {
       for (int kk = 0; kk < kn; ++kk) {
         const int k = k0 + kk;
-        if ((k & 3) == 0)
+        if ((k & 3) == 0) {
           w = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, ctr2, tr.offset), tr.seed_lo, tr.seed_hi);
+          z4 = *reinterpret_cast<const float4 *>(zrow + k);
+        }
         const uint32_t word = (k & 3) == 0 ? w.x : (k & 3) == 1 ? w.y : (k & 3) == 2 ? w.z : w.w;
         const bool keep = word >= tr.thr;
         if (dead) {
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
           }
           continue;
         }
-        const float z = zrow[k];
+        const float z = (k & 3) == 0 ? z4.x : (k & 3) == 1 ? z4.y : (k & 3) == 2 ? z4.z : z4.w;
         if (z == -INFINITY) continue;  // masked key: weight exactly 0
         float s = z;
 #pragma unroll
