@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
   constexpr int KT = 64;                    // keys per LDS tile
   constexpr int QW = 256;                   // query columns per workgroup
   __shared__ float ks[KT][DH];              // k of the tile's keys (read as broadcasts)
-  __shared__ float vs[DH][KT];              // v^T of the tile's keys
+  __shared__ float vs[KT][DH];              // v of the tile's keys (key-major, like ks)
   const int N = a.N, Np = a.Np, nch = a.nchunk;
   const int H = tr.h, NB = tr.h * DH / 16;
   const int nq = (N + QW - 1) / QW;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
     }
     for (int e = tid; e < KT * DH; e += QW) {
       const int u = e / KT, kk = e - u * KT, k = k0 + kk;
-      vs[u][kk] = k < N ? ld_elem<T>(a.vt, vbase + (size_t)u * Np + k) : 0.f;
+      vs[kk][u] = k < N ? ld_elem<T>(a.vt, vbase + (size_t)u * Np + k) : 0.f;
     }
     __syncthreads();
     const int kn = min(KT, N - k0);
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
         if (dead) {
           if (keep) {
 #pragma unroll
-            for (int u = 0; u < DH; ++u) o[u] += vs[u][kk];
+            for (int u = 0; u < DH; ++u) o[u] += vs[kk][u];
           }
           continue;
         }
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
         l += p;
         if (keep) {
 #pragma unroll
-          for (int u = 0; u < DH; ++u) o[u] = fmaf(p, vs[u][kk], o[u]);
+          for (int u = 0; u < DH; ++u) o[u] = fmaf(p, vs[kk][u], o[u]);
         }
       }
     }
