@@ -19,10 +19,10 @@
 // NaN, as the definition does.
 //
 // One workgroup per (b, i, t, 256 query columns), one lane per column, a
-// running maximum over the keys in float32. Tiles of 64 keys of k and v go
-// through LDS (every lane reads the same key: broadcasts); each lane forms
-// its own scores with FMAs and draws its own numbers (one generator call per
-// four keys). A column with no valid key is known from kernel 1's per-chunk
+// running maximum over the keys in float32, updated once per four keys.
+// Tiles of 64 keys of k and v go through LDS (every lane reads the same key:
+// broadcasts); each lane forms its own scores with FMAs and draws its own
+// numbers (one generator call per four keys). A column with no valid key is known from kernel 1's per-chunk
 // bias maxima, so its uniform-weight sum runs in the same loop.
 #include "device_common.h"
 #include "tri_attn.h"
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
 #pragma unroll
   for (int u = 0; u < DH; ++u) o[u] = 0.f;
   uint4 w = make_uint4(0, 0, 0, 0);
-  float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);  // bias of the current four keys (rows run to Np)
+  float4 z4;  // bias of the current four keys (rows run to Np)
   for (int k0 = 0; k0 < N; k0 += KT) {
     // stage the tile (keys past N as zeros)
     for (int e = tid; e < KT * DH; e += QW) {
@@ -109,40 +109,43 @@ __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {
       vs[kk][u] = k < N ? ld_elem<T>(a.vt, vbase + (size_t)u * Np + k) : 0.f;
     }
     __syncthreads();
-    const int kn = min(KT, N - k0);
+    const int kn = min(KT, N - k0);  // keys past N in the tile: zero k and v, bias -inf
     if (active) {
-      for (int kk = 0; kk < kn; ++kk) {
+      for (int kk = 0; kk < kn; kk += 4) {
         const int k = k0 + kk;
-        if ((k & 3) == 0) {
-          w = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, ctr2, tr.offset), tr.seed_lo, tr.seed_hi);
-          z4 = *reinterpret_cast<const float4 *>(zrow + k);
-        }
-        const uint32_t word = (k & 3) == 0 ? w.x : (k & 3) == 1 ? w.y : (k & 3) == 2 ? w.z : w.w;
-        const bool keep = word >= tr.thr;
+        w = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, ctr2, tr.offset), tr.seed_lo, tr.seed_hi);
+        const bool keep[4] = {w.x >= tr.thr, w.y >= tr.thr, w.z >= tr.thr, w.w >= tr.thr};
         if (dead) {
-          if (keep) {
 #pragma unroll
-            for (int u = 0; u < DH; ++u) o[u] += vs[kk][u];
-          }
+          for (int e = 0; e < 4; ++e)
+            if (keep[e]) {
+#pragma unroll
+              for (int u = 0; u < DH; ++u) o[u] += vs[kk + e][u];
+            }
           continue;
         }
-        const float z = (k & 3) == 0 ? z4.x : (k & 3) == 1 ? z4.y : (k & 3) == 2 ? z4.z : z4.w;
-        if (z == -INFINITY) continue;  // masked key: weight exactly 0
-        float s = z;
+        z4 = *reinterpret_cast<const float4 *>(zrow + k);
+        float s4[4] = {z4.x, z4.y, z4.z, z4.w};  // -inf for masked keys stays -inf
 #pragma unroll
-        for (int u = 0; u < DH; ++u) s = fmaf(q[u], ks[kk][u], s);
-        if (s > m) {
-          const float c = exp2f(m - s);  // 0 for the first live key
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int u = 0; u < DH; ++u) s4[e] = fmaf(q[u], ks[kk + e][u], s4[e]);
+        const float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+        if (mx > m) {
+          const float c = exp2f(m - mx);  // 0 for the first live keys
           l *= c;
 #pragma unroll
           for (int u = 0; u < DH; ++u) o[u] *= c;
-          m = s;
+          m = mx;
         }
-        const float p = exp2f(s - m);
-        l += p;
-        if (keep) {
+        if (m == -INFINITY) continue;  // no live key yet
 #pragma unroll
-          for (int u = 0; u < DH; ++u) o[u] = fmaf(p, vs[kk][u], o[u]);
+        for (int e = 0; e < 4; ++e) {
+          const float p = exp2f(s4[e] - m);  // masked: 0
+          l += p;
+          const float pk = keep[e] ? p : 0.f;
+#pragma unroll
+          for (int u = 0; u < DH; ++u) o[u] = fmaf(pk, vs[kk + e][u], o[u]);
         }
       }
     }
