@@ -131,7 +131,9 @@ int tri_attn_forward(tri_attn_t h, const void *pair_repr, const uint8_t *pair_ma
  *         ln sum_k exp(s[b,i,t,j,k]) over the masked scores (fill included:
  *         a fully masked column has fill + ln N); may be NULL.
  * dropout_rate in [0, 1), else TRI_ATTN_ERR_INVALID_ARG; rate 0 gives the
- * inference output. Ending-node handles: TRI_ATTN_ERR_UNSUPPORTED. The
+ * inference output. Ending-node handles run the starting-node computation of
+ * the transposed pair representation and mask: the dropout counters and lse
+ * use its indices, so lse[b][j][t][i] belongs to output position (b, i, j). The
  * attention step is a plain kernel (one lane per query column, key tiles in
  * LDS), several times slower than the inference one. */
 int tri_attn_forward_train(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, void *out, float *lse,

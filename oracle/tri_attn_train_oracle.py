@@ -173,6 +173,16 @@ def forward_train(inp: dict, rate: float, seed: int, offset: int = 0, fill: floa
     return y.reshape(B, N, N, D), lse.reshape(B, N, h, N)
 
 
+def forward_train_ending(inp: dict, rate: float, seed: int, offset: int = 0, fill: float = O.MASK_FILL,
+                         eps: float = O.LN_EPS):
+    """Ending-node training forward: the starting-node training forward of
+    the pair representation and mask with both residue axes swapped, y
+    swapped back. The dropout counters and lse use the indices of that
+    swapped problem: lse[b, j, t, i] belongs to output position (b, i, j)."""
+    y, lse = forward_train(O._transposed(inp), rate, seed, offset, fill, eps)
+    return np.swapaxes(y, 1, 2), lse
+
+
 def lse_fully_masked(N: int, fill: float = O.MASK_FILL) -> float:
     """lse of a query column whose keys are all masked: every score is FILL."""
     return fill + math.log(N)

@@ -97,12 +97,29 @@ def test_train_argument_errors():
             assert rc == B.TRI_ATTN_ERR_INVALID_ARG
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("dtype,shape,mask", [("f32", (2, 40, 64, 4), ("bernoulli", 0.8)),
+                                              ("bf16", (1, 70, 128, 4), ("pad", 50)),
+                                              ("f32", (1, 66, 128, 8), ("pad", 60))])
+def test_train_ending_node(dtype, shape, mask):
+    """Ending-node handles: the transposed problem's decisions and lse."""
+    Bn, N, D, h = shape
+    inp = make_inputs(Workload("train_end", Bn, N, D, h, dtype, mask, seed=74))
     e = Gpu(inp, ending=True)
     try:
+        lse = torch.empty((e.B, e.N, e.h, e.N), dtype=torch.float32, device=e.dev)
         out = torch.empty_like(e.P)
-        rc = B.raw_call("tri_attn_forward_train", e.handle, e.P.data_ptr(), e.M.data_ptr(), out.data_ptr(), None,
-                        e.B, e.N, B.ctypes.c_double(0.1), B.ctypes.c_uint64(1), B.ctypes.c_uint32(0),
-                        e.ws.data_ptr(), e.ws_bytes, None)
-        assert rc == B.TRI_ATTN_ERR_UNSUPPORTED
+        B.tri_attn_forward_train(e.handle, e.P, e.M, out, lse, e.B, e.N, 0.3, 99, 5, e.ws, e.ws_bytes,
+                                 torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        y, lse = y_numpy(out), lse.double().cpu().numpy()
     finally:
         e.close()
+    ref, ref_lse = TO.forward_train_ending(inp, 0.3, 99, 5)
+    err, idx = max_err(y, ref)
+    log(f"train ending node {dtype} {shape}: y max abs err {err:.3e} at {idx}")
+    assert err <= TOL[dtype]
+    live = np.swapaxes(np.asarray(inp["pair_mask"]), 1, 2).any(-1)  # the transposed problem's columns
+    live = np.broadcast_to(live[:, None, None, :], ref_lse.shape)
+    assert np.abs(lse - ref_lse)[live].max() <= LSE_TOL[dtype]

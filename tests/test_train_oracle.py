@@ -188,6 +188,14 @@ def test_lse_normalises_scores_and_fully_masked_columns():
     assert not cap["keep"].all() and cap["keep"].any()
 
 
+def test_ending_node_rate_zero_is_the_inference_ending_forward():
+    inp = small(B=2, N=6, D=8, h=2, mask=("pad", 4))
+    y, lse = TO.forward_train_ending(inp, 0.0, 8)
+    np.testing.assert_allclose(y, O.forward_ending(inp), rtol=0, atol=1e-13)
+    _, lse_t = TO.forward_train(O._transposed(inp), 0.0, 8)
+    np.testing.assert_array_equal(lse, lse_t)
+
+
 def test_rate_and_seed_validation():
     with pytest.raises(ValueError):
         TO.drop_threshold(1.0)

@@ -301,7 +301,6 @@ int tri_attn_forward_train(tri_attn_t t, const void *pair_repr, const uint8_t *p
                            size_t ws_bytes, void *stream) {
   if (!t) return TRI_ATTN_ERR_INVALID_ARG;
   if (!(dropout_rate >= 0.0 && dropout_rate < 1.0)) return TRI_ATTN_ERR_INVALID_ARG;
-  if (t->cfg.ending_node) return TRI_ATTN_ERR_UNSUPPORTED;
   K2TrainArgs tr{};
   const double thr = std::min(std::nearbyint(dropout_rate * 4294967296.0), 4294967295.0);
   tr.thr = (uint32_t)thr;
