@@ -335,6 +335,22 @@ def main():
     except RuntimeError as e:  # capture unsupported: report no graph timing
         print(f"bench.py: graph timing skipped ({e})", file=sys.stderr)
     torch.cuda.synchronize()
+    # cold: a 512 MiB buffer is written before every timed forward, so that
+    # neither the MALL (256 MB) nor the L2 caches hold the inputs
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    reps = max(5, min(50, args.steps // 10))
+    cold = 0.0
+    for _ in range(reps):
+        flush.fill_(1)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        fwd()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold += c0.elapsed_time(c1)
+    ms_cold = cold / reps
+    del flush
     # the training-mode forward (dropout 0.1, log-sum-exp saved) on the same
     # workload, for comparison; `value` stays the inference forward
     train = None
@@ -388,6 +404,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "tflops": tflops,
         "ms_per_step_graph_replay": ms_graph,
+        "ms_per_step_cold": ms_cold,
         "kernels_ms": ms_k,
         "kernels_roofline": {k: roofline_of(k, w, m, v, inp["pair_mask"]) for k, v in ms_k.items()},
         "attention_floor": attention_floor(w, m, ms_k2, inp["pair_mask"]),
