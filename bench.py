@@ -7,11 +7,14 @@ A step is one tri_attn_forward (kernel 1: LayerNorm + fused projection;
 kernel 2: attention + gate; kernel 3: output projection) over one batch of
 seeded synthetic inputs already resident in HBM. Prints ONE JSON line.
 
-The default workload is B=1, N=128, D=128, h=4 (d=32), float32, Bernoulli(0.9)
-mask with the diagonal set. `--config k` selects another of the five
-workloads (1..5). Each kernel is also timed alone (stage entry points
-tri_attn_project / tri_attn_attend / tri_attn_output) with HIP events on the
-stream it runs on; the slowest one is reported in `roofline`.
+The default workload is the largest of the five: B=4, N=512, D=128, h=8
+(d=16), bf16 storage with float32 accumulation, a per-batch valid length
+L_b in [384, 512] masking the trailing rows and columns. `--config k`
+selects another of the five workloads (1..5). Each kernel is also timed
+through its stage entry point (tri_attn_project / tri_attn_attend /
+tri_attn_output), one launch at a time between HIP events on the stream it
+runs on, each on the data its predecessors just wrote; the slowest one is
+reported in `roofline`.
 
 `--copy-probe` runs only a plain device copy of a known size (the reference
 for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes).
@@ -97,8 +100,9 @@ def work_model(w):
 def roofline_of(kernel, w, m, ms, mask=None):
     """The bound of one kernel: HBM where its arithmetic intensity is below the
     ridge of its dtype's matrix-core peak, else the matrix cores. For the
-    attention kernel with a mask, also the rate and fraction on the valid
-    (j, k) score pairs only (the work that must be computed)."""
+    attention kernel with a mask, `achieved` counts the valid (j, k) score
+    pairs only (the work that must be computed); the dense rate is kept as
+    `achieved_dense`."""
     mfma = PEAK["mfma_f32_TFLOPs"] if w.dtype == "f32" else PEAK["mfma_bf16_TFLOPs"]
     ridge = mfma * 1e12 / (PEAK["hbm_GBps"] * 1e9)
     fl, by = m[kernel]["flops"], m[kernel]["bytes"]
@@ -108,9 +112,14 @@ def roofline_of(kernel, w, m, ms, mask=None):
         r = {"bound": "mfma", "achieved": fl / (ms * 1e-3) / 1e12, "peak": mfma, "unit": "TFLOP/s"}
     r["frac"] = r["achieved"] / r["peak"]
     if kernel == "k2_attention" and mask is not None:
+        # the work that must be computed: the valid (j, k) score pairs only
+        # (a fully masked query column has a closed form); `achieved` and
+        # `frac` count those, the dense counts stay beside them
         valid = int((mask != 0).sum())  # (b, j, k) pairs, each scored for all N rows i
-        r["achieved_valid_pairs"] = 4 * w.N * w.D * valid / (ms * 1e-3) / 1e12
-        r["frac_valid_pairs"] = r["achieved_valid_pairs"] / r["peak"]
+        r["achieved_dense"], r["frac_dense"] = r["achieved"], r["frac"]
+        r["achieved"] = 4 * w.N * w.D * valid / (ms * 1e-3) / 1e12
+        r["frac"] = r["achieved"] / r["peak"]
+        r["count"] = "valid (j, k) score pairs"
     if w.dtype == "f32" and kernel in SPLIT_KERNELS and r["bound"] == "mfma":
         # the matrix cores run six bf16 products per float32 product
         ceil = PEAK["mfma_bf16_TFLOPs"] / 6
@@ -161,61 +170,42 @@ def stored_traffic(workload: str, kernel: str, dtype: str = "bf16"):
 
 
 def cpu_baseline(inp, w, seconds, ending_node=False):
-    """The oracle as it stands on the host cores: all N rows of batch 0 (with
-    that batch's LayerNorm and pair bias), repeated until `seconds` elapse
-    (ending-node: all N columns of batch 0)."""
-    import numpy as np  # noqa: F401
+    """The oracle as it stands, on the host's cores: all N rows of batch 0
+    (all N columns for the ending-node variant), one contiguous chunk of rows
+    per worker process (each worker computes its batch's LayerNorm and pair
+    bias once per pass, as one oracle call does), passes repeated until
+    `seconds` elapse. `cores` is the number of worker processes, each
+    single-threaded. A short single-process run is reported beside it."""
+    from oracle import pool
     from oracle.tri_attn_oracle import forward_ending_cols, forward_rows
 
-    if ending_node:
-        forward_rows = forward_ending_cols  # noqa: F811 (same work, the other residue axis)
-
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     rows = [(0, i) for i in range(w.N)]
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        forward_rows(inp, rows)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    pos = done * w.N * w.N
+    r = pool.time_rows(inp, rows, seconds, ending=ending_node)
+    pos = r["rows"] * w.N
+    what = "columns" if ending_node else "rows"
     result = {
-        "value": pos / el,
+        "value": pos / r["seconds"],
         "unit": "pair-positions/s",
-        "cores": int(cores),
+        "cores": r["workers"],
         "kind": "oracle",
-        "sample": f"{done} x all {w.N} {'columns' if ending_node else 'rows'} of batch 0 of {w.name} "
-                  f"({pos} pair positions, "
-                  f"{el:.1f} s, float64 numpy, BLAS threads = {cores})",
+        "sample": f"{r['passes']} x all {w.N} {what} of batch 0 of {w.name} ({pos} pair positions, "
+                  f"{r['seconds']:.1f} s wall; float64 numpy on {r['workers']} worker processes, one BLAS "
+                  f"thread each, one contiguous chunk of {what} per worker per pass)",
     }
-    # the same oracle on one thread, for a few seconds (all rows where a pass
-    # is short, else the first 32 rows with their batch's full pair bias)
+    fn = forward_ending_cols if ending_node else forward_rows
     try:
         from threadpoolctl import threadpool_limits
     except Exception:
         return result
-    sub = rows if w.N <= 256 else rows[:32]
-    done1 = 0
+    sub = rows[:8]
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        while True:
-            forward_rows(inp, sub)
-            done1 += 1
-            el1 = time.perf_counter() - t0
-            if el1 >= max(1.0, seconds / 3):
-                break
-    pos1 = done1 * len(sub) * w.N
-    result["single_thread"] = {
-        "value": pos1 / el1, "unit": "pair-positions/s", "cores": 1,
-        "sample": f"{done1} x {len(sub)} {'columns' if ending_node else 'rows'} of batch 0 ({pos1} pair positions, "
-                  f"{el1:.1f} s)",
+        fn(inp, sub)
+        el = time.perf_counter() - t0
+    result["single_process"] = {
+        "value": len(sub) * w.N / el, "unit": "pair-positions/s", "cores": 1,
+        "sample": f"the first {len(sub)} {what} of batch 0 in one oracle call on one thread, with their batch's "
+                  f"LayerNorm and pair bias ({len(sub) * w.N} pair positions, {el:.1f} s)",
     }
     return result
 
@@ -236,7 +226,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true", help="skip timing the training-mode forward")
@@ -269,7 +259,7 @@ def main():
     M = torch.from_numpy(inp["pair_mask"]).to(dev).contiguous()
     out = torch.empty_like(P)
     stream = torch.cuda.current_stream(dev)
-    cfg = B.tri_attn_config(w.D, w.h, B.TRI_ATTN_F32 if w.dtype == "f32" else B.TRI_ATTN_BF16, 1e-5, -1e9, 0.0,
+    cfg = B.tri_attn_config(w.D, w.h, B.TRI_ATTN_F32 if w.dtype == "f32" else B.TRI_ATTN_BF16, 1e-5, -1e9,
                             int(args.ending_node))
     h = B.tri_attn_create(cfg, weights, stream)
     nws = B.tri_attn_workspace_size(h, w.B, w.N)
@@ -306,15 +296,28 @@ def main():
     ms_fwd_ev = timed(fwd, args.steps)
     wall = time.perf_counter() - t0
     ms_fwd = max(ms_fwd_ev, 0.0)
-    # each kernel alone, same stream, for the roofline
-    # (repeated attention calls consume the gate they overwrite: same work, other values)
-    for _ in range(5):
-        k1()
-        k2()
-        k3()
-    ms_k1 = timed(k1, args.steps)
-    ms_k2 = timed(k2, args.steps)
-    ms_k3 = timed(k3, args.steps)
+    # each kernel alone through its stage entry point, for the roofline: one
+    # launch at a time between HIP events on the kernels' stream, each on the
+    # data its predecessors just wrote (the attention kernel consumes the gate
+    # region, so every timed attention or output launch follows fresh
+    # projections, as inside a forward)
+    def per_launch(before, fn, steps):
+        tot = 0.0
+        for _ in range(steps):
+            before()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            tot += e0.elapsed_time(e1)
+        return tot / steps
+
+    nk = max(10, min(args.steps, 200))
+    ms_k1 = per_launch(lambda: None, k1, nk)
+    ms_k2 = per_launch(k1, k2, nk)
+    ms_k3 = per_launch(lambda: (k1(), k2()), k3, nk)
     torch.cuda.synchronize()
     # the same forward replayed from a captured HIP graph (a serving loop's
     # launch path), for comparison; `value` stays the direct forward call
@@ -363,14 +366,7 @@ def main():
         for _ in range(3):
             trn()
         ms_train = timed(trn, max(1, args.steps // 5))
-        # its attention step (a plain FMA kernel): the forward less kernels 1 and 3 timed alone
-        ms_att = max(ms_train - ms_k1 - ms_k3, 1e-6)
-        att_flops = 4.0 * w.B * w.N ** 3 * w.D  # q.k and a'.v, dense
-        train = {"dropout_rate": 0.1, "ms_per_step": ms_train, "ratio_to_inference": ms_train / ms_fwd,
-                 "attention_ms_est": ms_att,
-                 "attention_alu": {"bound": "alu", "achieved": att_flops / (ms_att * 1e-3) / 1e12,
-                                   "peak": PEAK["valu_f32_TFLOPs"], "unit": "TFLOP/s",
-                                   "frac": att_flops / (ms_att * 1e-3) / 1e12 / PEAK["valu_f32_TFLOPs"]}}
+        train = {"dropout_rate": 0.1, "ms_per_step": ms_train, "ratio_to_inference": ms_train / ms_fwd}
     torch.cuda.synchronize()
     B.tri_attn_destroy(h)
 

@@ -66,10 +66,6 @@ typedef struct {
    * (the transcripts' kernels use -1e9). -INFINITY reproduces the module's
    * masked_fill(-inf): such columns give NaN. */
   float mask_fill;
-  /* Testing aid, 0 in normal use: a positive value is added to the per-column
-   * softmax shift, which pushes the kernel into its exact-maximum recovery
-   * path. Results are unchanged. */
-  float shift_slack;
   /* 0: starting-node attention, the variant the transcripts work through
    * (each pair row i attends along its columns: scores q[i,j].k[i,k] plus the
    * bias z[j,k], mask M[j,k]). 1: ending-node attention, the counterpart
@@ -94,18 +90,30 @@ typedef struct {
   const void *w_out, *b_out;              /* [D, D], [D]              */
 } tri_attn_weights;
 
-/* Build a handle: validates cfg, copies and packs the weights into
- * handle-owned device memory on the current device (the caller may free its
- * copies when this returns; the call synchronises `stream`).
- * Supported: D in {64, 128} with d in {16, 32}; otherwise
- * TRI_ATTN_ERR_UNSUPPORTED. On error *out is set to NULL. */
+/* Build a handle: the module's construction from (pair_dim, num_heads) and
+ * its parameters ("Kimi-K2.6 / l2_p6" transcript: the layer list, with
+ * head_dim = pair_dim // num_heads, and the harness that builds the module
+ * once and then calls its forward). Validates cfg, copies and packs the
+ * weights into handle-owned device memory on the current device (the caller
+ * may free its copies when this returns; the call synchronises `stream`).
+ * Supported: D in {64, 128} with d in {16, 32}; other shapes with D % h == 0
+ * return TRI_ATTN_ERR_UNSUPPORTED (each supported shape is its own set of
+ * kernel instantiations with a register and LDS budget of its own; d = 64 and
+ * D = 256 are not built). On error *out is set to NULL. */
 int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void *stream, tri_attn_t *out);
 
-/* Bytes of device workspace tri_attn_forward needs for (B, N). B == 0 or
- * N == 0 needs 0 bytes. */
+/* Bytes of device workspace tri_attn_forward needs for (B, N): the
+ * projections of steps (2)-(4) of the forward listing ("Kimi-K2.6 / l2_p6")
+ * kept between the kernels, never the (B, N, h, N, N) scores. B == 0 or
+ * N == 0 needs 0 bytes. Errors: INVALID_ARG (NULL handle or bytes, negative
+ * sizes), UNSUPPORTED (sizes past the kernels' 32-bit item counts). */
 int tri_attn_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
 
-/* y = forward(pair_repr, pair_mask), enqueued on `stream`, asynchronous.
+/* y = forward(pair_repr, pair_mask): the module's inference forward
+ * ("Kimi-K2.6 / l2_p6" transcript: the forward listing from LayerNorm to the
+ * output projection, dropout the identity in eval mode; "FW-GLM-5-1 / l2_p6":
+ * the restated forward with the bias and mask broadcast over rows i), enqueued
+ * on `stream`, asynchronous.
  *   pair_repr [B, N, N, D] contiguous, config dtype, device memory
  *   pair_mask [B, N, N] uint8, 0 = masked, device memory
  *   out       [B, N, N, D] contiguous, config dtype, device memory
@@ -140,10 +148,11 @@ int tri_attn_forward_train(tri_attn_t h, const void *pair_repr, const uint8_t *p
                            int B, int N, double dropout_rate, uint64_t seed, uint32_t offset, void *workspace,
                            size_t ws_bytes, void *stream);
 
-/* Free everything the handle owns (synchronises the device). NULL is a no-op. */
+/* Free everything the handle owns (synchronises the device). NULL is a no-op.
+ * Returns TRI_ATTN_ERR_HIP if a runtime call fails (everything is still freed). */
 int tri_attn_destroy(tri_attn_t h);
 
-/* Static message for an error code. */
+/* Static message for an error code (never NULL; unknown codes get a generic text). */
 const char *tri_attn_strerror(int code);
 
 /* ---------------------------------------------------------------------------
@@ -179,6 +188,13 @@ typedef struct {
 } tri_attn_workspace_layout;
 
 int tri_attn_get_workspace_layout(tri_attn_t h, int B, int N, tri_attn_workspace_layout *out);
+
+/* Testing aid: add `slack` (finite, >= 0; default 0) to every per-column
+ * softmax shift of later calls on this handle. Softmax does not depend on
+ * the shift, so results are unchanged; a slack above 64 (log2 units) pushes
+ * every work item into the attention kernel's exact-maximum recovery path,
+ * which tests use to exercise it. Errors: INVALID_ARG. */
+int tri_attn_set_shift_slack(tri_attn_t h, float slack);
 
 /* Run only the LayerNorm + projection kernel (arguments as tri_attn_forward). */
 int tri_attn_project(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, int B, int N,

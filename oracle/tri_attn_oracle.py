@@ -78,7 +78,6 @@ __all__ = [
     "row_attention",
     "forward",
     "forward_rows",
-    "flops",
 ]
 
 
@@ -218,8 +217,7 @@ def forward(inp: dict, fill: float = MASK_FILL, eps: float = LN_EPS, capture: Op
     With ``capture`` (a dict), the per-step intermediates of every row are
     stored in it: x, z, and g, q, k, v, a, o stacked over (b, i).
     """
-    P = _f64(inp["pair_repr"])
-    B, N, _, D = P.shape
+    B, N, _, D = np.shape(inp["pair_repr"])
     rows = [(b, i) for b in range(B) for i in range(N)]
     y = forward_rows(inp, rows, fill=fill, eps=eps, capture=capture)
     return y.reshape(B, N, N, D)
@@ -235,9 +233,10 @@ def forward_rows(
     """y[b, i] for the listed rows (b, i) only: (len(rows), N, D) float64.
 
     A row needs the LayerNorm of its own N positions and the pair bias of its
-    batch, which comes from all N*N positions of that batch.
+    batch, which comes from all N*N positions of that batch. Only the batches
+    the rows touch are read (and widened to float64 by layer_norm).
     """
-    P = _f64(inp["pair_repr"])
+    P = inp["pair_repr"]
     M = np.asarray(inp["pair_mask"])
     h = int(inp["num_heads"])
     prm = _params(inp)
@@ -285,12 +284,3 @@ def forward_ending_cols(inp: dict, cols: Sequence[Tuple[int, int]], fill: float 
     """Ending-node y[b, :, j] for the listed columns (b, j): (len(cols), N, D)."""
     return forward_rows(_transposed(inp), cols, fill=fill, eps=eps)
 
-
-def flops(B: int, N: int, D: int, h: int) -> dict:
-    """Multiply-add count x 2 of the dense method (LayerNorm, sigmoid and other
-    elementwise work excluded): projections, attention core, output projection."""
-    P = B * N * N
-    proj = 2 * P * D * (4 * D + h)
-    core = 4 * B * N ** 3 * D
-    out = 2 * P * D * D
-    return {"projection": proj, "attention": core, "output": out, "total": proj + core + out}

@@ -131,7 +131,7 @@ def forward_train_rows(
 ):
     """(y (len(rows), N, D), lse (len(rows), h, N)) float64 for the listed rows.
     With ``capture``, the per-row s, a, keep, a_drop and lse stacked over rows."""
-    P = O._f64(inp["pair_repr"])
+    P = inp["pair_repr"]  # widened per batch by layer_norm
     M = np.asarray(inp["pair_mask"])
     h = int(inp["num_heads"])
     prm = O._params(inp)

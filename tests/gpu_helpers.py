@@ -35,9 +35,11 @@ class Gpu:
         self.P = torch.from_numpy(P).to(self.dev).to(self.dt).contiguous()
         self.M = torch.from_numpy(inp["pair_mask"]).to(self.dev).contiguous()
         code = B.TRI_ATTN_F32 if inp["dtype"] == "f32" else B.TRI_ATTN_BF16
-        self.cfg = B.tri_attn_config(self.D, self.h, code, 1e-5, fill if math.isfinite(fill) else -math.inf, slack,
+        self.cfg = B.tri_attn_config(self.D, self.h, code, 1e-5, fill if math.isfinite(fill) else -math.inf,
                                      int(ending))
         self.handle = B.tri_attn_create(self.cfg, self.w, torch.cuda.current_stream())
+        if slack:
+            B.tri_attn_set_shift_slack(self.handle, slack)
         self.ws_bytes = B.tri_attn_workspace_size(self.handle, self.B, self.N)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.dev)
 

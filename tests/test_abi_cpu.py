@@ -67,7 +67,7 @@ def test_strerror():
 
 
 def _create_rc(**kw):
-    base = dict(pair_dim=128, num_heads=4, dtype=B.TRI_ATTN_BF16, ln_eps=1e-5, mask_fill=-1e9, shift_slack=0.0)
+    base = dict(pair_dim=128, num_heads=4, dtype=B.TRI_ATTN_BF16, ln_eps=1e-5, mask_fill=-1e9)
     base.update(kw)
     cfg = B.tri_attn_config(**base)
     w = B.tri_attn_weights(**{k: 16 for k in B.WEIGHT_FIELDS})  # never dereferenced: rejected first
@@ -84,7 +84,6 @@ def _create_rc(**kw):
     (dict(ln_eps=math.nan), B.TRI_ATTN_ERR_INVALID_ARG),
     (dict(mask_fill=-1.0), B.TRI_ATTN_ERR_INVALID_ARG),              # not a masking value
     (dict(mask_fill=math.nan), B.TRI_ATTN_ERR_INVALID_ARG),
-    (dict(shift_slack=-1.0), B.TRI_ATTN_ERR_INVALID_ARG),
     (dict(ending_node=2), B.TRI_ATTN_ERR_INVALID_ARG),               # 0 or 1 only
     (dict(ending_node=-1), B.TRI_ATTN_ERR_INVALID_ARG),
     (dict(pair_dim=96, num_heads=3), B.TRI_ATTN_ERR_UNSUPPORTED),     # d = 32 but D = 96
@@ -100,7 +99,7 @@ def test_create_rejects_bad_config(kw, code):
 def test_create_null_arguments():
     h = ctypes.c_void_p()
     assert B.raw_call("tri_attn_create", None, None, None, ctypes.byref(h)) == B.TRI_ATTN_ERR_INVALID_ARG
-    cfg = B.tri_attn_config(128, 4, B.TRI_ATTN_F32, 1e-5, -1e9, 0.0)
+    cfg = B.tri_attn_config(128, 4, B.TRI_ATTN_F32, 1e-5, -1e9)
     assert B.raw_call("tri_attn_create", ctypes.byref(cfg), None, None, ctypes.byref(h)) == B.TRI_ATTN_ERR_INVALID_ARG
     w = B.tri_attn_weights(**{k: 16 for k in B.WEIGHT_FIELDS})
     w.b_out = None

@@ -56,9 +56,10 @@ def test_attention_roofline_on_valid_pairs():
     mask = np.zeros((4, 512, 512), np.uint8)
     mask[:, :100, :200] = 1
     r = bench.roofline_of("k2_attention", w, m, 1.0, mask)
-    assert r["achieved_valid_pairs"] == pytest.approx(4 * 512 * 128 * (4 * 100 * 200) / 1e-3 / 1e12)
-    assert r["frac_valid_pairs"] == pytest.approx(r["achieved_valid_pairs"] / 2500.0)
-    assert "achieved_valid_pairs" not in bench.roofline_of("k1_ln_proj", w, m, 1.0, mask)
+    assert r["achieved"] == pytest.approx(4 * 512 * 128 * (4 * 100 * 200) / 1e-3 / 1e12)
+    assert r["frac"] == pytest.approx(r["achieved"] / 2500.0)
+    assert r["achieved_dense"] == pytest.approx(m["k2_attention"]["flops"] / 1e-3 / 1e12)
+    assert "achieved_dense" not in bench.roofline_of("k1_ln_proj", w, m, 1.0, mask)
 
 
 def test_split_products_ceiling():

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 from gpu_helpers import TOL, Gpu, log, max_err, y_numpy
+from oracle import pool
 from oracle import tri_attn_oracle as O
 from oracle import tri_attn_train_oracle as TO
 from triangular_pair_attention_amd import binding as B
@@ -77,6 +78,56 @@ def test_train_workload(k):
     w = WORKLOADS[k]
     log(f"train {w.name}")
     check_train(make_inputs(w), 0.15, seed=12345, offset=0, what=f"train {w.name}")
+
+
+def check_train_pool(inp, rows, rate, seed, offset, what):
+    """The training forward (y and lse) on the listed rows against the
+    training oracle, the rows spread over host worker processes."""
+    dtype = inp["dtype"]
+    y, lse, _ = run_train(inp, rate, seed, offset)
+    r = pool.compare_rows(inp, y.astype(np.float32), rows, train={"rate": rate, "seed": seed, "offset": offset},
+                          lse=lse.astype(np.float32))
+    log(f"{what}: y max abs err {r['y']['max_abs_err']:.3e} at {r['y']['where']}; lse max abs err "
+        f"{r['lse']['max_abs_err']:.3e} on columns with a valid key, max rel err "
+        f"{r['lse_dead_rel']['max_abs_err']:.1e} on fully masked ones")
+    assert r["y"]["same_nan_pattern"] and r["lse"]["same_nan_pattern"]
+    assert r["y"]["max_abs_err"] <= TOL[dtype]
+    assert r["lse"]["max_abs_err"] <= LSE_TOL[dtype]
+    assert r["lse_dead_rel"]["max_abs_err"] <= 1e-6
+
+
+def test_train_workload4_full():
+    """B=1, N=384, h=4 (d = 32): every row, so the attention kernel's second
+    256-column query block of each row is compared too."""
+    w = WORKLOADS[4]
+    log(f"train {w.name}: all rows (worker processes)")
+    check_train_pool(make_inputs(w), [(0, i) for i in range(w.N)], 0.1, 777, 3, f"train {w.name}")
+
+
+def test_train_workload5_sampled_rows():
+    """B=4, N=512, h=8 (d = 16): 40 rows spread over the four batches (first,
+    last valid, first padded and last rows of each, and random ones), all
+    columns and heads of each."""
+    w = WORKLOADS[5]
+    inp = make_inputs(w)
+    M = inp["pair_mask"]
+    rng = np.random.default_rng(3)
+    rows = []
+    for b in range(w.B):
+        L = int(M[b].diagonal().sum())
+        cand = {0, L - 1, min(L, w.N - 1), w.N - 1} | {int(x) for x in rng.integers(0, w.N, 6)}
+        rows += [(b, i) for i in sorted(cand)]
+    log(f"train {w.name}: {len(rows)} sampled rows (worker processes)")
+    check_train_pool(inp, rows, 0.1, 2**40 + 17, 0, f"train {w.name} sampled")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_train_ragged_300(dtype):
+    """N = 300, padded to 270, head size 32: two 256-column query blocks per
+    row (the second ragged), dropout 0.2, every row."""
+    w = Workload("train300", 1, 300, 128, 4, dtype, ("pad", 270), seed=75)
+    log(f"train N=300 {dtype}")
+    check_train_pool(make_inputs(w), [(0, i) for i in range(w.N)], 0.2, 5, 1, f"train N=300 {dtype}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

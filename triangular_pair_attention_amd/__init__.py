@@ -38,7 +38,7 @@ class TriangularAttention:
     """
 
     def __init__(self, weights: dict, num_heads: int, ln_eps: float = 1e-5, mask_fill: float = -1e9,
-                 shift_slack: float = 0.0, ending_node: bool = False):
+                 ending_node: bool = False):
         import torch
 
         w0 = weights["w_query"]
@@ -58,7 +58,7 @@ class TriangularAttention:
                 raise ValueError(f"weight {k} must be contiguous {w0.dtype} on {w0.device}")
         cfg = tri_attn_config(pair_dim=self.D, num_heads=self.h, dtype=code, ln_eps=ln_eps,
                               mask_fill=mask_fill if math.isfinite(mask_fill) else -math.inf,
-                              shift_slack=shift_slack, ending_node=int(bool(ending_node)))
+                              ending_node=int(bool(ending_node)))
         self._weights = weights  # kept alive until create has copied them
         self.handle = tri_attn_create(cfg, weights, torch.cuda.current_stream(self.device))
         self._ws = None

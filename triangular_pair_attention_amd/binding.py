@@ -37,7 +37,6 @@ class tri_attn_config(ctypes.Structure):
         ("dtype", ctypes.c_int),
         ("ln_eps", ctypes.c_float),
         ("mask_fill", ctypes.c_float),
-        ("shift_slack", ctypes.c_float),
         ("ending_node", ctypes.c_int),
     ]
 
@@ -82,11 +81,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tri_attn_project.argtypes = [vp, vp, vp, i, i, vp, sz, vp]
     lib.tri_attn_attend.argtypes = [vp, i, i, vp, sz, vp]
     lib.tri_attn_output.argtypes = [vp, vp, i, i, vp, sz, vp]
+    lib.tri_attn_set_shift_slack.argtypes = [vp, ctypes.c_float]
     lib.tri_attn_forward_train.argtypes = [vp, vp, vp, vp, vp, i, i, ctypes.c_double, ctypes.c_uint64,
                                            ctypes.c_uint32, vp, sz, vp]
     for name in ("tri_attn_create", "tri_attn_workspace_size", "tri_attn_forward", "tri_attn_destroy",
                  "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend",
-                 "tri_attn_output", "tri_attn_forward_train"):
+                 "tri_attn_output", "tri_attn_forward_train", "tri_attn_set_shift_slack"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -183,6 +183,10 @@ def tri_attn_attend(handle: int, B: int, N: int, workspace, ws_bytes: int, strea
 def tri_attn_output(handle: int, out, B: int, N: int, workspace, ws_bytes: int, stream=None) -> None:
     _check(load_library().tri_attn_output(handle, _ptr(out), B, N, _ptr(workspace), ws_bytes, _stream(stream)),
            "tri_attn_output")
+
+
+def tri_attn_set_shift_slack(handle: int, slack: float) -> None:
+    _check(load_library().tri_attn_set_shift_slack(handle, float(slack)), "tri_attn_set_shift_slack")
 
 
 def raw_call(name: str, *args) -> int:

@@ -13,6 +13,7 @@
 
 struct tri_attn {
   tri_attn_config cfg;
+  float shift_slack;  // testing aid (tri_attn_set_shift_slack), 0 in normal use
   int D, h, dh, elem;
   int device;
   int k1_grid;     // persistent grid of kernel 1 (resident workgroups)
@@ -74,7 +75,6 @@ static int check_config(const tri_attn_config *cfg) {
   if (!(cfg->ln_eps > 0.f) || !std::isfinite(cfg->ln_eps)) return TRI_ATTN_ERR_INVALID_ARG;
   const float f = cfg->mask_fill;
   if (std::isnan(f) || !(f == -INFINITY || (std::isfinite(f) && f <= -1e4f))) return TRI_ATTN_ERR_INVALID_ARG;
-  if (!std::isfinite(cfg->shift_slack) || cfg->shift_slack < 0.f) return TRI_ATTN_ERR_INVALID_ARG;
   if (cfg->ending_node != 0 && cfg->ending_node != 1) return TRI_ATTN_ERR_INVALID_ARG;
   if (!supported(cfg->pair_dim, cfg->pair_dim / cfg->num_heads)) return TRI_ATTN_ERR_UNSUPPORTED;
   return TRI_ATTN_OK;
@@ -92,6 +92,7 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
   tri_attn *t = new (std::nothrow) tri_attn();
   if (!t) return TRI_ATTN_ERR_OOM;
   t->cfg = *cfg;
+  t->shift_slack = 0.f;
   t->D = cfg->pair_dim;
   t->h = cfg->num_heads;
   t->dh = t->D / t->h;
@@ -260,7 +261,7 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a2.q = a1.q, a2.k = a1.k, a2.vt = a1.vt, a2.g = a1.g;
   a2.zm = a1.zm, a2.zmax = a1.zmax, a2.kmax = a1.kmax, a2.vsum = a1.vsum;
   a2.mask_fill = t->cfg.mask_fill;
-  a2.shift_slack = t->cfg.shift_slack;
+  a2.shift_slack = t->shift_slack;
   a2.B = B, a2.N = N, a2.Np = L.Np, a2.nchunk = L.nchunk;
   a2.items = k2_items(t->cfg.dtype, D, t->dh, B, N);
   // persistent workgroups; with more items than that, a multiple of 8 so that
@@ -324,6 +325,12 @@ int tri_attn_attend(tri_attn_t t, int B, int N, void *workspace, size_t ws_bytes
 
 int tri_attn_output(tri_attn_t t, void *out, int B, int N, void *workspace, size_t ws_bytes, void *stream) {
   return run(t, nullptr, nullptr, out, B, N, workspace, ws_bytes, stream, 4);
+}
+
+int tri_attn_set_shift_slack(tri_attn_t t, float slack) {
+  if (!t || !std::isfinite(slack) || slack < 0.f) return TRI_ATTN_ERR_INVALID_ARG;
+  t->shift_slack = slack;
+  return TRI_ATTN_OK;
 }
 
 int tri_attn_destroy(tri_attn_t t) {
