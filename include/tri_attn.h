@@ -148,6 +148,28 @@ int tri_attn_forward_train(tri_attn_t h, const void *pair_repr, const uint8_t *p
                            int B, int N, double dropout_rate, uint64_t seed, uint32_t offset, void *workspace,
                            size_t ws_bytes, void *stream);
 
+/* Largest workspace tri_attn_forward_noalloc can use: the size of the static
+ * device array that holds it (256 MiB per GPU). */
+#define TRI_ATTN_NOALLOC_MAX_BYTES ((size_t)256 << 20)
+
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): tri_attn_forward
+ * with its workspace in a static device array of TRI_ATTN_NOALLOC_MAX_BYTES
+ * that the library holds, one copy per GPU, until the process ends. Arguments
+ * as tri_attn_forward without the workspace; same kernels, same result bit for
+ * bit. Allocates nothing: no hipMalloc, hipFree or allocating library call.
+ * Errors as tri_attn_forward, and TRI_ATTN_ERR_WORKSPACE when
+ * tri_attn_workspace_size(h, B, N) exceeds TRI_ATTN_NOALLOC_MAX_BYTES (B = 4,
+ * N = 512, D = 128 in bf16 needs about 1.1 GB: use tri_attn_forward there),
+ * TRI_ATTN_ERR_HIP if the array's device address could not be found when the
+ * handle was created. Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (from other streams, handles or threads)
+ * race and corrupt each other's results; order them on one stream or
+ * synchronise between them. The forward writes every workspace byte before
+ * it reads it, so nothing is cleared between calls. */
+int tri_attn_forward_noalloc(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, void *out, int B,
+                             int N, void *stream);
+
 /* Free everything the handle owns (synchronises the device). NULL is a no-op.
  * Returns TRI_ATTN_ERR_HIP if a runtime call fails (everything is still freed). */
 int tri_attn_destroy(tri_attn_t h);

@@ -82,11 +82,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tri_attn_attend.argtypes = [vp, i, i, vp, sz, vp]
     lib.tri_attn_output.argtypes = [vp, vp, i, i, vp, sz, vp]
     lib.tri_attn_set_shift_slack.argtypes = [vp, ctypes.c_float]
+    lib.tri_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, i, i, vp]
     lib.tri_attn_forward_train.argtypes = [vp, vp, vp, vp, vp, i, i, ctypes.c_double, ctypes.c_uint64,
                                            ctypes.c_uint32, vp, sz, vp]
     for name in ("tri_attn_create", "tri_attn_workspace_size", "tri_attn_forward", "tri_attn_destroy",
                  "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend",
-                 "tri_attn_output", "tri_attn_forward_train", "tri_attn_set_shift_slack"):
+                 "tri_attn_output", "tri_attn_forward_train", "tri_attn_set_shift_slack",
+                 "tri_attn_forward_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -149,6 +151,11 @@ def tri_attn_forward(handle: int, pair_repr, pair_mask, out, B: int, N: int, wor
                      stream=None) -> None:
     _check(load_library().tri_attn_forward(handle, _ptr(pair_repr), _ptr(pair_mask), _ptr(out), B, N,
                                            _ptr(workspace), ws_bytes, _stream(stream)), "tri_attn_forward")
+
+
+def tri_attn_forward_noalloc(handle: int, pair_repr, pair_mask, out, B: int, N: int, stream=None) -> None:
+    _check(load_library().tri_attn_forward_noalloc(handle, _ptr(pair_repr), _ptr(pair_mask), _ptr(out), B, N,
+                                                   _stream(stream)), "tri_attn_forward_noalloc")
 
 
 def tri_attn_forward_train(handle: int, pair_repr, pair_mask, out, lse, B: int, N: int, dropout_rate: float,

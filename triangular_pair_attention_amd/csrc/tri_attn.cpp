@@ -24,6 +24,8 @@ struct tri_attn {
   void *wfrag;     // Wq; Wk; Wv; Wg, then Wo, in fragment order
   void *wsplit;    // float32 handles: the same five matrices as three bf16 planes in fragment order
   size_t wpack_bytes, vecs_bytes, wfrag_bytes, wsplit_plane;
+  void *scratch;   // this device's static workspace array (tri_attn_forward_noalloc)
+  int scratch_rc;  // status of its address lookup at creation
 };
 
 namespace tpa {
@@ -113,6 +115,8 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
                                                  : k1_blocks_per_cu(cfg->dtype, t->D, t->dh));
   t->k2_grid = cus * k2_blocks_per_cu(cfg->dtype, t->D, t->dh);
   t->k3_grid = cus * k3_blocks_per_cu(cfg->dtype, t->D);
+  // the static workspace array's address on this device, looked up once per device
+  t->scratch_rc = scratch_address(t->device, &t->scratch);
 
   t->wpack_bytes = (size_t)(4 * D + 16) * D * e;
   t->vecs_bytes = (size_t)4 * D * e + (size_t)D * D * e;
@@ -295,6 +299,16 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
 int tri_attn_forward(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
                      void *workspace, size_t ws_bytes, void *stream) {
   return run(t, pair_repr, pair_mask, out, B, N, workspace, ws_bytes, stream, 7);
+}
+
+int tri_attn_forward_noalloc(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
+                             void *stream) {
+  size_t need = 0;
+  const int rc = tri_attn_workspace_size(t, B, N, &need);
+  if (rc) return rc;
+  if (need > TRI_ATTN_NOALLOC_MAX_BYTES) return TRI_ATTN_ERR_WORKSPACE;
+  if (t->scratch_rc || !t->scratch) return TRI_ATTN_ERR_HIP;
+  return run(t, pair_repr, pair_mask, out, B, N, t->scratch, TRI_ATTN_NOALLOC_MAX_BYTES, stream, 7);
 }
 
 int tri_attn_forward_train(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, float *lse,

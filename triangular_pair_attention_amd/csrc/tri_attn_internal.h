@@ -87,5 +87,8 @@ int k1_blocks_per_cu(int dtype, int D, int dh);  // resident workgroups of kerne
 hipError_t launch_k1_split(int D, int dh, const K1Args &a, int grid, hipStream_t s);
 int k1_split_blocks_per_cu(int D, int dh);
 bool supported(int D, int dh);
+// Device address of this GPU's static workspace array (noalloc.hip), looked up
+// once per device; `device` must be current. Returns a TRI_ATTN_* code.
+int scratch_address(int device, void **ptr);
 
 }  // namespace tpa
