@@ -148,6 +148,44 @@ int tri_attn_forward_train(tri_attn_t h, const void *pair_repr, const uint8_t *p
                            int B, int N, double dropout_rate, uint64_t seed, uint32_t offset, void *workspace,
                            size_t ws_bytes, void *stream);
 
+/* Gradients of the training-mode forward, float32 DEVICE pointers in the
+ * shapes of the inputs they belong to (every one must be given). */
+typedef struct {
+  float *d_pair_repr;                      /* [B, N, N, D]  */
+  float *d_ln_weight, *d_ln_bias;          /* [D]           */
+  float *d_w_query, *d_w_key, *d_w_value;  /* [D, D]        */
+  float *d_w_gate, *d_b_gate;              /* [D, D], [D]   */
+  float *d_w_bias_proj;                    /* [h, D]        */
+  float *d_w_out, *d_b_out;                /* [D, D], [D]   */
+} tri_attn_grads;
+
+/* Bytes of device workspace tri_attn_backward_train needs for (B, N): the
+ * forward's intermediates in float32 (LayerNorm output, the five
+ * projections, the attention output and row statistics), their gradients and
+ * the partial sums of the weight gradients; about 4(5D + h) * B * N^2 * 2
+ * bytes. B == 0 or N == 0 needs 0 bytes. */
+int tri_attn_backward_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
+
+/* Backward of tri_attn_forward_train: with dy = dL/dy [B, N, N, D] (config
+ * dtype, device), writes dL/d(pair_repr) and dL/d(every parameter) for the
+ * same pair_repr, pair_mask, dropout_rate, seed and offset (hence the same
+ * dropout decisions) into `grads`. It follows the forward's steps in reverse
+ * (the forward listing of "Kimi-K2.6 / l2_p6"; dropout after the softmax as
+ * restated in "FW-GLM-5-1 / l2_p6"): the output projection and the gate, the
+ * value sum, dropout, the softmax (whose row sum of a * da is do . o), the
+ * masked scores (masked entries pass no gradient: the fill is a constant),
+ * the pair bias (summed over the rows i that share it), the projections and
+ * the LayerNorm. Everything is recomputed from the inputs in float32 arithmetic,
+ * whatever the config dtype, so nothing from the forward call is needed.
+ * Sums over positions are split into fixed chunks and added in a fixed order:
+ * deterministic, no atomics. Asynchronous on `stream`; pointers borrowed until
+ * the stream work completes. Errors: INVALID_ARG (NULL pointers, sizes, rate
+ * outside [0, 1)), WORKSPACE, HIP, UNSUPPORTED (ending-node handles: not
+ * built). B == 0 or N == 0 is a no-op. */
+int tri_attn_backward_train(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, const void *dy, int B,
+                            int N, double dropout_rate, uint64_t seed, uint32_t offset,
+                            const tri_attn_grads *grads, void *workspace, size_t ws_bytes, void *stream);
+
 /* Largest workspace tri_attn_forward_noalloc can use: the size of the static
  * device array that holds it (256 MiB per GPU). */
 #define TRI_ATTN_NOALLOC_MAX_BYTES ((size_t)256 << 20)

@@ -36,7 +36,7 @@ def test_struct_layouts_match_header(tmp_path):
     import shutil
 
     structs = (("tri_attn_config", B.tri_attn_config), ("tri_attn_weights", B.tri_attn_weights),
-               ("tri_attn_workspace_layout", B.tri_attn_workspace_layout))
+               ("tri_attn_workspace_layout", B.tri_attn_workspace_layout), ("tri_attn_grads", B.tri_attn_grads))
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no C compiler")
@@ -117,6 +117,10 @@ def test_null_handle_paths():
     assert B.raw_call("tri_attn_output", None, 1, 1, 8, 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
     assert B.raw_call("tri_attn_forward_train", None, 1, 1, 1, None, 1, 8, ctypes.c_double(0.1), ctypes.c_uint64(1),
                       ctypes.c_uint32(0), 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
+    g = B.tri_attn_grads()
+    assert B.raw_call("tri_attn_backward_workspace_size", None, 1, 8, ctypes.byref(n)) == B.TRI_ATTN_ERR_INVALID_ARG
+    assert B.raw_call("tri_attn_backward_train", None, 1, 1, 1, 1, 8, ctypes.c_double(0.1), ctypes.c_uint64(1),
+                      ctypes.c_uint32(0), ctypes.byref(g), 1, 1 << 20, None) == B.TRI_ATTN_ERR_INVALID_ARG
     lay = B.tri_attn_workspace_layout()
     assert B.raw_call("tri_attn_get_workspace_layout", None, 1, 8, ctypes.byref(lay)) == B.TRI_ATTN_ERR_INVALID_ARG
     assert B.raw_call("tri_attn_destroy", None) == B.TRI_ATTN_OK

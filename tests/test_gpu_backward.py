@@ -1,0 +1,142 @@
+"""GPU parity of the training-mode backward (tri_attn_backward_train) with
+the backward oracle (hand back-propagation in float64, itself pinned by
+finite differences and autograd): dL/d(pair_repr) and dL/d(every parameter)
+for the same dropout decisions.
+
+Tolerance: the GPU computes every step in float32 from the same inputs, so
+each gradient tensor must agree with the oracle's to 1e-3 of its largest
+magnitude (the longest float32 sums run over all B*N*N positions; their
+rounding error grows like sqrt(B*N*N) * 2^-24 relative, about 2e-5 at
+B*N*N = 65536, well inside the bound)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import Gpu, log
+from oracle import tri_attn_backward_oracle as BO
+from triangular_pair_attention_amd import binding as B
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-3
+SHAPE = {"d_pair_repr": "pair_repr", "d_ln_weight": "ln_weight", "d_ln_bias": "ln_bias", "d_w_query": "w_query",
+         "d_w_key": "w_key", "d_w_value": "w_value", "d_w_gate": "w_gate", "d_b_gate": "b_gate",
+         "d_w_bias_proj": "w_bias_proj", "d_w_out": "w_out", "d_b_out": "b_out"}
+
+
+def run_backward(inp, dy, rate, seed, offset, fill=-1e9):
+    g = Gpu(inp, fill=fill)
+    try:
+        grads = {k: torch.zeros(np.shape(inp[v]), dtype=torch.float32, device=g.dev) for k, v in SHAPE.items()}
+        n = B.tri_attn_backward_workspace_size(g.handle, g.B, g.N)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=g.dev)
+        dyt = torch.from_numpy(dy).to(g.dev).to(g.dt).contiguous()
+        B.tri_attn_backward_train(g.handle, g.P, g.M, dyt, g.B, g.N, rate, seed, offset, grads, ws, n,
+                                  torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return {k: v.double().cpu().numpy() for k, v in grads.items()}
+    finally:
+        g.close()
+
+
+def make_dy(inp, seed):
+    rng = np.random.default_rng(seed)
+    dy = rng.standard_normal(np.shape(inp["pair_repr"])).astype(np.float32)
+    if inp["dtype"] == "bf16":
+        from workloads import round_to_bf16
+        dy = round_to_bf16(dy)
+    return dy
+
+
+def check_backward(inp, rate, seed, offset, what, fill=-1e9):
+    dy = make_dy(inp, 99)
+    got = run_backward(inp, dy, rate, seed, offset, fill)
+    ref = BO.backward_train(inp, dy.astype(np.float64), rate, seed, offset, fill=fill)
+    worst = 0.0
+    for k in SHAPE:
+        r, gk = ref[k], got[k]
+        assert r.shape == gk.shape, k
+        fin = np.isfinite(r)
+        assert (np.isfinite(gk) == fin).all(), f"{what} {k}: NaN pattern differs"
+        scale = float(np.abs(r[fin]).max()) if fin.any() else 0.0
+        err = float(np.abs(gk[fin] - r[fin]).max()) if fin.any() else 0.0
+        rel = err / scale if scale > 0 else err
+        worst = max(worst, rel)
+        log(f"{what} {k}: max abs err {err:.3e}, max |ref| {scale:.3e}, relative {rel:.2e}")
+        assert err <= RTOL * scale + 1e-12, f"{what} {k}: error {err} > {RTOL} * {scale}"
+    return worst
+
+
+SHAPES = [((2, 20, 64, 4), ("bernoulli", 0.8)), ((1, 33, 128, 4), ("pad", 25)), ((1, 40, 128, 8), ("pad", 31)),
+          ((2, 17, 64, 2), ("bernoulli", 0.6)), ((1, 70, 128, 4), ("bernoulli", 0.9))]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,mask", SHAPES, ids=lambda s: str(s))
+@pytest.mark.parametrize("rate", [0.0, 0.3])
+def test_backward_small(shape, mask, dtype, rate):
+    """Small and ragged shapes, both head sizes, fully masked columns (padding)."""
+    Bn, N, D, h = shape
+    inp = make_inputs(Workload("bwd", Bn, N, D, h, dtype, mask, seed=81 + N))
+    check_backward(inp, rate, seed=2**35 + 3, offset=5, what=f"backward {dtype} {shape} {mask} rate {rate}")
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_backward_workload(k):
+    """Workloads 1-3 (B=2 N=32 D=64 h=4 f32; B=1 N=128 D=128 h=4 f32; B=1
+    N=256 D=128 h=4 bf16 with 16 padded residues), dropout 0.1."""
+    w = WORKLOADS[k]
+    log(f"backward {w.name}")
+    check_backward(make_inputs(w), 0.1, seed=4242, offset=1, what=f"backward {w.name}")
+
+
+def test_backward_minus_inf_fill():
+    """-inf fill on a mask where every query column keeps a valid key."""
+    inp = make_inputs(Workload("bwd_ninf", 1, 24, 64, 4, "f32", ("bernoulli", 0.7), seed=83))
+    check_backward(inp, 0.2, seed=7, offset=0, what="backward -inf fill", fill=-math.inf)
+
+
+def test_backward_deterministic():
+    """Two calls give the same bits (fixed-order sums, no atomics)."""
+    inp = make_inputs(Workload("bwd_det", 1, 40, 128, 4, "bf16", ("pad", 33), seed=84))
+    dy = make_dy(inp, 5)
+    a = run_backward(inp, dy, 0.2, 9, 0)
+    b = run_backward(inp, dy, 0.2, 9, 0)
+    for k in SHAPE:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_argument_errors():
+    inp = make_inputs(Workload("bwd_err", 1, 8, 64, 4, "f32", ("ones",), seed=85))
+    g = Gpu(inp)
+    try:
+        n = B.tri_attn_backward_workspace_size(g.handle, g.B, g.N)
+        ws = torch.empty(n, dtype=torch.uint8, device=g.dev)
+        grads = {k: torch.zeros(np.shape(inp[v]), dtype=torch.float32, device=g.dev) for k, v in SHAPE.items()}
+        dy = torch.zeros_like(g.P)
+        for rate in (1.0, -0.5, float("nan")):
+            with pytest.raises(B.TriAttnError) as e:
+                B.tri_attn_backward_train(g.handle, g.P, g.M, dy, g.B, g.N, rate, 1, 0, grads, ws, n)
+            assert e.value.code == B.TRI_ATTN_ERR_INVALID_ARG
+        with pytest.raises(B.TriAttnError) as e:
+            B.tri_attn_backward_train(g.handle, g.P, g.M, dy, g.B, g.N, 0.1, 1, 0, grads, ws, n - 1)
+        assert e.value.code == B.TRI_ATTN_ERR_WORKSPACE
+        bad = dict(grads)
+        bad["d_w_out"] = 0
+        with pytest.raises(B.TriAttnError) as e:
+            B.tri_attn_backward_train(g.handle, g.P, g.M, dy, g.B, g.N, 0.1, 1, 0, bad, ws, n)
+        assert e.value.code == B.TRI_ATTN_ERR_INVALID_ARG
+        B.tri_attn_backward_train(g.handle, 0, 0, 0, 0, g.N, 0.1, 1, 0, grads, 0, 0)  # B == 0: no-op
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+    e = Gpu(inp, ending=True)
+    try:
+        with pytest.raises(B.TriAttnError) as err:
+            B.tri_attn_backward_train(e.handle, e.P, e.M, torch.zeros_like(e.P), e.B, e.N, 0.1, 1, 0, grads, ws, n)
+        assert err.value.code == B.TRI_ATTN_ERR_UNSUPPORTED
+    finally:
+        e.close()

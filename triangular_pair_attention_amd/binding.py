@@ -45,6 +45,14 @@ class tri_attn_weights(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in WEIGHT_FIELDS]
 
 
+GRAD_FIELDS = ("d_pair_repr", "d_ln_weight", "d_ln_bias", "d_w_query", "d_w_key", "d_w_value", "d_w_gate",
+               "d_b_gate", "d_w_bias_proj", "d_w_out", "d_b_out")
+
+
+class tri_attn_grads(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in GRAD_FIELDS]
+
+
 class tri_attn_workspace_layout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_size_t) for name in ("q", "k", "vt", "g", "zm", "zmax", "kmax", "vsum", "total")] + [
         ("padded_n", ctypes.c_int)
@@ -82,13 +90,16 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tri_attn_attend.argtypes = [vp, i, i, vp, sz, vp]
     lib.tri_attn_output.argtypes = [vp, vp, i, i, vp, sz, vp]
     lib.tri_attn_set_shift_slack.argtypes = [vp, ctypes.c_float]
+    lib.tri_attn_backward_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
+    lib.tri_attn_backward_train.argtypes = [vp, vp, vp, vp, i, i, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint32,
+                                            ctypes.POINTER(tri_attn_grads), vp, sz, vp]
     lib.tri_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, i, i, vp]
     lib.tri_attn_forward_train.argtypes = [vp, vp, vp, vp, vp, i, i, ctypes.c_double, ctypes.c_uint64,
                                            ctypes.c_uint32, vp, sz, vp]
     for name in ("tri_attn_create", "tri_attn_workspace_size", "tri_attn_forward", "tri_attn_destroy",
                  "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend",
                  "tri_attn_output", "tri_attn_forward_train", "tri_attn_set_shift_slack",
-                 "tri_attn_forward_noalloc"):
+                 "tri_attn_forward_noalloc", "tri_attn_backward_workspace_size", "tri_attn_backward_train"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -194,6 +205,23 @@ def tri_attn_output(handle: int, out, B: int, N: int, workspace, ws_bytes: int, 
 
 def tri_attn_set_shift_slack(handle: int, slack: float) -> None:
     _check(load_library().tri_attn_set_shift_slack(handle, float(slack)), "tri_attn_set_shift_slack")
+
+
+def tri_attn_backward_workspace_size(handle: int, B: int, N: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().tri_attn_backward_workspace_size(handle, B, N, ctypes.byref(n)),
+           "tri_attn_backward_workspace_size")
+    return n.value
+
+
+def tri_attn_backward_train(handle: int, pair_repr, pair_mask, dy, B: int, N: int, dropout_rate: float, seed: int,
+                            offset: int, grads: dict, workspace, ws_bytes: int, stream=None) -> None:
+    """grads: dict name -> float32 device pointer (see GRAD_FIELDS)."""
+    g = tri_attn_grads(**{k: _ptr(grads[k]) for k in GRAD_FIELDS})
+    _check(load_library().tri_attn_backward_train(handle, _ptr(pair_repr), _ptr(pair_mask), _ptr(dy), B, N,
+                                                  float(dropout_rate), int(seed), int(offset), ctypes.byref(g),
+                                                  _ptr(workspace), ws_bytes, _stream(stream)),
+           "tri_attn_backward_train")
 
 
 def raw_call(name: str, *args) -> int:

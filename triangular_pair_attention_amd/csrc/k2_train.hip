@@ -30,25 +30,6 @@
 
 namespace tpa {
 
-__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
-    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
-  return c;
-}
-
-template <typename T>
-__device__ __forceinline__ float ld_elem(const void *p, size_t i) {
-  if constexpr (is_bf16<T>::value)
-    return bf2f(reinterpret_cast<const uint16_t *>(p)[i]);
-  else
-    return reinterpret_cast<const float *>(p)[i];
-}
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k2_train(K2Args a, K2TrainArgs tr) {

@@ -328,6 +328,43 @@ int tri_attn_forward_train(tri_attn_t t, const void *pair_repr, const uint8_t *p
   return run(t, pair_repr, pair_mask, out, B, N, workspace, ws_bytes, stream, 7, &tr);
 }
 
+int tri_attn_backward_workspace_size(tri_attn_t t, int B, int N, size_t *bytes) {
+  if (!bytes) return TRI_ATTN_ERR_INVALID_ARG;
+  const int rc = check_sizes(t, B, N);
+  if (rc) return rc;
+  *bytes = (B == 0 || N == 0) ? 0 : bwd_workspace_bytes(B, N, t->D, t->h);
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_backward_train(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, const void *dy, int B,
+                            int N, double dropout_rate, uint64_t seed, uint32_t offset, const tri_attn_grads *grads,
+                            void *workspace, size_t ws_bytes, void *stream) {
+  if (!t) return TRI_ATTN_ERR_INVALID_ARG;
+  if (!(dropout_rate >= 0.0 && dropout_rate < 1.0)) return TRI_ATTN_ERR_INVALID_ARG;
+  int rc = check_sizes(t, B, N);
+  if (rc) return rc;
+  if (t->cfg.ending_node) return TRI_ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0) return TRI_ATTN_OK;
+  if (!pair_repr || !pair_mask || !dy || !grads) return TRI_ATTN_ERR_INVALID_ARG;
+  const tri_attn_grads &g = *grads;
+  if (!g.d_pair_repr || !g.d_ln_weight || !g.d_ln_bias || !g.d_w_query || !g.d_w_key || !g.d_w_value ||
+      !g.d_w_gate || !g.d_b_gate || !g.d_w_bias_proj || !g.d_w_out || !g.d_b_out)
+    return TRI_ATTN_ERR_INVALID_ARG;
+  const size_t need = bwd_workspace_bytes(B, N, t->D, t->h);
+  if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TRI_ATTN_ERR_WORKSPACE;
+  BwdRunArgs r{};
+  r.P = pair_repr, r.mask = pair_mask, r.dy = dy, r.wpack = t->wpack, r.vecs = t->vecs, r.g = g, r.ws = workspace;
+  r.eps = t->cfg.ln_eps, r.fill = t->cfg.mask_fill;
+  const double thr = std::min(std::nearbyint(dropout_rate * 4294967296.0), 4294967295.0);
+  r.thr = (uint32_t)thr;
+  r.scale = (float)(4294967296.0 / (4294967296.0 - thr));
+  r.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu), r.seed_hi = (uint32_t)(seed >> 32), r.offset = offset;
+  r.B = B, r.N = N;
+  if (launch_bwd(t->cfg.dtype, t->D, t->dh, r, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return TRI_ATTN_ERR_HIP;
+  return TRI_ATTN_OK;
+}
+
 int tri_attn_project(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, int B, int N, void *workspace,
                      size_t ws_bytes, void *stream) {
   return run(t, pair_repr, pair_mask, nullptr, B, N, workspace, ws_bytes, stream, 1);

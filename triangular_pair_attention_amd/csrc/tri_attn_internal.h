@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "tri_attn.h"
+
 namespace tpa {
 
 constexpr int kChunk = 64;  // key chunk of the per-chunk maxima; also K1's position tile
@@ -87,6 +89,23 @@ int k1_blocks_per_cu(int dtype, int D, int dh);  // resident workgroups of kerne
 hipError_t launch_k1_split(int D, int dh, const K1Args &a, int grid, hipStream_t s);
 int k1_split_blocks_per_cu(int D, int dh);
 bool supported(int D, int dh);
+
+// Training-mode backward (bwd_train.hip): every argument of the C ABI call
+// plus the handle's packed weights.
+struct BwdRunArgs {
+  const void *P;          // [B][N][N][D] config dtype
+  const uint8_t *mask;    // [B][N][N]
+  const void *dy;         // [B][N][N][D] config dtype
+  const void *wpack;      // [(4D + 16)][D]: Wq; Wk; Wv; Wg; Wz; zero rows (config dtype)
+  const void *vecs;       // gamma, beta, bg, bo ([D] each), then Wo [D][D] (config dtype)
+  tri_attn_grads g;       // outputs, float32
+  void *ws;
+  float eps, fill, scale;
+  uint32_t thr, seed_lo, seed_hi, offset;
+  int B, N;
+};
+hipError_t launch_bwd(int dtype, int D, int dh, const BwdRunArgs &r, hipStream_t s);
+size_t bwd_workspace_bytes(int B, int N, int D, int h);
 // Device address of this GPU's static workspace array (noalloc.hip), looked up
 // once per device; `device` must be current. Returns a TRI_ATTN_* code.
 int scratch_address(int device, void **ptr);
