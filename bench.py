@@ -52,6 +52,11 @@ KERNEL_SOURCES = {
     "k2_attention": "triangular_pair_attention_amd/csrc/k2_attention.hip",
     "k3_out_proj": "triangular_pair_attention_amd/csrc/k3_out_proj.hip",
 }
+# kernels of the one-pass variant (tri_attn_forward_onepass)
+VARIANT_SOURCES = {
+    "op_bias": "triangular_pair_attention_amd/csrc/onepass.hip",
+    "op_fused": "triangular_pair_attention_amd/csrc/onepass.hip",
+}
 # float32 tensors run kernel 1 from its own source (split products)
 F32_SOURCES = {"k1_ln_proj": "triangular_pair_attention_amd/csrc/k1_split.hip"}
 # float32 kernels whose products run as six bf16 products each (three-way split
@@ -69,7 +74,8 @@ def _code_only(text: str) -> str:
 
 
 def kernel_source(kernel: str, dtype: str = "bf16") -> str:
-    return F32_SOURCES.get(kernel, KERNEL_SOURCES[kernel]) if dtype == "f32" else KERNEL_SOURCES[kernel]
+    src = KERNEL_SOURCES.get(kernel) or VARIANT_SOURCES[kernel]
+    return F32_SOURCES.get(kernel, src) if dtype == "f32" else src
 
 
 def source_hash(kernel: str, dtype: str = "bf16") -> str:
@@ -233,6 +239,10 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--ending-node", action="store_true",
                     help="the ending-node variant (attention along the other residue axis)")
+    ap.add_argument("--peaked", type=float, default=1.0,
+                    help="scale the query and pair-bias weights by this factor (peaked softmax: a looser "
+                         "bound for the attention kernel's shift; the share of recomputed items is reported)")
+    ap.add_argument("--no-onepass", action="store_true", help="skip timing the one-pass variant")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -254,6 +264,10 @@ def main():
     torch.cuda.set_device(dev)
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     inp = make_inputs(w)
+    if args.peaked != 1.0:
+        inp["w_query"] = inp["w_query"] * args.peaked
+        inp["w_bias_proj"] = inp["w_bias_proj"] * args.peaked
+    wname = w.name + ("_ending_node" if args.ending_node else "")
     weights = {k: torch.from_numpy(inp[k]).to(dev).to(dt).contiguous() for k in WEIGHT_NAMES}
     P = torch.from_numpy(inp["pair_repr"]).to(dev).to(dt).contiguous()
     M = torch.from_numpy(inp["pair_mask"]).to(dev).contiguous()
@@ -296,6 +310,12 @@ def main():
     ms_fwd_ev = timed(fwd, args.steps)
     wall = time.perf_counter() - t0
     ms_fwd = max(ms_fwd_ev, 0.0)
+    # the attention work items of the last forward that found their softmax
+    # bound too loose and were recomputed with the exact maximum
+    lay = B.tri_attn_get_workspace_layout(h, w.B, w.N)
+    flags = ws[lay.recover_flags:lay.recover_flags + lay.attention_items].cpu()
+    recovery = {"items": lay.attention_items, "recovered": int(flags.sum()),
+                "recovered_fraction": float(flags.float().mean())}
     # each kernel alone through its stage entry point, for the roofline: one
     # launch at a time between HIP events on the kernels' stream, each on the
     # data its predecessors just wrote (the attention kernel consumes the gate
@@ -367,6 +387,44 @@ def main():
             trn()
         ms_train = timed(trn, max(1, args.steps // 5))
         train = {"dropout_rate": 0.1, "ms_per_step": ms_train, "ratio_to_inference": ms_train / ms_fwd}
+        del lse
+        # the backward (all gradients) of the same training step
+        nbw = B.tri_attn_backward_workspace_size(h, w.B, w.N)
+        wsb = torch.empty(nbw, dtype=torch.uint8, device=dev)
+        shapes = {"d_pair_repr": P.shape, "d_ln_weight": (w.D,), "d_ln_bias": (w.D,), "d_w_query": (w.D, w.D),
+                  "d_w_key": (w.D, w.D), "d_w_value": (w.D, w.D), "d_w_gate": (w.D, w.D), "d_b_gate": (w.D,),
+                  "d_w_bias_proj": (w.h, w.D), "d_w_out": (w.D, w.D), "d_b_out": (w.D,)}
+        grads = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
+        dy = torch.randn(P.shape, device=dev, dtype=torch.float32).to(dt)
+
+        def bwd():
+            B.tri_attn_backward_train(h, P, M, dy, w.B, w.N, 0.1, 12345, 0, grads, wsb, nbw, stream)
+
+        bwd()
+        train["backward_ms_per_step"] = timed(bwd, 2)
+        train["backward_workspace_bytes"] = nbw
+        del wsb, grads, dy
+    # the one-pass variant (bias pre-pass, then one fused kernel per pair row)
+    onepass = None
+    if not args.no_onepass and w.N <= 512:
+        nop = B.tri_attn_onepass_workspace_size(h, w.B, w.N)
+        wso = torch.empty(max(nop, 256), dtype=torch.uint8, device=dev)
+
+        def op():
+            B.tri_attn_forward_onepass(h, P, M, out, w.B, w.N, wso, nop, stream)
+
+        for _ in range(3):
+            op()
+        ms_op = timed(op, max(1, args.steps // 5))
+        s_ = 2 if w.dtype == "bf16" else 4
+        tb = [stored_traffic(wname, k, w.dtype) for k in VARIANT_SOURCES]
+        t3 = [stored_traffic(wname, k, w.dtype) for k in KERNEL_SOURCES]
+        onepass = {"ms_per_step": ms_op, "value": w.B * w.N * w.N / (ms_op * 1e-3),
+                   "ratio_to_three_kernel": ms_op / ms_fwd,
+                   "hbm_bytes": None if None in tb else sum(tb),
+                   "three_kernel_hbm_bytes": None if None in t3 else sum(t3),
+                   "min_bytes": 2 * w.B * w.N * w.N * w.D * s_ + w.B * w.N * w.N}
+        del wso
     torch.cuda.synchronize()
     B.tri_attn_destroy(h)
 
@@ -377,7 +435,7 @@ def main():
     ms_k = {"k1_ln_proj": ms_k1, "k2_attention": ms_k2, "k3_out_proj": ms_k3}
     dom = max(ms_k, key=ms_k.get)
     roof = roofline_of(dom, w, m, ms_k[dom], inp["pair_mask"])
-    roof["traffic"] = stored_traffic(w.name, dom, w.dtype)
+    roof["traffic"] = stored_traffic(wname, dom, w.dtype)
     roof["kernel"] = dom
     roof["kernel_ms"] = ms_k[dom]
 
@@ -394,8 +452,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name + ("_ending_node" if args.ending_node else ""), "B": w.B, "N": w.N,
-                   "D": w.D, "h": w.h, "d": w.d, "mask": list(w.mask), "seed": w.seed,
+        "config": {"workload": wname + (f"_peaked{args.peaked:g}" if args.peaked != 1.0 else ""), "B": w.B,
+                   "N": w.N, "D": w.D, "h": w.h, "d": w.d, "mask": list(w.mask), "seed": w.seed,
+                   "peaked": args.peaked,
                    "variant": "ending-node" if args.ending_node else "starting-node",
                    "parallelism": "none (1 GPU)"},
         "tflops": tflops,
@@ -407,6 +466,8 @@ def main():
         "wall_s_timed": wall,
         "roofline": roof,
         "train": train,
+        "onepass": onepass,
+        "recovery": recovery,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds, args.ending_node)

@@ -186,6 +186,25 @@ int tri_attn_backward_train(tri_attn_t h, const void *pair_repr, const uint8_t *
                             int N, double dropout_rate, uint64_t seed, uint32_t offset,
                             const tri_attn_grads *grads, void *workspace, size_t ws_bytes, void *stream);
 
+/* Bytes of device workspace tri_attn_forward_onepass needs for (B, N): the
+ * pair bias with the mask folded in, float32 [B][h][N][Np], Np = N rounded up
+ * to 64. UNSUPPORTED for N > 512. B == 0 or N == 0 needs 0 bytes. */
+int tri_attn_onepass_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
+
+/* One-pass variant of tri_attn_forward (same arguments and result, to
+ * rounding; the single fused kernel approach of "Kimi-K2.6 / l2_p6", one
+ * workgroup per (b, i) row, with the pre-pass for the pair bias that its
+ * Option A / Option B comparison says the bias needs): a pre-pass computes
+ * LayerNorm and the pair bias of every position; then one kernel per pair row
+ * recomputes LayerNorm and the q, k, v and gate projections of that row on
+ * chip, attends with a running-maximum softmax, gates, and applies the output
+ * projection, writing y once. q, k, v and the gate never go to device memory.
+ * Starting- and ending-node handles, both dtypes, N <= 512 (UNSUPPORTED
+ * above). Errors as tri_attn_forward. Asynchronous on `stream`; pointers
+ * borrowed until the stream work completes. */
+int tri_attn_forward_onepass(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
+                             void *workspace, size_t ws_bytes, void *stream);
+
 /* Largest workspace tri_attn_forward_noalloc can use: the size of the static
  * device array that holds it (256 MiB per GPU). */
 #define TRI_ATTN_NOALLOC_MAX_BYTES ((size_t)256 << 20)
@@ -240,11 +259,19 @@ const char *tri_attn_strerror(int code);
  *             the squared norm of k over one 16-channel block.
  *   vsum    : [B][N][Np/64][D] float32: sum of v over each 64-column chunk
  *             (for the uniform weights of fully masked query columns;
- *             chunk-major: consecutive channels are adjacent). */
+ *             chunk-major: consecutive channels are adjacent).
+ *   recover_flags : [attention_items] uint8, written by every inference
+ *             forward (tri_attn_forward, tri_attn_attend): 1 where the
+ *             attention work item found its softmax bound too loose (a column
+ *             sum below 2^-64) and recomputed with the exact maximum, else 0.
+ *             A work item is one head of a block of rows and query columns;
+ *             the fraction of ones is the share of the attention work done
+ *             twice. */
 typedef struct {
-  size_t q, k, vt, g, zm, zmax, kmax, vsum;
+  size_t q, k, vt, g, zm, zmax, kmax, vsum, recover_flags;
   size_t total;
   int padded_n;
+  int attention_items;
 } tri_attn_workspace_layout;
 
 int tri_attn_get_workspace_layout(tri_attn_t h, int B, int N, tri_attn_workspace_layout *out);

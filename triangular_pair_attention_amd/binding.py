@@ -54,8 +54,9 @@ class tri_attn_grads(ctypes.Structure):
 
 
 class tri_attn_workspace_layout(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_size_t) for name in ("q", "k", "vt", "g", "zm", "zmax", "kmax", "vsum", "total")] + [
-        ("padded_n", ctypes.c_int)
+    _fields_ = [(name, ctypes.c_size_t)
+                for name in ("q", "k", "vt", "g", "zm", "zmax", "kmax", "vsum", "recover_flags", "total")] + [
+        ("padded_n", ctypes.c_int), ("attention_items", ctypes.c_int)
     ]
 
 
@@ -90,6 +91,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tri_attn_attend.argtypes = [vp, i, i, vp, sz, vp]
     lib.tri_attn_output.argtypes = [vp, vp, i, i, vp, sz, vp]
     lib.tri_attn_set_shift_slack.argtypes = [vp, ctypes.c_float]
+    lib.tri_attn_onepass_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
+    lib.tri_attn_forward_onepass.argtypes = [vp, vp, vp, vp, i, i, vp, sz, vp]
     lib.tri_attn_backward_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.tri_attn_backward_train.argtypes = [vp, vp, vp, vp, i, i, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint32,
                                             ctypes.POINTER(tri_attn_grads), vp, sz, vp]
@@ -99,7 +102,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for name in ("tri_attn_create", "tri_attn_workspace_size", "tri_attn_forward", "tri_attn_destroy",
                  "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend",
                  "tri_attn_output", "tri_attn_forward_train", "tri_attn_set_shift_slack",
-                 "tri_attn_forward_noalloc", "tri_attn_backward_workspace_size", "tri_attn_backward_train"):
+                 "tri_attn_forward_noalloc", "tri_attn_backward_workspace_size", "tri_attn_backward_train",
+                 "tri_attn_onepass_workspace_size", "tri_attn_forward_onepass"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -205,6 +209,20 @@ def tri_attn_output(handle: int, out, B: int, N: int, workspace, ws_bytes: int, 
 
 def tri_attn_set_shift_slack(handle: int, slack: float) -> None:
     _check(load_library().tri_attn_set_shift_slack(handle, float(slack)), "tri_attn_set_shift_slack")
+
+
+def tri_attn_onepass_workspace_size(handle: int, B: int, N: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().tri_attn_onepass_workspace_size(handle, B, N, ctypes.byref(n)),
+           "tri_attn_onepass_workspace_size")
+    return n.value
+
+
+def tri_attn_forward_onepass(handle: int, pair_repr, pair_mask, out, B: int, N: int, workspace, ws_bytes: int,
+                             stream=None) -> None:
+    _check(load_library().tri_attn_forward_onepass(handle, _ptr(pair_repr), _ptr(pair_mask), _ptr(out), B, N,
+                                                   _ptr(workspace), ws_bytes, _stream(stream)),
+           "tri_attn_forward_onepass")
 
 
 def tri_attn_backward_workspace_size(handle: int, B: int, N: int) -> int:

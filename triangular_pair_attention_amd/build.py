@@ -21,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "lib", "libtri_attn.so")
 CALIB = os.path.join(PKG, "lib", "tri_attn_calib")
 SOURCES = ("tri_attn.cpp", "pack_weights.hip", "k1_ln_proj.hip", "k1_split.hip", "k2_attention.hip",
-           "k2_train.hip", "k3_out_proj.hip", "noalloc.hip", "bwd_train.hip")
+           "k2_train.hip", "k3_out_proj.hip", "noalloc.hip", "bwd_train.hip", "onepass.hip")
 # further compilation units: (source, object name, extra flags). The bf16
 # head-size-16 attention kernel is built on its own with LLVM's
 # max-memory-clause scheduler (its key loop measured 3% faster; the other

@@ -24,11 +24,14 @@
 // of its columns, so the L2 traffic per score is shared WQ (WR) ways.
 //
 // Softmax without a running maximum. Per (row i, query j) the kernel fixes
-// the shift m = |q'_j| * max_k |k_k| + max_k zm[j, k] before the key loop
-// (Cauchy-Schwarz: m >= every score of the row, so exp2(s - m) <= 1 and
-// nothing overflows). Softmax is invariant to the shift, so the result is
-// exact up to rounding; the loop needs no max, no rescaling and no cross-lane
-// traffic. For bf16 the shift rides in the MFMA (d = 16: a spare contraction
+// the shift m = |q'_j| * max_k |k_k| + max_k zm[j, k] - H before the key
+// loop. Cauchy-Schwarz makes m + H >= every score of the row, so exp2(s - m)
+// <= 2^H; with the headroom H = 96 nothing overflows (a column sum stays
+// below N * 2^96) while a bound up to 64 + 96 above the column's true maximum
+// still leaves its sum above 2^-64 (peaked inputs, with large query norms and
+// bias, make the Cauchy-Schwarz bound loose by much more than 64). Softmax is
+// invariant to the shift, so the result is exact up to rounding; the loop
+// needs no max, no rescaling and no cross-lane traffic. For bf16 the shift rides in the MFMA (d = 16: a spare contraction
 // slot holds q' = -m against k = 1; d = 32: one more MFMA), the score
 // accumulator starts from the zm tile and the row sum comes from a row of
 // ones in the PV MFMA: the VALU work per score is one exp2 and half a bf16
@@ -57,6 +60,11 @@
 #include "tri_attn.h"
 
 namespace tpa {
+
+// Headroom of the softmax shift below its Cauchy-Schwarz bound (log2 units):
+// exp2 of a score is at most 2^96, so column sums (N keys) and the value sums
+// stay far inside the float32 range.
+constexpr float kShiftHeadroom = 96.f;
 
 // IG rows x JW 16-query blocks per wave; WR x WQ waves per workgroup.
 template <typename T, int D, int DH>
@@ -435,7 +443,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
           for (int s = 0; s < QS; ++s) n2 += qf[i][jb][s] * qf[i][jb][s];
         }
         n2 = group4_sum(n2);
-        msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : sqrtf(n2 * kn2[i]) + zmx[jb] + a.shift_slack;
+        msh[i][jb] = (zmx[jb] == -INFINITY) ? 0.f : sqrtf(n2 * kn2[i]) + zmx[jb] + a.shift_slack - kShiftHeadroom;
       }
     set_shift(msh);
     if constexpr (SPLITQK) {
@@ -452,8 +460,8 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         }
     }
     // bf16, d = 32: the shift costs two more MFMAs per score tile. Where every
-    // bound of the wave is at most 64, exp2 of a score cannot overflow (2^64
-    // per key, sums far below the fp32 range) and the wave goes without it;
+    // shift of the wave is at most 0 (bound at most H), exp2 of a score cannot
+    // overflow without it (at most 2^H per key) and the wave goes without it;
     // scores far below their bound only risk a tiny sum, which the recovery
     // below catches either way.
     shift_on = true;
@@ -462,7 +470,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
       for (int i = 0; i < IG; ++i)
 #pragma unroll
-        for (int jb = 0; jb < JW; ++jb) big |= !(msh[i][jb] <= 64.f);
+        for (int jb = 0; jb < JW; ++jb) big |= !(msh[i][jb] <= 0.f);
       shift_on = __ballot(big) != 0;
     }
   };
@@ -755,6 +763,7 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
         if (zmx[jb] > -INFINITY && !(lsum[i][jb] >= 0x1p-64f)) need = true;
     if (__ballot(need) != 0 && lane == 0) need_s[buf] = 1;
     lds_barrier();  // also: every wave is done with the ring
+    if (a.rflag && threadIdx.x == 0) a.rflag[v] = (uint8_t)need_s[buf];
     if (need_s[buf]) {
       float mx[IG][JW];
 #pragma unroll

@@ -47,6 +47,8 @@ Layout make_layout(int B, int N, int D, int h, int elem) {
   L.zmax = off, off = align256(off + (size_t)B * h * N * L.nchunk * 4);
   L.kmax = off, off = align256(off + (size_t)B * N * (D / 16) * L.nchunk * 4);
   L.vsum = off, off = align256(off + (size_t)B * N * D * L.nchunk * 4);
+  L.items = k2_items(elem == 2 ? TRI_ATTN_BF16 : TRI_ATTN_F32, D, D / h, B, N);
+  L.rflag = off, off = align256(off + (size_t)L.items);
   L.total = off;
   return L;
 }
@@ -206,6 +208,8 @@ int tri_attn_get_workspace_layout(tri_attn_t t, int B, int N, tri_attn_workspace
   const Layout L = make_layout(B, N, t->D, t->h, t->elem);
   out->q = L.q, out->k = L.k, out->vt = L.vt, out->g = L.g;
   out->zm = L.zm, out->zmax = L.zmax, out->kmax = L.kmax, out->vsum = L.vsum;
+  out->recover_flags = L.rflag;
+  out->attention_items = L.items;
   out->total = L.total;
   out->padded_n = L.Np;
   return TRI_ATTN_OK;
@@ -267,7 +271,8 @@ static int run(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, vo
   a2.mask_fill = t->cfg.mask_fill;
   a2.shift_slack = t->shift_slack;
   a2.B = B, a2.N = N, a2.Np = L.Np, a2.nchunk = L.nchunk;
-  a2.items = k2_items(t->cfg.dtype, D, t->dh, B, N);
+  a2.items = L.items;
+  a2.rflag = reinterpret_cast<uint8_t *>(w + L.rflag);
   // persistent workgroups; with more items than that, a multiple of 8 so that
   // each keeps its XCD from item to item
   int grid2 = a2.items;
@@ -361,6 +366,35 @@ int tri_attn_backward_train(tri_attn_t t, const void *pair_repr, const uint8_t *
   r.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu), r.seed_hi = (uint32_t)(seed >> 32), r.offset = offset;
   r.B = B, r.N = N;
   if (launch_bwd(t->cfg.dtype, t->D, t->dh, r, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return TRI_ATTN_ERR_HIP;
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_onepass_workspace_size(tri_attn_t t, int B, int N, size_t *bytes) {
+  if (!bytes) return TRI_ATTN_ERR_INVALID_ARG;
+  const int rc = check_sizes(t, B, N);
+  if (rc) return rc;
+  if (N > kOnePassMaxN) return TRI_ATTN_ERR_UNSUPPORTED;
+  const size_t Np = ((size_t)N + 63) / 64 * 64;
+  *bytes = (B == 0 || N == 0) ? 0 : (size_t)B * t->h * N * Np * sizeof(float);
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_forward_onepass(tri_attn_t t, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
+                             void *workspace, size_t ws_bytes, void *stream) {
+  size_t need = 0;
+  const int rc = tri_attn_onepass_workspace_size(t, B, N, &need);
+  if (rc) return rc;
+  if (B == 0 || N == 0) return TRI_ATTN_OK;
+  if (!pair_repr || !pair_mask || !out) return TRI_ATTN_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TRI_ATTN_ERR_WORKSPACE;
+  OnePassArgs a{};
+  a.P = pair_repr, a.mask = pair_mask, a.W = t->wpack, a.vecs = t->vecs;
+  a.zm = static_cast<float *>(workspace), a.out = out;
+  a.eps = t->cfg.ln_eps, a.fill = t->cfg.mask_fill;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)t->dh));
+  a.B = B, a.N = N, a.Np = (N + 63) / 64 * 64, a.h = t->h, a.transposed = t->cfg.ending_node;
+  if (launch_onepass(t->cfg.dtype, t->D, t->dh, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return TRI_ATTN_ERR_HIP;
   return TRI_ATTN_OK;
 }

@@ -14,9 +14,10 @@ constexpr int kChunk = 64;  // key chunk of the per-chunk maxima; also K1's posi
 
 // Workspace regions (byte offsets); see tri_attn_workspace_layout in the header.
 struct Layout {
-  size_t q, k, vt, g, zm, zmax, kmax, vsum, total;
+  size_t q, k, vt, g, zm, zmax, kmax, vsum, rflag, total;
   int Np;      // N rounded up to kChunk
   int nchunk;  // Np / kChunk
+  int items;   // attention work items (one recovery flag byte each)
 };
 
 Layout make_layout(int B, int N, int D, int h, int elem_bytes);
@@ -45,6 +46,7 @@ struct K2Args {
   const float *zm, *zmax, *kmax, *vsum;
   float mask_fill;  // finite (uniform rule on fully masked columns) or -inf (NaN there)
   float shift_slack;
+  uint8_t *rflag;   // [items]: 1 where the item took the exact-maximum recovery, else 0 (null: not recorded)
   int B, N, Np, nchunk, items;
 };
 
@@ -106,6 +108,22 @@ struct BwdRunArgs {
 };
 hipError_t launch_bwd(int dtype, int D, int dh, const BwdRunArgs &r, hipStream_t s);
 size_t bwd_workspace_bytes(int B, int N, int D, int h);
+// One-pass variant (onepass.hip): the pre-pass writes zm, the fused row
+// kernel does everything else.
+struct OnePassArgs {
+  const void *P;         // pair_repr [B][N][N][D], config dtype
+  const uint8_t *mask;   // [B][N][N]
+  const void *W;         // [(4D + 16)][D]: Wq; Wk; Wv; Wg; Wz; zero rows (config dtype)
+  const void *vecs;      // gamma, beta, bg, bo ([D] each), then Wo [D][D] (config dtype)
+  float *zm;             // [B][h][N][Np] float32: z * log2(e), -inf where masked and for k >= N
+  void *out;             // y [B][N][N][D], config dtype
+  float eps, fill, qscale;  // qscale = log2(e) / sqrt(d)
+  int B, N, Np, h;
+  int transposed;        // ending-node: position (b, i, j) reads and writes (b, j, i)
+};
+constexpr int kOnePassMaxN = 512;
+hipError_t launch_onepass(int dtype, int D, int dh, const OnePassArgs &a, hipStream_t s);
+
 // Device address of this GPU's static workspace array (noalloc.hip), looked up
 // once per device; `device` must be current. Returns a TRI_ATTN_* code.
 int scratch_address(int device, void **ptr);
