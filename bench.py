@@ -100,6 +100,12 @@ def work_model(w):
         "k2_attention": {"flops": 4 * B * N ** 3 * D, "bytes": 4 * P * D * s + 4 * B * h * N * N + P * D * s},
         # output projection: read g*o, write y
         "k3_out_proj": {"flops": 2 * P * D * D, "bytes": 2 * P * D * s},
+        # one-pass variant: the bias pre-pass reads pair_repr and the mask and
+        # writes the float32 bias+mask tile; the fused row kernel reads
+        # pair_repr and that tile once and writes y
+        "op_bias": {"flops": 2 * P * D * h, "bytes": P * D * s + P + 4 * B * h * N * N},
+        "op_fused": {"flops": 2 * P * D * 4 * D + 4 * B * N ** 3 * D + 2 * P * D * D,
+                     "bytes": 2 * P * D * s + 4 * B * h * N * N},
     }
 
 
