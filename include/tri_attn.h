@@ -205,6 +205,15 @@ int tri_attn_onepass_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
 int tri_attn_forward_onepass(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, void *out, int B, int N,
                              void *workspace, size_t ws_bytes, void *stream);
 
+/* Testing hook (fault injection for tests of the error paths, not for use
+ * in production): arms the next tri_attn_create call, on any thread, so that
+ * its nth device allocation (1-based) fails as if the device were out of
+ * memory; that create then returns TRI_ATTN_ERR_OOM after freeing what it had
+ * allocated. The next create call disarms the hook whether or not it reaches
+ * the nth allocation (a create makes three allocations, four for float32
+ * handles); nth = 0 disarms it. Returns TRI_ATTN_OK, or INVALID_ARG for nth < 0. */
+int tri_attn_set_alloc_fault(int nth);
+
 /* Largest workspace tri_attn_forward_noalloc can use: the size of the static
  * device array that holds it (256 MiB per GPU). */
 #define TRI_ATTN_NOALLOC_MAX_BYTES ((size_t)256 << 20)

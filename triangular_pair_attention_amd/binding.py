@@ -91,6 +91,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tri_attn_attend.argtypes = [vp, i, i, vp, sz, vp]
     lib.tri_attn_output.argtypes = [vp, vp, i, i, vp, sz, vp]
     lib.tri_attn_set_shift_slack.argtypes = [vp, ctypes.c_float]
+    lib.tri_attn_set_alloc_fault.argtypes = [i]
     lib.tri_attn_onepass_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.tri_attn_forward_onepass.argtypes = [vp, vp, vp, vp, i, i, vp, sz, vp]
     lib.tri_attn_backward_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
@@ -103,7 +104,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                  "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend",
                  "tri_attn_output", "tri_attn_forward_train", "tri_attn_set_shift_slack",
                  "tri_attn_forward_noalloc", "tri_attn_backward_workspace_size", "tri_attn_backward_train",
-                 "tri_attn_onepass_workspace_size", "tri_attn_forward_onepass"):
+                 "tri_attn_onepass_workspace_size", "tri_attn_forward_onepass", "tri_attn_set_alloc_fault"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -209,6 +210,11 @@ def tri_attn_output(handle: int, out, B: int, N: int, workspace, ws_bytes: int, 
 
 def tri_attn_set_shift_slack(handle: int, slack: float) -> None:
     _check(load_library().tri_attn_set_shift_slack(handle, float(slack)), "tri_attn_set_shift_slack")
+
+
+def tri_attn_set_alloc_fault(nth: int) -> None:
+    """Testing hook: the next tri_attn_create fails its nth device allocation."""
+    _check(load_library().tri_attn_set_alloc_fault(nth), "tri_attn_set_alloc_fault")
 
 
 def tri_attn_onepass_workspace_size(handle: int, B: int, N: int) -> int:

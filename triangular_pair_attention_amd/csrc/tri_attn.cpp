@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -84,11 +85,26 @@ static int check_config(const tri_attn_config *cfg) {
   return TRI_ATTN_OK;
 }
 
+// fault injection for tests: the armed create call fails its nth device allocation
+static std::atomic<int> g_alloc_fault{0};
+
+int tri_attn_set_alloc_fault(int nth) {
+  if (nth < 0) return TRI_ATTN_ERR_INVALID_ARG;
+  g_alloc_fault.store(nth);
+  return TRI_ATTN_OK;
+}
+
 int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void *stream, tri_attn_t *out) {
   if (!out) return TRI_ATTN_ERR_INVALID_ARG;
   *out = nullptr;
   int rc = check_config(cfg);
   if (rc) return rc;
+  const int fault = g_alloc_fault.exchange(0);
+  int nalloc = 0;
+  auto device_alloc = [&](void **p, size_t bytes) -> hipError_t {
+    if (++nalloc == fault) return hipErrorOutOfMemory;
+    return hipMalloc(p, bytes);
+  };
   if (!w || !w->ln_weight || !w->ln_bias || !w->w_query || !w->w_key || !w->w_value || !w->w_gate ||
       !w->b_gate || !w->w_bias_proj || !w->w_out || !w->b_out)
     return TRI_ATTN_ERR_INVALID_ARG;
@@ -122,24 +138,24 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
 
   t->wpack_bytes = (size_t)(4 * D + 16) * D * e;
   t->vecs_bytes = (size_t)4 * D * e + (size_t)D * D * e;
-  if (hipMalloc(&t->wpack, t->wpack_bytes) != hipSuccess) {
+  if (device_alloc(&t->wpack, t->wpack_bytes) != hipSuccess) {
     delete t;
     return TRI_ATTN_ERR_OOM;
   }
-  if (hipMalloc(&t->vecs, t->vecs_bytes) != hipSuccess) {
+  if (device_alloc(&t->vecs, t->vecs_bytes) != hipSuccess) {
     (void)hipFree(t->wpack);
     delete t;
     return TRI_ATTN_ERR_OOM;
   }
   t->wfrag_bytes = (size_t)5 * D * D * e;
-  if (hipMalloc(&t->wfrag, t->wfrag_bytes) != hipSuccess) {
+  if (device_alloc(&t->wfrag, t->wfrag_bytes) != hipSuccess) {
     (void)hipFree(t->wpack);
     (void)hipFree(t->vecs);
     delete t;
     return TRI_ATTN_ERR_OOM;
   }
   t->wsplit_plane = (size_t)5 * D * D * 2;
-  if (cfg->dtype == TRI_ATTN_F32 && hipMalloc(&t->wsplit, 3 * t->wsplit_plane) != hipSuccess) {
+  if (cfg->dtype == TRI_ATTN_F32 && device_alloc(&t->wsplit, 3 * t->wsplit_plane) != hipSuccess) {
     (void)hipFree(t->wpack);
     (void)hipFree(t->vecs);
     (void)hipFree(t->wfrag);
