@@ -175,6 +175,15 @@ __global__ __launch_bounds__(512) void k2_train(K2Args a, K2TrainArgs tr) {
     const L *kb_ = kbuf[buf];
     const L *vb_ = vtb[buf];
     const int k0 = c * KT;
+    // the chunk's dropout words, all calls first: independent chains the
+    // scheduler can interleave (one call's rounds are a serial chain)
+    uint4 wd[QPW][4];
+#pragma unroll
+    for (int m = 0; m < QPW; ++m)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        wd[m][kb] = philox4x32_10(make_uint4((uint32_t)((k0 >> 2) + kb * 4 + g), (uint32_t)jq[m], ctr2, tr.offset),
+                                  tr.seed_lo, tr.seed_hi);
 #pragma unroll
     for (int m = 0; m < QPW; ++m) {
       const int jc = min(jq[m], N - 1);
@@ -221,9 +230,7 @@ __global__ __launch_bounds__(512) void k2_train(K2Args a, K2TrainArgs tr) {
       for (int cb = 0; cb < CB; ++cb) ot[m][cb] *= alpha;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const uint4 w = philox4x32_10(make_uint4((uint32_t)((k0 >> 2) + kb * 4 + g), (uint32_t)jq[m], ctr2,
-                                                 tr.offset),
-                                      tr.seed_lo, tr.seed_hi);
+        const uint4 w = wd[m][kb];
         const uint32_t wv[4] = {w.x, w.y, w.z, w.w};  // keys k0 + 16 kb + 4g + r
         float p[4];
 #pragma unroll
