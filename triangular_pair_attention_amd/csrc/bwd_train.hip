@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   __shared__ float As[16][68];
   __shared__ float Bs[16][68];
   const int tid = threadIdx.x;
-  const long long m0 = (long long)blockIdx.y * 64, n0 = (long long)blockIdx.x * 64;
+  // grid x: row blocks (M can be large), y: column blocks, z: K chunks
+  const long long m0 = (long long)blockIdx.x * 64, n0 = (long long)blockIdx.y * 64;
   const long long kb = (long long)blockIdx.z * g.kchunk;
   const long long ke = min(kb + g.kchunk, g.K);
   const int tm = tid >> 4, tn = tid & 15;
@@ -216,8 +217,8 @@ __global__ __launch_bounds__(256) void bwd_attn_fwd(BwdAttnArgs a) {
   constexpr int KT = 64;
   __shared__ float ks[KT][DH], vs[KT][DH];
   const int N = a.N, D = a.D, h = a.h, C = a.C;
-  const int bi = blockIdx.y / h, t = blockIdx.y - bi * h, b = bi / N, i = bi - b * N;
-  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int bi = blockIdx.x / h, t = blockIdx.x - bi * h, b = bi / N, i = bi - b * N;
+  const int j = blockIdx.y * 256 + threadIdx.x;
   const bool live = j < N;
   const size_t rowp = (size_t)bi * N;  // position of (b, i, 0)
   float q[DH];
@@ -275,8 +276,8 @@ __global__ __launch_bounds__(256) void bwd_attn_dq(BwdAttnArgs a) {
   constexpr int KT = 64;
   __shared__ float ks[KT][DH], vs[KT][DH];
   const int N = a.N, D = a.D, h = a.h, C = a.C;
-  const int bi = blockIdx.y / h, t = blockIdx.y - bi * h, b = bi / N, i = bi - b * N;
-  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int bi = blockIdx.x / h, t = blockIdx.x - bi * h, b = bi / N, i = bi - b * N;
+  const int j = blockIdx.y * 256 + threadIdx.x;
   const bool live = j < N;
   const size_t rowp = (size_t)bi * N;
   float q[DH], dov[DH], dq[DH];
@@ -334,8 +335,8 @@ __global__ __launch_bounds__(256) void bwd_attn_dkv(BwdAttnArgs a) {
   constexpr int QT = 64;
   __shared__ float qs[QT][DH], dos[QT][DH], ms[QT], ls[QT], Ds[QT];
   const int N = a.N, D = a.D, h = a.h, C = a.C;
-  const int bi = blockIdx.y / h, t = blockIdx.y - bi * h, b = bi / N, i = bi - b * N;
-  const int k = blockIdx.x * 256 + threadIdx.x;
+  const int bi = blockIdx.x / h, t = blockIdx.x - bi * h, b = bi / N, i = bi - b * N;
+  const int k = blockIdx.y * 256 + threadIdx.x;
   const bool live = k < N;
   const size_t rowp = (size_t)bi * N;
   float kv[DH], vv[DH], dk[DH], dv[DH];
@@ -545,7 +546,7 @@ static hipError_t gemm(const void *A, long long sam, long long sak, const void *
                        float *C, long long scz, long long scm, long long M, long long N, long long K,
                        long long kchunk, int nz, hipStream_t s) {
   GemmArgs g{A, Bm, C, M, N, K, kchunk, sam, sak, sbk, sbn, scz, scm};
-  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)nz);
+  const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)nz);
   hipLaunchKernelGGL((bwd_gemm<TA, TB>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
@@ -592,7 +593,7 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   aa.fill = r.fill, aa.scale = r.scale, aa.rsd = 1.0f / sqrtf((float)DH);
   aa.thr = r.thr, aa.seed_lo = r.seed_lo, aa.seed_hi = r.seed_hi, aa.offset = r.offset;
   aa.B = B, aa.N = N, aa.D = D, aa.h = h, aa.C = (int)C;
-  const dim3 ga((unsigned)((N + 255) / 256), (unsigned)(B * N * h));
+  const dim3 ga((unsigned)(B * N * h), (unsigned)((N + 255) / 256));  // x: (b, i, t), y: column block
   hipLaunchKernelGGL((bwd_attn_fwd<DH>), ga, dim3(256), 0, s, aa);
   TPA_CHECK(hipGetLastError());
   // output projection and gate
