@@ -188,249 +188,474 @@ __global__ __launch_bounds__(D) void bwd_ln_back(const float *dx, const float *x
 }
 
 // ------------------------------------------------------------------ attention
+// Scores in the log2 domain: sl = (q.k / sqrt(d) + z) * log2(e), FILL * log2(e)
+// where masked, -inf for keys past N; m2 and l are a column's maximum and sum
+// of exp2(sl - m2) over the keys (undropped), so a = exp2(sl - m2) / l.
 struct BwdAttnArgs {
-  const float *proj;   // [P][C]: q | k | v | gate (before the sigmoid and its bias) | z
-  const float *zt;     // [B][h][N][N]: z[b,t,j,k]
-  const uint8_t *mask; // [B][N][N]
-  float *m, *l, *Dj;   // [B][N][h][N]: row maximum, row sum, sum_k a da
-  float *o;            // [P][D]: o after dropout
-  const float *dob;    // [P][D]: d o
-  float *dcat;         // [P][C]: dq | dk | dv | dgp | dz
-  float fill, scale, rsd;
+  const float *proj;     // [P][C]: q | k | v | gate (before the sigmoid and its bias) | z
+  const float *zt;       // [B][h][N][N]: z[b,t,j,k] * log2(e), FILL * log2(e) where masked
+  const uint8_t *mask;   // [B][N][N]
+  const uint32_t *bits;  // [B][N][h][N][NW]: bit k%32 of word k/32 set where key k is kept
+  float *m, *l, *Dj;     // [B][N][h][N]: m2, l, sum_k a da (= do . o)
+  float *o;              // [P][D]: o after dropout
+  const float *dob;      // [P][D]: d o
+  float *dcat;           // [P][C]: dq | dk | dv | dgp | dz
+  float fill2, scale, qs;  // fill * log2(e); keep scale; log2(e) / sqrt(d)
+  float rsd;             // 1 / sqrt(d)
   uint32_t thr, seed_lo, seed_hi, offset;
-  int B, N, D, h, C;
+  int B, N, D, h, C, NW;
 };
 
-__device__ __forceinline__ uint32_t keep_word(const BwdAttnArgs &a, int b, int i, int t, int j, int k) {
-  const uint4 r = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, (uint32_t)((b * a.N + i) * a.h + t),
-                                           a.offset),
-                                a.seed_lo, a.seed_hi);
-  const int w = k & 3;
-  return w == 0 ? r.x : w == 1 ? r.y : w == 2 ? r.z : r.w;
+// The dropout decisions, one bit per (b, i, t, j, key), from the forward's
+// generator words: thread n computes word n (32 keys, eight calls of four).
+__global__ __launch_bounds__(256) void bwd_keep_bits(BwdAttnArgs a, uint32_t *bits, long long nwords) {
+  const long long n = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (n >= nwords) return;
+  const long long rowj = n / a.NW;  // ((b*N + i)*h + t)*N + j
+  const int kw = (int)(n - rowj * a.NW);
+  const int j = (int)(rowj % a.N);
+  const uint32_t ctr2 = (uint32_t)(rowj / a.N);  // (b*N + i)*h + t
+  uint32_t word = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int k = kw * 32 + 4 * c;
+    if (k < a.N) {
+      const uint4 r = philox4x32_10(make_uint4((uint32_t)(k >> 2), (uint32_t)j, ctr2, a.offset), a.seed_lo, a.seed_hi);
+      word |= ((uint32_t)(r.x >= a.thr) | (uint32_t)(r.y >= a.thr) << 1 | (uint32_t)(r.z >= a.thr) << 2 |
+               (uint32_t)(r.w >= a.thr) << 3)
+              << (4 * c);
+    }
+  }
+  bits[n] = word;
 }
 
-// Attention forward again, per (b, i, t), one thread per query column j:
-// running maximum m and sum l over the keys (undropped weights), and
-// o = scale * sum_k keep * exp(s - m) v_k / l.
+__device__ __forceinline__ const uint32_t *keep_row(const BwdAttnArgs &a, int bi, int t, int j) {
+  return a.bits + (((size_t)bi * a.h + t) * a.N + j) * a.NW;
+}
+
+// The attention steps run on float32 matrix cores (16x16x4), with the score
+// tile transposed, S^T = k q^T (keys in rows), in the forward and dq kernels:
+// lane l = 16 g + r16 holds keys 4g + r of query column r16, which is the
+// k-slice of the P^T / dS^T operand of o^T = v^T P^T and dq^T = k^T dS^T.
+// In step e of a 16-slice, lane group g takes channel (or key) 4g + e in both
+// operands. Work item: (b, i, t, 128 query columns), 8 waves of 16 columns;
+// keys through LDS in chunks of 64.
 template <int DH>
-__global__ __launch_bounds__(256) void bwd_attn_fwd(BwdAttnArgs a) {
-  constexpr int KT = 64;
-  __shared__ float ks[KT][DH], vs[KT][DH];
-  const int N = a.N, D = a.D, h = a.h, C = a.C;
-  const int bi = blockIdx.x / h, t = blockIdx.x - bi * h, b = bi / N, i = bi - b * N;
-  const int j = blockIdx.y * 256 + threadIdx.x;
-  const bool live = j < N;
-  const size_t rowp = (size_t)bi * N;  // position of (b, i, 0)
-  float q[DH];
-#pragma unroll
-  for (int u = 0; u < DH; ++u) q[u] = live ? a.proj[(rowp + j) * C + t * DH + u] * a.rsd : 0.f;
-  float m = -INFINITY, l = 0.f, o[DH];
-#pragma unroll
-  for (int u = 0; u < DH; ++u) o[u] = 0.f;
-  const float *zrow = a.zt + ((size_t)(b * h + t) * N + (live ? j : 0)) * N;
-  const uint8_t *mrow = a.mask + ((size_t)b * N + (live ? j : 0)) * N;
-  for (int k0 = 0; k0 < N; k0 += KT) {
-    for (int e = threadIdx.x; e < KT * DH; e += 256) {
-      const int kk = e / DH, u = e - kk * DH, k = k0 + kk;
-      ks[kk][u] = k < N ? a.proj[(rowp + k) * C + D + t * DH + u] : 0.f;
-      vs[kk][u] = k < N ? a.proj[(rowp + k) * C + 2 * D + t * DH + u] : 0.f;
+struct BwdTile {
+  static constexpr int NW = 8, QB = NW * 16, KT = 64, CB = DH / 16;
+  static constexpr int KP = DH + 4;   // [key][c] row pitch (floats)
+  static constexpr int TP = KT + 4;   // [c][key] row pitch (floats)
+};
+
+// stage the chunk's k (or v) rows of head t as [key][c] and/or [c][key]
+template <int DH>
+__device__ __forceinline__ void stage_rows(const BwdAttnArgs &a, size_t rowp, int col0, int k0, float *rows,
+                                           float *cols) {
+  using S = BwdTile<DH>;
+  constexpr int V4 = S::KT * DH / 4;  // float4 pieces
+  for (int e = threadIdx.x; e < V4; e += S::NW * 64) {
+    const int kk = e / (DH / 4), u4 = (e - kk * (DH / 4)) * 4, k = k0 + kk;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < a.N) v = ldg<float4>(a.proj + (rowp + k) * a.C + col0 + u4);
+    if (rows) *reinterpret_cast<float4 *>(rows + kk * S::KP + u4) = v;
+    if (cols) {
+      cols[(u4 + 0) * S::TP + kk] = v.x;
+      cols[(u4 + 1) * S::TP + kk] = v.y;
+      cols[(u4 + 2) * S::TP + kk] = v.z;
+      cols[(u4 + 3) * S::TP + kk] = v.w;
     }
+  }
+}
+
+// S^T tile of 16 keys (kb) x the lane's query: bias, q.k, mask, padding;
+// bit r of *valid is set where key 4g + r is in range and not masked
+template <int DH>
+__device__ __forceinline__ f32x4 score_tile_t(const BwdAttnArgs &a, const float *kbuf, const f32x4 (&qf)[DH / 16],
+                                              const float *zq, int k0, int kb, int g, int r16, uint32_t *valid) {
+  using S = BwdTile<DH>;
+  const int kq = k0 + kb * 16 + 4 * g;  // first of the lane's four keys
+  f32x4 st;
+  if (kq + 3 < a.N && (a.N & 3) == 0) {  // rows of z are 16-byte aligned when N % 4 == 0
+    const float4 z4 = ldg<float4>(zq + kq);
+    st = (f32x4){z4.x, z4.y, z4.z, z4.w};
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st[r] = kq + r < a.N ? zq[kq + r] : 0.f;
+  }
+  const f32x4 z0 = st;
+#pragma unroll
+  for (int cb = 0; cb < S::CB; ++cb) {
+    const float4 kv = *reinterpret_cast<const float4 *>(kbuf + (kb * 16 + r16) * S::KP + 16 * cb + 4 * g);
+    st = mfma(kv.x, qf[cb][0], st);
+    st = mfma(kv.y, qf[cb][1], st);
+    st = mfma(kv.z, qf[cb][2], st);
+    st = mfma(kv.w, qf[cb][3], st);
+  }
+  uint32_t v = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool in = kq + r < a.N, live = in && z0[r] != a.fill2;
+    st[r] = !in ? -INFINITY : (live ? st[r] : a.fill2);
+    v |= (uint32_t)live << r;
+  }
+  *valid = v;
+  return st;
+}
+
+// Attention forward again: m2, l and o = scale * sum_k keep * a v.
+template <int DH>
+__global__ __launch_bounds__(512) void bwd_attn_fwd(BwdAttnArgs a) {
+  using S = BwdTile<DH>;
+  constexpr int CB = S::CB, KT = S::KT;
+  __shared__ __align__(16) float kbuf[KT * S::KP];
+  __shared__ __align__(16) float vT[DH * S::TP];
+  const int N = a.N, D = a.D, h = a.h, C = a.C;
+  const int nq = (N + S::QB - 1) / S::QB;
+  const int item = blockIdx.x, qc = item % nq, bt = item / nq, bi = bt / h, t = bt - bi * h, b = bi / N;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  const int j = qc * S::QB + wave * 16 + r16, jc = min(j, N - 1);
+  const size_t rowp = (size_t)bi * N;
+  f32x4 qf[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const float4 q4 = ldg<float4>(a.proj + (rowp + jc) * C + t * DH + 16 * cb + 4 * g);
+    qf[cb] = (f32x4){q4.x, q4.y, q4.z, q4.w} * a.qs;
+  }
+  const float *zq = a.zt + ((size_t)(b * h + t) * N + jc) * N;
+  const uint32_t *kr = keep_row(a, bi, t, jc);
+  float mrun = -INFINITY, lsum = 0.f;
+  f32x4 ot[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) ot[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < N; k0 += KT) {
+    stage_rows<DH>(a, rowp, D + t * DH, k0, kbuf, nullptr);
+    stage_rows<DH>(a, rowp, 2 * D + t * DH, k0, nullptr, vT);
     __syncthreads();
-    const int kn = min(KT, N - k0);
-    if (live) {
-      for (int kk = 0; kk < kn; ++kk) {
-        const int k = k0 + kk;
-        float s = zrow[k];
+    f32x4 st[4];
 #pragma unroll
-        for (int u = 0; u < DH; ++u) s += q[u] * ks[kk][u];
-        if (!mrow[k]) s = a.fill;
-        if (s > m) {
-          const float f = (m == -INFINITY) ? 0.f : expf(m - s);
-          l *= f;
+    for (int kb = 0; kb < 4; ++kb) {
+      uint32_t vm;
+      st[kb] = score_tile_t<DH>(a, kbuf, qf, zq, k0, kb, g, r16, &vm);
+    }
+    float mx = -INFINITY;
 #pragma unroll
-          for (int u = 0; u < DH; ++u) o[u] *= f;
-          m = s;
-        }
-        const float p = (s == -INFINITY) ? 0.f : expf(s - m);
-        l += p;
-        if (keep_word(a, b, i, t, j, k) >= a.thr) {
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int u = 0; u < DH; ++u) o[u] += p * vs[kk][u];
-        }
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[kb][r]);
+    mx = group4_max(mx);
+    const float mnew = fmaxf(mrun, mx);
+    const float msh = mnew == -INFINITY ? 0.f : mnew;  // every lane stays in the step
+    const float alpha = fast_exp2(mrun - msh);
+    mrun = mnew;
+    lsum *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) ot[cb] *= alpha;
+    const uint32_t w32[2] = {k0 < N ? kr[k0 >> 5] : 0u, k0 + 32 < N ? kr[(k0 >> 5) + 1] : 0u};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t nib = w32[kb >> 1] >> (16 * (kb & 1) + 4 * g);
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = fast_exp2(st[kb][r] - msh);
+        lsum += e;
+        p[r] = (nib >> r) & 1u ? e : 0.f;
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float4 vv = *reinterpret_cast<const float4 *>(vT + (16 * cb + r16) * S::TP + kb * 16 + 4 * g);
+        ot[cb] = mfma(vv.x, p[0], ot[cb]);
+        ot[cb] = mfma(vv.y, p[1], ot[cb]);
+        ot[cb] = mfma(vv.z, p[2], ot[cb]);
+        ot[cb] = mfma(vv.w, p[3], ot[cb]);
       }
     }
     __syncthreads();
   }
-  if (!live) return;
-  const size_t st = ((size_t)bi * h + t) * N + j;
-  a.m[st] = m;
-  a.l[st] = l;
-  const float inv = a.scale / l;
+  const float lt = group4_sum(lsum);
+  if (j >= N) return;
+  const size_t st_ = ((size_t)bi * h + t) * N + j;
+  if (g == 0) {
+    a.m[st_] = mrun;
+    a.l[st_] = lt;
+  }
+  const float inv = a.scale / lt;
 #pragma unroll
-  for (int u = 0; u < DH; ++u) a.o[(rowp + j) * D + t * DH + u] = o[u] * inv;
+  for (int cb = 0; cb < CB; ++cb)
+    stg<float4>(a.o + (rowp + j) * D + t * DH + 16 * cb + 4 * g,
+                make_float4(ot[cb][0] * inv, ot[cb][1] * inv, ot[cb][2] * inv, ot[cb][3] * inv));
 }
 
-// dq, and sum_k a da = do_j . o_j, per (b, i, t), one thread per query column j.
+// dq, and D = sum_k a da = do . o per query column.
 template <int DH>
-__global__ __launch_bounds__(256) void bwd_attn_dq(BwdAttnArgs a) {
-  constexpr int KT = 64;
-  __shared__ float ks[KT][DH], vs[KT][DH];
+__global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
+  using S = BwdTile<DH>;
+  constexpr int CB = S::CB, KT = S::KT;
+  __shared__ __align__(16) float kbuf[KT * S::KP];
+  __shared__ __align__(16) float kT[DH * S::TP];
+  __shared__ __align__(16) float vbuf[KT * S::KP];
   const int N = a.N, D = a.D, h = a.h, C = a.C;
-  const int bi = blockIdx.x / h, t = blockIdx.x - bi * h, b = bi / N, i = bi - b * N;
-  const int j = blockIdx.y * 256 + threadIdx.x;
-  const bool live = j < N;
+  const int nq = (N + S::QB - 1) / S::QB;
+  const int item = blockIdx.x, qc = item % nq, bt = item / nq, bi = bt / h, t = bt - bi * h, b = bi / N;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  const int j = qc * S::QB + wave * 16 + r16, jc = min(j, N - 1);
   const size_t rowp = (size_t)bi * N;
-  float q[DH], dov[DH], dq[DH];
-  float Dv = 0.f;
+  f32x4 qf[CB], df[CB];
+  float dsum = 0.f;
 #pragma unroll
-  for (int u = 0; u < DH; ++u) {
-    q[u] = live ? a.proj[(rowp + j) * C + t * DH + u] * a.rsd : 0.f;
-    dov[u] = live ? a.dob[(rowp + j) * D + t * DH + u] : 0.f;
-    Dv += live ? dov[u] * a.o[(rowp + j) * D + t * DH + u] : 0.f;
-    dq[u] = 0.f;
+  for (int cb = 0; cb < CB; ++cb) {
+    const float4 q4 = ldg<float4>(a.proj + (rowp + jc) * C + t * DH + 16 * cb + 4 * g);
+    qf[cb] = (f32x4){q4.x, q4.y, q4.z, q4.w} * a.qs;
+    const float4 d4 = ldg<float4>(a.dob + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
+    const float4 o4 = ldg<float4>(a.o + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
+    df[cb] = (f32x4){d4.x, d4.y, d4.z, d4.w};
+    dsum += d4.x * o4.x + d4.y * o4.y + d4.z * o4.z + d4.w * o4.w;
   }
-  const size_t st = ((size_t)bi * h + t) * N + (live ? j : 0);
-  const float m = a.m[st], l = a.l[st];
-  if (live) a.Dj[st] = Dv;
-  const float *zrow = a.zt + ((size_t)(b * h + t) * N + (live ? j : 0)) * N;
-  const uint8_t *mrow = a.mask + ((size_t)b * N + (live ? j : 0)) * N;
+  const float Dv = group4_sum(dsum);
+  const size_t st_ = ((size_t)bi * h + t) * N + jc;
+  const float m2 = a.m[st_], linv = 1.f / a.l[st_];
+  if (j < N && g == 0) a.Dj[st_] = Dv;
+  const float *zq = a.zt + ((size_t)(b * h + t) * N + jc) * N;
+  const uint32_t *kr = keep_row(a, bi, t, jc);
+  f32x4 dq[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) dq[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < N; k0 += KT) {
-    for (int e = threadIdx.x; e < KT * DH; e += 256) {
-      const int kk = e / DH, u = e - kk * DH, k = k0 + kk;
-      ks[kk][u] = k < N ? a.proj[(rowp + k) * C + D + t * DH + u] : 0.f;
-      vs[kk][u] = k < N ? a.proj[(rowp + k) * C + 2 * D + t * DH + u] : 0.f;
-    }
+    stage_rows<DH>(a, rowp, D + t * DH, k0, kbuf, kT);
+    stage_rows<DH>(a, rowp, 2 * D + t * DH, k0, vbuf, nullptr);
     __syncthreads();
-    const int kn = min(KT, N - k0);
-    if (live) {
-      for (int kk = 0; kk < kn; ++kk) {
-        const int k = k0 + kk;
-        if (!mrow[k]) continue;  // masked: no gradient reaches q
-        float s = zrow[k];
+    const uint32_t w32[2] = {k0 < N ? kr[k0 >> 5] : 0u, k0 + 32 < N ? kr[(k0 >> 5) + 1] : 0u};
 #pragma unroll
-        for (int u = 0; u < DH; ++u) s += q[u] * ks[kk][u];
-        const float p = expf(s - m) / l;
-        float da = 0.f;
-        if (keep_word(a, b, i, t, j, k) >= a.thr) {
+    for (int kb = 0; kb < 4; ++kb) {
+      uint32_t vm;
+      const f32x4 st = score_tile_t<DH>(a, kbuf, qf, zq, k0, kb, g, r16, &vm);
+      // dP^T = v do^T (keys x the lane's query)
+      f32x4 dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int u = 0; u < DH; ++u) da += dov[u] * vs[kk][u];
-          da *= a.scale;
-        }
-        const float ds = p * (da - Dv);
+      for (int cb = 0; cb < CB; ++cb) {
+        const float4 vv = *reinterpret_cast<const float4 *>(vbuf + (kb * 16 + r16) * S::KP + 16 * cb + 4 * g);
+        dp = mfma(vv.x, df[cb][0], dp);
+        dp = mfma(vv.y, df[cb][1], dp);
+        dp = mfma(vv.z, df[cb][2], dp);
+        dp = mfma(vv.w, df[cb][3], dp);
+      }
+      const uint32_t nib = w32[kb >> 1] >> (16 * (kb & 1) + 4 * g);
+      float ds[4];
 #pragma unroll
-        for (int u = 0; u < DH; ++u) dq[u] += ds * ks[kk][u];
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = (vm >> r) & 1u;
+        const float p = fast_exp2(st[r] - m2) * linv;
+        const float da = (nib >> r) & 1u ? dp[r] * a.scale : 0.f;
+        ds[r] = valid ? p * (da - Dv) : 0.f;
+      }
+      // dq^T += k^T dS^T
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float4 kv = *reinterpret_cast<const float4 *>(kT + (16 * cb + r16) * S::TP + kb * 16 + 4 * g);
+        dq[cb] = mfma(kv.x, ds[0], dq[cb]);
+        dq[cb] = mfma(kv.y, ds[1], dq[cb]);
+        dq[cb] = mfma(kv.z, ds[2], dq[cb]);
+        dq[cb] = mfma(kv.w, ds[3], dq[cb]);
       }
     }
     __syncthreads();
   }
-  if (!live) return;
+  if (j >= N) return;
 #pragma unroll
-  for (int u = 0; u < DH; ++u) a.dcat[(rowp + j) * C + t * DH + u] = dq[u] * a.rsd;
+  for (int cb = 0; cb < CB; ++cb)
+    stg<float4>(a.dcat + (rowp + j) * C + t * DH + 16 * cb + 4 * g,
+                make_float4(dq[cb][0] * a.rsd, dq[cb][1] * a.rsd, dq[cb][2] * a.rsd, dq[cb][3] * a.rsd));
 }
 
-// dk and dv per (b, i, t), one thread per key column k; the queries' q, do,
-// m, l and sum_k a da pass through LDS in tiles.
+// dk and dv per (b, i, t, 128 key columns), 8 waves of 16 keys, queries in
+// chunks of 64 through LDS. Here the score tile is S = q k^T (queries in
+// rows): lane l holds queries 4g + r of key r16, the k-slice of the P and dS
+// operands of dv^T = do^T P' and dk^T = q^T dS.
 template <int DH>
-__global__ __launch_bounds__(256) void bwd_attn_dkv(BwdAttnArgs a) {
-  constexpr int QT = 64;
-  __shared__ float qs[QT][DH], dos[QT][DH], ms[QT], ls[QT], Ds[QT];
+__global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
+  using S = BwdTile<DH>;
+  constexpr int CB = S::CB, QT = S::KT;
+  __shared__ __align__(16) float qbuf[QT * S::KP];
+  __shared__ __align__(16) float qT[DH * S::TP];
+  __shared__ __align__(16) float dbuf[QT * S::KP];
+  __shared__ __align__(16) float dT[DH * S::TP];
+  __shared__ float ms[QT], ls[QT], Ds[QT];
+  // the chunk's bias, mask and keep bits for the workgroup's 128 keys
+  __shared__ __align__(16) float zs[QT][S::QB + 4];
+  __shared__ uint32_t kbits[QT][S::QB / 32];
   const int N = a.N, D = a.D, h = a.h, C = a.C;
-  const int bi = blockIdx.x / h, t = blockIdx.x - bi * h, b = bi / N, i = bi - b * N;
-  const int k = blockIdx.y * 256 + threadIdx.x;
-  const bool live = k < N;
+  const int nk = (N + S::QB - 1) / S::QB;
+  const int item = blockIdx.x, kc = item % nk, bt = item / nk, bi = bt / h, t = bt - bi * h, b = bi / N;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  const int k = kc * S::QB + wave * 16 + r16, kcl = min(k, N - 1);
   const size_t rowp = (size_t)bi * N;
-  float kv[DH], vv[DH], dk[DH], dv[DH];
+  f32x4 kf[CB], vf[CB];  // lane: key r16, channels 16 cb + 4g + e (k pre-scaled)
 #pragma unroll
-  for (int u = 0; u < DH; ++u) {
-    kv[u] = live ? a.proj[(rowp + k) * C + D + t * DH + u] : 0.f;
-    vv[u] = live ? a.proj[(rowp + k) * C + 2 * D + t * DH + u] : 0.f;
-    dk[u] = dv[u] = 0.f;
+  for (int cb = 0; cb < CB; ++cb) {
+    const float4 k4 = ldg<float4>(a.proj + (rowp + kcl) * C + D + t * DH + 16 * cb + 4 * g);
+    const float4 v4 = ldg<float4>(a.proj + (rowp + kcl) * C + 2 * D + t * DH + 16 * cb + 4 * g);
+    kf[cb] = (f32x4){k4.x, k4.y, k4.z, k4.w} * a.qs;
+    vf[cb] = (f32x4){v4.x, v4.y, v4.z, v4.w};
   }
-  const size_t st0 = ((size_t)bi * h + t) * N;
+  f32x4 dk[CB], dv[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) dk[cb] = dv[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const float *zb = a.zt + (size_t)(b * h + t) * N * N;
   for (int j0 = 0; j0 < N; j0 += QT) {
-    for (int e = threadIdx.x; e < QT * DH; e += 256) {
-      const int jj = e / DH, u = e - jj * DH, j = j0 + jj;
-      qs[jj][u] = j < N ? a.proj[(rowp + j) * C + t * DH + u] * a.rsd : 0.f;
-      dos[jj][u] = j < N ? a.dob[(rowp + j) * D + t * DH + u] : 0.f;
-    }
-    for (int jj = threadIdx.x; jj < QT; jj += 256) {
-      const int j = j0 + jj;
-      ms[jj] = j < N ? a.m[st0 + j] : 0.f;
-      ls[jj] = j < N ? a.l[st0 + j] : 1.f;
-      Ds[jj] = j < N ? a.Dj[st0 + j] : 0.f;
+    // the chunk's q and do rows of head t ([query][c] and [c][query]) and statistics
+    {
+      constexpr int V4 = QT * DH / 4;
+      for (int e = threadIdx.x; e < V4; e += S::NW * 64) {
+        const int jj = e / (DH / 4), u4 = (e - jj * (DH / 4)) * 4, jq = j0 + jj;
+        float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f), d4 = q4;
+        if (jq < N) {
+          q4 = ldg<float4>(a.proj + (rowp + jq) * C + t * DH + u4);
+          d4 = ldg<float4>(a.dob + (rowp + jq) * D + t * DH + u4);
+        }
+        *reinterpret_cast<float4 *>(qbuf + jj * S::KP + u4) = q4;
+        *reinterpret_cast<float4 *>(dbuf + jj * S::KP + u4) = d4;
+        const float qa[4] = {q4.x, q4.y, q4.z, q4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          qT[(u4 + c) * S::TP + jj] = qa[c];
+          dT[(u4 + c) * S::TP + jj] = da[c];
+        }
+      }
+      for (int jj = threadIdx.x; jj < QT; jj += S::NW * 64) {
+        const int jq = j0 + jj;
+        const size_t st_ = ((size_t)bi * h + t) * N + jq;
+        ms[jj] = jq < N ? a.m[st_] : 0.f;
+        ls[jj] = jq < N ? a.l[st_] : 1.f;
+        Ds[jj] = jq < N ? a.Dj[st_] : 0.f;
+      }
+      const int kw0 = (kc * S::QB) >> 5;
+      for (int e = threadIdx.x; e < QT * S::QB; e += S::NW * 64) {
+        const int jj = e / S::QB, kk = e - jj * S::QB, jq = j0 + jj, kq = kc * S::QB + kk;
+        const bool in = jq < N && kq < N;
+        zs[jj][kk] = in ? zb[(size_t)jq * N + kq] : 0.f;
+      }
+      for (int e = threadIdx.x; e < QT * (S::QB / 32); e += S::NW * 64) {
+        const int jj = e / (S::QB / 32), w = e - jj * (S::QB / 32), jq = j0 + jj;
+        kbits[jj][w] = (jq < N && kw0 + w < a.NW) ? keep_row(a, bi, t, jq)[kw0 + w] : 0u;
+      }
     }
     __syncthreads();
-    const int jn = min(QT, N - j0);
-    if (live) {
-      for (int jj = 0; jj < jn; ++jj) {
-        const int j = j0 + jj;
-        const bool valid = a.mask[((size_t)b * N + j) * N + k] != 0;
-        float s = a.zt[((size_t)(b * h + t) * N + j) * N + k];
 #pragma unroll
-        for (int u = 0; u < DH; ++u) s += qs[jj][u] * kv[u];
-        if (!valid) s = a.fill;
-        const float p = (s == -INFINITY) ? 0.f : expf(s - ms[jj]) / ls[jj];
-        const bool kept = keep_word(a, b, i, t, j, k) >= a.thr;
-        float da = 0.f;
-        if (kept) {
-          const float pw = p * a.scale;
+    for (int qb = 0; qb < 4; ++qb) {
+      const int jb = j0 + qb * 16 + 4 * g;  // the lane's queries jb + r
+      // S = q k^T (queries x keys): bias, product, mask, padding
+      const int kk = wave * 16 + r16;  // the lane's key within the workgroup's 128
+      f32x4 s;
 #pragma unroll
-          for (int u = 0; u < DH; ++u) {
-            dv[u] += pw * dos[jj][u];
-            da += dos[jj][u] * vv[u];
-          }
-          da *= a.scale;
-        }
-        if (valid) {
-          const float ds = p * (da - Ds[jj]);
+      for (int r = 0; r < 4; ++r) s[r] = zs[qb * 16 + 4 * g + r][kk];
+      const f32x4 s0 = s;
 #pragma unroll
-          for (int u = 0; u < DH; ++u) dk[u] += ds * qs[jj][u];
-        }
+      for (int cb = 0; cb < CB; ++cb) {
+        const float4 qv = *reinterpret_cast<const float4 *>(qbuf + (qb * 16 + r16) * S::KP + 16 * cb + 4 * g);
+        s = mfma(qv.x, kf[cb][0], s);
+        s = mfma(qv.y, kf[cb][1], s);
+        s = mfma(qv.z, kf[cb][2], s);
+        s = mfma(qv.w, kf[cb][3], s);
+      }
+      // dP = do v^T
+      f32x4 dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float4 dv4 = *reinterpret_cast<const float4 *>(dbuf + (qb * 16 + r16) * S::KP + 16 * cb + 4 * g);
+        dp = mfma(dv4.x, vf[cb][0], dp);
+        dp = mfma(dv4.y, vf[cb][1], dp);
+        dp = mfma(dv4.z, vf[cb][2], dp);
+        dp = mfma(dv4.w, vf[cb][3], dp);
+      }
+      float pk[4], ds[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jq = jb + r, jj = qb * 16 + 4 * g + r;
+        const bool in = jq < N && k < N;
+        const bool valid = in && s0[r] != a.fill2;
+        const float sl = !in ? -INFINITY : (valid ? s[r] : a.fill2);
+        const float p = sl == -INFINITY ? 0.f : fast_exp2(sl - ms[jj]) / ls[jj];
+        const bool kp = in && ((kbits[jj][kk >> 5] >> (kk & 31)) & 1u);
+        const float da = kp ? dp[r] * a.scale : 0.f;
+        pk[r] = kp ? p * a.scale : 0.f;
+        ds[r] = valid ? p * (da - Ds[jj]) : 0.f;
+      }
+      // dv^T += do^T P', dk^T += q^T dS
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float4 dv4 = *reinterpret_cast<const float4 *>(dT + (16 * cb + r16) * S::TP + qb * 16 + 4 * g);
+        const float4 qv = *reinterpret_cast<const float4 *>(qT + (16 * cb + r16) * S::TP + qb * 16 + 4 * g);
+        dv[cb] = mfma(dv4.x, pk[0], dv[cb]);
+        dv[cb] = mfma(dv4.y, pk[1], dv[cb]);
+        dv[cb] = mfma(dv4.z, pk[2], dv[cb]);
+        dv[cb] = mfma(dv4.w, pk[3], dv[cb]);
+        dk[cb] = mfma(qv.x, ds[0], dk[cb]);
+        dk[cb] = mfma(qv.y, ds[1], dk[cb]);
+        dk[cb] = mfma(qv.z, ds[2], dk[cb]);
+        dk[cb] = mfma(qv.w, ds[3], dk[cb]);
       }
     }
     __syncthreads();
   }
-  if (!live) return;
+  if (k >= N) return;
+  // lane: channels 16 cb + 4g + r of key r16
 #pragma unroll
-  for (int u = 0; u < DH; ++u) {
-    a.dcat[(rowp + k) * C + D + t * DH + u] = dk[u];
-    a.dcat[(rowp + k) * C + 2 * D + t * DH + u] = dv[u];
+  for (int cb = 0; cb < CB; ++cb) {
+    stg<float4>(a.dcat + (rowp + k) * C + D + t * DH + 16 * cb + 4 * g,
+                make_float4(dk[cb][0] * a.rsd, dk[cb][1] * a.rsd, dk[cb][2] * a.rsd, dk[cb][3] * a.rsd));
+    stg<float4>(a.dcat + (rowp + k) * C + 2 * D + t * DH + 16 * cb + 4 * g,
+                make_float4(dv[cb][0], dv[cb][1], dv[cb][2], dv[cb][3]));
   }
 }
 
-// dz[b,t,j,k] = sum over rows i of ds, masked, per (b, t, 16 query columns j,
-// 64 key columns k): each thread owns one query and four keys; per row i the
-// keys' k and v and the queries' q, do, m, l and sum a da pass through LDS.
+// dz[b,t,j,k] = sum over rows i of ds, masked, per (b, t, 64 query columns j,
+// 64 key columns k): thread (tj, tk) owns queries j0 + tj + 16a and keys
+// k0 + tk + 16c (a, c = 0..3, a 4 x 4 register block); per row i the keys' k
+// and v, the queries' q, do, m2, l and sum a da, and the keep bits pass
+// through LDS.
 template <int DH>
 __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
-  constexpr int JT = 16, KT = 64;
-  __shared__ float ks[KT][DH + 1], vs[KT][DH + 1], qs[JT][DH], dos[JT][DH], ms[JT], ls[JT], Ds[JT];
+  constexpr int JT = 64, KT = 64, RP = DH + 4;
+  __shared__ __align__(16) float ks[KT][RP], vs[KT][RP], qs[JT][RP], dos[JT][RP];
+  __shared__ float ms[JT], ls[JT], Ds[JT];
+  __shared__ uint32_t kb[JT][2];
   const int N = a.N, D = a.D, h = a.h, C = a.C;
   const int nkt = (N + KT - 1) / KT;
   const int bt = blockIdx.y, b = bt / h, t = bt - b * h;
   const int j0 = (blockIdx.x / nkt) * JT, k0 = (blockIdx.x % nkt) * KT;
-  const int jj = threadIdx.x >> 4, j = j0 + jj;
-  float dz[4] = {0.f, 0.f, 0.f, 0.f};
+  const int tj = threadIdx.x >> 4, tk = threadIdx.x & 15;
+  float dz[4][4], zr[4][4];
+  uint32_t valid = 0;  // bit 4 qa + c
   // the bias and the mask of (j, k) are the same for every row i
-  float zr[4];
-  bool valid[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int k = k0 + (threadIdx.x & 15) + 16 * r;
-    valid[r] = j < N && k < N && a.mask[((size_t)b * N + j) * N + k] != 0;
-    zr[r] = valid[r] ? a.zt[((size_t)(b * h + t) * N + j) * N + k] : 0.f;
-  }
+  for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = j0 + tj + 16 * qa, k = k0 + tk + 16 * c;
+      const float zl = (j < N && k < N) ? a.zt[((size_t)(b * h + t) * N + j) * N + k] : a.fill2;
+      const bool v = j < N && k < N && zl != a.fill2;
+      valid |= (uint32_t)v << (4 * qa + c);
+      zr[qa][c] = v ? zl : 0.f;
+      dz[qa][c] = 0.f;
+    }
   for (int i = 0; i < N; ++i) {
     const size_t rowp = ((size_t)b * N + i) * N;
-    for (int e = threadIdx.x; e < KT * DH; e += 256) {
-      const int kk = e / DH, u = e - kk * DH, k = k0 + kk;
-      ks[kk][u] = k < N ? a.proj[(rowp + k) * C + D + t * DH + u] : 0.f;
-      vs[kk][u] = k < N ? a.proj[(rowp + k) * C + 2 * D + t * DH + u] : 0.f;
-    }
-    for (int e = threadIdx.x; e < JT * DH; e += 256) {
-      const int q = e / DH, u = e - q * DH, jq = j0 + q;
-      qs[q][u] = jq < N ? a.proj[(rowp + jq) * C + t * DH + u] * a.rsd : 0.f;
-      dos[q][u] = jq < N ? a.dob[(rowp + jq) * D + t * DH + u] : 0.f;
+    for (int e = threadIdx.x; e < KT * DH / 4; e += 256) {
+      const int r = e / (DH / 4), u4 = (e - r * (DH / 4)) * 4;
+      const int k = k0 + r, j = j0 + r;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv, qv = kv, dv = kv;
+      if (k < N) {
+        kv = ldg<float4>(a.proj + (rowp + k) * C + D + t * DH + u4);
+        vv = ldg<float4>(a.proj + (rowp + k) * C + 2 * D + t * DH + u4);
+      }
+      if (j < N) {
+        qv = ldg<float4>(a.proj + (rowp + j) * C + t * DH + u4);
+        dv = ldg<float4>(a.dob + (rowp + j) * D + t * DH + u4);
+      }
+      *reinterpret_cast<float4 *>(&ks[r][u4]) = kv;
+      *reinterpret_cast<float4 *>(&vs[r][u4]) = vv;
+      *reinterpret_cast<float4 *>(&qs[r][u4]) = make_float4(qv.x * a.qs, qv.y * a.qs, qv.z * a.qs, qv.w * a.qs);
+      *reinterpret_cast<float4 *>(&dos[r][u4]) = dv;
     }
     if (threadIdx.x < JT) {
       const int jq = j0 + threadIdx.x;
@@ -438,44 +663,69 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
       ms[threadIdx.x] = jq < N ? a.m[st] : 0.f;
       ls[threadIdx.x] = jq < N ? a.l[st] : 1.f;
       Ds[threadIdx.x] = jq < N ? a.Dj[st] : 0.f;
+      const uint32_t *kr = keep_row(a, b * N + i, t, jq < N ? jq : 0);
+      const int w0 = k0 >> 5;
+      kb[threadIdx.x][0] = jq < N ? kr[w0] : 0u;
+      kb[threadIdx.x][1] = (jq < N && w0 + 1 < a.NW) ? kr[w0 + 1] : 0u;
     }
     __syncthreads();
-    if (j < N) {
+    float sq[4][4], da[4][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = (threadIdx.x & 15) + 16 * r, k = k0 + kk;
-        if (!valid[r]) continue;
-        float s = zr[r];
+    for (int qa = 0; qa < 4; ++qa)
 #pragma unroll
-        for (int u = 0; u < DH; ++u) s += qs[jj][u] * ks[kk][u];
-        const float p = expf(s - ms[jj]) / ls[jj];
-        float da = 0.f;
-        if (keep_word(a, b, i, t, j, k) >= a.thr) {
+      for (int c = 0; c < 4; ++c) sq[qa][c] = da[qa][c] = 0.f;
+#pragma unroll 1
+    for (int u = 0; u < DH; u += 4) {
+      float4 q4[4], d4[4], k4[4], v4[4];
 #pragma unroll
-          for (int u = 0; u < DH; ++u) da += dos[jj][u] * vs[kk][u];
-          da *= a.scale;
+      for (int x = 0; x < 4; ++x) {
+        q4[x] = *reinterpret_cast<const float4 *>(&qs[tj + 16 * x][u]);
+        d4[x] = *reinterpret_cast<const float4 *>(&dos[tj + 16 * x][u]);
+        k4[x] = *reinterpret_cast<const float4 *>(&ks[tk + 16 * x][u]);
+        v4[x] = *reinterpret_cast<const float4 *>(&vs[tk + 16 * x][u]);
+      }
+#pragma unroll
+      for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          sq[qa][c] += q4[qa].x * k4[c].x + q4[qa].y * k4[c].y + q4[qa].z * k4[c].z + q4[qa].w * k4[c].w;
+          da[qa][c] += d4[qa].x * v4[c].x + d4[qa].y * v4[c].y + d4[qa].z * v4[c].z + d4[qa].w * v4[c].w;
         }
-        dz[r] += p * (da - Ds[jj]);
+    }
+#pragma unroll
+    for (int qa = 0; qa < 4; ++qa) {
+      const int jj = tj + 16 * qa;
+      const float m2 = ms[jj], linv = 1.f / ls[jj], Dv = Ds[jj];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int kk = tk + 16 * c;
+        const float p = fast_exp2(zr[qa][c] + sq[qa][c] - m2) * linv;
+        const float dav = (kb[jj][kk >> 5] >> (kk & 31)) & 1u ? da[qa][c] * a.scale : 0.f;
+        if ((valid >> (4 * qa + c)) & 1u) dz[qa][c] += p * (dav - Dv);
       }
     }
     __syncthreads();
   }
-  if (j >= N) return;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int k = k0 + (threadIdx.x & 15) + 16 * r;
-    if (k < N) a.dcat[(((size_t)b * N + j) * N + k) * C + 4 * D + t] = dz[r];
-  }
+  for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = j0 + tj + 16 * qa, k = k0 + tk + 16 * c;
+      if (j < N && k < N) a.dcat[(((size_t)b * N + j) * N + k) * C + 4 * D + t] = dz[qa][c];
+    }
 }
 
-// z[b,t,j,k] from the projection columns, into a [B][h][N][N] copy
-__global__ __launch_bounds__(256) void bwd_ztrans(const float *proj, int B, int N, int D, int h, int C, float *zt) {
+// z[b,t,j,k] * log2(e) from the projection columns, FILL * log2(e) where the
+// mask is 0, into a [B][h][N][N] copy: the attention kernels tell a masked
+// key by that exact value and read no mask
+__global__ __launch_bounds__(256) void bwd_ztrans(const float *proj, const uint8_t *mask, float fill2, int B, int N,
+                                                   int D, int h, int C, float *zt) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long total = (long long)B * h * N * N;
   if (e >= total) return;
   const long long jk = e % ((long long)N * N), bt = e / ((long long)N * N);
   const int b = (int)(bt / h), t = (int)(bt - (long long)b * h);
-  zt[e] = proj[((size_t)b * N * N + jk) * C + 4 * D + t];
+  zt[e] = mask[(size_t)b * N * N + jk] ? proj[((size_t)b * N * N + jk) * C + 4 * D + t] * kLog2e : fill2;
 }
 
 // Output and gate step per (position, head): dg, dgp (into dcat), do, g * o.
@@ -497,7 +747,7 @@ __global__ __launch_bounds__(256) void bwd_gate(const float *dgo, const float *p
 
 // ------------------------------------------------------------------ host side
 struct BwdLayout {
-  size_t x, xhat, rstd, proj, zt, m, l, Dj, o, dgo, dob, go, dcat, dx, part, vpart, total;
+  size_t x, xhat, rstd, proj, zt, m, l, Dj, o, dgo, dob, go, dcat, dx, part, vpart, bits, total;
   long long S, kchunk, nvblk, vper;
 };
 
@@ -535,6 +785,7 @@ static BwdLayout bwd_layout(int B, int N, int D, int h) {
   L.dx = take((size_t)P * D * 4);
   L.part = take((size_t)L.S * C * D * 4);
   L.vpart = take((size_t)2 * L.nvblk * D * 4);
+  L.bits = take((size_t)B * N * h * N * ((N + 31) / 32) * 4);
   L.total = off;
   return L;
 }
@@ -582,19 +833,31 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
                      xhat, rstd);
   TPA_CHECK(hipGetLastError());
   TPA_CHECK((gemm<float, T>(x, D, 1, r.wpack, 1, D, proj, 0, C, P, C, D, D, 1, s)));
-  hipLaunchKernelGGL(bwd_ztrans, dim3((unsigned)(((long long)B * h * N * N + 255) / 256)), dim3(256), 0, s, proj, B,
-                     N, D, h, (int)C, zt);
+  hipLaunchKernelGGL(bwd_ztrans, dim3((unsigned)(((long long)B * h * N * N + 255) / 256)), dim3(256), 0, s, proj,
+                     r.mask, r.fill * kLog2e, B, N, D, h, (int)C, zt);
   TPA_CHECK(hipGetLastError());
   BwdAttnArgs aa{};
   aa.proj = proj, aa.zt = zt, aa.mask = r.mask;
   aa.m = reinterpret_cast<float *>(w + L.m), aa.l = reinterpret_cast<float *>(w + L.l);
   aa.Dj = reinterpret_cast<float *>(w + L.Dj);
   aa.o = o, aa.dob = dob, aa.dcat = dcat;
-  aa.fill = r.fill, aa.scale = r.scale, aa.rsd = 1.0f / sqrtf((float)DH);
+  aa.fill2 = r.fill * kLog2e, aa.scale = r.scale, aa.rsd = 1.0f / sqrtf((float)DH);
+  aa.qs = kLog2e * aa.rsd;
   aa.thr = r.thr, aa.seed_lo = r.seed_lo, aa.seed_hi = r.seed_hi, aa.offset = r.offset;
   aa.B = B, aa.N = N, aa.D = D, aa.h = h, aa.C = (int)C;
-  const dim3 ga((unsigned)(B * N * h), (unsigned)((N + 255) / 256));  // x: (b, i, t), y: column block
-  hipLaunchKernelGGL((bwd_attn_fwd<DH>), ga, dim3(256), 0, s, aa);
+  aa.NW = (N + 31) / 32;
+  uint32_t *bits = reinterpret_cast<uint32_t *>(w + L.bits);
+  aa.bits = bits;
+  {
+    const long long nwords = (long long)B * N * h * N * aa.NW;
+    hipLaunchKernelGGL(bwd_keep_bits, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s, aa, bits, nwords);
+    TPA_CHECK(hipGetLastError());
+  }
+  // work items (b, i, t, 128 columns): x only, so no grid limit applies
+  const long long items = (long long)B * N * h * ((N + BwdTile<DH>::QB - 1) / BwdTile<DH>::QB);
+  if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 ga((unsigned)items);
+  hipLaunchKernelGGL((bwd_attn_fwd<DH>), ga, dim3(512), 0, s, aa);
   TPA_CHECK(hipGetLastError());
   // output projection and gate
   TPA_CHECK((gemm<T, T>(r.dy, D, 1, Wo, D, 1, dgo, 0, D, P, D, D, D, 1, s)));
@@ -602,11 +865,11 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
                      (int)C, dcat, dob, go);
   TPA_CHECK(hipGetLastError());
   // attention
-  hipLaunchKernelGGL((bwd_attn_dq<DH>), ga, dim3(256), 0, s, aa);
+  hipLaunchKernelGGL((bwd_attn_dq<DH>), ga, dim3(512), 0, s, aa);
   TPA_CHECK(hipGetLastError());
-  hipLaunchKernelGGL((bwd_attn_dkv<DH>), ga, dim3(256), 0, s, aa);
+  hipLaunchKernelGGL((bwd_attn_dkv<DH>), ga, dim3(512), 0, s, aa);
   TPA_CHECK(hipGetLastError());
-  const int nkt = (N + 63) / 64, njt = (N + 15) / 16;
+  const int nkt = (N + 63) / 64, njt = (N + 63) / 64;
   hipLaunchKernelGGL((bwd_attn_dz<DH>), dim3((unsigned)(njt * nkt), (unsigned)(B * h)), dim3(256), 0, s, aa);
   TPA_CHECK(hipGetLastError());
   // projections and LayerNorm
