@@ -34,14 +34,26 @@ namespace tpa {
 // ------------------------------------------------------------------ products
 // C[z][m][n] = sum over k in chunk z of A[m, k] B[k, n]; A(m, k) at
 // A[m*sam + k*sak], B(k, n) at B[k*sbk + n*sbn], C(z, m, n) at
-// C[z*scz + m*scm + n]. 64x64 tile per workgroup, 4x4 outputs per thread, K
-// in steps of 16 through LDS, loads laid out along the contiguous index.
+// C[z*scz + m*scm + n]. 64x64 tile per workgroup on the float32 matrix
+// cores, K in steps of 16 through LDS, loads laid out along the contiguous
+// index.
 struct GemmArgs {
   const void *A, *B;
   float *C;
   long long M, N, K, kchunk;
   long long sam, sak, sbk, sbn, scz, scm;
 };
+
+// four consecutive elements (the first one's index a multiple of 4), as floats
+template <typename T>
+__device__ __forceinline__ float4 ld4(const void *p, size_t i) {
+  if constexpr (is_bf16<T>::value) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p) + i);
+    return make_float4(bflo(u.x), bfhi(u.x), bflo(u.y), bfhi(u.y));
+  } else {
+    return *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p) + i);
+  }
+}
 
 template <typename TA, typename TB>
 __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
@@ -52,49 +64,94 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   const long long m0 = (long long)blockIdx.x * 64, n0 = (long long)blockIdx.y * 64;
   const long long kb = (long long)blockIdx.z * g.kchunk;
   const long long ke = min(kb + g.kchunk, g.K);
-  const int tm = tid >> 4, tn = tid & 15;
-  float acc[4][4];
+  // wave w computes the 32 x 32 quadrant (w / 2, w % 2) as 2 x 2 float32
+  // 16x16x4 matrix-core tiles; in step s of a 16-deep K slice, lane group g
+  // takes k = 4s + g for both operands
+  const int lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x4 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const bool a_m_contig = g.sam == 1, b_n_contig = g.sbn == 1;
   for (long long k0 = kb; k0 < ke; k0 += 16) {
+    // each thread stages four consecutive elements of A and of B along
+    // their contiguous index (one 16- or 8-byte load when all four are in range)
+    {
+      const int lin = a_m_contig ? ((tid & 15) * 4) : ((tid & 3) * 4);  // 4 along the contiguous index
+      const int oth = a_m_contig ? (tid >> 4) : (tid >> 2);             // the other index
+      const long long am = m0 + (a_m_contig ? lin : oth), ak = k0 + (a_m_contig ? oth : lin);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool full = a_m_contig ? (am + 3 < g.M && ak < ke) : (am < g.M && ak + 3 < ke);
+      if (full) {
+        v = ld4<TA>(g.A, (size_t)(am * g.sam + ak * g.sak));
+      } else {
+        float t4[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = tid + 256 * e;
-      const int mm = a_m_contig ? (idx & 63) : (idx >> 4), ka = a_m_contig ? (idx >> 6) : (idx & 15);
-      const long long am = m0 + mm, ak = k0 + ka;
-      As[ka][mm] = (am < g.M && ak < ke) ? ld_elem<TA>(g.A, (size_t)(am * g.sam + ak * g.sak)) : 0.f;
-      const int nn = b_n_contig ? (idx & 63) : (idx >> 4), kbk = b_n_contig ? (idx >> 6) : (idx & 15);
-      const long long bn = n0 + nn, bk = k0 + kbk;
-      Bs[kbk][nn] = (bn < g.N && bk < ke) ? ld_elem<TB>(g.B, (size_t)(bk * g.sbk + bn * g.sbn)) : 0.f;
+        for (int c = 0; c < 4; ++c) {
+          const long long mm = am + (a_m_contig ? c : 0), kk = ak + (a_m_contig ? 0 : c);
+          t4[c] = (mm < g.M && kk < ke) ? ld_elem<TA>(g.A, (size_t)(mm * g.sam + kk * g.sak)) : 0.f;
+        }
+        v = make_float4(t4[0], t4[1], t4[2], t4[3]);
+      }
+      if (a_m_contig) {
+        *reinterpret_cast<float4 *>(&As[oth][lin]) = v;
+      } else {
+        As[lin + 0][oth] = v.x, As[lin + 1][oth] = v.y, As[lin + 2][oth] = v.z, As[lin + 3][oth] = v.w;
+      }
+    }
+    {
+      const int lin = b_n_contig ? ((tid & 15) * 4) : ((tid & 3) * 4);
+      const int oth = b_n_contig ? (tid >> 4) : (tid >> 2);
+      const long long bn = n0 + (b_n_contig ? lin : oth), bk = k0 + (b_n_contig ? oth : lin);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool full = b_n_contig ? (bn + 3 < g.N && bk < ke) : (bn < g.N && bk + 3 < ke);
+      if (full) {
+        v = ld4<TB>(g.B, (size_t)(bk * g.sbk + bn * g.sbn));
+      } else {
+        float t4[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const long long nn = bn + (b_n_contig ? c : 0), kk = bk + (b_n_contig ? 0 : c);
+          t4[c] = (nn < g.N && kk < ke) ? ld_elem<TB>(g.B, (size_t)(kk * g.sbk + nn * g.sbn)) : 0.f;
+        }
+        v = make_float4(t4[0], t4[1], t4[2], t4[3]);
+      }
+      if (b_n_contig) {
+        *reinterpret_cast<float4 *>(&Bs[oth][lin]) = v;
+      } else {
+        Bs[lin + 0][oth] = v.x, Bs[lin + 1][oth] = v.y, Bs[lin + 2][oth] = v.z, Bs[lin + 3][oth] = v.w;
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
+    for (int st = 0; st < 4; ++st) {
+      const int kk = 4 * st + g4;
+      float av[2], bv[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[kk][tm * 4 + i];
+      for (int i = 0; i < 2; ++i) av[i] = As[kk][32 * wm + 16 * i + r16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tn * 4 + j];
+      for (int j = 0; j < 2; ++j) bv[j] = Bs[kk][32 * wn + 16 * j + r16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(av[i], bv[j], acc[i][j]);
     }
     __syncthreads();
   }
+  // lane: rows 4 g4 + r, column r16 of each tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const long long m = m0 + tm * 4 + i;
-    if (m >= g.M) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long long n = n0 + tn * 4 + j;
-      if (n < g.N) g.C[(size_t)(blockIdx.z * g.scz + m * g.scm + n)] = acc[i][j];
+    for (int j = 0; j < 2; ++j) {
+      const long long n = n0 + 32 * wn + 16 * j + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const long long m = m0 + 32 * wm + 16 * i + 4 * g4 + r;
+        if (m < g.M && n < g.N) g.C[(size_t)(blockIdx.z * g.scz + m * g.scm + n)] = acc[i][j][r];
+      }
     }
-  }
 }
 
 // out[e] = sum over z of part[z*stride + e], z = 0..nz-1 in order
@@ -107,15 +164,33 @@ __global__ __launch_bounds__(256) void bwd_reduce(const float *part, long long n
   out[e] = s;
 }
 
-// part[blk][c] = sum over positions p of block blk of X[p*ldx + c] (c < ncol)
+// part[blk][c] = sum over positions p of block blk of X[p*ldx + c] (c < ncol):
+// the block's 256 threads cover 256 / ncol groups of positions (each thread
+// one column), eight independent partial sums per thread, then the groups
+// are added in a fixed order through LDS
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_colsum(const void *X, long long P, int ncol, long long ldx,
                                                    long long per_blk, float *part) {
+  __shared__ float red[256];
   const long long p0 = (long long)blockIdx.x * per_blk, p1 = min(p0 + per_blk, P);
-  for (int c = threadIdx.x; c < ncol; c += 256) {
-    float s = 0.f;
-    for (long long p = p0; p < p1; ++p) s += ld_elem<T>(X, (size_t)(p * ldx + c));
-    part[(size_t)blockIdx.x * ncol + c] = s;
+  const int ng = 256 / ncol, grp = threadIdx.x / ncol, c = threadIdx.x - grp * ncol;
+  float s = 0.f;
+  if (grp < ng) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    long long p = p0 + grp;
+    for (; p + 7 * ng < p1; p += 8 * ng) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += ld_elem<T>(X, (size_t)((p + u * ng) * ldx + c));
+    }
+    for (; p < p1; p += ng) acc[0] += ld_elem<T>(X, (size_t)(p * ldx + c));
+    s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < ncol) {
+    float t = 0.f;
+    for (int q = 0; q < ng; ++q) t += red[q * ncol + threadIdx.x];
+    part[(size_t)blockIdx.x * ncol + threadIdx.x] = t;
   }
 }
 
@@ -153,38 +228,56 @@ __global__ __launch_bounds__(256) void bwd_ln(const void *P, const void *gamma, 
   if (lane == 0) rstd[p] = r;
 }
 
-// LayerNorm backward per position, and per-block partial sums of dx * x-hat
-// (for dgamma) and dx (for dbeta): block blk covers positions blk*per .. .
+// LayerNorm backward per position, one wave per position (4 waves per
+// block, stepping through the block's positions), and per-block partial sums
+// of dx * x-hat (for dgamma) and dx (for dbeta): block blk covers positions
+// blk*per .. ; the four waves' partials are added in a fixed order.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void bwd_ln_back(const float *dx, const float *xhat, const float *rstd,
-                                                  const void *gamma, long long npos, long long per_blk, float *dP,
-                                                  float *part_g, float *part_b) {
-  __shared__ float red[2][D / 64];
-  const int c = threadIdx.x, lane = c & 63, wave = c >> 6;
-  const float gm = ld_elem<T>(gamma, c);
+__global__ __launch_bounds__(256) void bwd_ln_back(const float *dx, const float *xhat, const float *rstd,
+                                                    const void *gamma, long long npos, long long per_blk, float *dP,
+                                                    float *part_g, float *part_b) {
+  constexpr int PER = D / 64;
+  __shared__ float red[2][4][D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float gm[PER], sg[PER], sb[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    gm[e] = ld_elem<T>(gamma, lane + 64 * e);
+    sg[e] = sb[e] = 0.f;
+  }
   const long long p0 = (long long)blockIdx.x * per_blk, p1 = min(p0 + per_blk, npos);
-  float sg = 0.f, sb = 0.f;
-  for (long long p = p0; p < p1; ++p) {
-    const float d = dx[p * D + c], xh = xhat[p * D + c];
-    sg += d * xh;
-    sb += d;
-    const float dxh = d * gm;
-    float s1 = dxh, s2 = dxh * xh;
+  for (long long p = p0 + wave; p < p1; p += 4) {
+    float d[PER], xh[PER], s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      d[e] = dx[p * D + lane + 64 * e];
+      xh[e] = xhat[p * D + lane + 64 * e];
+      sg[e] += d[e] * xh[e];
+      sb[e] += d[e];
+      const float dxh = d[e] * gm[e];
+      s1 += dxh;
+      s2 += dxh * xh[e];
+    }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       s1 += __shfl_xor(s1, m, 64);
       s2 += __shfl_xor(s2, m, 64);
     }
-    if (lane == 0) red[0][wave] = s1, red[1][wave] = s2;
-    __syncthreads();
-    float t1 = 0.f, t2 = 0.f;
+    const float r = rstd[p];
 #pragma unroll
-    for (int w = 0; w < D / 64; ++w) t1 += red[0][w], t2 += red[1][w];
-    __syncthreads();
-    dP[p * D + c] = (dxh - t1 / D - xh * (t2 / D)) * rstd[p];
+    for (int e = 0; e < PER; ++e)
+      dP[p * D + lane + 64 * e] = (d[e] * gm[e] - s1 / D - xh[e] * (s2 / D)) * r;
   }
-  part_g[(size_t)blockIdx.x * D + c] = sg;
-  part_b[(size_t)blockIdx.x * D + c] = sb;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    red[0][wave][lane + 64 * e] = sg[e];
+    red[1][wave][lane + 64 * e] = sb[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += 256) {
+    part_g[(size_t)blockIdx.x * D + c] = (red[0][0][c] + red[0][1][c]) + (red[0][2][c] + red[0][3][c]);
+    part_b[(size_t)blockIdx.x * D + c] = (red[1][0][c] + red[1][1][c]) + (red[1][2][c] + red[1][3][c]);
+  }
 }
 
 // ------------------------------------------------------------------ attention
@@ -874,7 +967,7 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   TPA_CHECK(hipGetLastError());
   // projections and LayerNorm
   TPA_CHECK((gemm<float, T>(dcat, C, 1, r.wpack, D, 1, dx, 0, D, P, D, C, C, 1, s)));
-  hipLaunchKernelGGL((bwd_ln_back<T, D>), dim3((unsigned)L.nvblk), dim3(D), 0, s, dx, xhat, rstd, gamma, P, L.vper,
+  hipLaunchKernelGGL((bwd_ln_back<T, D>), dim3((unsigned)L.nvblk), dim3(256), 0, s, dx, xhat, rstd, gamma, P, L.vper,
                      r.g.d_pair_repr, vpart, vpart + (size_t)L.nvblk * D);
   TPA_CHECK(hipGetLastError());
   TPA_CHECK(reduce(vpart, D, (int)L.nvblk, D, r.g.d_ln_weight, s));
