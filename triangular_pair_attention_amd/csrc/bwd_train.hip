@@ -622,10 +622,18 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
         Ds[jj] = jq < N ? a.Dj[st_] : 0.f;
       }
       const int kw0 = (kc * S::QB) >> 5;
-      for (int e = threadIdx.x; e < QT * S::QB; e += S::NW * 64) {
-        const int jj = e / S::QB, kk = e - jj * S::QB, jq = j0 + jj, kq = kc * S::QB + kk;
-        const bool in = jq < N && kq < N;
-        zs[jj][kk] = in ? zb[(size_t)jq * N + kq] : 0.f;
+      for (int e = threadIdx.x; e < QT * S::QB / 4; e += S::NW * 64) {
+        const int jj = e / (S::QB / 4), kk = (e - jj * (S::QB / 4)) * 4, jq = j0 + jj, kq = kc * S::QB + kk;
+        float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (jq < N && kq + 3 < N && (N & 3) == 0) {  // rows of z are 16-byte aligned when N % 4 == 0
+          z4 = ldg<float4>(zb + (size_t)jq * N + kq);
+        } else if (jq < N) {
+          float t4[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) t4[c] = kq + c < N ? zb[(size_t)jq * N + kq + c] : 0.f;
+          z4 = make_float4(t4[0], t4[1], t4[2], t4[3]);
+        }
+        *reinterpret_cast<float4 *>(&zs[jj][kk]) = z4;
       }
       for (int e = threadIdx.x; e < QT * (S::QB / 32); e += S::NW * 64) {
         const int jj = e / (S::QB / 32), w = e - jj * (S::QB / 32), jq = j0 + jj;
