@@ -23,8 +23,12 @@
 // fixed chunks whose partial results are added in a fixed order by a second
 // pass: no atomics, the same bits on every call.
 //
-// The kernels are plain float32 code (tiled FMAs for the products): the
-// backward is checked against the oracle's gradients, not tuned.
+// All arithmetic is float32. The products (the projection GEMMs and the
+// attention's score, value and gradient tiles) run on the float32 matrix
+// cores (16x16x4); the dropout decisions are computed once into a bit array
+// (one generator call per four keys) that every attention step reads; the
+// backward's copy of the pair bias carries the mask (FILL where masked), so
+// no attention step reads the mask itself.
 #include "device_common.h"
 #include "tri_attn.h"
 #include "tri_attn_internal.h"
