@@ -162,8 +162,10 @@ typedef struct {
 /* Bytes of device workspace tri_attn_backward_train needs for (B, N): the
  * forward's intermediates in float32 (LayerNorm output, the five
  * projections, the attention output and row statistics), their gradients and
- * the partial sums of the weight gradients; about 4(5D + h) * B * N^2 * 2
- * bytes. B == 0 or N == 0 needs 0 bytes. */
+ * the partial sums of the weight gradients, and the dropout decisions (one
+ * bit per score); about 4(5D + h) * B * N^2 * 2 + B * h * N^3 / 8 bytes, plus
+ * transposed copies of the inputs for ending-node handles. B == 0 or N == 0
+ * needs 0 bytes. */
 int tri_attn_backward_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
 
 /* Backward of tri_attn_forward_train: with dy = dL/dy [B, N, N, D] (config
@@ -179,9 +181,12 @@ int tri_attn_backward_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
  * whatever the config dtype, so nothing from the forward call is needed.
  * Sums over positions are split into fixed chunks and added in a fixed order:
  * deterministic, no atomics. Asynchronous on `stream`; pointers borrowed until
- * the stream work completes. Errors: INVALID_ARG (NULL pointers, sizes, rate
- * outside [0, 1)), WORKSPACE, HIP, UNSUPPORTED (ending-node handles: not
- * built). B == 0 or N == 0 is a no-op. */
+ * the stream work completes. Ending-node handles: the starting-node backward
+ * of the problem with both residue axes of pair_repr, pair_mask and dy
+ * swapped, dL/d(pair_repr) swapped back (the ending-node training forward is
+ * the starting-node one of that transposed problem, dropout counters
+ * included). Errors: INVALID_ARG (NULL pointers, sizes, rate outside
+ * [0, 1)), WORKSPACE, HIP. B == 0 or N == 0 is a no-op. */
 int tri_attn_backward_train(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, const void *dy, int B,
                             int N, double dropout_rate, uint64_t seed, uint32_t offset,
                             const tri_attn_grads *grads, void *workspace, size_t ws_bytes, void *stream);

@@ -16,6 +16,7 @@ import torch
 
 from gpu_helpers import Gpu, log
 from oracle import tri_attn_backward_oracle as BO
+from oracle import tri_attn_oracle as O
 from triangular_pair_attention_amd import binding as B
 from workloads import WORKLOADS, Workload, make_inputs
 
@@ -27,8 +28,8 @@ SHAPE = {"d_pair_repr": "pair_repr", "d_ln_weight": "ln_weight", "d_ln_bias": "l
          "d_w_bias_proj": "w_bias_proj", "d_w_out": "w_out", "d_b_out": "b_out"}
 
 
-def run_backward(inp, dy, rate, seed, offset, fill=-1e9):
-    g = Gpu(inp, fill=fill)
+def run_backward(inp, dy, rate, seed, offset, fill=-1e9, ending=False):
+    g = Gpu(inp, fill=fill, ending=ending)
     try:
         grads = {k: torch.zeros(np.shape(inp[v]), dtype=torch.float32, device=g.dev) for k, v in SHAPE.items()}
         n = B.tri_attn_backward_workspace_size(g.handle, g.B, g.N)
@@ -133,10 +134,26 @@ def test_backward_argument_errors():
         torch.cuda.synchronize()
     finally:
         g.close()
-    e = Gpu(inp, ending=True)
-    try:
-        with pytest.raises(B.TriAttnError) as err:
-            B.tri_attn_backward_train(e.handle, e.P, e.M, torch.zeros_like(e.P), e.B, e.N, 0.1, 1, 0, grads, ws, n)
-        assert err.value.code == B.TRI_ATTN_ERR_UNSUPPORTED
-    finally:
-        e.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,mask", [((2, 20, 64, 4), ("bernoulli", 0.8)), ((1, 33, 128, 4), ("pad", 25)),
+                                        ((1, 40, 128, 8), ("pad", 31))], ids=["B2N20", "N33pad", "N40h8"])
+def test_backward_ending_node(shape, mask, dtype):
+    """Ending-node handles: the ending-node forward is the starting-node one
+    of the problem with both residue axes swapped (dropout counters
+    included), so its gradients are the backward oracle's on the swapped
+    pair_repr, mask and dy, with dL/d(pair_repr) swapped back and every
+    parameter gradient unchanged."""
+    Bn, N, D, h = shape
+    inp = make_inputs(Workload("bwd_end", Bn, N, D, h, dtype, mask, seed=86 + N))
+    dy = make_dy(inp, 98)
+    got = run_backward(inp, dy, 0.25, 3, 1, ending=True)
+    ref = BO.backward_train(O._transposed(inp), np.swapaxes(dy, 1, 2).astype(np.float64), 0.25, 3, 1)
+    ref["d_pair_repr"] = np.swapaxes(ref["d_pair_repr"], 1, 2)
+    for k in SHAPE:
+        r, gk = ref[k], got[k]
+        scale = float(np.abs(r).max())
+        err = float(np.abs(gk - r).max())
+        log(f"backward ending {dtype} {shape} {k}: max abs err {err:.3e}, relative {err / scale:.2e}")
+        assert err <= RTOL * scale + 1e-12, k

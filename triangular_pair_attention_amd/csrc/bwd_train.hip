@@ -33,6 +33,8 @@
 #include "tri_attn.h"
 #include "tri_attn_internal.h"
 
+#include <type_traits>
+
 namespace tpa {
 
 // ------------------------------------------------------------------ products
@@ -852,13 +854,13 @@ __global__ __launch_bounds__(256) void bwd_gate(const float *dgo, const float *p
 
 // ------------------------------------------------------------------ host side
 struct BwdLayout {
-  size_t x, xhat, rstd, proj, zt, m, l, Dj, o, dgo, dob, go, dcat, dx, part, vpart, bits, total;
+  size_t x, xhat, rstd, proj, zt, m, l, Dj, o, dgo, dob, go, dcat, dx, part, vpart, bits, pt, mt, dyt, dpt, total;
   long long S, kchunk, nvblk, vper;
 };
 
 static size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
-static BwdLayout bwd_layout(int B, int N, int D, int h) {
+static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed) {
   BwdLayout L{};
   const long long P = (long long)B * N * N, C = 4LL * D + h;
   // split-K chunks of the weight gradients (sums over all positions): at most
@@ -891,11 +893,39 @@ static BwdLayout bwd_layout(int B, int N, int D, int h) {
   L.part = take((size_t)L.S * C * D * 4);
   L.vpart = take((size_t)2 * L.nvblk * D * 4);
   L.bits = take((size_t)B * N * h * N * ((N + 31) / 32) * 4);
+  if (transposed) {  // ending-node: pair_repr, mask and dy with both residue axes swapped, and dP before swapping back
+    L.pt = take((size_t)P * D * elem);
+    L.mt = take((size_t)P);
+    L.dyt = take((size_t)P * D * elem);
+    L.dpt = take((size_t)P * D * 4);
+  }
   L.total = off;
   return L;
 }
 
-size_t bwd_workspace_bytes(int B, int N, int D, int h) { return bwd_layout(B, N, D, h).total; }
+size_t bwd_workspace_bytes(int B, int N, int D, int h, int elem, int transposed) {
+  return bwd_layout(B, N, D, h, elem, transposed).total;
+}
+
+// dst[b][i][j][:] = src[b][j][i][:] (W elements per position): the two
+// residue axes swapped
+template <typename E>
+__global__ __launch_bounds__(256) void bwd_swap_axes(const E *src, E *dst, int B, int N, int W) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long total = (long long)B * N * N * W;
+  if (e >= total) return;
+  const long long pos = e / W, w = e - pos * W;
+  const long long bi = pos / N, j = pos - bi * N, b = bi / N, i = bi - b * N;
+  dst[e] = src[((b * N + j) * N + i) * W + w];
+}
+
+template <typename E>
+static hipError_t swap_axes(const void *src, void *dst, int B, int N, int W, hipStream_t s) {
+  const long long total = (long long)B * N * N * W;
+  hipLaunchKernelGGL((bwd_swap_axes<E>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const E *>(src), static_cast<E *>(dst), B, N, W);
+  return hipGetLastError();
+}
 
 template <typename TA, typename TB>
 static hipError_t gemm(const void *A, long long sam, long long sak, const void *Bm, long long sbk, long long sbn,
@@ -916,7 +946,7 @@ template <typename T, int D, int DH>
 static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   const int B = r.B, N = r.N, h = D / DH;
   const long long P = (long long)B * N * N, C = 4LL * D + h;
-  const BwdLayout L = bwd_layout(B, N, D, h);
+  const BwdLayout L = bwd_layout(B, N, D, h, (int)sizeof(T) == 2 ? 2 : 4, r.transposed);
   char *w = static_cast<char *>(r.ws);
   float *x = reinterpret_cast<float *>(w + L.x), *xhat = reinterpret_cast<float *>(w + L.xhat);
   float *rstd = reinterpret_cast<float *>(w + L.rstd), *proj = reinterpret_cast<float *>(w + L.proj);
@@ -933,16 +963,28 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   do {                                   \
     if ((e = (x)) != hipSuccess) return e; \
   } while (0)
+  // ending-node: the starting-node backward of the transposed problem
+  using E = typename std::conditional<sizeof(T) == 2, uint16_t, float>::type;
+  const void *Pin = r.P, *dyin = r.dy;
+  const uint8_t *Min = r.mask;
+  float *dPout = r.g.d_pair_repr;
+  if (r.transposed) {
+    TPA_CHECK(swap_axes<E>(r.P, w + L.pt, B, N, D, s));
+    TPA_CHECK(swap_axes<uint8_t>(r.mask, w + L.mt, B, N, 1, s));
+    TPA_CHECK(swap_axes<E>(r.dy, w + L.dyt, B, N, D, s));
+    Pin = w + L.pt, Min = reinterpret_cast<const uint8_t *>(w + L.mt), dyin = w + L.dyt;
+    dPout = reinterpret_cast<float *>(w + L.dpt);
+  }
   // LayerNorm and the five projections, in float32
-  hipLaunchKernelGGL((bwd_ln<T, D>), dim3((unsigned)((P + 3) / 4)), dim3(256), 0, s, r.P, gamma, beta, r.eps, P, x,
+  hipLaunchKernelGGL((bwd_ln<T, D>), dim3((unsigned)((P + 3) / 4)), dim3(256), 0, s, Pin, gamma, beta, r.eps, P, x,
                      xhat, rstd);
   TPA_CHECK(hipGetLastError());
   TPA_CHECK((gemm<float, T>(x, D, 1, r.wpack, 1, D, proj, 0, C, P, C, D, D, 1, s)));
   hipLaunchKernelGGL(bwd_ztrans, dim3((unsigned)(((long long)B * h * N * N + 255) / 256)), dim3(256), 0, s, proj,
-                     r.mask, r.fill * kLog2e, B, N, D, h, (int)C, zt);
+                     Min, r.fill * kLog2e, B, N, D, h, (int)C, zt);
   TPA_CHECK(hipGetLastError());
   BwdAttnArgs aa{};
-  aa.proj = proj, aa.zt = zt, aa.mask = r.mask;
+  aa.proj = proj, aa.zt = zt, aa.mask = Min;
   aa.m = reinterpret_cast<float *>(w + L.m), aa.l = reinterpret_cast<float *>(w + L.l);
   aa.Dj = reinterpret_cast<float *>(w + L.Dj);
   aa.o = o, aa.dob = dob, aa.dcat = dcat;
@@ -965,7 +1007,7 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   hipLaunchKernelGGL((bwd_attn_fwd<DH>), ga, dim3(512), 0, s, aa);
   TPA_CHECK(hipGetLastError());
   // output projection and gate
-  TPA_CHECK((gemm<T, T>(r.dy, D, 1, Wo, D, 1, dgo, 0, D, P, D, D, D, 1, s)));
+  TPA_CHECK((gemm<T, T>(dyin, D, 1, Wo, D, 1, dgo, 0, D, P, D, D, D, 1, s)));
   hipLaunchKernelGGL((bwd_gate<T>), dim3((unsigned)((P * D + 255) / 256)), dim3(256), 0, s, dgo, proj, o, bg, P, D,
                      (int)C, dcat, dob, go);
   TPA_CHECK(hipGetLastError());
@@ -980,7 +1022,7 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   // projections and LayerNorm
   TPA_CHECK((gemm<float, T>(dcat, C, 1, r.wpack, D, 1, dx, 0, D, P, D, C, C, 1, s)));
   hipLaunchKernelGGL((bwd_ln_back<T, D>), dim3((unsigned)L.nvblk), dim3(256), 0, s, dx, xhat, rstd, gamma, P, L.vper,
-                     r.g.d_pair_repr, vpart, vpart + (size_t)L.nvblk * D);
+                     dPout, vpart, vpart + (size_t)L.nvblk * D);
   TPA_CHECK(hipGetLastError());
   TPA_CHECK(reduce(vpart, D, (int)L.nvblk, D, r.g.d_ln_weight, s));
   TPA_CHECK(reduce(vpart + (size_t)L.nvblk * D, D, (int)L.nvblk, D, r.g.d_ln_bias, s));
@@ -989,10 +1031,10 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   float *dst[5] = {r.g.d_w_query, r.g.d_w_key, r.g.d_w_value, r.g.d_w_gate, r.g.d_w_bias_proj};
   for (int q = 0; q < 5; ++q)
     TPA_CHECK(reduce(part + (size_t)q * D * D, (q < 4 ? D : h) * (long long)D, (int)L.S, C * D, dst[q], s));
-  TPA_CHECK((gemm<T, float>(r.dy, 1, D, go, D, 1, part, (long long)D * D, D, D, D, P, L.kchunk, (int)L.S, s)));
+  TPA_CHECK((gemm<T, float>(dyin, 1, D, go, D, 1, part, (long long)D * D, D, D, D, P, L.kchunk, (int)L.S, s)));
   TPA_CHECK(reduce(part, (long long)D * D, (int)L.S, (long long)D * D, r.g.d_w_out, s));
   // bias gradients: column sums over positions
-  hipLaunchKernelGGL((bwd_colsum<T>), dim3((unsigned)L.nvblk), dim3(256), 0, s, r.dy, P, D, (long long)D, L.vper,
+  hipLaunchKernelGGL((bwd_colsum<T>), dim3((unsigned)L.nvblk), dim3(256), 0, s, dyin, P, D, (long long)D, L.vper,
                      vpart);
   TPA_CHECK(hipGetLastError());
   TPA_CHECK(reduce(vpart, D, (int)L.nvblk, D, r.g.d_b_out, s));
@@ -1000,6 +1042,7 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
                      vpart);
   TPA_CHECK(hipGetLastError());
   TPA_CHECK(reduce(vpart, D, (int)L.nvblk, D, r.g.d_b_gate, s));
+  if (r.transposed) TPA_CHECK(swap_axes<float>(dPout, r.g.d_pair_repr, B, N, D, s));
 #undef TPA_CHECK
   return hipSuccess;
 }

@@ -353,7 +353,7 @@ int tri_attn_backward_workspace_size(tri_attn_t t, int B, int N, size_t *bytes) 
   if (!bytes) return TRI_ATTN_ERR_INVALID_ARG;
   const int rc = check_sizes(t, B, N);
   if (rc) return rc;
-  *bytes = (B == 0 || N == 0) ? 0 : bwd_workspace_bytes(B, N, t->D, t->h);
+  *bytes = (B == 0 || N == 0) ? 0 : bwd_workspace_bytes(B, N, t->D, t->h, t->elem, t->cfg.ending_node);
   return TRI_ATTN_OK;
 }
 
@@ -364,14 +364,13 @@ int tri_attn_backward_train(tri_attn_t t, const void *pair_repr, const uint8_t *
   if (!(dropout_rate >= 0.0 && dropout_rate < 1.0)) return TRI_ATTN_ERR_INVALID_ARG;
   int rc = check_sizes(t, B, N);
   if (rc) return rc;
-  if (t->cfg.ending_node) return TRI_ATTN_ERR_UNSUPPORTED;
   if (B == 0 || N == 0) return TRI_ATTN_OK;
   if (!pair_repr || !pair_mask || !dy || !grads) return TRI_ATTN_ERR_INVALID_ARG;
   const tri_attn_grads &g = *grads;
   if (!g.d_pair_repr || !g.d_ln_weight || !g.d_ln_bias || !g.d_w_query || !g.d_w_key || !g.d_w_value ||
       !g.d_w_gate || !g.d_b_gate || !g.d_w_bias_proj || !g.d_w_out || !g.d_b_out)
     return TRI_ATTN_ERR_INVALID_ARG;
-  const size_t need = bwd_workspace_bytes(B, N, t->D, t->h);
+  const size_t need = bwd_workspace_bytes(B, N, t->D, t->h, t->elem, t->cfg.ending_node);
   if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TRI_ATTN_ERR_WORKSPACE;
   BwdRunArgs r{};
   r.P = pair_repr, r.mask = pair_mask, r.dy = dy, r.wpack = t->wpack, r.vecs = t->vecs, r.g = g, r.ws = workspace;
@@ -381,6 +380,7 @@ int tri_attn_backward_train(tri_attn_t t, const void *pair_repr, const uint8_t *
   r.scale = (float)(4294967296.0 / (4294967296.0 - thr));
   r.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu), r.seed_hi = (uint32_t)(seed >> 32), r.offset = offset;
   r.B = B, r.N = N;
+  r.transposed = t->cfg.ending_node;
   if (launch_bwd(t->cfg.dtype, t->D, t->dh, r, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return TRI_ATTN_ERR_HIP;
   return TRI_ATTN_OK;

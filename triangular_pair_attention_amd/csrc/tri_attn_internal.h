@@ -105,9 +105,10 @@ struct BwdRunArgs {
   float eps, fill, scale;
   uint32_t thr, seed_lo, seed_hi, offset;
   int B, N;
+  int transposed;  // ending-node handle: the starting-node backward of the transposed problem
 };
 hipError_t launch_bwd(int dtype, int D, int dh, const BwdRunArgs &r, hipStream_t s);
-size_t bwd_workspace_bytes(int B, int N, int D, int h);
+size_t bwd_workspace_bytes(int B, int N, int D, int h, int elem_bytes, int transposed);
 // One-pass variant (onepass.hip): the pre-pass writes zm, the fused row
 // kernel does everything else.
 struct OnePassArgs {
