@@ -716,13 +716,15 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
 }
 
 // dz[b,t,j,k] = sum over rows i of ds, masked, per (b, t, 64 query columns j,
-// 64 key columns k): thread (tj, tk) owns queries j0 + tj + 16a and keys
-// k0 + tk + 16c (a, c = 0..3, a 4 x 4 register block); per row i the keys' k
-// and v, the queries' q, do, m2, l and sum a da, and the keep bits pass
-// through LDS.
+// 64 key columns k), 4 waves: wave w owns query columns j0 + 16w .. +15 and
+// all 64 keys. Per row i the rows' q, do, k and v and the queries' m2, l,
+// sum a da and keep bits pass through LDS; S = q k^T and dP = do v^T come
+// from float32 matrix-core tiles (lane: queries 4g + r, key r16), and ds is
+// summed over i in registers. The bias and the mask of (j, k) are the same
+// for every row i and stay in registers.
 template <int DH>
 __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
-  constexpr int JT = 64, KT = 64, RP = DH + 4;
+  constexpr int JT = 64, KT = 64, RP = DH + 4, CB = DH / 16;
   __shared__ __align__(16) float ks[KT][RP], vs[KT][RP], qs[JT][RP], dos[JT][RP];
   __shared__ float ms[JT], ls[JT], Ds[JT];
   __shared__ uint32_t kb[JT][2];
@@ -730,20 +732,19 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
   const int nkt = (N + KT - 1) / KT;
   const int bt = blockIdx.y, b = bt / h, t = bt - b * h;
   const int j0 = (blockIdx.x / nkt) * JT, k0 = (blockIdx.x % nkt) * KT;
-  const int tj = threadIdx.x >> 4, tk = threadIdx.x & 15;
-  float dz[4][4], zr[4][4];
-  uint32_t valid = 0;  // bit 4 qa + c
-  // the bias and the mask of (j, k) are the same for every row i
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  float zl[4][4], dz[4][4];  // [key block][r]: query j0 + 16 wave + 4g + r, key k0 + 16 kb + r16
+  uint32_t valid = 0;        // bit 4 kb + r
 #pragma unroll
-  for (int qa = 0; qa < 4; ++qa)
+  for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = j0 + tj + 16 * qa, k = k0 + tk + 16 * c;
-      const float zl = (j < N && k < N) ? a.zt[((size_t)(b * h + t) * N + j) * N + k] : a.fill2;
-      const bool v = j < N && k < N && zl != a.fill2;
-      valid |= (uint32_t)v << (4 * qa + c);
-      zr[qa][c] = v ? zl : 0.f;
-      dz[qa][c] = 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + 16 * wave + 4 * g + r, k = k0 + 16 * kbk + r16;
+      const float z = (j < N && k < N) ? a.zt[((size_t)(b * h + t) * N + j) * N + k] : a.fill2;
+      const bool v = j < N && k < N && z != a.fill2;
+      valid |= (uint32_t)v << (4 * kbk + r);
+      zl[kbk][r] = v ? z : 0.f;
+      dz[kbk][r] = 0.f;
     }
   for (int i = 0; i < N; ++i) {
     const size_t rowp = ((size_t)b * N + i) * N;
@@ -759,9 +760,9 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
         qv = ldg<float4>(a.proj + (rowp + j) * C + t * DH + u4);
         dv = ldg<float4>(a.dob + (rowp + j) * D + t * DH + u4);
       }
-      *reinterpret_cast<float4 *>(&ks[r][u4]) = kv;
+      *reinterpret_cast<float4 *>(&ks[r][u4]) = make_float4(kv.x * a.qs, kv.y * a.qs, kv.z * a.qs, kv.w * a.qs);
       *reinterpret_cast<float4 *>(&vs[r][u4]) = vv;
-      *reinterpret_cast<float4 *>(&qs[r][u4]) = make_float4(qv.x * a.qs, qv.y * a.qs, qv.z * a.qs, qv.w * a.qs);
+      *reinterpret_cast<float4 *>(&qs[r][u4]) = qv;
       *reinterpret_cast<float4 *>(&dos[r][u4]) = dv;
     }
     if (threadIdx.x < JT) {
@@ -776,49 +777,48 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
       kb[threadIdx.x][1] = (jq < N && w0 + 1 < a.NW) ? kr[w0 + 1] : 0u;
     }
     __syncthreads();
-    float sq[4][4], da[4][4];
+    float m2[4], linv[4], Dv[4];
+    uint32_t w2[4][2];
 #pragma unroll
-    for (int qa = 0; qa < 4; ++qa)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sq[qa][c] = da[qa][c] = 0.f;
-#pragma unroll 1
-    for (int u = 0; u < DH; u += 4) {
-      float4 q4[4], d4[4], k4[4], v4[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        q4[x] = *reinterpret_cast<const float4 *>(&qs[tj + 16 * x][u]);
-        d4[x] = *reinterpret_cast<const float4 *>(&dos[tj + 16 * x][u]);
-        k4[x] = *reinterpret_cast<const float4 *>(&ks[tk + 16 * x][u]);
-        v4[x] = *reinterpret_cast<const float4 *>(&vs[tk + 16 * x][u]);
-      }
-#pragma unroll
-      for (int qa = 0; qa < 4; ++qa)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          sq[qa][c] += q4[qa].x * k4[c].x + q4[qa].y * k4[c].y + q4[qa].z * k4[c].z + q4[qa].w * k4[c].w;
-          da[qa][c] += d4[qa].x * v4[c].x + d4[qa].y * v4[c].y + d4[qa].z * v4[c].z + d4[qa].w * v4[c].w;
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int jj = 16 * wave + 4 * g + r;
+      m2[r] = ms[jj], linv[r] = 1.f / ls[jj], Dv[r] = Ds[jj];
+      w2[r][0] = kb[jj][0], w2[r][1] = kb[jj][1];
     }
 #pragma unroll
-    for (int qa = 0; qa < 4; ++qa) {
-      const int jj = tj + 16 * qa;
-      const float m2 = ms[jj], linv = 1.f / ls[jj], Dv = Ds[jj];
+    for (int kbk = 0; kbk < 4; ++kbk) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = sc;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int kk = tk + 16 * c;
-        const float p = fast_exp2(zr[qa][c] + sq[qa][c] - m2) * linv;
-        const float dav = (kb[jj][kk >> 5] >> (kk & 31)) & 1u ? da[qa][c] * a.scale : 0.f;
-        if ((valid >> (4 * qa + c)) & 1u) dz[qa][c] += p * (dav - Dv);
+      for (int cb = 0; cb < CB; ++cb) {
+        const float4 qv = *reinterpret_cast<const float4 *>(&qs[16 * wave + r16][16 * cb + 4 * g]);
+        const float4 dv = *reinterpret_cast<const float4 *>(&dos[16 * wave + r16][16 * cb + 4 * g]);
+        const float4 kv = *reinterpret_cast<const float4 *>(&ks[16 * kbk + r16][16 * cb + 4 * g]);
+        const float4 vv = *reinterpret_cast<const float4 *>(&vs[16 * kbk + r16][16 * cb + 4 * g]);
+        sc = mfma(qv.x, kv.x, sc);
+        sc = mfma(qv.y, kv.y, sc);
+        sc = mfma(qv.z, kv.z, sc);
+        sc = mfma(qv.w, kv.w, sc);
+        dp = mfma(dv.x, vv.x, dp);
+        dp = mfma(dv.y, vv.y, dp);
+        dp = mfma(dv.z, vv.z, dp);
+        dp = mfma(dv.w, vv.w, dp);
+      }
+      const int kk = 16 * kbk + r16;  // the lane's key within the tile
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(zl[kbk][r] + sc[r] - m2[r]) * linv[r];
+        const float dav = (w2[r][kk >> 5] >> (kk & 31)) & 1u ? dp[r] * a.scale : 0.f;
+        if ((valid >> (4 * kbk + r)) & 1u) dz[kbk][r] += p * (dav - Dv[r]);
       }
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int qa = 0; qa < 4; ++qa)
+  for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = j0 + tj + 16 * qa, k = k0 + tk + 16 * c;
-      if (j < N && k < N) a.dcat[(((size_t)b * N + j) * N + k) * C + 4 * D + t] = dz[qa][c];
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + 16 * wave + 4 * g + r, k = k0 + 16 * kbk + r16;
+      if (j < N && k < N) a.dcat[(((size_t)b * N + j) * N + k) * C + 4 * D + t] = dz[kbk][r];
     }
 }
 
