@@ -578,7 +578,7 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
   __shared__ __align__(16) float qT[DH * S::TP];
   __shared__ __align__(16) float dbuf[QT * S::KP];
   __shared__ __align__(16) float dT[DH * S::TP];
-  __shared__ float ms[QT], ls[QT], Ds[QT];
+  __shared__ __align__(16) float ms[QT], ls[QT], Ds[QT];
   // the chunk's bias, mask and keep bits for the workgroup's 128 keys
   __shared__ __align__(16) float zs[QT][S::QB + 4];
   __shared__ uint32_t kbits[QT][S::QB / 32];
@@ -675,17 +675,23 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
         dp = mfma(dv4.w, vf[cb][3], dp);
       }
       float pk[4], ds[4];
+      // statistics of the lane's four queries (16-byte LDS reads)
+      const float4 m4 = *reinterpret_cast<const float4 *>(&ms[qb * 16 + 4 * g]);
+      const float4 l4 = *reinterpret_cast<const float4 *>(&ls[qb * 16 + 4 * g]);
+      const float4 d4 = *reinterpret_cast<const float4 *>(&Ds[qb * 16 + 4 * g]);
+      const float mq[4] = {m4.x, m4.y, m4.z, m4.w}, lq[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dq4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int jq = jb + r, jj = qb * 16 + 4 * g + r;
         const bool in = jq < N && k < N;
         const bool valid = in && s0[r] != a.fill2;
         const float sl = !in ? -INFINITY : (valid ? s[r] : a.fill2);
-        const float p = sl == -INFINITY ? 0.f : fast_exp2(sl - ms[jj]) / ls[jj];
+        const float p = sl == -INFINITY ? 0.f : fast_exp2(sl - mq[r]) / lq[r];
         const bool kp = in && ((kbits[jj][kk >> 5] >> (kk & 31)) & 1u);
         const float da = kp ? dp[r] * a.scale : 0.f;
         pk[r] = kp ? p * a.scale : 0.f;
-        ds[r] = valid ? p * (da - Ds[jj]) : 0.f;
+        ds[r] = valid ? p * (da - dq4[r]) : 0.f;
       }
       // dv^T += do^T P', dk^T += q^T dS
 #pragma unroll
