@@ -142,8 +142,10 @@ int tri_attn_forward(tri_attn_t h, const void *pair_repr, const uint8_t *pair_ma
  * inference output. Ending-node handles run the starting-node computation of
  * the transposed pair representation and mask: the dropout counters and lse
  * use its indices, so lse[b][j][t][i] belongs to output position (b, i, j). The
- * attention step is a plain kernel (one lane per query column, key tiles in
- * LDS), several times slower than the inference one. */
+ * attention step runs on the matrix cores with a running-maximum softmax (no
+ * bound on the scores is needed) and draws the dropout words inside the key
+ * loop; generating them makes it several times slower than the inference
+ * attention step. */
 int tri_attn_forward_train(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, void *out, float *lse,
                            int B, int N, double dropout_rate, uint64_t seed, uint32_t offset, void *workspace,
                            size_t ws_bytes, void *stream);
@@ -292,9 +294,12 @@ int tri_attn_get_workspace_layout(tri_attn_t h, int B, int N, tri_attn_workspace
 
 /* Testing aid: add `slack` (finite, >= 0; default 0) to every per-column
  * softmax shift of later calls on this handle. Softmax does not depend on
- * the shift, so results are unchanged; a slack above 64 (log2 units) pushes
- * every work item into the attention kernel's exact-maximum recovery path,
- * which tests use to exercise it. Errors: INVALID_ARG. */
+ * the shift, so results are unchanged. The shift normally sits 96 (log2
+ * units) below the columns' Cauchy-Schwarz bound; once slack lifts it more
+ * than 64 above a column's true maximum (a slack of a few hundred on ordinary
+ * inputs), that column's sum falls below 2^-64 and its work item takes the
+ * attention kernel's exact-maximum recovery path, which tests use to exercise
+ * it. Errors: INVALID_ARG. */
 int tri_attn_set_shift_slack(tri_attn_t h, float slack);
 
 /* Run only the LayerNorm + projection kernel (arguments as tri_attn_forward). */
