@@ -299,28 +299,46 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
   constexpr int LA = NS - 1;  // steps in flight
   static_assert(LA >= 1 && LA <= 3, "");
 
-  // ---- setup loads. The per-chunk maxima are spread over the lanes and
-  // reduced across lanes; the first round of every one of these loads is
-  // issued before any of them is used (one round trip); rows longer than
-  // that first round (more than 64 key chunks for |k|, 16 for the bias, 8
-  // for the v sums) continue in loops.
+  // ---- setup loads. The per-chunk maxima and sums are spread over the
+  // lanes and reduced across lanes; the first round of every one of these
+  // loads is issued before any of them is used (one round trip); rows longer
+  // than that first round (more than 64 / IG key chunks for |k|, 16 for the
+  // bias, 8 for the v sums) continue in loops.
   // |k|^2 <= sum over the head's 16-channel blocks of each block's chunk
-  // maxima: lane l takes chunks l, l + 64, ... of each row's block.
+  // maxima: the wave's lanes form IG groups of KL, group kr takes the wave's
+  // row kr, its lanes chunks kc, kc + KL, ...
   // Bias+mask maximum and last live key chunk of this wave's query columns:
   // lane (g, r16) takes chunks g, g + 4, ... of column r16.
   // Sum of v over all keys of each (row, channel) of the workgroup, from
   // kernel 1's per-chunk sums (the uniform weights of a fully masked column,
-  // finite fill): one thread per (row, channel).
+  // finite fill): VQ adjacent threads per (row, channel), each taking VS of
+  // its eight partial-sum slots. bf16 with d = 16 spreads them over every
+  // thread of the workgroup (measured faster at B = 4, N = 512, h = 8); the
+  // other shapes keep one thread per (row, channel) (measured faster there).
   constexpr int ZR = 4;
-  float kmx[IG][MB], zfirst[JW][ZR], sv[8];
+  constexpr int KL = 64 / IG;
+  static_assert(64 % IG == 0, "");
+  constexpr int VQ = (BF && DH == 16) ? (NW * 64) / (RB * DH) : 1;
+  static_assert(VQ * RB * DH <= NW * 64 && (VQ == 1 || VQ == 2 || VQ == 4 || VQ == 8), "v-sum threads");
+  constexpr int VS = 8 / VQ;
+  const bool vthread = VQ * RB * DH == NW * 64 || threadIdx.x < VQ * RB * DH;
+  float kmx[MB], zfirst[JW][ZR], sv[VS];
+  auto kmax_row = [&](int mb) {  // this lane's row of the |k| chunk maxima, block mb of head t
+    const int kr = lane / KL;
+    const int row = min(i0 + wr * IG + kr, N - 1);
+    return a.kmax + ((size_t)(b * N + row) * NB + t * MB + mb) * nch;
+  };
+  auto vsum_row = [&]() {  // this thread's (row, channel) of the per-chunk v sums
+    const int rc = threadIdx.x / VQ, r = rc / DH, ch = rc - r * DH;
+    // [b][i][chunk][channel]
+    return a.vsum + (size_t)(b * N + min(i0 + r, N - 1)) * nch * D + t * DH + ch;
+  };
   auto load_setup = [&]() {
+    {
+      const int kc = lane % KL;
 #pragma unroll
-    for (int i = 0; i < IG; ++i)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
-        kmx[i][mb] = lane < nch ? kp[lane] : 0.f;
-      }
+      for (int mb = 0; mb < MB; ++mb) kmx[mb] = kc < nch ? kmax_row(mb)[kc] : 0.f;
+    }
 #pragma unroll
     for (int jb = 0; jb < JW; ++jb) {
       const int j = j0 + (wq * JW + jb) * 16 + r16;
@@ -329,14 +347,11 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
 #pragma unroll
       for (int u = 0; u < ZR; ++u) zfirst[jb][u] = (j < N && g + 4 * u < nch) ? zp[(size_t)(g + 4 * u) * N] : -INFINITY;
     }
-    static_assert(RB * DH <= NW * 64, "one (row, channel) v sum per thread");
-    const int x = threadIdx.x;
-    if (x < RB * DH) {
-      const int r = x / DH, ch = x - r * DH;
-      // [b][i][chunk][channel]: consecutive threads read consecutive channels
-      const float *p = a.vsum + (size_t)(b * N + min(i0 + r, N - 1)) * nch * D + t * DH + ch;
+    if (vthread) {
+      const float *p = vsum_row();
+      const int q = threadIdx.x % VQ;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sv[u] = u < nch ? p[(size_t)u * D] : 0.f;
+      for (int k = 0; k < VS; ++k) sv[k] = q * VS + k < nch ? p[(size_t)(q * VS + k) * D] : 0.f;
     }
   };
 
@@ -363,35 +378,44 @@ __global__ __launch_bounds__((K2Shape<T, D, DH>::NW * 64)) void k2_attention(K2A
     }
   };
   auto setup = [&](int buf) {
-    {
-      const int x = threadIdx.x;
-      if (x < RB * DH) {
-        const int r = x / DH, ch = x - r * DH;
-        const float *p = a.vsum + (size_t)(b * N + min(i0 + r, N - 1)) * nch * D + t * DH + ch;
-        float s8[8];
+    if (vthread) {
+      // slot u of a (row, channel) sums chunks u, u + 8, ...; the eight slots
+      // are added in one fixed tree, ((s0 + s1) + (s2 + s3)) + ((s4 + s5) +
+      // (s6 + s7)), its lower levels inside a thread and its upper levels
+      // across the VQ lanes: deterministic
+      const float *p = vsum_row();
+      const int q = threadIdx.x % VQ;
+      float sk[VS];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s8[u] = sv[u];
-        for (int c = 8; c < nch; c += 8) {
+      for (int k = 0; k < VS; ++k) sk[k] = sv[k];
+      for (int c = 8; c < nch; c += 8) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) s8[u] += c + u < nch ? p[(size_t)(c + u) * D] : 0.f;
-        }
-        // a fixed summation order: deterministic
-        vsum_s[buf][x] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+        for (int k = 0; k < VS; ++k) sk[k] += c + q * VS + k < nch ? p[(size_t)(c + q * VS + k) * D] : 0.f;
       }
-    }
 #pragma unroll
-    for (int i = 0; i < IG; ++i) {
+      for (int w = 1; w < VS; w <<= 1)
+#pragma unroll
+        for (int k = 0; k < VS; k += 2 * w) sk[k] += sk[k + w];
+      float part = sk[0];
+#pragma unroll
+      for (int m = 1; m < VQ; m <<= 1) part += __shfl_xor(part, m, 64);
+      if (q == 0) vsum_s[buf][threadIdx.x / VQ] = part;
+    }
+    {
+      const int kc = lane % KL;
       float m2 = 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const float *kp = a.kmax + ((size_t)(b * N + rows[i]) * NB + t * MB + mb) * nch;
-        float m = kmx[i][mb];
-        for (int c = lane + 64; c < nch; c += 64) m = fmaxf(m, kp[c]);
+        const float *kp = kmax_row(mb);
+        float m = kmx[mb];
+        for (int c = kc + KL; c < nch; c += KL) m = fmaxf(m, kp[c]);
 #pragma unroll
-        for (int x = 1; x < 64; x <<= 1) m = xor_max(m, x);
+        for (int x = 1; x < KL; x <<= 1) m = xor_max(m, x);
         m2 += m;
       }
-      kn2[i] = m2;
+      // lane group i holds row i's bound
+#pragma unroll
+      for (int i = 0; i < IG; ++i) kn2[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m2), i * KL));
     }
     int kend = 0;
 #pragma unroll
