@@ -624,7 +624,7 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
         const int jq = j0 + jj;
         const size_t st_ = ((size_t)bi * h + t) * N + jq;
         ms[jj] = jq < N ? a.m[st_] : 0.f;
-        ls[jj] = jq < N ? a.l[st_] : 1.f;
+        ls[jj] = jq < N ? 1.f / a.l[st_] : 1.f;  // 1 / l: one division per query, not per score
         Ds[jj] = jq < N ? a.Dj[st_] : 0.f;
       }
       const int kw0 = (kc * S::QB) >> 5;
@@ -675,7 +675,7 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
         dp = mfma(dv4.w, vf[cb][3], dp);
       }
       float pk[4], ds[4];
-      // statistics of the lane's four queries (16-byte LDS reads)
+      // statistics of the lane's four queries (16-byte LDS reads; l as 1 / l)
       const float4 m4 = *reinterpret_cast<const float4 *>(&ms[qb * 16 + 4 * g]);
       const float4 l4 = *reinterpret_cast<const float4 *>(&ls[qb * 16 + 4 * g]);
       const float4 d4 = *reinterpret_cast<const float4 *>(&Ds[qb * 16 + 4 * g]);
@@ -687,8 +687,10 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
         const bool in = jq < N && k < N;
         const bool valid = in && s0[r] != a.fill2;
         const float sl = !in ? -INFINITY : (valid ? s[r] : a.fill2);
-        const float p = sl == -INFINITY ? 0.f : fast_exp2(sl - mq[r]) / lq[r];
-        const bool kp = in && ((kbits[jj][kk >> 5] >> (kk & 31)) & 1u);
+        const float p = sl == -INFINITY ? 0.f : fast_exp2(sl - mq[r]) * lq[r];
+        // read unconditionally (in bounds for every lane), so that no branch
+        // is taken around the read
+        const bool kp = in & (((kbits[jj][kk >> 5] >> (kk & 31)) & 1u) != 0u);
         const float da = kp ? dp[r] * a.scale : 0.f;
         pk[r] = kp ? p * a.scale : 0.f;
         ds[r] = valid ? p * (da - dq4[r]) : 0.f;
