@@ -149,14 +149,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // with the published multipliers and key increments. The dropout decisions of
 // the training-mode kernels come from it.
 // Each round's two 32x32 -> 64-bit products are written as 64-bit products,
-// one v_mad_u64_u32 each (measured 1.3x the throughput of a mul_hi/mul_lo pair).
+// one v_mad_u64_u32 each (measured 1.3x the throughput of a mul_hi/mul_lo pair),
+// and each three-way exclusive or as one gfx950 three-input bit operation
+// (truth table 0x96: the parity of the three input bits).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
     const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
     const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    c = make_uint4(xor3(hi1, c.y, k0), lo1, xor3(hi0, c.w, k1), lo0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
