@@ -600,56 +600,103 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) dk[cb] = dv[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float *zb = a.zt + (size_t)(b * h + t) * N * N;
-  for (int j0 = 0; j0 < N; j0 += QT) {
-    // the chunk's q and do rows of head t ([query][c] and [c][query]) and statistics
-    {
-      constexpr int V4 = QT * DH / 4;
-      for (int e = threadIdx.x; e < V4; e += S::NW * 64) {
-        const int jj = e / (DH / 4), u4 = (e - jj * (DH / 4)) * 4, jq = j0 + jj;
-        float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f), d4 = q4;
-        if (jq < N) {
-          q4 = ldg<float4>(a.proj + (rowp + jq) * C + t * DH + u4);
-          d4 = ldg<float4>(a.dob + (rowp + jq) * D + t * DH + u4);
-        }
-        *reinterpret_cast<float4 *>(qbuf + jj * S::KP + u4) = q4;
-        *reinterpret_cast<float4 *>(dbuf + jj * S::KP + u4) = d4;
-        const float qa[4] = {q4.x, q4.y, q4.z, q4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          qT[(u4 + c) * S::TP + jj] = qa[c];
-          dT[(u4 + c) * S::TP + jj] = da[c];
-        }
-      }
-      for (int jj = threadIdx.x; jj < QT; jj += S::NW * 64) {
-        const int jq = j0 + jj;
-        const size_t st_ = ((size_t)bi * h + t) * N + jq;
-        ms[jj] = jq < N ? a.m[st_] : 0.f;
-        ls[jj] = jq < N ? 1.f / a.l[st_] : 1.f;  // 1 / l: one division per query, not per score
-        Ds[jj] = jq < N ? a.Dj[st_] : 0.f;
-      }
-      const int kw0 = (kc * S::QB) >> 5;
-      for (int e = threadIdx.x; e < QT * S::QB / 4; e += S::NW * 64) {
-        const int jj = e / (S::QB / 4), kk = (e - jj * (S::QB / 4)) * 4, jq = j0 + jj, kq = kc * S::QB + kk;
-        float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (jq < N && kq + 3 < N && (N & 3) == 0) {  // rows of z are 16-byte aligned when N % 4 == 0
-          z4 = ldg<float4>(zb + (size_t)jq * N + kq);
-        } else if (jq < N) {
-          float t4[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) t4[c] = kq + c < N ? zb[(size_t)jq * N + kq + c] : 0.f;
-          z4 = make_float4(t4[0], t4[1], t4[2], t4[3]);
-        }
-        *reinterpret_cast<float4 *>(&zs[jj][kk]) = z4;
-      }
-      for (int e = threadIdx.x; e < QT * (S::QB / 32); e += S::NW * 64) {
-        const int jj = e / (S::QB / 32), w = e - jj * (S::QB / 32), jq = j0 + jj;
-        kbits[jj][w] = (jq < N && kw0 + w < a.NW) ? keep_row(a, bi, t, jq)[kw0 + w] : 0u;
+  // A query chunk's q and do rows of head t ([query][c] and [c][query]),
+  // statistics, bias tile and keep bits pass through LDS. With d = 16 each
+  // thread loads its share of chunk c + 1 into registers while chunk c is
+  // computed (load_chunk), and writes it to LDS after chunk c's products
+  // (store_chunk): the loads' round trip overlaps the products. Shares: at
+  // most one q/do piece, one statistic, ZP bias pieces and one keep word.
+  constexpr int V4 = QT * DH / 4, ZP = QT * S::QB / 4 / (S::NW * 64), KW = QT * (S::QB / 32);
+  static_assert(V4 <= S::NW * 64 && KW <= S::NW * 64 && ZP * S::NW * 64 == QT * S::QB / 4, "chunk shares");
+  const int kw0 = (kc * S::QB) >> 5;
+  struct Chunk {
+    float4 q, d, z[ZP];
+    float m, il, Dq;
+    uint32_t kw;
+  };
+  auto load_chunk = [&](int j0) {
+    Chunk c;
+    const int e = threadIdx.x;
+    c.q = c.d = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e < V4) {
+      const int jj = e / (DH / 4), u4 = (e - jj * (DH / 4)) * 4, jq = j0 + jj;
+      if (jq < N) {
+        c.q = ldg<float4>(a.proj + (rowp + jq) * C + t * DH + u4);
+        c.d = ldg<float4>(a.dob + (rowp + jq) * D + t * DH + u4);
       }
     }
+    // m and 1 / l (one division per query, not per score); a column past N,
+    // or one whose every score is -inf (-inf fill, all keys masked), gets
+    // m = 0 and 1 / l = 0, so that its weights below come out 0 without a
+    // test per score
+    c.m = 0.f, c.il = 0.f, c.Dq = 0.f;
+    if (e < QT) {
+      const int jq = j0 + e;
+      const size_t st_ = ((size_t)bi * h + t) * N + jq;
+      const float mj = jq < N ? a.m[st_] : -INFINITY;
+      if (mj != -INFINITY) c.m = mj, c.il = 1.f / a.l[st_];
+      if (jq < N) c.Dq = a.Dj[st_];
+    }
+#pragma unroll
+    for (int u = 0; u < ZP; ++u) {
+      const int x = e + u * S::NW * 64;
+      const int jj = x / (S::QB / 4), kk = (x - jj * (S::QB / 4)) * 4, jq = j0 + jj, kq = kc * S::QB + kk;
+      // -inf past N (query or key): such a score is -inf whatever q.k is
+      float4 z4 = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (jq < N && kq + 3 < N && (N & 3) == 0) {  // rows of z are 16-byte aligned when N % 4 == 0
+        z4 = ldg<float4>(zb + (size_t)jq * N + kq);
+      } else if (jq < N) {
+        float t4[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) t4[cc] = kq + cc < N ? zb[(size_t)jq * N + kq + cc] : -INFINITY;
+        z4 = make_float4(t4[0], t4[1], t4[2], t4[3]);
+      }
+      c.z[u] = z4;
+    }
+    c.kw = 0u;
+    if (e < KW) {
+      const int jj = e / (S::QB / 32), w = e - jj * (S::QB / 32), jq = j0 + jj;
+      if (jq < N && kw0 + w < a.NW) c.kw = keep_row(a, bi, t, jq)[kw0 + w];
+    }
+    return c;
+  };
+  auto store_chunk = [&](const Chunk &c) {
+    const int e = threadIdx.x;
+    if (e < V4) {
+      const int jj = e / (DH / 4), u4 = (e - jj * (DH / 4)) * 4;
+      *reinterpret_cast<float4 *>(qbuf + jj * S::KP + u4) = c.q;
+      *reinterpret_cast<float4 *>(dbuf + jj * S::KP + u4) = c.d;
+      const float qa[4] = {c.q.x, c.q.y, c.q.z, c.q.w}, da[4] = {c.d.x, c.d.y, c.d.z, c.d.w};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        qT[(u4 + cc) * S::TP + jj] = qa[cc];
+        dT[(u4 + cc) * S::TP + jj] = da[cc];
+      }
+    }
+    if (e < QT) ms[e] = c.m, ls[e] = c.il, Ds[e] = c.Dq;
+#pragma unroll
+    for (int u = 0; u < ZP; ++u) {
+      const int x = e + u * S::NW * 64;
+      const int jj = x / (S::QB / 4), kk = (x - jj * (S::QB / 4)) * 4;
+      *reinterpret_cast<float4 *>(&zs[jj][kk]) = c.z[u];
+    }
+    if (e < KW) kbits[e / (S::QB / 32)][e % (S::QB / 32)] = c.kw;
+  };
+  // d = 32 loads each chunk just before it is used: the prefetch registers
+  // would take it past the budget that two workgroups per CU leave a wave
+  constexpr bool PIPE = DH == 16;
+  Chunk nxt;
+  if constexpr (PIPE) nxt = load_chunk(0);
+  for (int j0 = 0; j0 < N; j0 += QT) {
+    if constexpr (PIPE)
+      store_chunk(nxt);
+    else
+      store_chunk(load_chunk(j0));
     __syncthreads();
+    if constexpr (PIPE)
+      if (j0 + QT < N) nxt = load_chunk(j0 + QT);
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const int jb = j0 + qb * 16 + 4 * g;  // the lane's queries jb + r
       // S = q k^T (queries x keys): bias, product, mask, padding
       const int kk = wave * 16 + r16;  // the lane's key within the workgroup's 128
       f32x4 s;
@@ -681,16 +728,17 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
       const float4 d4 = *reinterpret_cast<const float4 *>(&Ds[qb * 16 + 4 * g]);
       const float mq[4] = {m4.x, m4.y, m4.z, m4.w}, lq[4] = {l4.x, l4.y, l4.z, l4.w};
       const float dq4[4] = {d4.x, d4.y, d4.z, d4.w};
+      // A score past N (query or key) is -inf (its bias is), so its weight
+      // p is 0, and so are its terms below (a keep bit past N may be set: the
+      // generator draws keys in fours). Masked scores are FILL: they carry no
+      // gradient, and their weight is 0 unless the column is fully masked.
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int jq = jb + r, jj = qb * 16 + 4 * g + r;
-        const bool in = jq < N && k < N;
-        const bool valid = in && s0[r] != a.fill2;
-        const float sl = !in ? -INFINITY : (valid ? s[r] : a.fill2);
-        const float p = sl == -INFINITY ? 0.f : fast_exp2(sl - mq[r]) * lq[r];
-        // read unconditionally (in bounds for every lane), so that no branch
-        // is taken around the read
-        const bool kp = in & (((kbits[jj][kk >> 5] >> (kk & 31)) & 1u) != 0u);
+        const int jj = qb * 16 + 4 * g + r;
+        const bool valid = s0[r] != a.fill2;
+        const float sl = valid ? s[r] : a.fill2;
+        const float p = fast_exp2(sl - mq[r]) * lq[r];
+        const bool kp = ((kbits[jj][kk >> 5] >> (kk & 31)) & 1u) != 0u;
         const float da = kp ? dp[r] * a.scale : 0.f;
         pk[r] = kp ? p * a.scale : 0.f;
         ds[r] = valid ? p * (da - dq4[r]) : 0.f;
@@ -777,7 +825,7 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
       const int jq = j0 + threadIdx.x;
       const size_t st = (((size_t)b * N + i) * h + t) * N + jq;
       ms[threadIdx.x] = jq < N ? a.m[st] : 0.f;
-      ls[threadIdx.x] = jq < N ? a.l[st] : 1.f;
+      ls[threadIdx.x] = jq < N ? 1.f / a.l[st] : 1.f;  // 1 / l: one division per query and row
       Ds[threadIdx.x] = jq < N ? a.Dj[st] : 0.f;
       const uint32_t *kr = keep_row(a, b * N + i, t, jq < N ? jq : 0);
       const int w0 = k0 >> 5;
@@ -790,7 +838,7 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int jj = 16 * wave + 4 * g + r;
-      m2[r] = ms[jj], linv[r] = 1.f / ls[jj], Dv[r] = Ds[jj];
+      m2[r] = ms[jj], linv[r] = ls[jj], Dv[r] = Ds[jj];
       w2[r][0] = kb[jj][0], w2[r][1] = kb[jj][1];
     }
 #pragma unroll
