@@ -166,8 +166,9 @@ typedef struct {
  * projections, the attention output and row statistics), their gradients and
  * the partial sums of the weight gradients, and the dropout decisions (one
  * bit per score); about 4(5D + h) * B * N^2 * 2 + B * h * N^3 / 8 bytes, plus
- * transposed copies of the inputs for ending-node handles. B == 0 or N == 0
- * needs 0 bytes. */
+ * transposed copies of the inputs for ending-node handles and, when N is
+ * small, partial sums of the pair-bias gradient over ranges of rows (below
+ * 64 MiB). B == 0 or N == 0 needs 0 bytes. */
 int tri_attn_backward_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
 
 /* Backward of tri_attn_forward_train: with dy = dL/dy [B, N, N, D] (config

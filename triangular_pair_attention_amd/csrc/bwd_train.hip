@@ -33,6 +33,7 @@
 #include "tri_attn.h"
 #include "tri_attn_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace tpa {
@@ -303,6 +304,8 @@ struct BwdAttnArgs {
   float rsd;             // 1 / sqrt(d)
   uint32_t thr, seed_lo, seed_hi, offset;
   int B, N, D, h, C, NW;
+  float *zpart;      // [zsplit][B*h][N][N]: dz partial sums over row ranges (zsplit > 1)
+  int zsplit, zrows;  // row ranges of the dz step and rows per range
 };
 
 // The dropout decisions, one bit per (b, i, t, j, key), from the forward's
@@ -772,8 +775,11 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
 }
 
 // dz[b,t,j,k] = sum over rows i of ds, masked, per (b, t, 64 query columns j,
-// 64 key columns k), 4 waves: wave w owns query columns j0 + 16w .. +15 and
-// all 64 keys. Per row i the rows' q, do, k and v and the queries' m2, l,
+// 64 key columns k) and range of zrows rows i (blockIdx.z), 4 waves: wave w
+// owns query columns j0 + 16w .. +15 and all 64 keys. With one range the sum
+// goes straight to dcat; with several (small N, where the (j, k) tiles alone
+// would leave most CUs idle) each range writes its partial sum, and
+// bwd_dz_reduce adds the ranges in order. Per row i the rows' q, do, k and v and the queries' m2, l,
 // sum a da and keep bits pass through LDS; S = q k^T and dP = do v^T come
 // from float32 matrix-core tiles (lane: queries 4g + r, key r16), and ds is
 // summed over i in registers. The bias and the mask of (j, k) are the same
@@ -802,7 +808,8 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
       zl[kbk][r] = v ? z : 0.f;
       dz[kbk][r] = 0.f;
     }
-  for (int i = 0; i < N; ++i) {
+  const int i_begin = blockIdx.z * a.zrows, i_end = min(N, i_begin + a.zrows);
+  for (int i = i_begin; i < i_end; ++i) {
     const size_t rowp = ((size_t)b * N + i) * N;
     for (int e = threadIdx.x; e < KT * DH / 4; e += 256) {
       const int r = e / (DH / 4), u4 = (e - r * (DH / 4)) * 4;
@@ -874,8 +881,26 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = j0 + 16 * wave + 4 * g + r, k = k0 + 16 * kbk + r16;
-      if (j < N && k < N) a.dcat[(((size_t)b * N + j) * N + k) * C + 4 * D + t] = dz[kbk][r];
+      if (j < N && k < N) {
+        if (a.zsplit == 1)
+          a.dcat[(((size_t)b * N + j) * N + k) * C + 4 * D + t] = dz[kbk][r];
+        else
+          a.zpart[(((size_t)blockIdx.z * a.B * h + bt) * N + j) * N + k] = dz[kbk][r];
+      }
     }
+}
+
+// dz = the row ranges' partial sums added in range order, into dcat
+__global__ __launch_bounds__(256) void bwd_dz_reduce(BwdAttnArgs a) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // (b, t, j, k)
+  const int N = a.N, h = a.h;
+  const long long nz = (long long)a.B * h * N * N;
+  if (e >= nz) return;
+  float sum = 0.f;
+  for (int z = 0; z < a.zsplit; ++z) sum += a.zpart[z * nz + e];
+  const long long jk = e % ((long long)N * N), bt = e / ((long long)N * N);
+  const int b = (int)(bt / h), t = (int)(bt - (long long)b * h);
+  a.dcat[((size_t)b * N * N + jk) * a.C + 4 * a.D + t] = sum;
 }
 
 // z[b,t,j,k] * log2(e) from the projection columns, FILL * log2(e) where the
@@ -910,8 +935,9 @@ __global__ __launch_bounds__(256) void bwd_gate(const float *dgo, const float *p
 
 // ------------------------------------------------------------------ host side
 struct BwdLayout {
-  size_t x, xhat, rstd, proj, zt, m, l, Dj, o, dgo, dob, go, dcat, dx, part, vpart, bits, pt, mt, dyt, dpt, total;
+  size_t x, xhat, rstd, proj, zt, m, l, Dj, o, dgo, dob, go, dcat, dx, part, vpart, bits, zpart, pt, mt, dyt, dpt, total;
   long long S, kchunk, nvblk, vper;
+  int zsplit, zrows;
 };
 
 static size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -949,6 +975,17 @@ static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed
   L.part = take((size_t)L.S * C * D * 4);
   L.vpart = take((size_t)2 * L.nvblk * D * 4);
   L.bits = take((size_t)B * N * h * N * ((N + 31) / 32) * 4);
+  // dz row ranges: enough workgroups to fill the CUs several times over
+  // (2048), at least 8 rows per range
+  {
+    const long long tiles = (long long)((N + 63) / 64) * ((N + 63) / 64) * B * h;
+    long long zs = tiles >= 2048 ? 1 : (2048 + tiles - 1) / tiles;
+    zs = std::min(zs, (long long)std::max(1, (N + 7) / 8));
+    L.zrows = (int)((N + zs - 1) / zs);
+    L.zsplit = (N + L.zrows - 1) / L.zrows;
+    if (L.zsplit < 1) L.zsplit = 1;
+  }
+  L.zpart = L.zsplit > 1 ? take((size_t)L.zsplit * B * h * N * N * 4) : 0;
   if (transposed) {  // ending-node: pair_repr, mask and dy with both residue axes swapped, and dP before swapping back
     L.pt = take((size_t)P * D * elem);
     L.mt = take((size_t)P);
@@ -1073,8 +1110,16 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   hipLaunchKernelGGL((bwd_attn_dkv<DH>), ga, dim3(512), 0, s, aa);
   TPA_CHECK(hipGetLastError());
   const int nkt = (N + 63) / 64, njt = (N + 63) / 64;
-  hipLaunchKernelGGL((bwd_attn_dz<DH>), dim3((unsigned)(njt * nkt), (unsigned)(B * h)), dim3(256), 0, s, aa);
+  aa.zsplit = L.zsplit, aa.zrows = L.zrows;
+  aa.zpart = reinterpret_cast<float *>(w + L.zpart);
+  hipLaunchKernelGGL((bwd_attn_dz<DH>), dim3((unsigned)(njt * nkt), (unsigned)(B * h), (unsigned)L.zsplit), dim3(256),
+                     0, s, aa);
   TPA_CHECK(hipGetLastError());
+  if (L.zsplit > 1) {
+    const long long nz = (long long)B * h * N * N;
+    hipLaunchKernelGGL(bwd_dz_reduce, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, s, aa);
+    TPA_CHECK(hipGetLastError());
+  }
   // projections and LayerNorm
   TPA_CHECK((gemm<float, T>(dcat, C, 1, r.wpack, D, 1, dx, 0, D, P, D, C, C, 1, s)));
   hipLaunchKernelGGL((bwd_ln_back<T, D>), dim3((unsigned)L.nvblk), dim3(256), 0, s, dx, xhat, rstd, gamma, P, L.vper,
