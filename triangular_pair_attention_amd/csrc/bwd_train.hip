@@ -162,12 +162,21 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
 }
 
 // out[e] = sum over z of part[z*stride + e], z = 0..nz-1 in order
+// (sixteen loads in flight at a time, added in the same order z = 0, 1, ...)
 __global__ __launch_bounds__(256) void bwd_reduce(const float *part, long long n, int nz, long long stride,
                                                    float *out) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   if (e >= n) return;
   float s = 0.f;
-  for (int z = 0; z < nz; ++z) s += part[(size_t)(z * stride + e)];
+  int z = 0;
+  for (; z + 16 <= nz; z += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = part[(size_t)((z + u) * stride + e)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += v[u];
+  }
+  for (; z < nz; ++z) s += part[(size_t)(z * stride + e)];
   out[e] = s;
 }
 
