@@ -67,8 +67,11 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   __shared__ float As[16][68];
   __shared__ float Bs[16][68];
   const int tid = threadIdx.x;
-  // grid x: row blocks (M can be large), y: column blocks, z: K chunks
-  const long long m0 = (long long)blockIdx.x * 64, n0 = (long long)blockIdx.y * 64;
+  // grid x: (row block, column block) with the column block fastest, so the
+  // workgroups that share a row block of A run together and it is read from
+  // memory once; z: K chunks
+  const long long ncb = (g.N + 63) / 64;
+  const long long m0 = ((long long)blockIdx.x / ncb) * 64, n0 = ((long long)blockIdx.x % ncb) * 64;
   const long long kb = (long long)blockIdx.z * g.kchunk;
   const long long ke = min(kb + g.kchunk, g.K);
   // wave w computes the 32 x 32 quadrant (w / 2, w % 2) as 2 x 2 float32
@@ -1034,7 +1037,9 @@ static hipError_t gemm(const void *A, long long sam, long long sak, const void *
                        float *C, long long scz, long long scm, long long M, long long N, long long K,
                        long long kchunk, int nz, hipStream_t s) {
   GemmArgs g{A, Bm, C, M, N, K, kchunk, sam, sak, sbk, sbn, scz, scm};
-  const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)nz);
+  const long long blocks = ((M + 63) / 64) * ((N + 63) / 64);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks, 1, (unsigned)nz);
   hipLaunchKernelGGL((bwd_gemm<TA, TB>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
