@@ -303,6 +303,16 @@ int tri_attn_get_workspace_layout(tri_attn_t h, int B, int N, tri_attn_workspace
  * it. Errors: INVALID_ARG. */
 int tri_attn_set_shift_slack(tri_attn_t h, float slack);
 
+/* Testing aid: the number of row ranges (1 .. N; more are clamped to N)
+ * that later tri_attn_backward_train calls on this handle split the
+ * pair-bias gradient step into, each range's partial sum added in range order
+ * afterwards; 0 (the default) chooses it from the sizes (one range once the
+ * (query, key) tiles alone fill the GPU, more below that). Results agree to
+ * float32 rounding whatever the count; tri_attn_backward_workspace_size
+ * depends on it, so query the size after setting it. Errors: INVALID_ARG
+ * (NULL handle, ranges < 0). */
+int tri_attn_set_backward_dz_ranges(tri_attn_t h, int ranges);
+
 /* Run only the LayerNorm + projection kernel (arguments as tri_attn_forward). */
 int tri_attn_project(tri_attn_t h, const void *pair_repr, const uint8_t *pair_mask, int B, int N,
                      void *workspace, size_t ws_bytes, void *stream);

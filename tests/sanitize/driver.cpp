@@ -111,6 +111,7 @@ int main() {
   EXPECT(tri_attn_forward_onepass(nullptr, p, m, p, 1, 8, p, 1 << 20, nullptr), TRI_ATTN_ERR_INVALID_ARG);
   EXPECT(tri_attn_forward_noalloc(nullptr, p, m, p, 1, 8, nullptr), TRI_ATTN_ERR_INVALID_ARG);
   EXPECT(tri_attn_set_shift_slack(nullptr, 1.f), TRI_ATTN_ERR_INVALID_ARG);
+  EXPECT(tri_attn_set_backward_dz_ranges(nullptr, 2), TRI_ATTN_ERR_INVALID_ARG);
   EXPECT(tri_attn_destroy(nullptr), TRI_ATTN_OK);
 
   if (failures) std::fprintf(stderr, "%d failures\n", failures);

@@ -13,7 +13,7 @@ int k1_blocks_per_cu(int, int, int) { return 1; }
 int k2_blocks_per_cu(int, int, int) { return 1; }
 int k3_blocks_per_cu(int, int) { return 1; }
 int k1_split_blocks_per_cu(int, int) { return 1; }
-size_t bwd_workspace_bytes(int B, int N, int D, int h, int, int) { return (size_t)B * N * N * (5 * D + h) * 16; }
+size_t bwd_workspace_bytes(int B, int N, int D, int h, int, int, int) { return (size_t)B * N * N * (5 * D + h) * 16; }
 int scratch_address(int, void **ptr) {
   *ptr = nullptr;
   return TRI_ATTN_ERR_HIP;

@@ -28,9 +28,11 @@ SHAPE = {"d_pair_repr": "pair_repr", "d_ln_weight": "ln_weight", "d_ln_bias": "l
          "d_w_bias_proj": "w_bias_proj", "d_w_out": "w_out", "d_b_out": "b_out"}
 
 
-def run_backward(inp, dy, rate, seed, offset, fill=-1e9, ending=False):
+def run_backward(inp, dy, rate, seed, offset, fill=-1e9, ending=False, dz_ranges=0):
     g = Gpu(inp, fill=fill, ending=ending)
     try:
+        if dz_ranges:
+            B.tri_attn_set_backward_dz_ranges(g.handle, dz_ranges)
         grads = {k: torch.zeros(np.shape(inp[v]), dtype=torch.float32, device=g.dev) for k, v in SHAPE.items()}
         n = B.tri_attn_backward_workspace_size(g.handle, g.B, g.N)
         ws = torch.empty(max(n, 256), dtype=torch.uint8, device=g.dev)
@@ -52,9 +54,9 @@ def make_dy(inp, seed):
     return dy
 
 
-def check_backward(inp, rate, seed, offset, what, fill=-1e9):
+def check_backward(inp, rate, seed, offset, what, fill=-1e9, dz_ranges=0):
     dy = make_dy(inp, 99)
-    got = run_backward(inp, dy, rate, seed, offset, fill)
+    got = run_backward(inp, dy, rate, seed, offset, fill, dz_ranges=dz_ranges)
     ref = BO.backward_train(inp, dy.astype(np.float64), rate, seed, offset, fill=fill)
     worst = 0.0
     for k in SHAPE:
@@ -83,6 +85,37 @@ def test_backward_small(shape, mask, dtype, rate):
     Bn, N, D, h = shape
     inp = make_inputs(Workload("bwd", Bn, N, D, h, dtype, mask, seed=81 + N))
     check_backward(inp, rate, seed=2**35 + 3, offset=5, what=f"backward {dtype} {shape} {mask} rate {rate}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ranges", [1, 3, 1000])
+def test_backward_pair_bias_step_row_ranges(dtype, ranges):
+    """The pair-bias gradient step sums over rows i in ranges whose partial
+    sums are added in order afterwards; small sizes choose several ranges,
+    large ones (from 2048 (query, key) tiles up, workload 5) a single range
+    written directly. Forcing 1, 3 and N ranges (1000 is clamped to N) here
+    runs every one of those paths against the oracle."""
+    inp = make_inputs(Workload("bwd_ranges", 1, 45, 128, 4, dtype, ("pad", 38), seed=88))
+    check_backward(inp, 0.2, seed=17, offset=2, what=f"backward {dtype} {ranges} row ranges", dz_ranges=ranges)
+
+
+def test_backward_row_range_setter_errors_and_workspace():
+    inp = make_inputs(Workload("bwd_ranges_err", 1, 45, 64, 4, "f32", ("ones",), seed=89))
+    g = Gpu(inp)
+    try:
+        with pytest.raises(B.TriAttnError) as e:
+            B.tri_attn_set_backward_dz_ranges(g.handle, -1)
+        assert e.value.code == B.TRI_ATTN_ERR_INVALID_ARG
+        n_auto = B.tri_attn_backward_workspace_size(g.handle, 1, 45)
+        B.tri_attn_set_backward_dz_ranges(g.handle, 1)
+        n_one = B.tri_attn_backward_workspace_size(g.handle, 1, 45)
+        B.tri_attn_set_backward_dz_ranges(g.handle, 5)
+        n_five = B.tri_attn_backward_workspace_size(g.handle, 1, 45)
+        # one range needs no partial sums; five ranges need five B*h*N*N float32 slices
+        assert n_one < n_auto
+        assert n_five - n_one >= 5 * 4 * 45 * 45 * 4
+    finally:
+        g.close()
 
 
 @pytest.mark.parametrize("k", [1, 2, 3])

@@ -92,6 +92,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.tri_attn_output.argtypes = [vp, vp, i, i, vp, sz, vp]
     lib.tri_attn_set_shift_slack.argtypes = [vp, ctypes.c_float]
     lib.tri_attn_set_alloc_fault.argtypes = [i]
+    lib.tri_attn_set_backward_dz_ranges.argtypes = [vp, i]
     lib.tri_attn_onepass_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.tri_attn_forward_onepass.argtypes = [vp, vp, vp, vp, i, i, vp, sz, vp]
     lib.tri_attn_backward_workspace_size.argtypes = [vp, i, i, ctypes.POINTER(sz)]
@@ -104,7 +105,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                  "tri_attn_get_workspace_layout", "tri_attn_project", "tri_attn_attend",
                  "tri_attn_output", "tri_attn_forward_train", "tri_attn_set_shift_slack",
                  "tri_attn_forward_noalloc", "tri_attn_backward_workspace_size", "tri_attn_backward_train",
-                 "tri_attn_onepass_workspace_size", "tri_attn_forward_onepass", "tri_attn_set_alloc_fault"):
+                 "tri_attn_onepass_workspace_size", "tri_attn_forward_onepass", "tri_attn_set_alloc_fault",
+                 "tri_attn_set_backward_dz_ranges"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -210,6 +212,10 @@ def tri_attn_output(handle: int, out, B: int, N: int, workspace, ws_bytes: int, 
 
 def tri_attn_set_shift_slack(handle: int, slack: float) -> None:
     _check(load_library().tri_attn_set_shift_slack(handle, float(slack)), "tri_attn_set_shift_slack")
+
+
+def tri_attn_set_backward_dz_ranges(handle: int, ranges: int) -> None:
+    _check(load_library().tri_attn_set_backward_dz_ranges(handle, int(ranges)), "tri_attn_set_backward_dz_ranges")
 
 
 def tri_attn_set_alloc_fault(nth: int) -> None:

@@ -954,7 +954,7 @@ struct BwdLayout {
 
 static size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
-static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed) {
+static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed, int dz_ranges) {
   BwdLayout L{};
   const long long P = (long long)B * N * N, C = 4LL * D + h;
   // split-K chunks of the weight gradients (sums over all positions): at most
@@ -988,11 +988,12 @@ static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed
   L.vpart = take((size_t)2 * L.nvblk * D * 4);
   L.bits = take((size_t)B * N * h * N * ((N + 31) / 32) * 4);
   // dz row ranges: enough workgroups to fill the CUs several times over
-  // (2048), at least 8 rows per range
+  // (2048), at least 8 rows per range; or the number the handle was given
   {
     const long long tiles = (long long)((N + 63) / 64) * ((N + 63) / 64) * B * h;
     long long zs = tiles >= 2048 ? 1 : (2048 + tiles - 1) / tiles;
     zs = std::min(zs, (long long)std::max(1, (N + 7) / 8));
+    if (dz_ranges > 0) zs = std::min(dz_ranges, std::max(N, 1));
     L.zrows = (int)((N + zs - 1) / zs);
     L.zsplit = (N + L.zrows - 1) / L.zrows;
     if (L.zsplit < 1) L.zsplit = 1;
@@ -1008,8 +1009,8 @@ static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed
   return L;
 }
 
-size_t bwd_workspace_bytes(int B, int N, int D, int h, int elem, int transposed) {
-  return bwd_layout(B, N, D, h, elem, transposed).total;
+size_t bwd_workspace_bytes(int B, int N, int D, int h, int elem, int transposed, int dz_ranges) {
+  return bwd_layout(B, N, D, h, elem, transposed, dz_ranges).total;
 }
 
 // dst[b][i][j][:] = src[b][j][i][:] (W elements per position): the two
@@ -1053,7 +1054,7 @@ template <typename T, int D, int DH>
 static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   const int B = r.B, N = r.N, h = D / DH;
   const long long P = (long long)B * N * N, C = 4LL * D + h;
-  const BwdLayout L = bwd_layout(B, N, D, h, (int)sizeof(T) == 2 ? 2 : 4, r.transposed);
+  const BwdLayout L = bwd_layout(B, N, D, h, (int)sizeof(T) == 2 ? 2 : 4, r.transposed, r.dz_ranges);
   char *w = static_cast<char *>(r.ws);
   float *x = reinterpret_cast<float *>(w + L.x), *xhat = reinterpret_cast<float *>(w + L.xhat);
   float *rstd = reinterpret_cast<float *>(w + L.rstd), *proj = reinterpret_cast<float *>(w + L.proj);

@@ -15,6 +15,7 @@
 struct tri_attn {
   tri_attn_config cfg;
   float shift_slack;  // testing aid (tri_attn_set_shift_slack), 0 in normal use
+  int bwd_dz_ranges;  // testing aid (tri_attn_set_backward_dz_ranges), 0 in normal use
   int D, h, dh, elem;
   int device;
   int k1_grid;     // persistent grid of kernel 1 (resident workgroups)
@@ -113,6 +114,7 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
   if (!t) return TRI_ATTN_ERR_OOM;
   t->cfg = *cfg;
   t->shift_slack = 0.f;
+  t->bwd_dz_ranges = 0;
   t->D = cfg->pair_dim;
   t->h = cfg->num_heads;
   t->dh = t->D / t->h;
@@ -353,7 +355,7 @@ int tri_attn_backward_workspace_size(tri_attn_t t, int B, int N, size_t *bytes) 
   if (!bytes) return TRI_ATTN_ERR_INVALID_ARG;
   const int rc = check_sizes(t, B, N);
   if (rc) return rc;
-  *bytes = (B == 0 || N == 0) ? 0 : bwd_workspace_bytes(B, N, t->D, t->h, t->elem, t->cfg.ending_node);
+  *bytes = (B == 0 || N == 0) ? 0 : bwd_workspace_bytes(B, N, t->D, t->h, t->elem, t->cfg.ending_node, t->bwd_dz_ranges);
   return TRI_ATTN_OK;
 }
 
@@ -370,7 +372,7 @@ int tri_attn_backward_train(tri_attn_t t, const void *pair_repr, const uint8_t *
   if (!g.d_pair_repr || !g.d_ln_weight || !g.d_ln_bias || !g.d_w_query || !g.d_w_key || !g.d_w_value ||
       !g.d_w_gate || !g.d_b_gate || !g.d_w_bias_proj || !g.d_w_out || !g.d_b_out)
     return TRI_ATTN_ERR_INVALID_ARG;
-  const size_t need = bwd_workspace_bytes(B, N, t->D, t->h, t->elem, t->cfg.ending_node);
+  const size_t need = bwd_workspace_bytes(B, N, t->D, t->h, t->elem, t->cfg.ending_node, t->bwd_dz_ranges);
   if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255)) return TRI_ATTN_ERR_WORKSPACE;
   BwdRunArgs r{};
   r.P = pair_repr, r.mask = pair_mask, r.dy = dy, r.wpack = t->wpack, r.vecs = t->vecs, r.g = g, r.ws = workspace;
@@ -381,6 +383,7 @@ int tri_attn_backward_train(tri_attn_t t, const void *pair_repr, const uint8_t *
   r.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu), r.seed_hi = (uint32_t)(seed >> 32), r.offset = offset;
   r.B = B, r.N = N;
   r.transposed = t->cfg.ending_node;
+  r.dz_ranges = t->bwd_dz_ranges;
   if (launch_bwd(t->cfg.dtype, t->D, t->dh, r, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return TRI_ATTN_ERR_HIP;
   return TRI_ATTN_OK;
@@ -431,6 +434,12 @@ int tri_attn_output(tri_attn_t t, void *out, int B, int N, void *workspace, size
 int tri_attn_set_shift_slack(tri_attn_t t, float slack) {
   if (!t || !std::isfinite(slack) || slack < 0.f) return TRI_ATTN_ERR_INVALID_ARG;
   t->shift_slack = slack;
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_set_backward_dz_ranges(tri_attn_t t, int ranges) {
+  if (!t || ranges < 0) return TRI_ATTN_ERR_INVALID_ARG;
+  t->bwd_dz_ranges = ranges;
   return TRI_ATTN_OK;
 }
 

@@ -106,9 +106,10 @@ struct BwdRunArgs {
   uint32_t thr, seed_lo, seed_hi, offset;
   int B, N;
   int transposed;  // ending-node handle: the starting-node backward of the transposed problem
+  int dz_ranges;   // row ranges of the pair-bias gradient step (0: chosen from the sizes)
 };
 hipError_t launch_bwd(int dtype, int D, int dh, const BwdRunArgs &r, hipStream_t s);
-size_t bwd_workspace_bytes(int B, int N, int D, int h, int elem_bytes, int transposed);
+size_t bwd_workspace_bytes(int B, int N, int D, int h, int elem_bytes, int transposed, int dz_ranges);
 // One-pass variant (onepass.hip): the pre-pass writes zm, the fused row
 // kernel does everything else.
 struct OnePassArgs {
