@@ -994,6 +994,7 @@ static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed
     long long zs = tiles >= 2048 ? 1 : (2048 + tiles - 1) / tiles;
     zs = std::min(zs, (long long)std::max(1, (N + 7) / 8));
     if (dz_ranges > 0) zs = std::min(dz_ranges, std::max(N, 1));
+    zs = std::min(zs, 65535LL);  // the grid's z dimension
     L.zrows = (int)((N + zs - 1) / zs);
     L.zsplit = (N + L.zrows - 1) / L.zrows;
     if (L.zsplit < 1) L.zsplit = 1;
