@@ -30,7 +30,7 @@ steps of the forward in reverse, in float64:
                                  dxh = dx * gamma
 """
 import math
-from typing import Optional
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -121,3 +121,73 @@ def backward_train(inp: dict, dy: np.ndarray, rate: float, seed: int, offset: in
     if capture is not None:
         capture["y"] = f["y"]
     return gr
+
+
+def pair_repr_grad_at(inp: dict, dy: np.ndarray, rate: float, seed: int, offset: int = 0,
+                      positions: Sequence[Tuple[int, int, int]] = (), fill: float = O.MASK_FILL,
+                      eps: float = O.LN_EPS) -> np.ndarray:
+    """dL/d(pair_repr) at the listed positions (b, r, c) only, (len, D)
+    float64: the steps of backward_train restricted to what those positions
+    need, for sizes where its whole (B, N, h, N, N) tensors do not fit in
+    memory. Position (b, r, c) enters pair row r as query column c (q and
+    the gate), as key c (k and v), and through the pair bias z[b, :, r, c]
+    every row i, as the score of query column r and key c."""
+    P = O._f64(inp["pair_repr"])
+    M = np.asarray(inp["pair_mask"])
+    h = int(inp["num_heads"])
+    prm = O._params(inp)
+    B, N, _, D = P.shape
+    d = D // h
+    dy = np.asarray(dy, np.float64)
+    thr = np.uint32(TO.drop_threshold(rate))
+    scale = TO.keep_scale(rate)
+    out = np.empty((len(positions), D))
+    cur, f = None, None
+    for n, (b, r, c) in enumerate(positions):
+        if b != cur:  # every tensor of batch b, positions (i, j)
+            cur = b
+            mu = P[b].mean(-1, keepdims=True)
+            var = ((P[b] - mu) ** 2).mean(-1, keepdims=True)
+            rstd = 1.0 / np.sqrt(var + eps)
+            xhat = (P[b] - mu) * rstd
+            x = xhat * prm["ln_weight"] + prm["ln_bias"]
+            g = 1.0 / (1.0 + np.exp(-(x @ prm["w_gate"].T + prm["b_gate"])))
+            heads = lambda y: y.reshape(N, N, h, d).transpose(0, 2, 1, 3)  # noqa: E731  (i, t, j, u)
+            dgo = dy[b] @ prm["w_out"]
+            f = dict(xhat=xhat, rstd=rstd, g=g, dgo=dgo, q=heads(x @ prm["w_query"].T), k=heads(x @ prm["w_key"].T),
+                     v=heads(x @ prm["w_value"].T), do=heads(dgo * g),
+                     z=np.moveaxis(x @ prm["w_bias_proj"].T, -1, 0), valid=M[b] != 0)
+        q, k, v, do, valid = f["q"], f["k"], f["v"], f["do"], f["valid"]
+        # row r: (7), (6'), (6), (5) for every query column j and key of the row
+        s = np.where(valid[None], q[r] @ np.swapaxes(k[r], -1, -2) / math.sqrt(d) + f["z"], fill)  # (t, j, k)
+        a = O.softmax(s, axis=-1)
+        keep = TO.row_uniforms(b, r, N, h, seed, offset) >= thr
+        a_drop = np.where(keep, a * scale, 0.0)
+        o_c = np.einsum("tk,tku->tu", a_drop[:, c, :], v[r]).reshape(D)  # o of query column c, channel t*d + u
+        da = np.where(keep, (do[r] @ np.swapaxes(v[r], -1, -2)) * scale, 0.0)
+        ds = a * (da - (a * da).sum(-1, keepdims=True))
+        dsm = np.where(valid[None], ds, 0.0)
+        dq_c = np.einsum("tk,tku->tu", dsm[:, c, :], k[r]) / math.sqrt(d)  # (t, u): query column c
+        dk_c = np.einsum("tj,tju->tu", dsm[:, :, c], q[r]) / math.sqrt(d)  # key c
+        dv_c = np.einsum("tj,tju->tu", a_drop[:, :, c], do[r])  # key c
+        # (8), (2): the gate of position (r, c)
+        g_c = f["g"][r, c]
+        dgp = f["dgo"][r, c] * o_c * g_c * (1.0 - g_c)
+        dx = dgp @ prm["w_gate"]
+        # (4)
+        for name, dt in (("w_query", dq_c), ("w_key", dk_c), ("w_value", dv_c)):
+            dx = dx + dt.reshape(D) @ prm[name]
+        # (3): dz[t, r, c] = sum over rows i of dsm[i, t, r, c] (query column r, key c)
+        qk = (q[:, :, r, None, :] @ np.swapaxes(k, -1, -2))[:, :, 0, :]  # (i, t, k)
+        s_col = np.where(valid[r][None, None], qk / math.sqrt(d) + f["z"][None, :, r, :], fill)
+        a_col = O.softmax(s_col, axis=-1)
+        keep_col = TO.column_uniforms(b, r, N, h, seed, offset) >= thr
+        da_col = np.where(keep_col, (do[:, :, r, None, :] @ np.swapaxes(v, -1, -2))[:, :, 0, :] * scale, 0.0)
+        ds_col = a_col * (da_col - (a_col * da_col).sum(-1, keepdims=True))
+        dz = ds_col[:, :, c].sum(0) if valid[r, c] else np.zeros(h)
+        dx = dx + dz @ prm["w_bias_proj"]
+        # (1)
+        dxh = dx * prm["ln_weight"]
+        xh = f["xhat"][r, c]
+        out[n] = (dxh - dxh.mean() - xh * (dxh * xh).mean()) * f["rstd"][r, c, 0]
+    return out

@@ -98,6 +98,22 @@ def row_uniforms(b: int, i: int, N: int, h: int, seed: int, offset: int = 0) -> 
     return words.reshape(h, N, Nk * 4)[:, :, :N]
 
 
+def column_uniforms(b: int, j: int, N: int, h: int, seed: int, offset: int = 0) -> np.ndarray:
+    """u[i, t, k] (N, h, N) uint32 of query column j in every pair row i of
+    batch b, as defined in (6'): the words row_uniforms(b, i, ...)[t, j, k]."""
+    Nk = (N + 3) // 4
+    i = np.arange(N, dtype=np.uint64)[:, None, None]
+    t = np.arange(h, dtype=np.uint64)[None, :, None]
+    kg = np.arange(Nk, dtype=np.uint64)[None, None, :]
+    ctr = np.empty((N, h, Nk, 4), dtype=np.uint32)
+    ctr[..., 0] = kg
+    ctr[..., 1] = np.uint32(j)
+    ctr[..., 2] = ((np.uint64(b * N) + i) * np.uint64(h) + t) & _MASK32
+    ctr[..., 3] = np.uint32(int(offset) & 0xFFFFFFFF)
+    words = philox4x32_10(ctr, seed_key(seed))  # (N, h, Nk, 4)
+    return words.reshape(N, h, Nk * 4)[:, :, :N]
+
+
 def row_attention_train(x_row, z_b, mask_b, prm, h, u, rate, fill=O.MASK_FILL, capture=None):
     """Steps (2), (4)-(8) of one pair row with dropout (6') on the attention
     weights; u holds the row's uniforms (h, N, N). Returns (y (N, D), lse (h, N))."""

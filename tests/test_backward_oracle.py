@@ -10,6 +10,10 @@ independent of its own code.
 * Planted mistakes in a copy of the backward oracle (the pair bias's
   gradient from one row instead of the sum over rows; the dropout mask left
   out of the backward) that the finite-difference pin must reject.
+* The position-sampled form (pair_repr_grad_at, for sizes where the whole
+  backward does not fit in memory) equals the whole backward's
+  dL/d(pair_repr) at every position of small inputs: padding with fully
+  masked columns, Bernoulli masks, the -inf fill, both dtypes' inputs.
 """
 import math
 
@@ -19,7 +23,7 @@ import torch
 
 import oracle.tri_attn_oracle as O
 import oracle.tri_attn_train_oracle as TO
-from oracle.tri_attn_backward_oracle import backward_train
+from oracle.tri_attn_backward_oracle import backward_train, pair_repr_grad_at
 from workloads import Workload, make_inputs
 
 backward_train_ref = backward_train  # restored after the planted-mistake tests
@@ -124,3 +128,25 @@ def test_planted_mistakes_are_caught(old, new, tmp_path):
             test_finite_differences(0.3, ("pad", 2))
         finally:
             globals()["backward_train"] = backward_train_ref
+
+
+# ------------------------------------------------------------------ position-sampled form
+@pytest.mark.parametrize("shape,mask,dtype,rate,fill", [
+    ((2, 20, 64, 4), ("bernoulli", 0.8), "f32", 0.3, O.MASK_FILL),
+    ((1, 33, 128, 4), ("pad", 25), "bf16", 0.0, O.MASK_FILL),
+    ((1, 17, 64, 2), ("pad", 12), "f32", 0.5, O.MASK_FILL),
+    ((2, 13, 64, 4), ("bernoulli", 0.7), "f32", 0.2, -math.inf),
+], ids=["B2N20bern", "N33pad-bf16", "N17pad-d32", "B2N13-inf"])
+def test_position_sampled_gradient_equals_whole_backward(shape, mask, dtype, rate, fill):
+    """Every position (b, r, c) of the inputs, in an order that switches batch
+    more than once, against the whole backward's dL/d(pair_repr)."""
+    B, N, D, h = shape
+    inp = make_inputs(Workload("sampled", B, N, D, h, dtype, mask, seed=5 + N))
+    dy = np.random.default_rng(3).standard_normal((B, N, N, D))
+    whole = backward_train(inp, dy, rate, 77, 2, fill=fill)["d_pair_repr"]
+    pos = [(b, r, c) for r in range(N) for c in range(N) for b in range(B)]
+    got = pair_repr_grad_at(inp, dy, rate, 77, 2, pos, fill=fill)
+    ref = np.array([whole[p] for p in pos])
+    assert (np.isfinite(got) == np.isfinite(ref)).all()
+    fin = np.isfinite(ref)
+    assert np.abs(got[fin] - ref[fin]).max() <= 1e-12 * max(1.0, np.abs(ref[fin]).max())

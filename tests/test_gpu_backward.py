@@ -118,13 +118,49 @@ def test_backward_row_range_setter_errors_and_workspace():
         g.close()
 
 
-@pytest.mark.parametrize("k", [1, 2, 3])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_backward_workload(k):
-    """Workloads 1-3 (B=2 N=32 D=64 h=4 f32; B=1 N=128 D=128 h=4 f32; B=1
-    N=256 D=128 h=4 bf16 with 16 padded residues), dropout 0.1."""
+    """Workloads 1-4 in full (B=2 N=32 D=64 h=4 f32; B=1 N=128 D=128 h=4 f32;
+    B=1 N=256 D=128 h=4 bf16 with 16 padded residues; B=1 N=384 D=128 h=4
+    bf16, Bernoulli mask), dropout 0.1."""
     w = WORKLOADS[k]
     log(f"backward {w.name}")
     check_backward(make_inputs(w), 0.1, seed=4242, offset=1, what=f"backward {w.name}")
+
+
+def test_backward_workload5_sampled_positions():
+    """Workload 5 (B=4 N=512 D=128 h=8 bf16, per-batch padding), the size and
+    launch configuration the benchmark times, dropout 0.1: the whole
+    backward runs on the GPU; dL/d(pair_repr) is compared with the
+    position-sampled backward oracle at 24 positions (per batch: the first
+    and the last valid position, a position in a padded row, one in a padded
+    column, the last position, a random valid one). Each such gradient draws
+    on every step of the backward: the gate, dq of its query column, dk and
+    dv of its key, and the pair bias's gradient summed over all 512 rows.
+    The parameter gradients are sums over all positions; at this size they
+    are checked for finiteness (workloads 1-4 compare them in full)."""
+    w = WORKLOADS[5]
+    inp = make_inputs(w)
+    M = np.asarray(inp["pair_mask"])
+    rng = np.random.default_rng(505)
+    pos = []
+    for b in range(w.B):
+        L = int(M[b].any(axis=1).sum())  # valid length: rows and columns >= L are padding
+        pos += [(b, 0, 0), (b, L - 1, L - 1), (b, min(L, w.N - 1), 3), (b, 7, min(L + 1, w.N - 1)),
+                (b, w.N - 1, w.N - 1), (b, int(rng.integers(0, L)), int(rng.integers(0, L)))]
+    log(f"backward {w.name}: GPU backward, then the oracle at {len(pos)} positions")
+    dy = make_dy(inp, 99)
+    got = run_backward(inp, dy, 0.1, 4242, 1)
+    for k in SHAPE:
+        assert np.isfinite(got[k]).all(), k
+    ref = BO.pair_repr_grad_at(inp, dy.astype(np.float64), 0.1, 4242, 1, pos)
+    gk = np.stack([got["d_pair_repr"][p] for p in pos])
+    scale = float(np.abs(ref).max())
+    err = np.abs(gk - ref).max(axis=1)
+    worst = int(err.argmax())
+    log(f"backward {w.name} d_pair_repr at {len(pos)} positions: max abs err {err[worst]:.3e} at {pos[worst]}, "
+        f"max |ref| {scale:.3e}, relative {err[worst] / scale:.2e}")
+    assert err[worst] <= RTOL * scale, f"error {err[worst]} at {pos[worst]} > {RTOL} * {scale}"
 
 
 def test_backward_minus_inf_fill():

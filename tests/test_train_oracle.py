@@ -164,6 +164,15 @@ def test_keep_fraction_and_uniform_words():
     assert chi2 < 255 + 6 * math.sqrt(2 * 255)
 
 
+def test_column_uniforms_are_the_row_uniforms():
+    """u of one query column in every row equals that column of each row's u."""
+    B, N, h, seed, offset = 3, 13, 3, 2**33 + 9, 4
+    for b in range(B):
+        rows = np.stack([TO.row_uniforms(b, i, N, h, seed, offset) for i in range(N)])  # (i, t, j, k)
+        for j in (0, 5, N - 1):
+            assert np.array_equal(TO.column_uniforms(b, j, N, h, seed, offset), rows[:, :, j, :])
+
+
 def test_decisions_depend_on_seed_offset_row_and_head():
     base = TO.row_uniforms(1, 2, 8, 2, 5, 0)
     assert np.array_equal(base, TO.row_uniforms(1, 2, 8, 2, 5, 0))
