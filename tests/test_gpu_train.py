@@ -104,21 +104,13 @@ def test_train_workload4_full():
     check_train_pool(make_inputs(w), [(0, i) for i in range(w.N)], 0.1, 777, 3, f"train {w.name}")
 
 
-def test_train_workload5_sampled_rows():
-    """B=4, N=512, h=8 (d = 16): 40 rows spread over the four batches (first,
-    last valid, first padded and last rows of each, and random ones), all
-    columns and heads of each."""
+def test_train_workload5_full():
+    """B=4, N=512, h=8 (d = 16): all 2048 rows (every column and head of
+    each, y and lse), the rows spread over host worker processes."""
     w = WORKLOADS[5]
-    inp = make_inputs(w)
-    M = inp["pair_mask"]
-    rng = np.random.default_rng(3)
-    rows = []
-    for b in range(w.B):
-        L = int(M[b].diagonal().sum())
-        cand = {0, L - 1, min(L, w.N - 1), w.N - 1} | {int(x) for x in rng.integers(0, w.N, 6)}
-        rows += [(b, i) for i in sorted(cand)]
-    log(f"train {w.name}: {len(rows)} sampled rows (worker processes)")
-    check_train_pool(inp, rows, 0.1, 2**40 + 17, 0, f"train {w.name} sampled")
+    rows = [(b, i) for b in range(w.B) for i in range(w.N)]
+    log(f"train {w.name}: all {len(rows)} rows (worker processes)")
+    check_train_pool(make_inputs(w), rows, 0.1, 2**40 + 17, 0, f"train {w.name}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
