@@ -482,6 +482,28 @@ def test_ending_node_large_sampled_columns(dtype):
     check(got, O.forward_ending_cols(inp, cols), dtype, f"ending N=300 {dtype} sampled columns")
 
 
+def test_ending_node_workload5_full():
+    """Ending-node handle at B=4, N=512, h=8 bf16 (per-batch padding): every
+    output column y[b, :, j] against the oracle's ending-node forward, which
+    is its starting-node forward of the pair representation and mask with
+    both residue axes swapped (columns spread over host worker processes)."""
+    w = WORKLOADS[5]
+    log(f"ending node {w.name}: full oracle comparison (worker processes)")
+    inp = make_inputs(w)
+    g = Gpu(inp, ending=True)
+    try:
+        y = g.forward().float().cpu().numpy()
+        torch.cuda.synchronize()
+    finally:
+        g.close()
+    cols = [(b, j) for b in range(w.B) for j in range(w.N)]
+    r = pool.compare_rows(O._transposed(inp), np.ascontiguousarray(np.swapaxes(y, 1, 2)), cols)["y"]
+    log(f"ending {w.name}: max abs err {r['max_abs_err']:.3e} at (b, j, i, c) {r['where']}, "
+        f"max|y| {r['max_abs_ref']:.3f}")
+    assert r["same_nan_pattern"]
+    assert r["max_abs_err"] <= TOL[w.dtype]
+
+
 # ------------------------------------------------------------------ ABI behaviour on the GPU
 def test_deterministic_and_stream():
     inp = make_inputs(WORKLOADS[3].replace(N=96))
