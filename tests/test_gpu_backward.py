@@ -3,11 +3,12 @@ the backward oracle (hand back-propagation in float64, itself pinned by
 finite differences and autograd): dL/d(pair_repr) and dL/d(every parameter)
 for the same dropout decisions.
 
-Tolerance: the GPU computes every step in float32 from the same inputs, so
-each gradient tensor must agree with the oracle's to 1e-3 of its largest
+Tolerance: the GPU computes every step in float32 from the same inputs,
+the attention products as split bf16 products (about 2^-16 relative error),
+so each gradient tensor must agree with the oracle's to 1e-3 of its largest
 magnitude (the longest float32 sums run over all B*N*N positions; their
 rounding error grows like sqrt(B*N*N) * 2^-24 relative, about 2e-5 at
-B*N*N = 65536, well inside the bound)."""
+B*N*N = 65536; both well inside the bound)."""
 import math
 
 import numpy as np

@@ -23,9 +23,10 @@
 // fixed chunks whose partial results are added in a fixed order by a second
 // pass: no atomics, the same bits on every call.
 //
-// All arithmetic is float32. The products (the projection GEMMs and the
-// attention's score, value and gradient tiles) run on the float32 matrix
-// cores (16x16x4); the dropout decisions are computed once into a bit array
+// All arithmetic is float32. The projection GEMMs run on the float32 matrix
+// cores (16x16x4); the attention's score, value and gradient tiles as split
+// bf16 products (two bf16 parts per float32 operand, three 16x16x16 products
+// per float32 product, ~2^-16 relative error); the dropout decisions are computed once into a bit array
 // (one generator call per four keys) that every attention step reads; the
 // backward's copy of the pair bias carries the mask (FILL where masked), so
 // no attention step reads the mask itself.
@@ -347,36 +348,73 @@ __device__ __forceinline__ const uint32_t *keep_row(const BwdAttnArgs &a, int bi
   return a.bits + (((size_t)bi * a.h + t) * a.N + j) * a.NW;
 }
 
-// The attention steps run on float32 matrix cores (16x16x4), with the score
+// Float32 products as split bf16 products: a = ah + al with ah = bf16(a) and
+// al = bf16(a - ah) (a - ah is exact in float32), and a b ~ ah bh + ah bl +
+// al bh, three bf16 16x16x16 products (each ~0.6 of a float32 16x16x4
+// product's cost here, for 4x the contraction); the dropped al bl and the
+// remainders a - ah - al are ~2^-16 relative. The lane layout is the float32
+// product's: lane group g holds contraction elements 4g..4g+3.
+struct Split4 {
+  bf16x4 h, l;
+};
+__device__ __forceinline__ Split4 split4(float a, float b, float c, float d) {
+  const uint32_t h0 = pack_bf16x2(a, b), h1 = pack_bf16x2(c, d);
+  const uint32_t l0 = pack_bf16x2(a - bflo(h0), b - bfhi(h0)), l1 = pack_bf16x2(c - bflo(h1), d - bfhi(h1));
+  return {__builtin_bit_cast(bf16x4, make_uint2(h0, h1)), __builtin_bit_cast(bf16x4, make_uint2(l0, l1))};
+}
+__device__ __forceinline__ f32x4 mma_split(const Split4 &a, const Split4 &b, f32x4 c) {
+  c = mfma(a.h, b.h, c);
+  c = mfma(a.h, b.l, c);
+  return mfma(a.l, b.h, c);
+}
+// four consecutive bf16 of a hi plane and of its lo plane
+__device__ __forceinline__ Split4 lds_split4(const uint16_t *hi, const uint16_t *lo) {
+  return {__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(hi)),
+          __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(lo))};
+}
+
+// The attention steps run as split bf16 products (above), with the score
 // tile transposed, S^T = k q^T (keys in rows), in the forward and dq kernels:
 // lane l = 16 g + r16 holds keys 4g + r of query column r16, which is the
 // k-slice of the P^T / dS^T operand of o^T = v^T P^T and dq^T = k^T dS^T.
-// In step e of a 16-slice, lane group g takes channel (or key) 4g + e in both
-// operands. Work item: (b, i, t, 128 query columns), 8 waves of 16 columns;
+// In a 16-slice, lane group g takes channels (or keys) 4g..4g+3 of both
+// operands. Staged operands are held in LDS as their hi and lo bf16 planes. Work item: (b, i, t, 128 query columns), 8 waves of 16 columns;
 // keys through LDS in chunks of 64.
 template <int DH>
 struct BwdTile {
   static constexpr int NW = 8, QB = NW * 16, KT = 64, CB = DH / 16;
-  static constexpr int KP = DH + 4;   // [key][c] row pitch (floats)
-  static constexpr int TP = KT + 4;   // [c][key] row pitch (floats)
+  static constexpr int KP = DH + 4;   // [key][c] row pitch (elements)
+  static constexpr int TP = KT + 4;   // [c][key] row pitch (elements)
 };
 
-// stage the chunk's k (or v) rows of head t as [key][c] and/or [c][key]
 template <int DH>
-__device__ __forceinline__ void stage_rows(const BwdAttnArgs &a, size_t rowp, int col0, int k0, float *rows,
-                                           float *cols) {
+constexpr int S_KP = BwdTile<DH>::KP;  // [key][c] row pitch
+constexpr int S_TP = BwdTile<16>::TP;  // [c][key] row pitch (independent of the head size)
+
+// stage the chunk's k (or v) rows of head t as split bf16 planes ([0] hi,
+// [1] lo), [key][c] and/or [c][key]
+template <int DH>
+__device__ __forceinline__ void stage_rows(const BwdAttnArgs &a, size_t rowp, int col0, int k0,
+                                           uint16_t (*rows)[S_KP<DH> * 64], uint16_t (*cols)[DH * S_TP]) {
   using S = BwdTile<DH>;
   constexpr int V4 = S::KT * DH / 4;  // float4 pieces
   for (int e = threadIdx.x; e < V4; e += S::NW * 64) {
     const int kk = e / (DH / 4), u4 = (e - kk * (DH / 4)) * 4, k = k0 + kk;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (k < a.N) v = ldg<float4>(a.proj + (rowp + k) * a.C + col0 + u4);
-    if (rows) *reinterpret_cast<float4 *>(rows + kk * S::KP + u4) = v;
+    const Split4 sp = split4(v.x, v.y, v.z, v.w);
+    const uint2 hv = __builtin_bit_cast(uint2, sp.h), lv = __builtin_bit_cast(uint2, sp.l);
+    if (rows) {
+      *reinterpret_cast<uint2 *>(rows[0] + kk * S::KP + u4) = hv;
+      *reinterpret_cast<uint2 *>(rows[1] + kk * S::KP + u4) = lv;
+    }
     if (cols) {
-      cols[(u4 + 0) * S::TP + kk] = v.x;
-      cols[(u4 + 1) * S::TP + kk] = v.y;
-      cols[(u4 + 2) * S::TP + kk] = v.z;
-      cols[(u4 + 3) * S::TP + kk] = v.w;
+      const uint32_t hw[2] = {hv.x, hv.y}, lw[2] = {lv.x, lv.y};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        cols[0][(u4 + cc) * S::TP + kk] = (uint16_t)(hw[cc >> 1] >> (16 * (cc & 1)));
+        cols[1][(u4 + cc) * S::TP + kk] = (uint16_t)(lw[cc >> 1] >> (16 * (cc & 1)));
+      }
     }
   }
 }
@@ -384,8 +422,9 @@ __device__ __forceinline__ void stage_rows(const BwdAttnArgs &a, size_t rowp, in
 // S^T tile of 16 keys (kb) x the lane's query: bias, q.k, mask, padding;
 // bit r of *valid is set where key 4g + r is in range and not masked
 template <int DH>
-__device__ __forceinline__ f32x4 score_tile_t(const BwdAttnArgs &a, const float *kbuf, const f32x4 (&qf)[DH / 16],
-                                              const float *zq, int k0, int kb, int g, int r16, uint32_t *valid) {
+__device__ __forceinline__ f32x4 score_tile_t(const BwdAttnArgs &a, const uint16_t (*kbuf)[S_KP<DH> * 64],
+                                              const Split4 (&qf)[DH / 16], const float *zq, int k0, int kb, int g,
+                                              int r16, uint32_t *valid) {
   using S = BwdTile<DH>;
   const int kq = k0 + kb * 16 + 4 * g;  // first of the lane's four keys
   f32x4 st;
@@ -399,11 +438,8 @@ __device__ __forceinline__ f32x4 score_tile_t(const BwdAttnArgs &a, const float 
   const f32x4 z0 = st;
 #pragma unroll
   for (int cb = 0; cb < S::CB; ++cb) {
-    const float4 kv = *reinterpret_cast<const float4 *>(kbuf + (kb * 16 + r16) * S::KP + 16 * cb + 4 * g);
-    st = mfma(kv.x, qf[cb][0], st);
-    st = mfma(kv.y, qf[cb][1], st);
-    st = mfma(kv.z, qf[cb][2], st);
-    st = mfma(kv.w, qf[cb][3], st);
+    const int o = (kb * 16 + r16) * S::KP + 16 * cb + 4 * g;
+    st = mma_split(lds_split4(kbuf[0] + o, kbuf[1] + o), qf[cb], st);
   }
   uint32_t v = 0;
 #pragma unroll
@@ -421,19 +457,19 @@ template <int DH>
 __global__ __launch_bounds__(512) void bwd_attn_fwd(BwdAttnArgs a) {
   using S = BwdTile<DH>;
   constexpr int CB = S::CB, KT = S::KT;
-  __shared__ __align__(16) float kbuf[KT * S::KP];
-  __shared__ __align__(16) float vT[DH * S::TP];
+  __shared__ __align__(16) uint16_t kbuf[2][KT * S::KP];
+  __shared__ __align__(16) uint16_t vT[2][DH * S::TP];
   const int N = a.N, D = a.D, h = a.h, C = a.C;
   const int nq = (N + S::QB - 1) / S::QB;
   const int item = blockIdx.x, qc = item % nq, bt = item / nq, bi = bt / h, t = bt - bi * h, b = bi / N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const int j = qc * S::QB + wave * 16 + r16, jc = min(j, N - 1);
   const size_t rowp = (size_t)bi * N;
-  f32x4 qf[CB];
+  Split4 qf[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const float4 q4 = ldg<float4>(a.proj + (rowp + jc) * C + t * DH + 16 * cb + 4 * g);
-    qf[cb] = (f32x4){q4.x, q4.y, q4.z, q4.w} * a.qs;
+    qf[cb] = split4(q4.x * a.qs, q4.y * a.qs, q4.z * a.qs, q4.w * a.qs);
   }
   const float *zq = a.zt + ((size_t)(b * h + t) * N + jc) * N;
   const uint32_t *kr = keep_row(a, bi, t, jc);
@@ -475,13 +511,11 @@ __global__ __launch_bounds__(512) void bwd_attn_fwd(BwdAttnArgs a) {
         lsum += e;
         p[r] = (nib >> r) & 1u ? e : 0.f;
       }
+      const Split4 ps = split4(p[0], p[1], p[2], p[3]);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float4 vv = *reinterpret_cast<const float4 *>(vT + (16 * cb + r16) * S::TP + kb * 16 + 4 * g);
-        ot[cb] = mfma(vv.x, p[0], ot[cb]);
-        ot[cb] = mfma(vv.y, p[1], ot[cb]);
-        ot[cb] = mfma(vv.z, p[2], ot[cb]);
-        ot[cb] = mfma(vv.w, p[3], ot[cb]);
+        const int o = (16 * cb + r16) * S::TP + kb * 16 + 4 * g;
+        ot[cb] = mma_split(lds_split4(vT[0] + o, vT[1] + o), ps, ot[cb]);
       }
     }
     __syncthreads();
@@ -505,24 +539,24 @@ template <int DH>
 __global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
   using S = BwdTile<DH>;
   constexpr int CB = S::CB, KT = S::KT;
-  __shared__ __align__(16) float kbuf[KT * S::KP];
-  __shared__ __align__(16) float kT[DH * S::TP];
-  __shared__ __align__(16) float vbuf[KT * S::KP];
+  __shared__ __align__(16) uint16_t kbuf[2][KT * S::KP];
+  __shared__ __align__(16) uint16_t kT[2][DH * S::TP];
+  __shared__ __align__(16) uint16_t vbuf[2][KT * S::KP];
   const int N = a.N, D = a.D, h = a.h, C = a.C;
   const int nq = (N + S::QB - 1) / S::QB;
   const int item = blockIdx.x, qc = item % nq, bt = item / nq, bi = bt / h, t = bt - bi * h, b = bi / N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const int j = qc * S::QB + wave * 16 + r16, jc = min(j, N - 1);
   const size_t rowp = (size_t)bi * N;
-  f32x4 qf[CB], df[CB];
+  Split4 qf[CB], df[CB];
   float dsum = 0.f;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const float4 q4 = ldg<float4>(a.proj + (rowp + jc) * C + t * DH + 16 * cb + 4 * g);
-    qf[cb] = (f32x4){q4.x, q4.y, q4.z, q4.w} * a.qs;
+    qf[cb] = split4(q4.x * a.qs, q4.y * a.qs, q4.z * a.qs, q4.w * a.qs);
     const float4 d4 = ldg<float4>(a.dob + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
     const float4 o4 = ldg<float4>(a.o + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
-    df[cb] = (f32x4){d4.x, d4.y, d4.z, d4.w};
+    df[cb] = split4(d4.x, d4.y, d4.z, d4.w);
     dsum += d4.x * o4.x + d4.y * o4.y + d4.z * o4.z + d4.w * o4.w;
   }
   const float Dv = group4_sum(dsum);
@@ -547,11 +581,8 @@ __global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
       f32x4 dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float4 vv = *reinterpret_cast<const float4 *>(vbuf + (kb * 16 + r16) * S::KP + 16 * cb + 4 * g);
-        dp = mfma(vv.x, df[cb][0], dp);
-        dp = mfma(vv.y, df[cb][1], dp);
-        dp = mfma(vv.z, df[cb][2], dp);
-        dp = mfma(vv.w, df[cb][3], dp);
+        const int o = (kb * 16 + r16) * S::KP + 16 * cb + 4 * g;
+        dp = mma_split(lds_split4(vbuf[0] + o, vbuf[1] + o), df[cb], dp);
       }
       const uint32_t nib = w32[kb >> 1] >> (16 * (kb & 1) + 4 * g);
       float ds[4];
@@ -563,13 +594,11 @@ __global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
         ds[r] = valid ? p * (da - Dv) : 0.f;
       }
       // dq^T += k^T dS^T
+      const Split4 dss = split4(ds[0], ds[1], ds[2], ds[3]);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float4 kv = *reinterpret_cast<const float4 *>(kT + (16 * cb + r16) * S::TP + kb * 16 + 4 * g);
-        dq[cb] = mfma(kv.x, ds[0], dq[cb]);
-        dq[cb] = mfma(kv.y, ds[1], dq[cb]);
-        dq[cb] = mfma(kv.z, ds[2], dq[cb]);
-        dq[cb] = mfma(kv.w, ds[3], dq[cb]);
+        const int o = (16 * cb + r16) * S::TP + kb * 16 + 4 * g;
+        dq[cb] = mma_split(lds_split4(kT[0] + o, kT[1] + o), dss, dq[cb]);
       }
     }
     __syncthreads();
@@ -589,10 +618,12 @@ template <int DH>
 __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
   using S = BwdTile<DH>;
   constexpr int CB = S::CB, QT = S::KT;
-  __shared__ __align__(16) float qbuf[QT * S::KP];
-  __shared__ __align__(16) float qT[DH * S::TP];
-  __shared__ __align__(16) float dbuf[QT * S::KP];
-  __shared__ __align__(16) float dT[DH * S::TP];
+  // q and do of the chunk as split bf16 planes (hi, lo): rows [query][c]
+  // and transposed [c][query]
+  __shared__ __align__(16) uint16_t qbuf[2][QT * S::KP];
+  __shared__ __align__(16) uint16_t qT[2][DH * S::TP];
+  __shared__ __align__(16) uint16_t dbuf[2][QT * S::KP];
+  __shared__ __align__(16) uint16_t dT[2][DH * S::TP];
   __shared__ __align__(16) float ms[QT], ls[QT], Ds[QT];
   // the chunk's bias, mask and keep bits for the workgroup's 128 keys
   __shared__ __align__(16) float zs[QT][S::QB + 4];
@@ -603,13 +634,13 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const int k = kc * S::QB + wave * 16 + r16, kcl = min(k, N - 1);
   const size_t rowp = (size_t)bi * N;
-  f32x4 kf[CB], vf[CB];  // lane: key r16, channels 16 cb + 4g + e (k pre-scaled)
+  Split4 kf[CB], vf[CB];  // lane: key r16, channels 16 cb + 4g .. +3 (k pre-scaled)
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const float4 k4 = ldg<float4>(a.proj + (rowp + kcl) * C + D + t * DH + 16 * cb + 4 * g);
     const float4 v4 = ldg<float4>(a.proj + (rowp + kcl) * C + 2 * D + t * DH + 16 * cb + 4 * g);
-    kf[cb] = (f32x4){k4.x, k4.y, k4.z, k4.w} * a.qs;
-    vf[cb] = (f32x4){v4.x, v4.y, v4.z, v4.w};
+    kf[cb] = split4(k4.x * a.qs, k4.y * a.qs, k4.z * a.qs, k4.w * a.qs);
+    vf[cb] = split4(v4.x, v4.y, v4.z, v4.w);
   }
   f32x4 dk[CB], dv[CB];
 #pragma unroll
@@ -679,13 +710,21 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
     const int e = threadIdx.x;
     if (e < V4) {
       const int jj = e / (DH / 4), u4 = (e - jj * (DH / 4)) * 4;
-      *reinterpret_cast<float4 *>(qbuf + jj * S::KP + u4) = c.q;
-      *reinterpret_cast<float4 *>(dbuf + jj * S::KP + u4) = c.d;
-      const float qa[4] = {c.q.x, c.q.y, c.q.z, c.q.w}, da[4] = {c.d.x, c.d.y, c.d.z, c.d.w};
+      const Split4 qs4 = split4(c.q.x, c.q.y, c.q.z, c.q.w), ds4 = split4(c.d.x, c.d.y, c.d.z, c.d.w);
+      const uint2 qh = __builtin_bit_cast(uint2, qs4.h), ql = __builtin_bit_cast(uint2, qs4.l);
+      const uint2 dh = __builtin_bit_cast(uint2, ds4.h), dl = __builtin_bit_cast(uint2, ds4.l);
+      *reinterpret_cast<uint2 *>(qbuf[0] + jj * S::KP + u4) = qh;
+      *reinterpret_cast<uint2 *>(qbuf[1] + jj * S::KP + u4) = ql;
+      *reinterpret_cast<uint2 *>(dbuf[0] + jj * S::KP + u4) = dh;
+      *reinterpret_cast<uint2 *>(dbuf[1] + jj * S::KP + u4) = dl;
+      const uint32_t w[4][2] = {{qh.x, qh.y}, {ql.x, ql.y}, {dh.x, dh.y}, {dl.x, dl.y}};
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        qT[(u4 + cc) * S::TP + jj] = qa[cc];
-        dT[(u4 + cc) * S::TP + jj] = da[cc];
+        const int sh = 16 * (cc & 1);
+        qT[0][(u4 + cc) * S::TP + jj] = (uint16_t)(w[0][cc >> 1] >> sh);
+        qT[1][(u4 + cc) * S::TP + jj] = (uint16_t)(w[1][cc >> 1] >> sh);
+        dT[0][(u4 + cc) * S::TP + jj] = (uint16_t)(w[2][cc >> 1] >> sh);
+        dT[1][(u4 + cc) * S::TP + jj] = (uint16_t)(w[3][cc >> 1] >> sh);
       }
     }
     if (e < QT) ms[e] = c.m, ls[e] = c.il, Ds[e] = c.Dq;
@@ -710,7 +749,7 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
     __syncthreads();
     if constexpr (PIPE)
       if (j0 + QT < N) nxt = load_chunk(j0 + QT);
-#pragma unroll
+#pragma unroll 1
     for (int qb = 0; qb < 4; ++qb) {
       // S = q k^T (queries x keys): bias, product, mask, padding
       const int kk = wave * 16 + r16;  // the lane's key within the workgroup's 128
@@ -720,21 +759,15 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
       const f32x4 s0 = s;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float4 qv = *reinterpret_cast<const float4 *>(qbuf + (qb * 16 + r16) * S::KP + 16 * cb + 4 * g);
-        s = mfma(qv.x, kf[cb][0], s);
-        s = mfma(qv.y, kf[cb][1], s);
-        s = mfma(qv.z, kf[cb][2], s);
-        s = mfma(qv.w, kf[cb][3], s);
+        const int o = (qb * 16 + r16) * S::KP + 16 * cb + 4 * g;
+        s = mma_split(lds_split4(qbuf[0] + o, qbuf[1] + o), kf[cb], s);
       }
       // dP = do v^T
       f32x4 dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float4 dv4 = *reinterpret_cast<const float4 *>(dbuf + (qb * 16 + r16) * S::KP + 16 * cb + 4 * g);
-        dp = mfma(dv4.x, vf[cb][0], dp);
-        dp = mfma(dv4.y, vf[cb][1], dp);
-        dp = mfma(dv4.z, vf[cb][2], dp);
-        dp = mfma(dv4.w, vf[cb][3], dp);
+        const int o = (qb * 16 + r16) * S::KP + 16 * cb + 4 * g;
+        dp = mma_split(lds_split4(dbuf[0] + o, dbuf[1] + o), vf[cb], dp);
       }
       float pk[4], ds[4];
       // statistics of the lane's four queries (16-byte LDS reads; l as 1 / l)
@@ -759,18 +792,12 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
         ds[r] = valid ? p * (da - dq4[r]) : 0.f;
       }
       // dv^T += do^T P', dk^T += q^T dS
+      const Split4 pks = split4(pk[0], pk[1], pk[2], pk[3]), dss = split4(ds[0], ds[1], ds[2], ds[3]);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float4 dv4 = *reinterpret_cast<const float4 *>(dT + (16 * cb + r16) * S::TP + qb * 16 + 4 * g);
-        const float4 qv = *reinterpret_cast<const float4 *>(qT + (16 * cb + r16) * S::TP + qb * 16 + 4 * g);
-        dv[cb] = mfma(dv4.x, pk[0], dv[cb]);
-        dv[cb] = mfma(dv4.y, pk[1], dv[cb]);
-        dv[cb] = mfma(dv4.z, pk[2], dv[cb]);
-        dv[cb] = mfma(dv4.w, pk[3], dv[cb]);
-        dk[cb] = mfma(qv.x, ds[0], dk[cb]);
-        dk[cb] = mfma(qv.y, ds[1], dk[cb]);
-        dk[cb] = mfma(qv.z, ds[2], dk[cb]);
-        dk[cb] = mfma(qv.w, ds[3], dk[cb]);
+        const int o = (16 * cb + r16) * S::TP + qb * 16 + 4 * g;
+        dv[cb] = mma_split(lds_split4(dT[0] + o, dT[1] + o), pks, dv[cb]);
+        dk[cb] = mma_split(lds_split4(qT[0] + o, qT[1] + o), dss, dk[cb]);
       }
     }
     __syncthreads();
@@ -793,13 +820,14 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
 // would leave most CUs idle) each range writes its partial sum, and
 // bwd_dz_reduce adds the ranges in order. Per row i the rows' q, do, k and v and the queries' m2, l,
 // sum a da and keep bits pass through LDS; S = q k^T and dP = do v^T come
-// from float32 matrix-core tiles (lane: queries 4g + r, key r16), and ds is
+// from split bf16 products (lane: queries 4g + r, key r16), and ds is
 // summed over i in registers. The bias and the mask of (j, k) are the same
 // for every row i and stay in registers.
 template <int DH>
 __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
   constexpr int JT = 64, KT = 64, RP = DH + 4, CB = DH / 16;
-  __shared__ __align__(16) float ks[KT][RP], vs[KT][RP], qs[JT][RP], dos[JT][RP];
+  // the row's k, v, q and do as split bf16 planes ([0] hi, [1] lo)
+  __shared__ __align__(16) uint16_t ks[2][KT][RP], vs[2][KT][RP], qs[2][JT][RP], dos[2][JT][RP];
   __shared__ float ms[JT], ls[JT], Ds[JT];
   __shared__ uint32_t kb[JT][2];
   const int N = a.N, D = a.D, h = a.h, C = a.C;
@@ -835,10 +863,14 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
         qv = ldg<float4>(a.proj + (rowp + j) * C + t * DH + u4);
         dv = ldg<float4>(a.dob + (rowp + j) * D + t * DH + u4);
       }
-      *reinterpret_cast<float4 *>(&ks[r][u4]) = make_float4(kv.x * a.qs, kv.y * a.qs, kv.z * a.qs, kv.w * a.qs);
-      *reinterpret_cast<float4 *>(&vs[r][u4]) = vv;
-      *reinterpret_cast<float4 *>(&qs[r][u4]) = qv;
-      *reinterpret_cast<float4 *>(&dos[r][u4]) = dv;
+      auto put = [&](uint16_t (*pl)[KT][RP], const Split4 &sp) {
+        *reinterpret_cast<uint2 *>(&pl[0][r][u4]) = __builtin_bit_cast(uint2, sp.h);
+        *reinterpret_cast<uint2 *>(&pl[1][r][u4]) = __builtin_bit_cast(uint2, sp.l);
+      };
+      put(ks, split4(kv.x * a.qs, kv.y * a.qs, kv.z * a.qs, kv.w * a.qs));
+      put(vs, split4(vv.x, vv.y, vv.z, vv.w));
+      put(qs, split4(qv.x, qv.y, qv.z, qv.w));
+      put(dos, split4(dv.x, dv.y, dv.z, dv.w));
     }
     if (threadIdx.x < JT) {
       const int jq = j0 + threadIdx.x;
@@ -865,18 +897,10 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = sc;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float4 qv = *reinterpret_cast<const float4 *>(&qs[16 * wave + r16][16 * cb + 4 * g]);
-        const float4 dv = *reinterpret_cast<const float4 *>(&dos[16 * wave + r16][16 * cb + 4 * g]);
-        const float4 kv = *reinterpret_cast<const float4 *>(&ks[16 * kbk + r16][16 * cb + 4 * g]);
-        const float4 vv = *reinterpret_cast<const float4 *>(&vs[16 * kbk + r16][16 * cb + 4 * g]);
-        sc = mfma(qv.x, kv.x, sc);
-        sc = mfma(qv.y, kv.y, sc);
-        sc = mfma(qv.z, kv.z, sc);
-        sc = mfma(qv.w, kv.w, sc);
-        dp = mfma(dv.x, vv.x, dp);
-        dp = mfma(dv.y, vv.y, dp);
-        dp = mfma(dv.z, vv.z, dp);
-        dp = mfma(dv.w, vv.w, dp);
+        const int cq = 16 * cb + 4 * g, jr = 16 * wave + r16, kr = 16 * kbk + r16;
+        sc = mma_split(lds_split4(&qs[0][jr][cq], &qs[1][jr][cq]), lds_split4(&ks[0][kr][cq], &ks[1][kr][cq]), sc);
+        dp = mma_split(lds_split4(&dos[0][jr][cq], &dos[1][jr][cq]), lds_split4(&vs[0][kr][cq], &vs[1][kr][cq]),
+                       dp);
       }
       const int kk = 16 * kbk + r16;  // the lane's key within the tile
 #pragma unroll
