@@ -23,10 +23,10 @@
 // fixed chunks whose partial results are added in a fixed order by a second
 // pass: no atomics, the same bits on every call.
 //
-// All arithmetic is float32. The projection GEMMs run on the float32 matrix
-// cores (16x16x4); the attention's score, value and gradient tiles as split
-// bf16 products (two bf16 parts per float32 operand, three 16x16x16 products
-// per float32 product, ~2^-16 relative error); the dropout decisions are computed once into a bit array
+// All arithmetic is float32, the products (the projection GEMMs and the
+// attention's score, value and gradient tiles) as split bf16 products (two
+// bf16 parts per float32 operand, three 16x16x16 matrix-core products per
+// float32 product, ~2^-16 relative error); the dropout decisions are computed once into a bit array
 // (one generator call per four keys) that every attention step reads; the
 // backward's copy of the pair bias carries the mask (FILL where masked), so
 // no attention step reads the mask itself.
@@ -39,12 +39,36 @@
 
 namespace tpa {
 
+// Float32 products as split bf16 products: a = ah + al with ah = bf16(a) and
+// al = bf16(a - ah) (a - ah is exact in float32), and a b ~ ah bh + ah bl +
+// al bh, three bf16 16x16x16 products (each ~0.6 of a float32 16x16x4
+// product's cost here, for 4x the contraction); the dropped al bl and the
+// remainders a - ah - al are ~2^-16 relative. The lane layout is the float32
+// product's: lane group g holds contraction elements 4g..4g+3.
+struct Split4 {
+  bf16x4 h, l;
+};
+__device__ __forceinline__ Split4 split4(float a, float b, float c, float d) {
+  const uint32_t h0 = pack_bf16x2(a, b), h1 = pack_bf16x2(c, d);
+  const uint32_t l0 = pack_bf16x2(a - bflo(h0), b - bfhi(h0)), l1 = pack_bf16x2(c - bflo(h1), d - bfhi(h1));
+  return {__builtin_bit_cast(bf16x4, make_uint2(h0, h1)), __builtin_bit_cast(bf16x4, make_uint2(l0, l1))};
+}
+__device__ __forceinline__ f32x4 mma_split(const Split4 &a, const Split4 &b, f32x4 c) {
+  c = mfma(a.h, b.h, c);
+  c = mfma(a.h, b.l, c);
+  return mfma(a.l, b.h, c);
+}
+// four consecutive bf16 of a hi plane and of its lo plane
+__device__ __forceinline__ Split4 lds_split4(const uint16_t *hi, const uint16_t *lo) {
+  return {__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(hi)),
+          __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(lo))};
+}
+
 // ------------------------------------------------------------------ products
 // C[z][m][n] = sum over k in chunk z of A[m, k] B[k, n]; A(m, k) at
 // A[m*sam + k*sak], B(k, n) at B[k*sbk + n*sbn], C(z, m, n) at
-// C[z*scz + m*scm + n]. 64x64 tile per workgroup on the float32 matrix
-// cores, K in steps of 16 through LDS, loads laid out along the contiguous
-// index.
+// C[z*scz + m*scm + n]. 64x64 tile per workgroup as split products, K in
+// steps of 16 through LDS, loads laid out along the contiguous index.
 struct GemmArgs {
   const void *A, *B;
   float *C;
@@ -65,8 +89,12 @@ __device__ __forceinline__ float4 ld4(const void *p, size_t i) {
 
 template <typename TA, typename TB>
 __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
-  __shared__ float As[16][68];
-  __shared__ float Bs[16][68];
+  // A and B tiles of one 16-deep K slice as split bf16 planes ([0] hi, [1]
+  // lo), each row a tile row (m, or n) with its 16 k contiguous, so a lane
+  // reads its four contraction elements 4g..4g+3 as one 8-byte load per plane
+  constexpr int PK = 16 + 4;  // row pitch (elements)
+  __shared__ __align__(16) uint16_t As[2][64 * PK];
+  __shared__ __align__(16) uint16_t Bs[2][64 * PK];
   const int tid = threadIdx.x;
   // grid x: (row block, column block) with the column block fastest, so the
   // workgroups that share a row block of A run together and it is read from
@@ -75,9 +103,8 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   const long long m0 = ((long long)blockIdx.x / ncb) * 64, n0 = ((long long)blockIdx.x % ncb) * 64;
   const long long kb = (long long)blockIdx.z * g.kchunk;
   const long long ke = min(kb + g.kchunk, g.K);
-  // wave w computes the 32 x 32 quadrant (w / 2, w % 2) as 2 x 2 float32
-  // 16x16x4 matrix-core tiles; in step s of a 16-deep K slice, lane group g
-  // takes k = 4s + g for both operands
+  // wave w computes the 32 x 32 quadrant (w / 2, w % 2) as 2 x 2 tiles of
+  // split products (three bf16 16x16x16 products per float32 product)
   const int lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, r16 = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
   f32x4 acc[2][2];
@@ -86,70 +113,71 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const bool a_m_contig = g.sam == 1, b_n_contig = g.sbn == 1;
+  // one operand's 64 x 16 slice: each thread loads four consecutive elements
+  // along the contiguous index (one 16- or 8-byte load when all four are in
+  // range; load), then writes their two bf16 parts to the planes (put)
+  auto load = [&](auto ta, const void *X, long long s_t, long long s_k, long long T, long long t0, bool t_contig,
+                  long long k0) {
+    using TX = decltype(ta);
+    const int lin = t_contig ? ((tid & 15) * 4) : ((tid & 3) * 4);  // 4 along the contiguous index
+    const int oth = t_contig ? (tid >> 4) : (tid >> 2);             // the other index
+    const long long tt = t0 + (t_contig ? lin : oth), kk = k0 + (t_contig ? oth : lin);
+    const bool full = t_contig ? (tt + 3 < T && kk < ke) : (tt < T && kk + 3 < ke);
+    if (full) return ld4<TX>(X, (size_t)(tt * s_t + kk * s_k));
+    float t4[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const long long t2 = tt + (t_contig ? c : 0), k2 = kk + (t_contig ? 0 : c);
+      t4[c] = (t2 < T && k2 < ke) ? ld_elem<TX>(X, (size_t)(t2 * s_t + k2 * s_k)) : 0.f;
+    }
+    return make_float4(t4[0], t4[1], t4[2], t4[3]);
+  };
+  auto put = [&](float4 v, bool t_contig, uint16_t (*pl)[64 * PK]) {
+    const int lin = t_contig ? ((tid & 15) * 4) : ((tid & 3) * 4);
+    const int oth = t_contig ? (tid >> 4) : (tid >> 2);
+    const Split4 sp = split4(v.x, v.y, v.z, v.w);
+    const uint2 hv = __builtin_bit_cast(uint2, sp.h), lv = __builtin_bit_cast(uint2, sp.l);
+    if (t_contig) {  // four tile rows, one k: scattered 2-byte writes
+      const uint32_t hw[2] = {hv.x, hv.y}, lw[2] = {lv.x, lv.y};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        pl[0][(lin + c) * PK + oth] = (uint16_t)(hw[c >> 1] >> (16 * (c & 1)));
+        pl[1][(lin + c) * PK + oth] = (uint16_t)(lw[c >> 1] >> (16 * (c & 1)));
+      }
+    } else {  // one tile row, four consecutive k
+      *reinterpret_cast<uint2 *>(&pl[0][oth * PK + lin]) = hv;
+      *reinterpret_cast<uint2 *>(&pl[1][oth * PK + lin]) = lv;
+    }
+  };
+  // the next slice's elements are loaded into registers while the current
+  // one is multiplied; the barriers wait for LDS traffic only, so those
+  // loads stay in flight across them
+  float4 va = load(TA{}, g.A, g.sam, g.sak, g.M, m0, a_m_contig, kb);
+  float4 vb = load(TB{}, g.B, g.sbn, g.sbk, g.N, n0, b_n_contig, kb);
   for (long long k0 = kb; k0 < ke; k0 += 16) {
-    // each thread stages four consecutive elements of A and of B along
-    // their contiguous index (one 16- or 8-byte load when all four are in range)
-    {
-      const int lin = a_m_contig ? ((tid & 15) * 4) : ((tid & 3) * 4);  // 4 along the contiguous index
-      const int oth = a_m_contig ? (tid >> 4) : (tid >> 2);             // the other index
-      const long long am = m0 + (a_m_contig ? lin : oth), ak = k0 + (a_m_contig ? oth : lin);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      const bool full = a_m_contig ? (am + 3 < g.M && ak < ke) : (am < g.M && ak + 3 < ke);
-      if (full) {
-        v = ld4<TA>(g.A, (size_t)(am * g.sam + ak * g.sak));
-      } else {
-        float t4[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const long long mm = am + (a_m_contig ? c : 0), kk = ak + (a_m_contig ? 0 : c);
-          t4[c] = (mm < g.M && kk < ke) ? ld_elem<TA>(g.A, (size_t)(mm * g.sam + kk * g.sak)) : 0.f;
-        }
-        v = make_float4(t4[0], t4[1], t4[2], t4[3]);
-      }
-      if (a_m_contig) {
-        *reinterpret_cast<float4 *>(&As[oth][lin]) = v;
-      } else {
-        As[lin + 0][oth] = v.x, As[lin + 1][oth] = v.y, As[lin + 2][oth] = v.z, As[lin + 3][oth] = v.w;
-      }
+    put(va, a_m_contig, As);
+    put(vb, b_n_contig, Bs);
+    lds_barrier();
+    if (k0 + 16 < ke) {
+      va = load(TA{}, g.A, g.sam, g.sak, g.M, m0, a_m_contig, k0 + 16);
+      vb = load(TB{}, g.B, g.sbn, g.sbk, g.N, n0, b_n_contig, k0 + 16);
     }
-    {
-      const int lin = b_n_contig ? ((tid & 15) * 4) : ((tid & 3) * 4);
-      const int oth = b_n_contig ? (tid >> 4) : (tid >> 2);
-      const long long bn = n0 + (b_n_contig ? lin : oth), bk = k0 + (b_n_contig ? oth : lin);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      const bool full = b_n_contig ? (bn + 3 < g.N && bk < ke) : (bn < g.N && bk + 3 < ke);
-      if (full) {
-        v = ld4<TB>(g.B, (size_t)(bk * g.sbk + bn * g.sbn));
-      } else {
-        float t4[4];
+    Split4 av[2], bv[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const long long nn = bn + (b_n_contig ? c : 0), kk = bk + (b_n_contig ? 0 : c);
-          t4[c] = (nn < g.N && kk < ke) ? ld_elem<TB>(g.B, (size_t)(kk * g.sbk + nn * g.sbn)) : 0.f;
-        }
-        v = make_float4(t4[0], t4[1], t4[2], t4[3]);
-      }
-      if (b_n_contig) {
-        *reinterpret_cast<float4 *>(&Bs[oth][lin]) = v;
-      } else {
-        Bs[lin + 0][oth] = v.x, Bs[lin + 1][oth] = v.y, Bs[lin + 2][oth] = v.z, Bs[lin + 3][oth] = v.w;
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int o = (32 * wm + 16 * i + r16) * PK + 4 * g4;
+      av[i] = lds_split4(&As[0][o], &As[1][o]);
     }
-    __syncthreads();
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kk = 4 * st + g4;
-      float av[2], bv[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) av[i] = As[kk][32 * wm + 16 * i + r16];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bv[j] = Bs[kk][32 * wn + 16 * j + r16];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(av[i], bv[j], acc[i][j]);
+    for (int j = 0; j < 2; ++j) {
+      const int o = (32 * wn + 16 * j + r16) * PK + 4 * g4;
+      bv[j] = lds_split4(&Bs[0][o], &Bs[1][o]);
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mma_split(av[i], bv[j], acc[i][j]);
+    lds_barrier();
   }
   // lane: rows 4 g4 + r, column r16 of each tile
 #pragma unroll
@@ -346,31 +374,6 @@ __global__ __launch_bounds__(256) void bwd_keep_bits(BwdAttnArgs a, uint32_t *bi
 
 __device__ __forceinline__ const uint32_t *keep_row(const BwdAttnArgs &a, int bi, int t, int j) {
   return a.bits + (((size_t)bi * a.h + t) * a.N + j) * a.NW;
-}
-
-// Float32 products as split bf16 products: a = ah + al with ah = bf16(a) and
-// al = bf16(a - ah) (a - ah is exact in float32), and a b ~ ah bh + ah bl +
-// al bh, three bf16 16x16x16 products (each ~0.6 of a float32 16x16x4
-// product's cost here, for 4x the contraction); the dropped al bl and the
-// remainders a - ah - al are ~2^-16 relative. The lane layout is the float32
-// product's: lane group g holds contraction elements 4g..4g+3.
-struct Split4 {
-  bf16x4 h, l;
-};
-__device__ __forceinline__ Split4 split4(float a, float b, float c, float d) {
-  const uint32_t h0 = pack_bf16x2(a, b), h1 = pack_bf16x2(c, d);
-  const uint32_t l0 = pack_bf16x2(a - bflo(h0), b - bfhi(h0)), l1 = pack_bf16x2(c - bflo(h1), d - bfhi(h1));
-  return {__builtin_bit_cast(bf16x4, make_uint2(h0, h1)), __builtin_bit_cast(bf16x4, make_uint2(l0, l1))};
-}
-__device__ __forceinline__ f32x4 mma_split(const Split4 &a, const Split4 &b, f32x4 c) {
-  c = mfma(a.h, b.h, c);
-  c = mfma(a.h, b.l, c);
-  return mfma(a.l, b.h, c);
-}
-// four consecutive bf16 of a hi plane and of its lo plane
-__device__ __forceinline__ Split4 lds_split4(const uint16_t *hi, const uint16_t *lo) {
-  return {__builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(hi)),
-          __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(lo))};
 }
 
 // The attention steps run as split bf16 products (above), with the score
