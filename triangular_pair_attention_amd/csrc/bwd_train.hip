@@ -276,55 +276,78 @@ __global__ __launch_bounds__(256) void bwd_ln(const void *P, const void *gamma, 
   if (lane == 0) rstd[p] = r;
 }
 
-// LayerNorm backward per position, one wave per position (4 waves per
-// block, stepping through the block's positions), and per-block partial sums
+// Sum over each row of 16 lanes, every lane getting its row's sum: DPP lane
+// moves on the VALU (swap neighbours, swap pairs, mirror within 8, mirror
+// within 16).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  return v + dpp_mov<0x140>(v);
+}
+
+// LayerNorm backward per position: 16 lanes per position (four channels per
+// lane and 16-byte access), four positions per wave and step, the two sums
+// over channels reduced within each row of 16 lanes; per-block partial sums
 // of dx * x-hat (for dgamma) and dx (for dbeta): block blk covers positions
-// blk*per .. ; the four waves' partials are added in a fixed order.
+// blk*per .. ; the 16 (wave, row) partials are added in a fixed order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_ln_back(const float *dx, const float *xhat, const float *rstd,
                                                     const void *gamma, long long npos, long long per_blk, float *dP,
                                                     float *part_g, float *part_b) {
-  constexpr int PER = D / 64;
-  __shared__ float red[2][4][D];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float gm[PER], sg[PER], sb[PER];
+  constexpr int PER = D / 64;  // 16-byte pieces per lane and position
+  __shared__ __align__(16) float red[2][16][D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, pr = lane >> 4, c16 = lane & 15;
+  float4 gm[PER], sg[PER], sb[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    gm[e] = ld_elem<T>(gamma, lane + 64 * e);
-    sg[e] = sb[e] = 0.f;
+    const int c = 4 * c16 + 64 * e;
+    gm[e] = make_float4(ld_elem<T>(gamma, c), ld_elem<T>(gamma, c + 1), ld_elem<T>(gamma, c + 2),
+                        ld_elem<T>(gamma, c + 3));
+    sg[e] = sb[e] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const long long p0 = (long long)blockIdx.x * per_blk, p1 = min(p0 + per_blk, npos);
-  for (long long p = p0 + wave; p < p1; p += 4) {
-    float d[PER], xh[PER], s1 = 0.f, s2 = 0.f;
+  for (long long pb = p0 + 4 * wave; pb < p1; pb += 16) {
+    const long long p = pb + pr;
+    const bool ok = p < p1;
+    float4 d[PER], xh[PER];
+    float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      d[e] = dx[p * D + lane + 64 * e];
-      xh[e] = xhat[p * D + lane + 64 * e];
-      sg[e] += d[e] * xh[e];
-      sb[e] += d[e];
-      const float dxh = d[e] * gm[e];
-      s1 += dxh;
-      s2 += dxh * xh[e];
+      const size_t off = (size_t)p * D + 4 * c16 + 64 * e;
+      d[e] = ok ? ldg<float4>(dx + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+      xh[e] = ok ? ldg<float4>(xhat + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+      sg[e].x += d[e].x * xh[e].x, sg[e].y += d[e].y * xh[e].y, sg[e].z += d[e].z * xh[e].z,
+          sg[e].w += d[e].w * xh[e].w;
+      sb[e].x += d[e].x, sb[e].y += d[e].y, sb[e].z += d[e].z, sb[e].w += d[e].w;
+      const float4 dh = make_float4(d[e].x * gm[e].x, d[e].y * gm[e].y, d[e].z * gm[e].z, d[e].w * gm[e].w);
+      s1 += (dh.x + dh.y) + (dh.z + dh.w);
+      s2 += (dh.x * xh[e].x + dh.y * xh[e].y) + (dh.z * xh[e].z + dh.w * xh[e].w);
     }
+    s1 = row16_sum(s1);
+    s2 = row16_sum(s2);
+    if (ok) {
+      const float r = rstd[p], m1 = s1 / D, m2 = s2 / D;
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      s1 += __shfl_xor(s1, m, 64);
-      s2 += __shfl_xor(s2, m, 64);
+      for (int e = 0; e < PER; ++e)
+        stg<float4>(dP + (size_t)p * D + 4 * c16 + 64 * e,
+                    make_float4((d[e].x * gm[e].x - m1 - xh[e].x * m2) * r, (d[e].y * gm[e].y - m1 - xh[e].y * m2) * r,
+                                (d[e].z * gm[e].z - m1 - xh[e].z * m2) * r,
+                                (d[e].w * gm[e].w - m1 - xh[e].w * m2) * r));
     }
-    const float r = rstd[p];
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-      dP[p * D + lane + 64 * e] = (d[e] * gm[e] - s1 / D - xh[e] * (s2 / D)) * r;
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    red[0][wave][lane + 64 * e] = sg[e];
-    red[1][wave][lane + 64 * e] = sb[e];
+    *reinterpret_cast<float4 *>(&red[0][wave * 4 + pr][4 * c16 + 64 * e]) = sg[e];
+    *reinterpret_cast<float4 *>(&red[1][wave * 4 + pr][4 * c16 + 64 * e]) = sb[e];
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < D; c += 256) {
-    part_g[(size_t)blockIdx.x * D + c] = (red[0][0][c] + red[0][1][c]) + (red[0][2][c] + red[0][3][c]);
-    part_b[(size_t)blockIdx.x * D + c] = (red[1][0][c] + red[1][1][c]) + (red[1][2][c] + red[1][3][c]);
+  for (int c = threadIdx.x; c < 2 * D; c += 256) {
+    const int w = c / D, ch = c - w * D;
+    float acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc += red[w][q][ch];
+    (w == 0 ? part_g : part_b)[(size_t)blockIdx.x * D + ch] = acc;
   }
 }
 
@@ -989,7 +1012,8 @@ static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed
   L.kchunk = ((P + 255) / 256 + 15) / 16 * 16;
   if (L.kchunk < 16) L.kchunk = 16;
   L.S = (P + L.kchunk - 1) / L.kchunk;
-  L.vper = (P + 255) / 256;
+  // column sums (bias gradients, dgamma, dbeta): at most 1024 blocks
+  L.vper = (P + 1023) / 1024;
   L.nvblk = (P + L.vper - 1) / L.vper;
   size_t off = 0;
   auto take = [&](size_t bytes) {
