@@ -213,15 +213,15 @@ __global__ __launch_bounds__(256) void bwd_reduce(const float *part, long long n
 }
 
 // part[blk][c] = sum over positions p of block blk of X[p*ldx + c] (c < ncol):
-// the block's 256 threads cover 256 / ncol groups of positions (each thread
+// the block's 1024 threads cover 1024 / ncol groups of positions (each thread
 // one column), eight independent partial sums per thread, then the groups
 // are added in a fixed order through LDS
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_colsum(const void *X, long long P, int ncol, long long ldx,
-                                                   long long per_blk, float *part) {
-  __shared__ float red[256];
+__global__ __launch_bounds__(1024) void bwd_colsum(const void *X, long long P, int ncol, long long ldx,
+                                                    long long per_blk, float *part) {
+  __shared__ float red[1024];
   const long long p0 = (long long)blockIdx.x * per_blk, p1 = min(p0 + per_blk, P);
-  const int ng = 256 / ncol, grp = threadIdx.x / ncol, c = threadIdx.x - grp * ncol;
+  const int ng = 1024 / ncol, grp = threadIdx.x / ncol, c = threadIdx.x - grp * ncol;
   float s = 0.f;
   if (grp < ng) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -289,14 +289,16 @@ __device__ __forceinline__ float row16_sum(float v) {
 // LayerNorm backward per position: 16 lanes per position (four channels per
 // lane and 16-byte access), four positions per wave and step, the two sums
 // over channels reduced within each row of 16 lanes; per-block partial sums
-// of dx * x-hat (for dgamma) and dx (for dbeta): block blk covers positions
-// blk*per .. ; the 16 (wave, row) partials are added in a fixed order.
+// of dx * x-hat (for dgamma) and dx (for dbeta): block blk (16 waves) covers
+// positions blk*per .. ; the 64 (wave, row) partials are added in a fixed
+// order.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_ln_back(const float *dx, const float *xhat, const float *rstd,
+__global__ __launch_bounds__(1024) void bwd_ln_back(const float *dx, const float *xhat, const float *rstd,
                                                     const void *gamma, long long npos, long long per_blk, float *dP,
                                                     float *part_g, float *part_b) {
   constexpr int PER = D / 64;  // 16-byte pieces per lane and position
-  __shared__ __align__(16) float red[2][16][D];
+  constexpr int NW = 16;
+  __shared__ __align__(16) float red[2][NW * 4][D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, pr = lane >> 4, c16 = lane & 15;
   float4 gm[PER], sg[PER], sb[PER];
 #pragma unroll
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(256) void bwd_ln_back(const float *dx, const float 
     sg[e] = sb[e] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   const long long p0 = (long long)blockIdx.x * per_blk, p1 = min(p0 + per_blk, npos);
-  for (long long pb = p0 + 4 * wave; pb < p1; pb += 16) {
+  for (long long pb = p0 + 4 * wave; pb < p1; pb += 4 * NW) {
     const long long p = pb + pr;
     const bool ok = p < p1;
     float4 d[PER], xh[PER];
@@ -342,11 +344,11 @@ __global__ __launch_bounds__(256) void bwd_ln_back(const float *dx, const float 
     *reinterpret_cast<float4 *>(&red[1][wave * 4 + pr][4 * c16 + 64 * e]) = sb[e];
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < 2 * D; c += 256) {
+  for (int c = threadIdx.x; c < 2 * D; c += NW * 64) {
     const int w = c / D, ch = c - w * D;
     float acc = 0.f;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) acc += red[w][q][ch];
+#pragma unroll 8
+    for (int q = 0; q < NW * 4; ++q) acc += red[w][q][ch];
     (w == 0 ? part_g : part_b)[(size_t)blockIdx.x * D + ch] = acc;
   }
 }
@@ -1012,8 +1014,9 @@ static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed
   L.kchunk = ((P + 255) / 256 + 15) / 16 * 16;
   if (L.kchunk < 16) L.kchunk = 16;
   L.S = (P + L.kchunk - 1) / L.kchunk;
-  // column sums (bias gradients, dgamma, dbeta): at most 1024 blocks
-  L.vper = (P + 1023) / 1024;
+  // column sums (bias gradients, dgamma, dbeta): at most 256 blocks of 16
+  // waves, so the ordered sum of their partials stays short
+  L.vper = (P + 255) / 256;
   L.nvblk = (P + L.vper - 1) / L.vper;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -1189,7 +1192,7 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   }
   // projections and LayerNorm
   TPA_CHECK((gemm<float, T>(dcat, C, 1, r.wpack, D, 1, dx, 0, D, P, D, C, C, 1, s)));
-  hipLaunchKernelGGL((bwd_ln_back<T, D>), dim3((unsigned)L.nvblk), dim3(256), 0, s, dx, xhat, rstd, gamma, P, L.vper,
+  hipLaunchKernelGGL((bwd_ln_back<T, D>), dim3((unsigned)L.nvblk), dim3(1024), 0, s, dx, xhat, rstd, gamma, P, L.vper,
                      dPout, vpart, vpart + (size_t)L.nvblk * D);
   TPA_CHECK(hipGetLastError());
   TPA_CHECK(reduce(vpart, D, (int)L.nvblk, D, r.g.d_ln_weight, s));
@@ -1202,11 +1205,11 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   TPA_CHECK((gemm<T, float>(dyin, 1, D, go, D, 1, part, (long long)D * D, D, D, D, P, L.kchunk, (int)L.S, s)));
   TPA_CHECK(reduce(part, (long long)D * D, (int)L.S, (long long)D * D, r.g.d_w_out, s));
   // bias gradients: column sums over positions
-  hipLaunchKernelGGL((bwd_colsum<T>), dim3((unsigned)L.nvblk), dim3(256), 0, s, dyin, P, D, (long long)D, L.vper,
+  hipLaunchKernelGGL((bwd_colsum<T>), dim3((unsigned)L.nvblk), dim3(1024), 0, s, dyin, P, D, (long long)D, L.vper,
                      vpart);
   TPA_CHECK(hipGetLastError());
   TPA_CHECK(reduce(vpart, D, (int)L.nvblk, D, r.g.d_b_out, s));
-  hipLaunchKernelGGL((bwd_colsum<float>), dim3((unsigned)L.nvblk), dim3(256), 0, s, dcat + 3 * D, P, D, C, L.vper,
+  hipLaunchKernelGGL((bwd_colsum<float>), dim3((unsigned)L.nvblk), dim3(1024), 0, s, dcat + 3 * D, P, D, C, L.vper,
                      vpart);
   TPA_CHECK(hipGetLastError());
   TPA_CHECK(reduce(vpart, D, (int)L.nvblk, D, r.g.d_b_gate, s));
