@@ -74,6 +74,7 @@ struct GemmArgs {
   float *C;
   long long M, N, K, kchunk;
   long long sam, sak, sbk, sbn, scz, scm;
+  long long nz;  // K chunks
 };
 
 // four consecutive elements (the first one's index a multiple of 4), as floats
@@ -96,12 +97,18 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   __shared__ __align__(16) uint16_t As[2][64 * PK];
   __shared__ __align__(16) uint16_t Bs[2][64 * PK];
   const int tid = threadIdx.x;
-  // grid x: (row block, column block) with the column block fastest, so the
-  // workgroups that share a row block of A run together and it is read from
-  // memory once; z: K chunks
-  const long long ncb = (g.N + 63) / 64;
-  const long long m0 = ((long long)blockIdx.x / ncb) * 64, n0 = ((long long)blockIdx.x % ncb) * 64;
-  const long long kb = (long long)blockIdx.z * g.kchunk;
+  // one-dimensional grid over tiles (K chunk, row block, column block),
+  // column block fastest, mapped XCD-aware: workgroup v runs on XCD v % 8,
+  // and each XCD takes a contiguous range of that order, so the workgroups
+  // sharing a row block of A (or, split over K, one chunk's A and B) run on
+  // one XCD and read them from memory into its L2 once
+  const long long ncb = (g.N + 63) / 64, ntile = ((g.M + 63) / 64) * ncb;
+  const long long total = ntile * g.nz, v = blockIdx.x;
+  const long long w8 = (total / 8) * 8;
+  const long long lin = v < w8 ? (v & 7) * (w8 / 8) + (v >> 3) : v;
+  const long long zc = lin / ntile, tile = lin - zc * ntile;
+  const long long m0 = (tile / ncb) * 64, n0 = (tile % ncb) * 64;
+  const long long kb = zc * g.kchunk;
   const long long ke = min(kb + g.kchunk, g.K);
   // wave w computes the 32 x 32 quadrant (w / 2, w % 2) as 2 x 2 tiles of
   // split products (three bf16 16x16x16 products per float32 product)
@@ -188,7 +195,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const long long m = m0 + 32 * wm + 16 * i + 4 * g4 + r;
-        if (m < g.M && n < g.N) g.C[(size_t)(blockIdx.z * g.scz + m * g.scm + n)] = acc[i][j][r];
+        if (m < g.M && n < g.N) g.C[(size_t)(zc * g.scz + m * g.scm + n)] = acc[i][j][r];
       }
     }
 }
@@ -1092,10 +1099,10 @@ template <typename TA, typename TB>
 static hipError_t gemm(const void *A, long long sam, long long sak, const void *Bm, long long sbk, long long sbn,
                        float *C, long long scz, long long scm, long long M, long long N, long long K,
                        long long kchunk, int nz, hipStream_t s) {
-  GemmArgs g{A, Bm, C, M, N, K, kchunk, sam, sak, sbk, sbn, scz, scm};
-  const long long blocks = ((M + 63) / 64) * ((N + 63) / 64);
+  GemmArgs g{A, Bm, C, M, N, K, kchunk, sam, sak, sbk, sbn, scz, scm, nz};
+  const long long blocks = ((M + 63) / 64) * ((N + 63) / 64) * nz;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks, 1, (unsigned)nz);
+  const dim3 grid((unsigned)blocks);
   hipLaunchKernelGGL((bwd_gemm<TA, TB>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
