@@ -625,8 +625,8 @@ __global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
       for (int r = 0; r < 4; ++r) {
         const bool valid = (vm >> r) & 1u;
         const float p = fast_exp2(st[r] - m2) * linv;
-        const float da = (nib >> r) & 1u ? dp[r] * a.scale : 0.f;
-        ds[r] = valid ? p * (da - Dv) : 0.f;
+        const float da = (nib >> r) & 1u ? dp[r] : 0.f;  // the keep scale enters below
+        ds[r] = valid ? p * fmaf(da, a.scale, -Dv) : 0.f;
       }
       // dq^T += k^T dS^T
       const Split4 dss = split4(ds[0], ds[1], ds[2], ds[3]);
@@ -822,9 +822,9 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
         const float sl = valid ? s[r] : a.fill2;
         const float p = fast_exp2(sl - mq[r]) * lq[r];
         const bool kp = ((kbits[jj][kk >> 5] >> (kk & 31)) & 1u) != 0u;
-        const float da = kp ? dp[r] * a.scale : 0.f;
-        pk[r] = kp ? p * a.scale : 0.f;
-        ds[r] = valid ? p * (da - dq4[r]) : 0.f;
+        const float da = kp ? dp[r] : 0.f;  // the keep scale enters below
+        pk[r] = kp ? p : 0.f;               // and in dv's store
+        ds[r] = valid ? p * fmaf(da, a.scale, -dq4[r]) : 0.f;
       }
       // dv^T += do^T P', dk^T += q^T dS
       const Split4 pks = split4(pk[0], pk[1], pk[2], pk[3]), dss = split4(ds[0], ds[1], ds[2], ds[3]);
@@ -844,7 +844,7 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
     stg<float4>(a.dcat + (rowp + k) * C + D + t * DH + 16 * cb + 4 * g,
                 make_float4(dk[cb][0] * a.rsd, dk[cb][1] * a.rsd, dk[cb][2] * a.rsd, dk[cb][3] * a.rsd));
     stg<float4>(a.dcat + (rowp + k) * C + 2 * D + t * DH + 16 * cb + 4 * g,
-                make_float4(dv[cb][0], dv[cb][1], dv[cb][2], dv[cb][3]));
+                make_float4(dv[cb][0] * a.scale, dv[cb][1] * a.scale, dv[cb][2] * a.scale, dv[cb][3] * a.scale));
   }
 }
 
@@ -941,8 +941,8 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = fast_exp2(zl[kbk][r] + sc[r] - m2[r]) * linv[r];
-        const float dav = (w2[r][kk >> 5] >> (kk & 31)) & 1u ? dp[r] * a.scale : 0.f;
-        if ((valid >> (4 * kbk + r)) & 1u) dz[kbk][r] += p * (dav - Dv[r]);
+        const float dav = (w2[r][kk >> 5] >> (kk & 31)) & 1u ? dp[r] : 0.f;  // the keep scale enters below
+        if ((valid >> (4 * kbk + r)) & 1u) dz[kbk][r] += p * fmaf(dav, a.scale, -Dv[r]);
       }
     }
     __syncthreads();
