@@ -377,6 +377,7 @@ struct BwdAttnArgs {
   float rsd;             // 1 / sqrt(d)
   uint32_t thr, seed_lo, seed_hi, offset;
   int B, N, D, h, C, NW;
+  const uint8_t *dead;  // [B][N]: 1 where query column j has no valid key (every M[b, j, k] is 0)
   float *zpart;      // [zsplit][B*h][N][N]: dz partial sums over row ranges (zsplit > 1)
   int zsplit, zrows;  // row ranges of the dz step and rows per range
 };
@@ -454,36 +455,37 @@ __device__ __forceinline__ void stage_rows(const BwdAttnArgs &a, size_t rowp, in
   }
 }
 
-// S^T tile of 16 keys (kb) x the lane's query: bias, q.k, mask, padding;
-// bit r of *valid is set where key 4g + r is in range and not masked
+// S^T tile of 16 keys (kb) x the lane's query: bias + q.k, -inf for keys past
+// N. A masked key's bias is FILL, so its score FILL + q.k has weight exactly 0
+// beside any valid key; a query column without a valid key has q = 0 (and do
+// = 0, D = 0) wherever it is staged, so its scores are FILL exactly (uniform
+// weights, the rule of a finite fill) and its dS is exactly 0, as the masked
+// entries' must be. No per-score mask test is needed.
 template <int DH>
 __device__ __forceinline__ f32x4 score_tile_t(const BwdAttnArgs &a, const uint16_t (*kbuf)[S_KP<DH> * 64],
                                               const Split4 (&qf)[DH / 16], const float *zq, int k0, int kb, int g,
-                                              int r16, uint32_t *valid) {
+                                              int r16) {
   using S = BwdTile<DH>;
   const int kq = k0 + kb * 16 + 4 * g;  // first of the lane's four keys
+  const bool full = kq + 3 < a.N;
   f32x4 st;
-  if (kq + 3 < a.N && (a.N & 3) == 0) {  // rows of z are 16-byte aligned when N % 4 == 0
+  if (full && (a.N & 3) == 0) {  // rows of z are 16-byte aligned when N % 4 == 0
     const float4 z4 = ldg<float4>(zq + kq);
     st = (f32x4){z4.x, z4.y, z4.z, z4.w};
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) st[r] = kq + r < a.N ? zq[kq + r] : 0.f;
   }
-  const f32x4 z0 = st;
 #pragma unroll
   for (int cb = 0; cb < S::CB; ++cb) {
     const int o = (kb * 16 + r16) * S::KP + 16 * cb + 4 * g;
     st = mma_split(lds_split4(kbuf[0] + o, kbuf[1] + o), qf[cb], st);
   }
-  uint32_t v = 0;
+  if (!full) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const bool in = kq + r < a.N, live = in && z0[r] != a.fill2;
-    st[r] = !in ? -INFINITY : (live ? st[r] : a.fill2);
-    v |= (uint32_t)live << r;
+    for (int r = 0; r < 4; ++r)
+      if (kq + r >= a.N) st[r] = -INFINITY;
   }
-  *valid = v;
   return st;
 }
 
@@ -501,10 +503,11 @@ __global__ __launch_bounds__(512) void bwd_attn_fwd(BwdAttnArgs a) {
   const int j = qc * S::QB + wave * 16 + r16, jc = min(j, N - 1);
   const size_t rowp = (size_t)bi * N;
   Split4 qf[CB];
+  const float qsc = a.dead[(size_t)b * N + jc] ? 0.f : a.qs;  // no valid key: q = 0
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const float4 q4 = ldg<float4>(a.proj + (rowp + jc) * C + t * DH + 16 * cb + 4 * g);
-    qf[cb] = split4(q4.x * a.qs, q4.y * a.qs, q4.z * a.qs, q4.w * a.qs);
+    qf[cb] = split4(q4.x * qsc, q4.y * qsc, q4.z * qsc, q4.w * qsc);
   }
   const float *zq = a.zt + ((size_t)(b * h + t) * N + jc) * N;
   const uint32_t *kr = keep_row(a, bi, t, jc);
@@ -518,10 +521,7 @@ __global__ __launch_bounds__(512) void bwd_attn_fwd(BwdAttnArgs a) {
     __syncthreads();
     f32x4 st[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      uint32_t vm;
-      st[kb] = score_tile_t<DH>(a, kbuf, qf, zq, k0, kb, g, r16, &vm);
-    }
+    for (int kb = 0; kb < 4; ++kb) st[kb] = score_tile_t<DH>(a, kbuf, qf, zq, k0, kb, g, r16);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -585,18 +585,23 @@ __global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
   const size_t rowp = (size_t)bi * N;
   Split4 qf[CB], df[CB];
   float dsum = 0.f;
+  // no valid key: q, do and D = 0, so the column's dS is exactly 0
+  const float live = a.dead[(size_t)b * N + jc] ? 0.f : 1.f;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const float4 q4 = ldg<float4>(a.proj + (rowp + jc) * C + t * DH + 16 * cb + 4 * g);
-    qf[cb] = split4(q4.x * a.qs, q4.y * a.qs, q4.z * a.qs, q4.w * a.qs);
-    const float4 d4 = ldg<float4>(a.dob + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
+    const float qsc = a.qs * live;
+    qf[cb] = split4(q4.x * qsc, q4.y * qsc, q4.z * qsc, q4.w * qsc);
+    float4 d4 = ldg<float4>(a.dob + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
     const float4 o4 = ldg<float4>(a.o + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
+    d4 = make_float4(d4.x * live, d4.y * live, d4.z * live, d4.w * live);
     df[cb] = split4(d4.x, d4.y, d4.z, d4.w);
     dsum += d4.x * o4.x + d4.y * o4.y + d4.z * o4.z + d4.w * o4.w;
   }
   const float Dv = group4_sum(dsum);
   const size_t st_ = ((size_t)bi * h + t) * N + jc;
-  const float m2 = a.m[st_], linv = 1.f / a.l[st_];
+  // every score -inf (-inf fill, no valid key): weights 0 (not 0 * inf)
+  const float m2r = a.m[st_], m2 = m2r == -INFINITY ? 0.f : m2r, linv = m2r == -INFINITY ? 0.f : 1.f / a.l[st_];
   if (j < N && g == 0) a.Dj[st_] = Dv;
   const float *zq = a.zt + ((size_t)(b * h + t) * N + jc) * N;
   const uint32_t *kr = keep_row(a, bi, t, jc);
@@ -610,8 +615,7 @@ __global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
     const uint32_t w32[2] = {k0 < N ? kr[k0 >> 5] : 0u, k0 + 32 < N ? kr[(k0 >> 5) + 1] : 0u};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      uint32_t vm;
-      const f32x4 st = score_tile_t<DH>(a, kbuf, qf, zq, k0, kb, g, r16, &vm);
+      const f32x4 st = score_tile_t<DH>(a, kbuf, qf, zq, k0, kb, g, r16);
       // dP^T = v do^T (keys x the lane's query)
       f32x4 dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -623,10 +627,9 @@ __global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
       float ds[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool valid = (vm >> r) & 1u;
         const float p = fast_exp2(st[r] - m2) * linv;
         const float da = (nib >> r) & 1u ? dp[r] : 0.f;  // the keep scale enters below
-        ds[r] = valid ? p * fmaf(da, a.scale, -Dv) : 0.f;
+        ds[r] = p * fmaf(da, a.scale, -Dv);
       }
       // dq^T += k^T dS^T
       const Split4 dss = split4(ds[0], ds[1], ds[2], ds[3]);
@@ -692,18 +695,20 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
   const int kw0 = (kc * S::QB) >> 5;
   struct Chunk {
     float4 q, d, z[ZP];
-    float m, il, Dq;
+    float m, il, Dq, live;  // live = 0: the query column has no valid key
     uint32_t kw;
   };
   auto load_chunk = [&](int j0) {
     Chunk c;
     const int e = threadIdx.x;
     c.q = c.d = make_float4(0.f, 0.f, 0.f, 0.f);
+    c.live = 0.f;
     if (e < V4) {
       const int jj = e / (DH / 4), u4 = (e - jj * (DH / 4)) * 4, jq = j0 + jj;
       if (jq < N) {
         c.q = ldg<float4>(a.proj + (rowp + jq) * C + t * DH + u4);
         c.d = ldg<float4>(a.dob + (rowp + jq) * D + t * DH + u4);
+        c.live = a.dead[(size_t)b * N + jq] ? 0.f : 1.f;
       }
     }
     // m and 1 / l (one division per query, not per score); a column past N,
@@ -745,13 +750,19 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
     const int e = threadIdx.x;
     if (e < V4) {
       const int jj = e / (DH / 4), u4 = (e - jj * (DH / 4)) * 4;
-      const Split4 qs4 = split4(c.q.x, c.q.y, c.q.z, c.q.w), ds4 = split4(c.d.x, c.d.y, c.d.z, c.d.w);
+      // a query column without a valid key: q = 0 (its scores are FILL
+      // exactly) and do = 0 in the dP operand (its dS is exactly 0); its do
+      // stays in the transposed planes, for dv
+      const float lv = c.live;
+      const Split4 qs4 = split4(c.q.x * lv, c.q.y * lv, c.q.z * lv, c.q.w * lv),
+                   ds4 = split4(c.d.x, c.d.y, c.d.z, c.d.w),
+                   dz4 = split4(c.d.x * lv, c.d.y * lv, c.d.z * lv, c.d.w * lv);
       const uint2 qh = __builtin_bit_cast(uint2, qs4.h), ql = __builtin_bit_cast(uint2, qs4.l);
       const uint2 dh = __builtin_bit_cast(uint2, ds4.h), dl = __builtin_bit_cast(uint2, ds4.l);
       *reinterpret_cast<uint2 *>(qbuf[0] + jj * S::KP + u4) = qh;
       *reinterpret_cast<uint2 *>(qbuf[1] + jj * S::KP + u4) = ql;
-      *reinterpret_cast<uint2 *>(dbuf[0] + jj * S::KP + u4) = dh;
-      *reinterpret_cast<uint2 *>(dbuf[1] + jj * S::KP + u4) = dl;
+      *reinterpret_cast<uint2 *>(dbuf[0] + jj * S::KP + u4) = __builtin_bit_cast(uint2, dz4.h);
+      *reinterpret_cast<uint2 *>(dbuf[1] + jj * S::KP + u4) = __builtin_bit_cast(uint2, dz4.l);
       const uint32_t w[4][2] = {{qh.x, qh.y}, {ql.x, ql.y}, {dh.x, dh.y}, {dl.x, dl.y}};
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
@@ -786,12 +797,12 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
       if (j0 + QT < N) nxt = load_chunk(j0 + QT);
 #pragma unroll 1
     for (int qb = 0; qb < 4; ++qb) {
-      // S = q k^T (queries x keys): bias, product, mask, padding
+      // S = q k^T (queries x keys): bias (FILL where masked, -inf past N) +
+      // product, with no per-score mask test (see score_tile_t)
       const int kk = wave * 16 + r16;  // the lane's key within the workgroup's 128
       f32x4 s;
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[r] = zs[qb * 16 + 4 * g + r][kk];
-      const f32x4 s0 = s;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int o = (qb * 16 + r16) * S::KP + 16 * cb + 4 * g;
@@ -813,18 +824,17 @@ __global__ __launch_bounds__(512) void bwd_attn_dkv(BwdAttnArgs a) {
       const float dq4[4] = {d4.x, d4.y, d4.z, d4.w};
       // A score past N (query or key) is -inf (its bias is), so its weight
       // p is 0, and so are its terms below (a keep bit past N may be set: the
-      // generator draws keys in fours). Masked scores are FILL: they carry no
-      // gradient, and their weight is 0 unless the column is fully masked.
+      // generator draws keys in fours). A masked score is FILL + q.k: weight
+      // 0 beside any valid key; in a column without one, q, do (in the dP
+      // operand) and D are 0, so its weights are uniform and its dS is 0.
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int jj = qb * 16 + 4 * g + r;
-        const bool valid = s0[r] != a.fill2;
-        const float sl = valid ? s[r] : a.fill2;
-        const float p = fast_exp2(sl - mq[r]) * lq[r];
+        const float p = fast_exp2(s[r] - mq[r]) * lq[r];
         const bool kp = ((kbits[jj][kk >> 5] >> (kk & 31)) & 1u) != 0u;
         const float da = kp ? dp[r] : 0.f;  // the keep scale enters below
         pk[r] = kp ? p : 0.f;               // and in dv's store
-        ds[r] = valid ? p * fmaf(da, a.scale, -dq4[r]) : 0.f;
+        ds[r] = p * fmaf(da, a.scale, -dq4[r]);
       }
       // dv^T += do^T P', dk^T += q^T dS
       const Split4 pks = split4(pk[0], pk[1], pk[2], pk[3]), dss = split4(ds[0], ds[1], ds[2], ds[3]);
@@ -870,8 +880,10 @@ __global__ __launch_bounds__(256) void bwd_attn_dz(BwdAttnArgs a) {
   const int bt = blockIdx.y, b = bt / h, t = bt - b * h;
   const int j0 = (blockIdx.x / nkt) * JT, k0 = (blockIdx.x % nkt) * KT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+  // the bias of the valid (j, k) (masked ones and those past N add nothing:
+  // bit 4 kb + r of valid)
   float zl[4][4], dz[4][4];  // [key block][r]: query j0 + 16 wave + 4g + r, key k0 + 16 kb + r16
-  uint32_t valid = 0;        // bit 4 kb + r
+  uint32_t valid = 0;
 #pragma unroll
   for (int kbk = 0; kbk < 4; ++kbk)
 #pragma unroll
@@ -974,6 +986,19 @@ __global__ __launch_bounds__(256) void bwd_dz_reduce(BwdAttnArgs a) {
   a.dcat[((size_t)b * N * N + jk) * a.C + 4 * a.D + t] = sum;
 }
 
+// dead[b][j] = 1 where query column j of batch b has no valid key (every
+// mask entry M[b, j, k] is 0): one wave per column
+__global__ __launch_bounds__(256) void bwd_dead_columns(const uint8_t *mask, long long ncol, int N, uint8_t *dead) {
+  const long long col = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (col >= ncol) return;  // the whole wave
+  const int lane = threadIdx.x & 63;
+  const uint8_t *row = mask + col * N;
+  bool any = false;
+  for (int k = lane; k < N; k += 64) any |= row[k] != 0;
+  const bool any_w = __ballot(any) != 0;
+  if (lane == 0) dead[col] = any_w ? 0 : 1;
+}
+
 // z[b,t,j,k] * log2(e) from the projection columns, FILL * log2(e) where the
 // mask is 0, into a [B][h][N][N] copy: the attention kernels tell a masked
 // key by that exact value and read no mask
@@ -1006,7 +1031,7 @@ __global__ __launch_bounds__(256) void bwd_gate(const float *dgo, const float *p
 
 // ------------------------------------------------------------------ host side
 struct BwdLayout {
-  size_t x, xhat, rstd, proj, zt, m, l, Dj, o, dgo, dob, go, dcat, dx, part, vpart, bits, zpart, pt, mt, dyt, dpt, total;
+  size_t x, xhat, rstd, proj, zt, dead, m, l, Dj, o, dgo, dob, go, dcat, dx, part, vpart, bits, zpart, pt, mt, dyt, dpt, total;
   long long S, kchunk, nvblk, vper;
   int zsplit, zrows;
 };
@@ -1036,6 +1061,7 @@ static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed
   L.rstd = take((size_t)P * 4);
   L.proj = take((size_t)P * C * 4);
   L.zt = take((size_t)B * h * N * N * 4);
+  L.dead = take((size_t)B * N);
   L.m = take((size_t)B * N * h * N * 4);
   L.l = take((size_t)B * N * h * N * 4);
   L.Dj = take((size_t)B * N * h * N * 4);
@@ -1165,6 +1191,13 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   aa.NW = (N + 31) / 32;
   uint32_t *bits = reinterpret_cast<uint32_t *>(w + L.bits);
   aa.bits = bits;
+  {
+    uint8_t *dead = reinterpret_cast<uint8_t *>(w + L.dead);
+    const long long ncol = (long long)B * N;
+    hipLaunchKernelGGL(bwd_dead_columns, dim3((unsigned)((ncol + 3) / 4)), dim3(256), 0, s, Min, ncol, N, dead);
+    TPA_CHECK(hipGetLastError());
+    aa.dead = dead;
+  }
   {
     const long long nwords = (long long)B * N * h * N * aa.NW;
     hipLaunchKernelGGL(bwd_keep_bits, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s, aa, bits, nwords);
