@@ -26,10 +26,11 @@
 // All arithmetic is float32, the products (the projection GEMMs and the
 // attention's score, value and gradient tiles) as split bf16 products (two
 // bf16 parts per float32 operand, three 16x16x16 matrix-core products per
-// float32 product, ~2^-16 relative error); the dropout decisions are computed once into a bit array
-// (one generator call per four keys) that every attention step reads; the
-// backward's copy of the pair bias carries the mask (FILL where masked), so
-// no attention step reads the mask itself.
+// float32 product, ~2^-16 relative error). The dropout decisions are
+// computed once into a bit array (one generator call per four keys) that
+// every attention step reads; the backward's copy of the pair bias carries
+// the mask (FILL where masked), and query columns without a valid key are
+// flagged once, so no attention step reads the mask itself.
 #include "device_common.h"
 #include "tri_attn.h"
 #include "tri_attn_internal.h"
