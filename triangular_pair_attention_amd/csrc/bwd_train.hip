@@ -121,41 +121,53 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const bool a_m_contig = g.sam == 1, b_n_contig = g.sbn == 1;
-  // one operand's 64 x 16 slice: each thread loads four consecutive elements
-  // along the contiguous index (one 16- or 8-byte load when all four are in
-  // range; load), then writes their two bf16 parts to the planes (put)
+  // one operand's 64 x 16 slice: each thread loads four elements (load) and
+  // writes their two bf16 parts to the planes (put). Contiguous along k: the
+  // four threads of a tile row read its 16 k as one 64-byte piece (one 16-
+  // or 8-byte load each) and each writes its four k as one 8-byte store per
+  // plane. Contiguous along the row index, float32: thread (row, k quad) reads
+  // its four k as four 4-byte loads, which the wave's 64 consecutive rows make
+  // coalesced, and writes them the same way. Contiguous along the row index,
+  // bf16 (2-byte loads would be too narrow): four consecutive rows of one k
+  // in one load, written to the planes as scattered 2-byte stores.
   auto load = [&](auto ta, const void *X, long long s_t, long long s_k, long long T, long long t0, bool t_contig,
                   long long k0) {
     using TX = decltype(ta);
-    const int lin = t_contig ? ((tid & 15) * 4) : ((tid & 3) * 4);  // 4 along the contiguous index
-    const int oth = t_contig ? (tid >> 4) : (tid >> 2);             // the other index
-    const long long tt = t0 + (t_contig ? lin : oth), kk = k0 + (t_contig ? oth : lin);
-    const bool full = t_contig ? (tt + 3 < T && kk < ke) : (tt < T && kk + 3 < ke);
-    if (full) return ld4<TX>(X, (size_t)(tt * s_t + kk * s_k));
+    if (t_contig && is_bf16<TX>::value) {
+      const int lin = (tid & 15) * 4, oth = tid >> 4;  // four rows, one k
+      const long long tt = t0 + lin, kk = k0 + oth;
+      if (tt + 3 < T && kk < ke) return ld4<TX>(X, (size_t)(tt * s_t + kk * s_k));
+      float t4[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) t4[c] = (tt + c < T && kk < ke) ? ld_elem<TX>(X, (size_t)((tt + c) * s_t + kk * s_k)) : 0.f;
+      return make_float4(t4[0], t4[1], t4[2], t4[3]);
+    }
+    const int r = t_contig ? (tid & 63) : (tid >> 2), kq = t_contig ? (tid >> 6) : (tid & 3);
+    const long long tt = t0 + r, kk = k0 + 4 * kq;
+    if (!t_contig && tt < T && kk + 3 < ke) return ld4<TX>(X, (size_t)(tt * s_t + kk * s_k));
     float t4[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const long long t2 = tt + (t_contig ? c : 0), k2 = kk + (t_contig ? 0 : c);
-      t4[c] = (t2 < T && k2 < ke) ? ld_elem<TX>(X, (size_t)(t2 * s_t + k2 * s_k)) : 0.f;
-    }
+    for (int c = 0; c < 4; ++c)
+      t4[c] = (tt < T && kk + c < ke) ? ld_elem<TX>(X, (size_t)(tt * s_t + (kk + c) * s_k)) : 0.f;
     return make_float4(t4[0], t4[1], t4[2], t4[3]);
   };
-  auto put = [&](float4 v, bool t_contig, uint16_t (*pl)[64 * PK]) {
-    const int lin = t_contig ? ((tid & 15) * 4) : ((tid & 3) * 4);
-    const int oth = t_contig ? (tid >> 4) : (tid >> 2);
+  auto put = [&](auto ta, float4 v, bool t_contig, uint16_t (*pl)[64 * PK]) {
+    using TX = decltype(ta);
     const Split4 sp = split4(v.x, v.y, v.z, v.w);
     const uint2 hv = __builtin_bit_cast(uint2, sp.h), lv = __builtin_bit_cast(uint2, sp.l);
-    if (t_contig) {  // four tile rows, one k: scattered 2-byte writes
+    if (t_contig && is_bf16<TX>::value) {
+      const int lin = (tid & 15) * 4, oth = tid >> 4;
       const uint32_t hw[2] = {hv.x, hv.y}, lw[2] = {lv.x, lv.y};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         pl[0][(lin + c) * PK + oth] = (uint16_t)(hw[c >> 1] >> (16 * (c & 1)));
         pl[1][(lin + c) * PK + oth] = (uint16_t)(lw[c >> 1] >> (16 * (c & 1)));
       }
-    } else {  // one tile row, four consecutive k
-      *reinterpret_cast<uint2 *>(&pl[0][oth * PK + lin]) = hv;
-      *reinterpret_cast<uint2 *>(&pl[1][oth * PK + lin]) = lv;
+      return;
     }
+    const int r = t_contig ? (tid & 63) : (tid >> 2), kq = t_contig ? (tid >> 6) : (tid & 3);
+    *reinterpret_cast<uint2 *>(&pl[0][r * PK + 4 * kq]) = hv;
+    *reinterpret_cast<uint2 *>(&pl[1][r * PK + 4 * kq]) = lv;
   };
   // the next slice's elements are loaded into registers while the current
   // one is multiplied; the barriers wait for LDS traffic only, so those
@@ -163,8 +175,8 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   float4 va = load(TA{}, g.A, g.sam, g.sak, g.M, m0, a_m_contig, kb);
   float4 vb = load(TB{}, g.B, g.sbn, g.sbk, g.N, n0, b_n_contig, kb);
   for (long long k0 = kb; k0 < ke; k0 += 16) {
-    put(va, a_m_contig, As);
-    put(vb, b_n_contig, Bs);
+    put(TA{}, va, a_m_contig, As);
+    put(TB{}, vb, b_n_contig, Bs);
     lds_barrier();
     if (k0 + 16 < ke) {
       va = load(TA{}, g.A, g.sam, g.sak, g.M, m0, a_m_contig, k0 + 16);
