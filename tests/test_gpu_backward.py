@@ -164,6 +164,15 @@ def test_backward_workload5_sampled_positions():
     assert err[worst] <= RTOL * scale, f"error {err[worst]} at {pos[worst]} > {RTOL} * {scale}"
 
 
+@pytest.mark.parametrize("dtype,h", [("f32", 4), ("bf16", 8)])
+def test_backward_ragged_several_blocks(dtype, h):
+    """N = 300 with 30 padded residues (fully masked query columns): three
+    128-key blocks in the dk/dv step and five 64-key chunks in the others,
+    the last of each ragged; five 64 x 64 pair-bias tiles per side."""
+    inp = make_inputs(Workload("bwd_n300", 1, 300, 128, h, dtype, ("pad", 270), seed=87))
+    check_backward(inp, 0.2, seed=23, offset=4, what=f"backward N=300 {dtype} h={h}")
+
+
 def test_backward_minus_inf_fill():
     """-inf fill on a mask where every query column keeps a valid key."""
     inp = make_inputs(Workload("bwd_ninf", 1, 24, 64, 4, "f32", ("bernoulli", 0.7), seed=83))
