@@ -139,7 +139,9 @@ def test_backward_workload5_sampled_positions():
     on every step of the backward: the gate, dq of its query column, dk and
     dv of its key, and the pair bias's gradient summed over all 512 rows.
     The parameter gradients are sums over all positions; at this size they
-    are checked for finiteness (workloads 1-4 compare them in full)."""
+    are checked for finiteness (workloads 1-4 compare them in full), and the
+    output bias's, which is the plain column sum of dy over every position,
+    against that sum in float64."""
     w = WORKLOADS[5]
     inp = make_inputs(w)
     M = np.asarray(inp["pair_mask"])
@@ -154,6 +156,11 @@ def test_backward_workload5_sampled_positions():
     got = run_backward(inp, dy, 0.1, 4242, 1)
     for k in SHAPE:
         assert np.isfinite(got[k]).all(), k
+    dbo = dy.astype(np.float64).reshape(-1, w.D).sum(axis=0)
+    err_bo = float(np.abs(got["d_b_out"] - dbo).max())
+    log(f"backward {w.name} d_b_out against the column sums of dy: max abs err {err_bo:.3e}, "
+        f"max |ref| {np.abs(dbo).max():.3e}")
+    assert err_bo <= RTOL * float(np.abs(dbo).max())
     ref = BO.pair_repr_grad_at(inp, dy.astype(np.float64), 0.1, 4242, 1, pos)
     gk = np.stack([got["d_pair_repr"][p] for p in pos])
     scale = float(np.abs(ref).max())
