@@ -383,8 +383,7 @@ struct BwdAttnArgs {
   const uint8_t *mask;   // [B][N][N]
   const uint32_t *bits;  // [B][N][h][N][NW]: bit k%32 of word k/32 set where key k is kept
   float *m, *l, *Dj;     // [B][N][h][N]: m2, l, sum_k a da (= do . o)
-  float *o;              // [P][D]: o after dropout
-  const float *dob;      // [P][D]: d o
+  float *dob;            // [P][D]: d o (written by the forward-and-dq step)
   float *dcat;           // [P][C]: dq | dk | dv | dgp | dz
   float fill2, scale, qs;  // fill * log2(e); keep scale; log2(e) / sqrt(d)
   float rsd;             // 1 / sqrt(d)
@@ -502,35 +501,44 @@ __device__ __forceinline__ f32x4 score_tile_t(const BwdAttnArgs &a, const uint16
   return st;
 }
 
-// Attention forward again: m2, l and o = scale * sum_k keep * a v.
-template <int DH>
-__global__ __launch_bounds__(512) void bwd_attn_fwd(BwdAttnArgs a) {
+// Attention forward again, with the output and gate step, per work item
+// (b, i, t, 128 query columns): m2, l and o = scale * sum_k keep * a v (kept
+// in registers, never stored); then, per query column and channel of head t,
+// g = sigmoid(gate pre-activation + bg) and, from d(g*o) = Wo^T dy,
+// dgp = d(g*o) o g (1 - g) (into dcat), do = d(g*o) g (for the dq, dk/dv and
+// dz steps), g*o (for dWo) and D = sum_k a da = do . o.
+template <typename T, int DH>
+__global__ __launch_bounds__(512) void bwd_attn_fwd(BwdAttnArgs a, const float *dgo, const void *bg, float *go) {
   using S = BwdTile<DH>;
   constexpr int CB = S::CB, KT = S::KT;
   __shared__ __align__(16) uint16_t kbuf[2][KT * S::KP];
-  __shared__ __align__(16) uint16_t vT[2][DH * S::TP];
+  __shared__ __align__(16) uint16_t cT[2][DH * S::TP];  // v transposed
   const int N = a.N, D = a.D, h = a.h, C = a.C;
   const int nq = (N + S::QB - 1) / S::QB;
   const int item = blockIdx.x, qc = item % nq, bt = item / nq, bi = bt / h, t = bt - bi * h, b = bi / N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const int j = qc * S::QB + wave * 16 + r16, jc = min(j, N - 1);
   const size_t rowp = (size_t)bi * N;
+  // no valid key: q = 0 (its scores are FILL exactly), and D = 0 (the dS
+  // path's do is zeroed where staged), so its dS is exactly 0
+  const float live = a.dead[(size_t)b * N + jc] ? 0.f : 1.f;
   Split4 qf[CB];
-  const float qsc = a.dead[(size_t)b * N + jc] ? 0.f : a.qs;  // no valid key: q = 0
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const float4 q4 = ldg<float4>(a.proj + (rowp + jc) * C + t * DH + 16 * cb + 4 * g);
+    const float qsc = a.qs * live;
     qf[cb] = split4(q4.x * qsc, q4.y * qsc, q4.z * qsc, q4.w * qsc);
   }
   const float *zq = a.zt + ((size_t)(b * h + t) * N + jc) * N;
   const uint32_t *kr = keep_row(a, bi, t, jc);
+  // running maximum, row sum and o^T (lane: channels 16 cb + 4g + r of query j)
   float mrun = -INFINITY, lsum = 0.f;
   f32x4 ot[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) ot[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < N; k0 += KT) {
     stage_rows<DH>(a, rowp, D + t * DH, k0, kbuf, nullptr);
-    stage_rows<DH>(a, rowp, 2 * D + t * DH, k0, nullptr, vT);
+    stage_rows<DH>(a, rowp, 2 * D + t * DH, k0, nullptr, cT);
     __syncthreads();
     f32x4 st[4];
 #pragma unroll
@@ -563,26 +571,49 @@ __global__ __launch_bounds__(512) void bwd_attn_fwd(BwdAttnArgs a) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int o = (16 * cb + r16) * S::TP + kb * 16 + 4 * g;
-        ot[cb] = mma_split(lds_split4(vT[0] + o, vT[1] + o), ps, ot[cb]);
+        ot[cb] = mma_split(lds_split4(cT[0] + o, cT[1] + o), ps, ot[cb]);
       }
     }
     __syncthreads();
   }
   const float lt = group4_sum(lsum);
-  if (j >= N) return;
-  const size_t st_ = ((size_t)bi * h + t) * N + j;
-  if (g == 0) {
+  const size_t st_ = ((size_t)bi * h + t) * N + jc;
+  if (j < N && g == 0) {
     a.m[st_] = mrun;
     a.l[st_] = lt;
   }
+  // ---- the output and gate step, and D
   const float inv = a.scale / lt;
+  float dsum = 0.f;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-    stg<float4>(a.o + (rowp + j) * D + t * DH + 16 * cb + 4 * g,
-                make_float4(ot[cb][0] * inv, ot[cb][1] * inv, ot[cb][2] * inv, ot[cb][3] * inv));
+  for (int cb = 0; cb < CB; ++cb) {
+    const int c0 = t * DH + 16 * cb + 4 * g;  // the lane's first channel
+    const size_t pc = (rowp + jc) * D + c0;
+    const float4 d4 = ldg<float4>(dgo + pc);
+    const float4 gp4 = ldg<float4>(a.proj + (rowp + jc) * C + 3 * D + c0);
+    const float dgv[4] = {d4.x, d4.y, d4.z, d4.w}, gpv[4] = {gp4.x, gp4.y, gp4.z, gp4.w};
+    float ov[4], dov[4], dgp[4], gov[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ov[r] = ot[cb][r] * inv;
+      const float gg = 1.0f / (1.0f + expf(-(gpv[r] + ld_elem<T>(bg, c0 + r))));
+      dov[r] = dgv[r] * gg;
+      dgp[r] = dgv[r] * ov[r] * gg * (1.0f - gg);
+      gov[r] = gg * ov[r];
+    }
+    if (j < N) {
+      stg<float4>(a.dcat + (rowp + j) * C + 3 * D + c0, make_float4(dgp[0], dgp[1], dgp[2], dgp[3]));
+      stg<float4>(a.dob + pc, make_float4(dov[0], dov[1], dov[2], dov[3]));
+      stg<float4>(go + pc, make_float4(gov[0], gov[1], gov[2], gov[3]));
+    }
+    dsum += live * ((dov[0] * ov[0] + dov[1] * ov[1]) + (dov[2] * ov[2] + dov[3] * ov[3]));
+  }
+  const float Dv = group4_sum(dsum);
+  if (j < N && g == 0) a.Dj[st_] = Dv;
 }
 
-// dq, and D = sum_k a da = do . o per query column.
+// dq per work item (b, i, t, 128 query columns), with the statistics, do and
+// D of the forward-and-gate step.
 template <int DH>
 __global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
   using S = BwdTile<DH>;
@@ -596,26 +627,22 @@ __global__ __launch_bounds__(512) void bwd_attn_dq(BwdAttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const int j = qc * S::QB + wave * 16 + r16, jc = min(j, N - 1);
   const size_t rowp = (size_t)bi * N;
-  Split4 qf[CB], df[CB];
-  float dsum = 0.f;
-  // no valid key: q, do and D = 0, so the column's dS is exactly 0
+  // no valid key: q, do = 0 (and D = 0 from the forward step), so the
+  // column's dS is exactly 0
   const float live = a.dead[(size_t)b * N + jc] ? 0.f : 1.f;
+  Split4 qf[CB], df[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const float4 q4 = ldg<float4>(a.proj + (rowp + jc) * C + t * DH + 16 * cb + 4 * g);
     const float qsc = a.qs * live;
     qf[cb] = split4(q4.x * qsc, q4.y * qsc, q4.z * qsc, q4.w * qsc);
-    float4 d4 = ldg<float4>(a.dob + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
-    const float4 o4 = ldg<float4>(a.o + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
-    d4 = make_float4(d4.x * live, d4.y * live, d4.z * live, d4.w * live);
-    df[cb] = split4(d4.x, d4.y, d4.z, d4.w);
-    dsum += d4.x * o4.x + d4.y * o4.y + d4.z * o4.z + d4.w * o4.w;
+    const float4 d4 = ldg<float4>(a.dob + (rowp + jc) * D + t * DH + 16 * cb + 4 * g);
+    df[cb] = split4(d4.x * live, d4.y * live, d4.z * live, d4.w * live);
   }
-  const float Dv = group4_sum(dsum);
   const size_t st_ = ((size_t)bi * h + t) * N + jc;
+  const float Dv = a.Dj[st_];
   // every score -inf (-inf fill, no valid key): weights 0 (not 0 * inf)
   const float m2r = a.m[st_], m2 = m2r == -INFINITY ? 0.f : m2r, linv = m2r == -INFINITY ? 0.f : 1.f / a.l[st_];
-  if (j < N && g == 0) a.Dj[st_] = Dv;
   const float *zq = a.zt + ((size_t)(b * h + t) * N + jc) * N;
   const uint32_t *kr = keep_row(a, bi, t, jc);
   f32x4 dq[CB];
@@ -1025,26 +1052,9 @@ __global__ __launch_bounds__(256) void bwd_ztrans(const float *proj, const uint8
   zt[e] = mask[(size_t)b * N * N + jk] ? proj[((size_t)b * N * N + jk) * C + 4 * D + t] * kLog2e : fill2;
 }
 
-// Output and gate step per (position, head): dg, dgp (into dcat), do, g * o.
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_gate(const float *dgo, const float *proj, const float *o,
-                                                 const void *bg, long long npos, int D, int C, float *dcat,
-                                                 float *dob, float *go) {
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= npos * D) return;
-  const long long p = e / D;
-  const int c = (int)(e - p * D);
-  const float gp = proj[p * C + 3 * D + c] + ld_elem<T>(bg, c);
-  const float g = 1.0f / (1.0f + expf(-gp));
-  const float ov = o[e], dv = dgo[e];
-  dcat[p * C + 3 * D + c] = dv * ov * g * (1.0f - g);
-  dob[e] = dv * g;
-  go[e] = g * ov;
-}
-
 // ------------------------------------------------------------------ host side
 struct BwdLayout {
-  size_t x, xhat, rstd, proj, zt, dead, m, l, Dj, o, dgo, dob, go, dcat, dx, part, vpart, bits, zpart, pt, mt, dyt, dpt, total;
+  size_t x, xhat, rstd, proj, zt, dead, m, l, Dj, dgo, dob, go, dcat, dx, part, vpart, bits, zpart, pt, mt, dyt, dpt, total;
   long long S, kchunk, nvblk, vper;
   int zsplit, zrows;
 };
@@ -1078,7 +1088,6 @@ static BwdLayout bwd_layout(int B, int N, int D, int h, int elem, int transposed
   L.m = take((size_t)B * N * h * N * 4);
   L.l = take((size_t)B * N * h * N * 4);
   L.Dj = take((size_t)B * N * h * N * 4);
-  L.o = take((size_t)P * D * 4);
   L.dgo = take((size_t)P * D * 4);
   L.dob = take((size_t)P * D * 4);
   L.go = take((size_t)P * D * 4);
@@ -1159,7 +1168,7 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   char *w = static_cast<char *>(r.ws);
   float *x = reinterpret_cast<float *>(w + L.x), *xhat = reinterpret_cast<float *>(w + L.xhat);
   float *rstd = reinterpret_cast<float *>(w + L.rstd), *proj = reinterpret_cast<float *>(w + L.proj);
-  float *zt = reinterpret_cast<float *>(w + L.zt), *o = reinterpret_cast<float *>(w + L.o);
+  float *zt = reinterpret_cast<float *>(w + L.zt);
   float *dgo = reinterpret_cast<float *>(w + L.dgo), *dob = reinterpret_cast<float *>(w + L.dob);
   float *go = reinterpret_cast<float *>(w + L.go), *dcat = reinterpret_cast<float *>(w + L.dcat);
   float *dx = reinterpret_cast<float *>(w + L.dx), *part = reinterpret_cast<float *>(w + L.part);
@@ -1196,7 +1205,7 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   aa.proj = proj, aa.zt = zt, aa.mask = Min;
   aa.m = reinterpret_cast<float *>(w + L.m), aa.l = reinterpret_cast<float *>(w + L.l);
   aa.Dj = reinterpret_cast<float *>(w + L.Dj);
-  aa.o = o, aa.dob = dob, aa.dcat = dcat;
+  aa.dob = dob, aa.dcat = dcat;
   aa.fill2 = r.fill * kLog2e, aa.scale = r.scale, aa.rsd = 1.0f / sqrtf((float)DH);
   aa.qs = kLog2e * aa.rsd;
   aa.thr = r.thr, aa.seed_lo = r.seed_lo, aa.seed_hi = r.seed_hi, aa.offset = r.offset;
@@ -1220,14 +1229,11 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   const long long items = (long long)B * N * h * ((N + BwdTile<DH>::QB - 1) / BwdTile<DH>::QB);
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 ga((unsigned)items);
-  hipLaunchKernelGGL((bwd_attn_fwd<DH>), ga, dim3(512), 0, s, aa);
-  TPA_CHECK(hipGetLastError());
-  // output projection and gate
+  // d(g*o) = Wo^T dy, then the attention forward again with the output and
+  // gate step, dq, dk/dv and the pair bias
   TPA_CHECK((gemm<T, T>(dyin, D, 1, Wo, D, 1, dgo, 0, D, P, D, D, D, 1, s)));
-  hipLaunchKernelGGL((bwd_gate<T>), dim3((unsigned)((P * D + 255) / 256)), dim3(256), 0, s, dgo, proj, o, bg, P, D,
-                     (int)C, dcat, dob, go);
+  hipLaunchKernelGGL((bwd_attn_fwd<T, DH>), ga, dim3(512), 0, s, aa, dgo, bg, go);
   TPA_CHECK(hipGetLastError());
-  // attention
   hipLaunchKernelGGL((bwd_attn_dq<DH>), ga, dim3(512), 0, s, aa);
   TPA_CHECK(hipGetLastError());
   hipLaunchKernelGGL((bwd_attn_dkv<DH>), ga, dim3(512), 0, s, aa);
