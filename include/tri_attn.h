@@ -162,10 +162,11 @@ typedef struct {
 } tri_attn_grads;
 
 /* Bytes of device workspace tri_attn_backward_train needs for (B, N): the
- * forward's intermediates in float32 (LayerNorm output, the five
- * projections, the attention output and row statistics), their gradients and
- * the partial sums of the weight gradients, and the dropout decisions (one
- * bit per score); about 4(5D + h) * B * N^2 * 2 + B * h * N^3 / 8 bytes, plus
+ * forward's intermediates in float32 (LayerNorm output and x-hat, the five
+ * projections, the pair bias, the attention's row statistics, d(g*o), do and
+ * g*o), their gradients and the partial sums of the weight gradients, and the
+ * dropout decisions (one bit per score); about 8(7D + 3h) * B * N^2 +
+ * B * h * N^3 / 8 bytes, plus
  * transposed copies of the inputs for ending-node handles and, when N is
  * small, partial sums of the pair-bias gradient over ranges of rows (below
  * 64 MiB). B == 0 or N == 0 needs 0 bytes. */
