@@ -180,6 +180,21 @@ def test_backward_ragged_several_blocks(dtype, h):
     check_backward(inp, 0.2, seed=23, offset=4, what=f"backward N=300 {dtype} h={h}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,mask", [((1, 2, 64, 4), ("ones",)), ((2, 3, 64, 2), ("pad", 2)),
+                                        ((1, 5, 128, 8), ("bernoulli", 0.5))], ids=["N2", "B2N3pad", "N5bern"])
+def test_backward_tiny(shape, mask, dtype):
+    """Sizes far below one tile: two keys per row, a padded (fully masked)
+    column among three, a sparse mask. (N = 1 is left out: a single key has
+    weight 1 whatever its score, so the query, key and pair-bias gradients
+    are exactly 0 only by cancellation, da * scale - D = 0; any float32
+    evaluation returns rounding-level values there, which a bar relative to
+    an exact 0 cannot take.)"""
+    Bn, N, D, h = shape
+    inp = make_inputs(Workload("bwd_tiny", Bn, N, D, h, dtype, mask, seed=90 + N))
+    check_backward(inp, 0.25, seed=31, offset=2, what=f"backward tiny {dtype} {shape} {mask}")
+
+
 def test_backward_minus_inf_fill():
     """-inf fill on a mask where every query column keeps a valid key."""
     inp = make_inputs(Workload("bwd_ninf", 1, 24, 64, 4, "f32", ("bernoulli", 0.7), seed=83))
