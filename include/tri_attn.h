@@ -95,7 +95,9 @@ typedef struct {
  * head_dim = pair_dim // num_heads, and the harness that builds the module
  * once and then calls its forward). Validates cfg, copies and packs the
  * weights into handle-owned device memory on the current device (the caller
- * may free its copies when this returns; the call synchronises `stream`).
+ * may free its copies when this returns; the call synchronises `stream`),
+ * and creates the handle's second stream (default priority, non-blocking)
+ * and two events for tri_attn_backward_train.
  * Supported: D in {64, 128} with d in {16, 32}; other shapes with D % h == 0
  * return TRI_ATTN_ERR_UNSUPPORTED (each supported shape is its own set of
  * kernel instantiations with a register and LDS budget of its own; d = 64 and
@@ -188,7 +190,11 @@ int tri_attn_backward_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
  * error).
  * Sums over positions are split into fixed chunks and added in a fixed order:
  * deterministic, no atomics. Asynchronous on `stream`; pointers borrowed until
- * the stream work completes. Ending-node handles: the starting-node backward
+ * the stream work completes. The dropout keep bits are made on the handle's
+ * own second stream, forked from `stream` by an event at the call's start
+ * and joined back by another before the attention steps read them, so the
+ * call stays ordered on `stream`.
+ * Ending-node handles: the starting-node backward
  * of the problem with both residue axes of pair_repr, pair_mask and dy
  * swapped, dL/d(pair_repr) swapped back (the ending-node training forward is
  * the starting-node one of that transposed problem, dropout counters

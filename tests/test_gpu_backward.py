@@ -211,6 +211,36 @@ def test_backward_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_backward_back_to_back_calls_on_one_workspace():
+    """The keep bits are made on the handle's second stream: calls issued back
+    to back on one stream and one workspace, with different seeds and no
+    synchronisation between them, must each give the bits of a call made on
+    its own (the fork orders a call's keep bits after the previous call's
+    attention steps, the join orders its attention steps after them)."""
+    inp = make_inputs(Workload("bwd_b2b", 1, 128, 128, 8, "bf16", ("pad", 100), seed=86))
+    dy = make_dy(inp, 6)
+    seeds = (9, 10, 9)
+    alone = {sd: run_backward(inp, dy, 0.3, sd, 0) for sd in set(seeds)}
+    g = Gpu(inp)
+    try:
+        n = B.tri_attn_backward_workspace_size(g.handle, g.B, g.N)
+        ws = torch.empty(n, dtype=torch.uint8, device=g.dev)
+        dyt = torch.from_numpy(dy).to(g.dev).to(g.dt).contiguous()
+        outs = []
+        for sd in seeds:
+            grads = {k: torch.zeros(np.shape(inp[v]), dtype=torch.float32, device=g.dev) for k, v in SHAPE.items()}
+            B.tri_attn_backward_train(g.handle, g.P, g.M, dyt, g.B, g.N, 0.3, sd, 0, grads, ws, n,
+                                      torch.cuda.current_stream())
+            outs.append(grads)
+        torch.cuda.synchronize()
+        for sd, grads in zip(seeds, outs):
+            for k in SHAPE:
+                assert np.array_equal(grads[k].double().cpu().numpy(), alone[sd][k]), (sd, k)
+        log("back-to-back backward calls on one workspace: bit-identical to separate calls")
+    finally:
+        g.close()
+
+
 def test_backward_argument_errors():
     inp = make_inputs(Workload("bwd_err", 1, 8, 64, 4, "f32", ("ones",), seed=85))
     g = Gpu(inp)

@@ -1181,6 +1181,51 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   do {                                   \
     if ((e = (x)) != hipSuccess) return e; \
   } while (0)
+  // whatever path this function leaves by, this stream ends up ordered after
+  // the second stream's work once the join event is recorded
+  struct JoinGuard {
+    hipStream_t s;
+    hipEvent_t ev;
+    bool armed;
+    ~JoinGuard() {
+      if (armed) (void)hipStreamWaitEvent(s, ev, 0);
+    }
+  } join{s, r.join, false};
+  BwdAttnArgs aa{};
+  aa.proj = proj, aa.zt = zt;
+  aa.m = reinterpret_cast<float *>(w + L.m), aa.l = reinterpret_cast<float *>(w + L.l);
+  aa.Dj = reinterpret_cast<float *>(w + L.Dj);
+  aa.dob = dob, aa.dcat = dcat;
+  aa.fill2 = r.fill * kLog2e, aa.scale = r.scale, aa.rsd = 1.0f / sqrtf((float)DH);
+  aa.qs = kLog2e * aa.rsd;
+  aa.thr = r.thr, aa.seed_lo = r.seed_lo, aa.seed_hi = r.seed_hi, aa.offset = r.offset;
+  aa.B = B, aa.N = N, aa.D = D, aa.h = h, aa.C = (int)C;
+  aa.NW = (N + 31) / 32;
+  uint32_t *bits = reinterpret_cast<uint32_t *>(w + L.bits);
+  aa.bits = bits;
+  {
+    // the keep bits need only the generator's key, counter offset and the
+    // sizes: on the handle's second stream they are made while the
+    // LayerNorm, the projection GEMM, the bias copy and the d(g*o) GEMM run
+    // on this one (latency-bound tiles that leave VALU issue slots free); the
+    // fork orders them after everything earlier on this stream (a previous
+    // call may still read the workspace), the join before the first
+    // attention step reads them
+    const long long nwords = (long long)B * N * h * N * aa.NW;
+    hipStream_t ks = s;
+    if (r.side) {
+      TPA_CHECK(hipEventRecord(r.fork, s));
+      TPA_CHECK(hipStreamWaitEvent(r.side, r.fork, 0));
+      ks = r.side;
+    }
+    hipLaunchKernelGGL(bwd_keep_bits, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, ks, aa, bits, nwords);
+    const hipError_t le = hipGetLastError();
+    if (r.side) {
+      TPA_CHECK(hipEventRecord(r.join, r.side));
+      join.armed = true;
+    }
+    TPA_CHECK(le);
+  }
   // ending-node: the starting-node backward of the transposed problem
   using E = typename std::conditional<sizeof(T) == 2, uint16_t, float>::type;
   const void *Pin = r.P, *dyin = r.dy;
@@ -1201,29 +1246,13 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   hipLaunchKernelGGL(bwd_ztrans, dim3((unsigned)(((long long)B * h * N * N + 255) / 256)), dim3(256), 0, s, proj,
                      Min, r.fill * kLog2e, B, N, D, h, (int)C, zt);
   TPA_CHECK(hipGetLastError());
-  BwdAttnArgs aa{};
-  aa.proj = proj, aa.zt = zt, aa.mask = Min;
-  aa.m = reinterpret_cast<float *>(w + L.m), aa.l = reinterpret_cast<float *>(w + L.l);
-  aa.Dj = reinterpret_cast<float *>(w + L.Dj);
-  aa.dob = dob, aa.dcat = dcat;
-  aa.fill2 = r.fill * kLog2e, aa.scale = r.scale, aa.rsd = 1.0f / sqrtf((float)DH);
-  aa.qs = kLog2e * aa.rsd;
-  aa.thr = r.thr, aa.seed_lo = r.seed_lo, aa.seed_hi = r.seed_hi, aa.offset = r.offset;
-  aa.B = B, aa.N = N, aa.D = D, aa.h = h, aa.C = (int)C;
-  aa.NW = (N + 31) / 32;
-  uint32_t *bits = reinterpret_cast<uint32_t *>(w + L.bits);
-  aa.bits = bits;
+  aa.mask = Min;
   {
     uint8_t *dead = reinterpret_cast<uint8_t *>(w + L.dead);
     const long long ncol = (long long)B * N;
     hipLaunchKernelGGL(bwd_dead_columns, dim3((unsigned)((ncol + 3) / 4)), dim3(256), 0, s, Min, ncol, N, dead);
     TPA_CHECK(hipGetLastError());
     aa.dead = dead;
-  }
-  {
-    const long long nwords = (long long)B * N * h * N * aa.NW;
-    hipLaunchKernelGGL(bwd_keep_bits, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s, aa, bits, nwords);
-    TPA_CHECK(hipGetLastError());
   }
   // work items (b, i, t, 128 columns): x only, so no grid limit applies
   const long long items = (long long)B * N * h * ((N + BwdTile<DH>::QB - 1) / BwdTile<DH>::QB);
@@ -1232,6 +1261,10 @@ static hipError_t run_bwd_t(const BwdRunArgs &r, hipStream_t s) {
   // d(g*o) = Wo^T dy, then the attention forward again with the output and
   // gate step, dq, dk/dv and the pair bias
   TPA_CHECK((gemm<T, T>(dyin, D, 1, Wo, D, 1, dgo, 0, D, P, D, D, D, 1, s)));
+  if (join.armed) {
+    TPA_CHECK(hipStreamWaitEvent(s, r.join, 0));
+    join.armed = false;
+  }
   hipLaunchKernelGGL((bwd_attn_fwd<T, DH>), ga, dim3(512), 0, s, aa, dgo, bg, go);
   TPA_CHECK(hipGetLastError());
   hipLaunchKernelGGL((bwd_attn_dq<DH>), ga, dim3(512), 0, s, aa);

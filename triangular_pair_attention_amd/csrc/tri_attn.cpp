@@ -28,6 +28,9 @@ struct tri_attn {
   size_t wpack_bytes, vecs_bytes, wfrag_bytes, wsplit_plane;
   void *scratch;   // this device's static workspace array (tri_attn_forward_noalloc)
   int scratch_rc;  // status of its address lookup at creation
+  // the backward's second stream (default priority) and its fork/join events
+  hipStream_t bwd_side;
+  hipEvent_t bwd_fork, bwd_join;
 };
 
 namespace tpa {
@@ -186,7 +189,14 @@ int tri_attn_create(const tri_attn_config *cfg, const tri_attn_weights *w, void 
                                         t->wsplit_plane, D / 16, s) == hipSuccess;
   }
   ok = ok && hipStreamSynchronize(s) == hipSuccess;
+  t->bwd_side = nullptr, t->bwd_fork = nullptr, t->bwd_join = nullptr;
+  ok = ok && hipStreamCreateWithFlags(&t->bwd_side, hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&t->bwd_fork, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&t->bwd_join, hipEventDisableTiming) == hipSuccess;
   if (!ok) {
+    if (t->bwd_side) (void)hipStreamDestroy(t->bwd_side);
+    if (t->bwd_fork) (void)hipEventDestroy(t->bwd_fork);
+    if (t->bwd_join) (void)hipEventDestroy(t->bwd_join);
     (void)hipGetLastError();
     (void)hipFree(t->wpack);
     (void)hipFree(t->vecs);
@@ -384,6 +394,7 @@ int tri_attn_backward_train(tri_attn_t t, const void *pair_repr, const uint8_t *
   r.B = B, r.N = N;
   r.transposed = t->cfg.ending_node;
   r.dz_ranges = t->bwd_dz_ranges;
+  r.side = t->bwd_side, r.fork = t->bwd_fork, r.join = t->bwd_join;
   if (launch_bwd(t->cfg.dtype, t->D, t->dh, r, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return TRI_ATTN_ERR_HIP;
   return TRI_ATTN_OK;
@@ -451,6 +462,9 @@ int tri_attn_destroy(tri_attn_t t) {
   if (hipFree(t->vecs) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
   if (hipFree(t->wfrag) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
   if (t->wsplit && hipFree(t->wsplit) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
+  if (hipStreamDestroy(t->bwd_side) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
+  if (hipEventDestroy(t->bwd_fork) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
+  if (hipEventDestroy(t->bwd_join) != hipSuccess) rc = TRI_ATTN_ERR_HIP;
   delete t;
   return rc;
 }

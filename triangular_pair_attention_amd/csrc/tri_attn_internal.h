@@ -107,6 +107,10 @@ struct BwdRunArgs {
   int B, N;
   int transposed;  // ending-node handle: the starting-node backward of the transposed problem
   int dz_ranges;   // row ranges of the pair-bias gradient step (0: chosen from the sizes)
+  // a second stream for the dropout keep bits, forked from and joined to the
+  // caller's stream by the two events (null: everything on the caller's stream)
+  hipStream_t side;
+  hipEvent_t fork, join;
 };
 hipError_t launch_bwd(int dtype, int D, int dh, const BwdRunArgs &r, hipStream_t s);
 size_t bwd_workspace_bytes(int B, int N, int D, int h, int elem_bytes, int transposed, int dz_ranges);
