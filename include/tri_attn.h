@@ -193,7 +193,8 @@ int tri_attn_backward_workspace_size(tri_attn_t h, int B, int N, size_t *bytes);
  * the stream work completes. The dropout keep bits are made on the handle's
  * own second stream, forked from `stream` by an event at the call's start
  * and joined back by another before the attention steps read them, so the
- * call stays ordered on `stream`.
+ * call stays ordered on `stream`; it enqueues kernels and events only and may
+ * be captured into a HIP graph from `stream`.
  * Ending-node handles: the starting-node backward
  * of the problem with both residue axes of pair_repr, pair_mask and dy
  * swapped, dL/d(pair_repr) swapped back (the ending-node training forward is

@@ -241,6 +241,47 @@ def test_backward_back_to_back_calls_on_one_workspace():
         g.close()
 
 
+def test_backward_captured_in_hip_graph():
+    """The backward enqueues kernels and events only (no memsets, no
+    allocation), its keep bits on the handle's second stream forked from and
+    joined to the capturing stream, so it can be captured in a HIP graph;
+    every replay, with eager backward calls of other seeds on the same
+    workspace between replays, must equal the eager backward bit for bit."""
+    inp = make_inputs(Workload("bwd_graph", 1, 64, 128, 4, "bf16", ("pad", 50), seed=87))
+    dy = make_dy(inp, 7)
+    eager = run_backward(inp, dy, 0.2, 21, 3)
+    g = Gpu(inp)
+    try:
+        n = B.tri_attn_backward_workspace_size(g.handle, g.B, g.N)
+        ws = torch.empty(n, dtype=torch.uint8, device=g.dev)
+        dyt = torch.from_numpy(dy).to(g.dev).to(g.dt).contiguous()
+        mk = lambda: {k: torch.zeros(np.shape(inp[v]), dtype=torch.float32, device=g.dev) for k, v in SHAPE.items()}
+        grads, other = mk(), mk()
+        call = lambda gr, sd, st: B.tri_attn_backward_train(g.handle, g.P, g.M, dyt, g.B, g.N, 0.2, sd, 3, gr, ws, n, st)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(grads, 21, side)  # warm-up on a side stream before capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call(grads, 21, torch.cuda.current_stream())
+        for r in range(3):
+            for v in grads.values():
+                v.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            for k in SHAPE:
+                assert np.array_equal(grads[k].double().cpu().numpy(), eager[k]), (r, k)
+            call(other, 22 + r, torch.cuda.current_stream())  # eager work between replays
+            torch.cuda.synchronize()
+        del graph
+        log("backward captured in a HIP graph: every replay equals the eager backward")
+    finally:
+        g.close()
+
+
 def test_backward_argument_errors():
     inp = make_inputs(Workload("bwd_err", 1, 8, 64, 4, "f32", ("ones",), seed=85))
     g = Gpu(inp)
